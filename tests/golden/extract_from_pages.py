@@ -1,0 +1,215 @@
+"""Write the worked examples printed on the operator pages as JSON fixtures.
+
+Reads the extracted page text at /root/reference/PAPER.md (available only in
+the build container) and writes, next to this script:
+
+  affine_grid_examples.json  -- the four worked examples of the AffineGrid page
+  grid_sample_examples.json  -- the eighteen worked examples of the
+                                "GridSample - version 20" page
+  resize_examples.json       -- the Resize (version 18) cubic and linear
+                                examples whose printed outputs are used as
+                                border-padded sampling cross-checks
+
+Only numbers the pages print are stored (inputs, attributes, printed outputs),
+each with the page title and example name it came from.  Nothing here computes
+an expected value.  Run:  python tests/golden/extract_from_pages.py
+"""
+
+from __future__ import annotations
+
+import json
+import os
+import re
+import sys
+
+PAGES = "/root/reference/PAPER.md"
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+NUM = re.compile(r"[-+]?(?:\d+\.?\d*|\.\d+)(?:[eE][-+]?\d+)?")
+
+
+def numbers(text: str):
+    return [float(t) for t in NUM.findall(text)]
+
+
+def prod(shape):
+    p = 1
+    for s in shape:
+        p *= s
+    return p
+
+
+def parse_shape(s: str):
+    return [int(v) for v in re.findall(r"\d+", s)]
+
+
+def page_text(lines, first_marker, last_marker):
+    start = next(i for i, l in enumerate(lines) if first_marker in l)
+    end = next(i for i, l in enumerate(lines) if i > start and last_marker in l)
+    return lines[start:end]
+
+
+def tensor_after(block: str, label: str):
+    """Shape and values of the tensor printed after 'label: shape=(...)'."""
+    m = re.search(re.escape(label) + r": shape=\(([^)]*)\), dtype=(\w+)", block)
+    if not m:
+        raise ValueError("no tensor %r" % label)
+    shape = parse_shape(m.group(1))
+    rest = block[m.end():]
+    # the values are the first bracketed block after the header
+    i = rest.index("[")
+    depth = 0
+    for j in range(i, len(rest)):
+        if rest[j] == "[":
+            depth += 1
+        elif rest[j] == "]":
+            depth -= 1
+            if depth == 0:
+                break
+    vals = numbers(rest[i:j + 1])
+    if len(vals) != prod(shape if shape else [1]):
+        raise ValueError("%s: %d values for shape %s" % (label, len(vals), shape))
+    return shape, m.group(2), vals
+
+
+def affine_grid_examples(lines):
+    text = page_text(lines, "page 1 of 5", "page 2 of 5")
+    names = [l.strip() for l in text if re.fullmatch(r"test_affine_grid_\w+", l.strip())]
+    joined = "\n".join(text)
+    out = []
+    for k, name in enumerate(names):
+        start = joined.index("\n" + name + "\n")
+        end = joined.index("\n" + names[k + 1] + "\n") if k + 1 < len(names) else len(joined)
+        block = joined[start:end]
+        ac = int(re.search(r"align_corners = (\d)", block).group(1))
+        th_shape, th_dtype, th = tensor_after(block, "theta")
+        sz_shape, _, sz = tensor_after(block, "size")
+        g_shape, g_dtype, g = tensor_after(block, "grid")
+        out.append({
+            "name": name,
+            "citation": "AffineGrid page (onnx-light, since version 20), Examples: " + name,
+            "align_corners": ac,
+            "theta_shape": th_shape, "theta": th,
+            "size": [int(v) for v in sz],
+            "grid_shape": g_shape, "grid_dtype": g_dtype, "grid": g,
+        })
+    return out
+
+
+def grid_sample_examples(lines):
+    text = page_text(lines, "page 3 of 5", "Differences with previous version")
+    joined = "\n".join(text)
+    heads = [(m.start(), m.group(1)) for m in re.finditer(r"\*\*(test_gridsample\w*)\*\*", joined)]
+    out = []
+    for k, (pos, name) in enumerate(heads):
+        end = heads[k + 1][0] if k + 1 < len(heads) else len(joined)
+        block = joined[pos:end]
+        attrs = block[:block.index("Inputs:")]
+        mode = re.search(r'mode = "(\w+)"', re.sub(r"padding_mode", "", attrs))
+        pad = re.search(r'padding_mode = "(\w+)"', attrs)
+        ac = re.search(r"align_corners = (\d)", attrs)
+        x_shape, x_dtype, x = tensor_after(block, "X")
+        g_shape, g_dtype, g = tensor_after(block, "Grid")
+        y_shape, y_dtype, y = tensor_after(block, "Y")
+        out.append({
+            "name": name,
+            "citation": "GridSample - version 20 page (onnx-light), Examples: " + name,
+            "mode": mode.group(1) if mode else None,
+            "padding_mode": pad.group(1) if pad else None,
+            "align_corners": int(ac.group(1)) if ac else None,
+            "X_shape": x_shape, "X_dtype": x_dtype, "X": x,
+            "grid_shape": g_shape, "grid_dtype": g_dtype, "grid": g,
+            "Y_shape": y_shape, "Y_dtype": y_dtype, "Y": y,
+        })
+    return out
+
+
+# Resize examples used as cross-checks: the cubic and linear ones with the
+# default cubic coefficient, exclude_outside=0 and no roi.
+RESIZE_NAMES = [
+    "test_resize_upsample_scales_cubic",
+    "test_resize_upsample_scales_cubic_align_corners",
+    "test_resize_downsample_scales_cubic",
+    "test_resize_downsample_scales_cubic_align_corners",
+    "test_resize_upsample_sizes_cubic",
+    "test_resize_downsample_sizes_cubic",
+    "test_resize_upsample_scales_cubic_asymmetric",
+    "test_resize_upsample_scales_linear",
+    "test_resize_upsample_scales_linear_align_corners",
+    "test_resize_downsample_scales_linear",
+    "test_resize_downsample_scales_linear_align_corners",
+]
+
+
+def bracket_block(s: str, i: int):
+    depth = 0
+    for j in range(i, len(s)):
+        if s[j] == "[":
+            depth += 1
+        elif s[j] == "]":
+            depth -= 1
+            if depth == 0:
+                return s[i:j + 1], j + 1
+    raise ValueError("unbalanced brackets")
+
+
+def resize_examples(lines):
+    # The Resize version 18 section is collapsed onto one very long line.
+    text = page_text(lines, "page 2 of 5", "page 3 of 5")
+    line = max(text, key=len)
+    out = []
+    for name in RESIZE_NAMES:
+        short = name[len("test"):]
+        head = line.index("**" + short + "**")
+        nxt = line.find("**_resize", head + 5)
+        block = line[head: nxt if nxt > 0 else len(line)]
+        if ('name="%s"' % name) not in block:
+            raise ValueError("example %s not delimited as expected" % name)
+        mode = re.search(r'mode="(\w+)"', block).group(1)
+        ctm = re.search(r'coordinate_transformation_mode="(\w+)"', block)
+        ctm = ctm.group(1) if ctm else "half_pixel"
+        d0 = block.index("data = np.array(") + len("data = np.array(")
+        data_txt, _ = bracket_block(block, block.index("[", d0))
+        data = numbers(data_txt)
+        depth = data_txt[:data_txt.index(next(c for c in data_txt if c.isdigit()))].count("[")
+        rows = re.findall(r"\[([^\[\]]+)\]", data_txt)
+        data_shape = [1] * (depth - 2) + [len(rows), len(numbers(rows[0]))]
+        scales = sizes = None
+        m = re.search(r"scales = np\.array\(\[([^\]]*)\]", block)
+        if m:
+            scales = numbers(m.group(1))
+        m = re.search(r"sizes = np\.array\(\[([^\]]*)\]", block)
+        if m:
+            sizes = [int(v) for v in numbers(m.group(1))]
+        # the printed expected output is the commented block before "output ="
+        c0 = block.index("# [[[[")
+        c1 = block.index("output =", c0)
+        expected = numbers(block[c0:c1].replace("#", " "))
+        out.append({
+            "name": name,
+            "citation": "Resize page (mlprodict, version 18), Examples: " + name,
+            "mode": mode,
+            "coordinate_transformation_mode": ctm,
+            "data_shape": data_shape, "data": data,
+            "scales": scales, "sizes": sizes,
+            "expected": expected,
+        })
+    return out
+
+
+def main():
+    if not os.path.exists(PAGES):
+        sys.exit("page text not found at " + PAGES)
+    with open(PAGES, encoding="utf-8") as f:
+        lines = f.read().split("\n")
+    for fname, items in (("affine_grid_examples.json", affine_grid_examples(lines)),
+                         ("grid_sample_examples.json", grid_sample_examples(lines)),
+                         ("resize_examples.json", resize_examples(lines))):
+        with open(os.path.join(HERE, fname), "w") as f:
+            json.dump(items, f, indent=0)
+            f.write("\n")
+        print("%s: %d examples" % (fname, len(items)))
+
+
+if __name__ == "__main__":
+    main()
