@@ -1,0 +1,201 @@
+// gs_api.cpp -- C ABI of libgsample: argument validation and kernel dispatch.
+//
+// Every check runs before any launch; a rejected call leaves all memory
+// untouched.  The library holds no state and allocates nothing.
+#include "gsample.h"
+#include "gs_launch.hpp"
+
+#include <stdint.h>
+
+namespace {
+
+constexpr int64_t kPlaneLimit = int64_t(1) << 28;   // elements per input/output plane
+constexpr int64_t kMaxBlocks = int64_t(1) << 24;    // thread blocks per launch
+constexpr int64_t kInt32Max = 0x7fffffff;
+constexpr int kBlockThreads = 256;
+
+int elem_bytes(int dtype) { return dtype == GS_F32 ? 4 : 2; }
+
+bool valid_x_dtype(int d) { return d == GS_F32 || d == GS_F16 || d == GS_BF16; }
+
+int check_attrs(int mode, int padding, int align_corners) {
+    if (mode < GS_MODE_LINEAR || mode > GS_MODE_CUBIC) return GS_ERR_ATTR;
+    if (padding < GS_PAD_ZEROS || padding > GS_PAD_REFLECTION) return GS_ERR_ATTR;
+    if (align_corners != 0 && align_corners != 1) return GS_ERR_ATTR;
+    return GS_OK;
+}
+
+// product of `n` non-negative extents; false if it exceeds `limit`
+bool product_within(const int64_t *e, int n, int64_t limit, int64_t *out) {
+    int64_t p = 1;
+    for (int i = 0; i < n; ++i) {
+        if (e[i] < 0) return false;
+        if (e[i] != 0 && p > limit / e[i]) return false;
+        p *= e[i];
+    }
+    *out = p;
+    return true;
+}
+
+struct Extents {
+    int d, h, w;
+};
+
+Extents spatial3(const int64_t *sp, int r) {
+    Extents e;
+    e.d = r == 3 ? (int)sp[0] : 1;
+    e.h = (int)sp[r - 2];
+    e.w = (int)sp[r - 1];
+    return e;
+}
+
+int hip_status(int rc) { return rc == 0 ? GS_OK : GS_ERR_HIP; }
+
+// Shared validation and launch of the sampler (fused or not).
+int sample(int r, const void *theta, const void *X, int x_dtype, const int64_t *x_shape,
+           const void *grid, const int64_t *out_sp, int mode, int padding, int align_corners,
+           void *Y, void *stream) {
+    for (int i = 0; i < r + 2; ++i)
+        if (x_shape[i] < 0) return GS_ERR_SHAPE;
+    for (int i = 0; i < r; ++i)
+        if (out_sp[i] < 0) return GS_ERR_SHAPE;
+    const int64_t N = x_shape[0], C = x_shape[1];
+    int64_t in_count = 0, out_count = 0;
+    if (N > kInt32Max || C > kInt32Max) return GS_ERR_TOO_LARGE;
+    if (!product_within(x_shape + 2, r, kPlaneLimit, &in_count)) return GS_ERR_TOO_LARGE;
+    if (!product_within(out_sp, r, kPlaneLimit, &out_count)) return GS_ERR_TOO_LARGE;
+    if (N == 0 || C == 0 || out_count == 0) return GS_OK;
+    if (in_count == 0) return GS_ERR_SHAPE;
+    if (!X || !Y || (!grid && !theta)) return GS_ERR_NULL;
+    const int64_t tiles = (out_count + kBlockThreads - 1) / kBlockThreads;
+    if (tiles > kMaxBlocks || N * tiles > kMaxBlocks) return GS_ERR_TOO_LARGE;
+
+    const int bytes = elem_bytes(x_dtype);
+    const Extents in = spatial3(x_shape + 2, r), out = spatial3(out_sp, r);
+    gs::SampleParams p;
+    p.X = X;
+    p.Y = Y;
+    p.grid = (const float *)grid;
+    p.theta = (const float *)theta;
+    p.N = (int)N;
+    p.C = (int)C;
+    p.in_d = in.d;
+    p.in_h = in.h;
+    p.in_w = in.w;
+    p.out_d = out.d;
+    p.out_h = out.h;
+    p.out_w = out.w;
+    p.out_count = (uint32_t)out_count;
+    p.in_plane_bytes = (uint32_t)(in_count * bytes);
+    p.out_plane_bytes = (uint32_t)(out_count * bytes);
+    p.align_corners = align_corners;
+    p.tiles_per_n = (int)tiles;
+    p.nblocks = (int)(N * tiles);
+    gs::FastDivHost dw = gs::make_fastdiv((uint32_t)out.w), dh = gs::make_fastdiv((uint32_t)out.h);
+    p.div_w_m = dw.m;
+    p.div_w_s = dw.s;
+    p.div_h_m = dh.m;
+    p.div_h_s = dh.s;
+    return hip_status(gs::launch_grid_sample(p, r, theta != nullptr, mode, padding, x_dtype,
+                                             (hipStream_t)stream));
+}
+
+int grid_sample_rank(int r, const void *X, int x_dtype, const int64_t *x_shape, const void *grid,
+                     int grid_dtype, const int64_t *grid_shape, int mode, int padding,
+                     int align_corners, void *Y, void *stream) {
+    if (!x_shape || !grid_shape) return GS_ERR_NULL;
+    if (!valid_x_dtype(x_dtype) || grid_dtype != GS_F32) return GS_ERR_DTYPE;
+    int rc = check_attrs(mode, padding, align_corners);
+    if (rc) return rc;
+    for (int i = 0; i < r + 2; ++i)
+        if (grid_shape[i] < 0) return GS_ERR_SHAPE;
+    if (grid_shape[0] != x_shape[0] || grid_shape[r + 1] != r) return GS_ERR_SHAPE;
+    return sample(r, nullptr, X, x_dtype, x_shape, grid, grid_shape + 1, mode, padding,
+                  align_corners, Y, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int gs_abi_version(void) { return GS_ABI_VERSION; }
+
+const char *gs_status_string(int status) {
+    switch (status) {
+    case GS_OK: return "ok";
+    case GS_ERR_NULL: return "a required pointer is NULL";
+    case GS_ERR_SHAPE: return "inconsistent or negative shape";
+    case GS_ERR_DTYPE: return "unsupported element type";
+    case GS_ERR_ATTR: return "mode, padding or align_corners out of range";
+    case GS_ERR_TOO_LARGE: return "tensor too large for the kernels' indexing";
+    case GS_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+    }
+}
+
+int gs_affine_grid(const void *theta, int theta_dtype, const int64_t *size, int size_len,
+                   int align_corners, void *grid, void *stream) {
+    if (!size) return GS_ERR_NULL;
+    if (size_len != 4 && size_len != 5) return GS_ERR_SHAPE;
+    if (theta_dtype != GS_F32) return GS_ERR_DTYPE;
+    if (align_corners != 0 && align_corners != 1) return GS_ERR_ATTR;
+    for (int i = 0; i < size_len; ++i)
+        if (size[i] < 0) return GS_ERR_SHAPE;
+    const int r = size_len - 2;
+    const int64_t N = size[0];
+    int64_t count = 0;
+    if (N > kInt32Max) return GS_ERR_TOO_LARGE;
+    if (!product_within(size + 2, r, kInt32Max, &count)) return GS_ERR_TOO_LARGE;
+    if (N == 0 || count == 0) return GS_OK;
+    if (!theta || !grid) return GS_ERR_NULL;
+    const int64_t tiles = (count + kBlockThreads - 1) / kBlockThreads;
+    if (tiles > kMaxBlocks || N * tiles > kMaxBlocks) return GS_ERR_TOO_LARGE;
+    const Extents out = spatial3(size + 2, r);
+    gs::AffineParams p;
+    p.theta = (const float *)theta;
+    p.grid = (float *)grid;
+    p.N = (int)N;
+    p.out_d = out.d;
+    p.out_h = out.h;
+    p.out_w = out.w;
+    p.out_count = (uint32_t)count;
+    p.align_corners = align_corners;
+    p.tiles_per_n = (int)tiles;
+    p.nblocks = (int)(N * tiles);
+    gs::FastDivHost dw = gs::make_fastdiv((uint32_t)out.w), dh = gs::make_fastdiv((uint32_t)out.h);
+    p.div_w_m = dw.m;
+    p.div_w_s = dw.s;
+    p.div_h_m = dh.m;
+    p.div_h_s = dh.s;
+    return hip_status(gs::launch_affine_grid(p, r, (hipStream_t)stream));
+}
+
+int gs_grid_sample_2d(const void *X, int x_dtype, const int64_t *x_shape, const void *grid,
+                      int grid_dtype, const int64_t *grid_shape, int mode, int padding,
+                      int align_corners, void *Y, void *stream) {
+    return grid_sample_rank(2, X, x_dtype, x_shape, grid, grid_dtype, grid_shape, mode, padding,
+                            align_corners, Y, stream);
+}
+
+int gs_grid_sample_3d(const void *X, int x_dtype, const int64_t *x_shape, const void *grid,
+                      int grid_dtype, const int64_t *grid_shape, int mode, int padding,
+                      int align_corners, void *Y, void *stream) {
+    return grid_sample_rank(3, X, x_dtype, x_shape, grid, grid_dtype, grid_shape, mode, padding,
+                            align_corners, Y, stream);
+}
+
+int gs_affine_grid_sample_fused(const void *theta, int theta_dtype, const void *X, int x_dtype,
+                                const int64_t *x_shape, int x_rank, const int64_t *out_spatial,
+                                int mode, int padding, int align_corners, void *Y, void *stream) {
+    if (!x_shape || !out_spatial) return GS_ERR_NULL;
+    if (x_rank != 4 && x_rank != 5) return GS_ERR_SHAPE;
+    if (theta_dtype != GS_F32 || !valid_x_dtype(x_dtype)) return GS_ERR_DTYPE;
+    int rc = check_attrs(mode, padding, align_corners);
+    if (rc) return rc;
+    const int r = x_rank - 2;
+    // a NULL theta with work to do is reported by sample() as GS_ERR_NULL
+    return sample(r, theta, X, x_dtype, x_shape, nullptr, out_spatial, mode, padding,
+                  align_corners, Y, stream);
+}
+
+}  // extern "C"

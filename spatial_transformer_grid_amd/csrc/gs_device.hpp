@@ -1,0 +1,199 @@
+// gs_device.hpp -- device-side building blocks of libgsample (gfx950).
+//
+// Coordinates: every helper that decides a pixel index (base positions of the
+// grid generator, un-normalisation, padding of a location) is written as a
+// sequence of individually rounded fp32 operations.  The library is compiled
+// with -ffp-contract=off so none of them is fused into an FMA; interpolation
+// uses explicit fmaf where it wants one.
+//
+// Memory: X and Y are addressed through raw buffer resources, one per
+// (image, channel) plane, with num_records = plane bytes.  A tap whose
+// location is outside the image gets the offset GS_OOB (>= any plane size),
+// which the buffer unit turns into a read of 0 (zeros padding) or a dropped
+// store, without touching memory.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gs {
+
+enum : int { MODE_LINEAR = 0, MODE_NEAREST = 1, MODE_CUBIC = 2 };
+enum : int { PAD_ZEROS = 0, PAD_BORDER = 1, PAD_REFLECTION = 2 };
+
+constexpr int kBlock = 256;              // threads per block: 4 wave64s
+constexpr uint32_t GS_OOB = 0x80000000u; // buffer offset that is always out of range
+constexpr float kCoordLimit = 16777216.0f;  // |p| clamp before float->int (2^24)
+constexpr float kCubicA = -0.75f;        // cubic convolution coefficient
+
+// Word 3 of a gfx9-family buffer resource: 32-bit data format, no swizzle.
+constexpr int kRsrcWord3 = 0x00020000;
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             kRsrcWord3);
+}
+
+// ------------------------------------------------------------------ types
+
+struct F32 {
+    static constexpr int bytes = 4;
+    typedef uint32_t raw_t;
+    __device__ __forceinline__ static float load(rsrc_t r, uint32_t off) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+    }
+    __device__ __forceinline__ static uint32_t load_raw(rsrc_t r, uint32_t off) {
+        return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+    }
+    __device__ __forceinline__ static void store(float v, rsrc_t r, uint32_t off) {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, 0);
+    }
+    __device__ __forceinline__ static void store_raw(uint32_t v, rsrc_t r, uint32_t off) {
+        __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
+    }
+};
+
+struct Half16Base {
+    static constexpr int bytes = 2;
+    typedef uint16_t raw_t;
+    __device__ __forceinline__ static uint16_t load_raw(rsrc_t r, uint32_t off) {
+        return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+    }
+    __device__ __forceinline__ static void store_raw(uint16_t v, rsrc_t r, uint32_t off) {
+        __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, 0, 0);
+    }
+};
+
+struct F16 : Half16Base {
+    __device__ __forceinline__ static float load(rsrc_t r, uint32_t off) {
+        return (float)__builtin_bit_cast(_Float16, load_raw(r, off));
+    }
+    // round to nearest even (v_cvt_f16_f32)
+    __device__ __forceinline__ static void store(float v, rsrc_t r, uint32_t off) {
+        store_raw(__builtin_bit_cast(uint16_t, (_Float16)v), r, off);
+    }
+};
+
+struct BF16 : Half16Base {
+    __device__ __forceinline__ static float load(rsrc_t r, uint32_t off) {
+        return __builtin_bit_cast(float, (uint32_t)load_raw(r, off) << 16);
+    }
+    // round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+    __device__ __forceinline__ static void store(float v, rsrc_t r, uint32_t off) {
+        store_raw(__builtin_bit_cast(uint16_t, (__bf16)v), r, off);
+    }
+};
+
+// ------------------------------------------------------- integer division
+
+// Division of non-negative 31-bit integers by a divisor fixed at launch
+// (Granlund & Montgomery): q = (umulhi(n, m) + n) >> s.
+struct FastDiv {
+    uint32_t d, m, s;
+};
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+    return (__umulhi(n, f.m) + n) >> f.s;
+}
+
+// ------------------------------------------------------------ coordinates
+
+// Position of sample i of m evenly spaced samples over [-1, 1]
+// (AffineGrid page, Summary; align_corners as described there).
+__device__ __forceinline__ float base_position(int i, int m, int align_corners) {
+    if (align_corners) {
+        if (m == 1) return 0.0f;
+        return (float)(2 * i) / (float)(m - 1) - 1.0f;
+    }
+    return (float)(2 * i + 1) / (float)m - 1.0f;
+}
+
+// Normalised location -> pixel coordinate along an axis of n pixels
+// (GridSample page, Attributes: align_corners).  (g+1)/2 is computed as
+// (g+1)*0.5, which rounds identically.
+__device__ __forceinline__ float unnormalize(float g, int n, int align_corners) {
+    if (align_corners) {
+        float u = (g + 1.0f) * 0.5f;
+        return u * (float)(n - 1);
+    }
+    float v = (g + 1.0f) * (float)n;
+    return (v - 1.0f) * 0.5f;
+}
+
+__device__ __forceinline__ float clampf(float v, float lo, float hi) {
+    return v < lo ? lo : (v > hi ? hi : v);
+}
+
+// Fold p into [lo, hi] by repeated reflection (GridSample page, padding_mode).
+__device__ __forceinline__ float reflect(float p, float lo, float hi) {
+    float span = hi - lo;
+    if (span <= 0.0f) return 0.0f;
+    float d = fabsf(p - lo);
+    float f = floorf(d / span);
+    float fs = f * span;
+    float e = d - fs;
+    float half = floorf(f * 0.5f);
+    bool odd = (f - 2.0f * half) != 0.0f;
+    return odd ? hi - e : lo + e;
+}
+
+__device__ __forceinline__ void reflect_bounds(int n, int align_corners, float &lo, float &hi) {
+    if (align_corners) {
+        lo = 0.0f;
+        hi = (float)(n - 1);
+    } else {
+        lo = -0.5f;
+        hi = (float)n - 0.5f;
+    }
+}
+
+// Location padding of nearest and linear modes.
+template <int PAD>
+__device__ __forceinline__ float pad_coordinate(float p, int n, int align_corners) {
+    if (PAD == PAD_BORDER) return clampf(p, 0.0f, (float)(n - 1));
+    if (PAD == PAD_REFLECTION) {
+        float lo, hi;
+        reflect_bounds(n, align_corners, lo, hi);
+        return clampf(reflect(p, lo, hi), 0.0f, (float)(n - 1));
+    }
+    return p;
+}
+
+// Keys' cubic convolution kernel for the four taps of fractional offset t:
+// w[0..3] weight pixels floor(p) - 1 .. floor(p) + 2.
+__device__ __forceinline__ void cubic_weights(float t, float w[4]) {
+    const float a = kCubicA;
+    float x0 = t + 1.0f;   // in [1, 2)
+    float x1 = t;          // in [0, 1)
+    float x2 = 1.0f - t;   // in (0, 1]
+    float x3 = 2.0f - t;   // in (1, 2]
+    w[0] = fmaf(fmaf(fmaf(a, x0, -5.0f * a), x0, 8.0f * a), x0, -4.0f * a);
+    w[1] = fmaf(fmaf(a + 2.0f, x1, -(a + 3.0f)), x1 * x1, 1.0f);
+    w[2] = fmaf(fmaf(a + 2.0f, x2, -(a + 3.0f)), x2 * x2, 1.0f);
+    w[3] = fmaf(fmaf(fmaf(a, x3, -5.0f * a), x3, 8.0f * a), x3, -4.0f * a);
+}
+
+// Tap index of cubic mode after per-tap padding (border / reflection).
+template <int PAD>
+__device__ __forceinline__ int pad_tap(int i, int n, int align_corners) {
+    if (PAD == PAD_BORDER) return i < 0 ? 0 : (i > n - 1 ? n - 1 : i);
+    float lo, hi;
+    reflect_bounds(n, align_corners, lo, hi);
+    return (int)clampf(reflect((float)i, lo, hi), 0.0f, (float)(n - 1));
+}
+
+// ----------------------------------------------------------- block order
+
+// Workgroups are handed to the 8 XCDs round-robin by launch index.  Remap so
+// that each XCD receives one contiguous run of logical tiles: neighbouring
+// tiles then share their halo rows in that XCD's L2.  The launch holds
+// 8 * ceil(n / 8) blocks; the surplus ones exit.
+__device__ __forceinline__ int xcd_logical_block(int nblocks) {
+    int per = (nblocks + 7) >> 3;
+    int b = blockIdx.x;
+    return (b & 7) * per + (b >> 3);
+}
+
+}  // namespace gs

@@ -1,0 +1,146 @@
+"""The C-ABI library loads, exports what include/gsample.h declares, and
+rejects bad arguments before any launch (no GPU is touched by these tests:
+every call here fails validation or has nothing to do)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "gsample.h")
+
+
+@pytest.fixture(scope="module")
+def gs():
+    from spatial_transformer_grid_amd import _binding
+
+    if not os.path.exists(_binding.LIB_PATH):
+        from spatial_transformer_grid_amd import build
+
+        build.build()
+    return _binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(gs_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_functions() == sorted([
+        "gs_abi_version", "gs_status_string", "gs_affine_grid", "gs_grid_sample_2d",
+        "gs_grid_sample_3d", "gs_affine_grid_sample_fused"])
+
+
+def test_library_exports_every_declared_symbol(gs):
+    handle = ctypes.CDLL(gs.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(handle, name), name
+    assert set(declared_functions()) == set(gs.SIGNATURES)
+
+
+def test_abi_version_and_status_strings(gs):
+    lib = gs.lib()
+    assert lib.gs_abi_version() == 1
+    for code in range(7):
+        s = lib.gs_status_string(code).decode()
+        assert s and s != "unknown status"
+    assert lib.gs_status_string(99).decode() == "unknown status"
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
+
+
+def sample2d(gs, **kw):
+    a = dict(X=FAKE, x_dtype=gs.GS_F32, x_shape=[2, 3, 4, 5], grid=FAKE, grid_dtype=gs.GS_F32,
+             grid_shape=[2, 6, 7, 2], mode=0, padding=0, ac=0, Y=FAKE)
+    a.update(kw)
+    return gs.lib().gs_grid_sample_2d(a["X"], a["x_dtype"], gs.int64_array(a["x_shape"]), a["grid"],
+                                      a["grid_dtype"], gs.int64_array(a["grid_shape"]), a["mode"],
+                                      a["padding"], a["ac"], a["Y"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x_dtype=7), 3),
+    (dict(grid_dtype=1), 3),
+    (dict(mode=3), 4),
+    (dict(mode=-1), 4),
+    (dict(padding=3), 4),
+    (dict(ac=2), 4),
+    (dict(grid_shape=[3, 6, 7, 2]), 2),          # batch mismatch
+    (dict(grid_shape=[2, 6, 7, 3]), 2),          # last grid dim must be 2
+    (dict(x_shape=[2, -3, 4, 5]), 2),
+    (dict(grid_shape=[2, 6, -7, 2]), 2),
+    (dict(x_shape=[2, 3, 0, 5]), 2),             # empty image, non-empty output
+    (dict(X=None), 1),
+    (dict(Y=None), 1),
+    (dict(grid=None), 1),
+    (dict(x_shape=[2, 3, 1 << 15, 1 << 14]), 5),  # input plane above 2^28
+    (dict(grid_shape=[2, 1 << 15, 1 << 14, 2]), 5),
+])
+def test_grid_sample_2d_rejects(gs, kw, status):
+    assert sample2d(gs, **kw) == status
+
+
+@pytest.mark.parametrize("kw", [
+    dict(x_shape=[0, 3, 4, 5], grid_shape=[0, 6, 7, 2]),
+    dict(x_shape=[2, 0, 4, 5]),
+    dict(grid_shape=[2, 0, 7, 2]),
+    dict(grid_shape=[2, 6, 0, 2], X=None, Y=None, grid=None),
+])
+def test_empty_work_returns_ok_without_launch(gs, kw):
+    assert sample2d(gs, **kw) == 0
+
+
+def test_grid_sample_3d_shape_rules(gs):
+    lib = gs.lib()
+    f = lambda xs, gsh, **k: lib.gs_grid_sample_3d(
+        FAKE, 0, gs.int64_array(xs), FAKE, 0, gs.int64_array(gsh), k.get("mode", 0), 0, 0, FAKE, None)
+    assert f([1, 2, 3, 4, 5], [1, 2, 3, 4, 2]) == 2
+    assert f([1, 2, 3, 4, 5], [2, 2, 3, 4, 3]) == 2
+    assert f([1, 2, 3, 4, 5], [1, 2, 3, 4, 3], mode=5) == 4
+    assert f([1, 2, 3, 4, 5], [1, 0, 3, 4, 3]) == 0
+
+
+def test_affine_grid_rejects(gs):
+    lib = gs.lib()
+    f = lambda size, n=None, dt=0, ac=0, theta=FAKE, grid=FAKE: lib.gs_affine_grid(
+        theta, dt, gs.int64_array(size), len(size) if n is None else n, ac, grid, None)
+    assert f([2, 3, 4, 5], n=3) == 2
+    assert f([2, 3, 4, 5], dt=1) == 3
+    assert f([2, 3, 4, 5], ac=-1) == 4
+    assert f([2, 3, -4, 5]) == 2
+    assert f([2, 3, 4, 5], theta=None) == 1
+    assert f([2, 3, 4, 5], grid=None) == 1
+    assert f([0, 3, 4, 5], theta=None, grid=None) == 0
+    assert f([2, 3, 1 << 16, 1 << 16]) == 5
+    assert lib.gs_affine_grid(FAKE, 0, None, 4, 0, FAKE, None) == 1
+
+
+def test_fused_rejects(gs):
+    lib = gs.lib()
+
+    def f(xs, out, rank=None, theta=FAKE, dt=0, xdt=0, mode=0):
+        return lib.gs_affine_grid_sample_fused(theta, dt, FAKE, xdt, gs.int64_array(xs),
+                                               len(xs) if rank is None else rank,
+                                               gs.int64_array(out), mode, 0, 0, FAKE, None)
+
+    assert f([1, 2, 3, 4], [5, 6], rank=3) == 2
+    assert f([1, 2, 3, 4], [5, 6], dt=2) == 3
+    assert f([1, 2, 3, 4], [5, 6], xdt=9) == 3
+    assert f([1, 2, 3, 4], [5, 6], mode=9) == 4
+    assert f([1, 2, 3, 4], [5, 6], theta=None) == 1
+    assert f([1, 2, 3, 4], [0, 6], theta=None) == 0
+    assert f([1, 2, 3, 4], [5, -6]) == 2
+
+
+def test_binding_refuses_host_tensors(gs):
+    torch = pytest.importorskip("torch")
+    from spatial_transformer_grid_amd import grid_sample
+
+    with pytest.raises(ValueError):
+        grid_sample(torch.zeros(1, 1, 2, 2), torch.zeros(1, 2, 2, 2))

@@ -1,0 +1,121 @@
+"""The five synthetic workloads on the GPU against the oracle.
+
+* reduced shapes (same distributions, several tiles, ragged tails): every
+  output element is compared;
+* full shapes, in exactly the launches the benchmark times: a random sample of
+  output elements plus the first and last elements of every image is computed
+  one by one by the oracle and compared.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from parity import check, from_gpu, note, to_gpu_f32, torch_mod, x_to_gpu
+
+pytestmark = pytest.mark.gpu
+
+REDUCED = {
+    "stn2d_tiny": ((2, 3, 16, 16), (5, 6)),
+    "stn2d_batch": ((3, 10, 37, 45), (39, 41)),
+    "flow2d_bicubic": ((2, 9, 40, 44), (35, 37)),
+    "vol3d": ((2, 5, 13, 14, 15), (11, 12, 13)),
+    "flow2d_half": ((2, 12, 40, 48), (33, 35)),
+}
+
+
+@pytest.fixture(scope="module")
+def gsa():
+    torch = torch_mod()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import spatial_transformer_grid_amd as gsa
+
+    gsa.lib()
+    return gsa
+
+
+def mode_list(w):
+    return [(w.mode, w.padding)] + list(w.extra_modes)
+
+
+def run_gpu(gsa, w, inp, kind, mode, pad, ac, fused):
+    """The same calls the benchmark makes: theta -> grid -> sample, or fused."""
+    Xd, Xin = x_to_gpu(inp["X"], kind)
+    n, c = inp["x_shape"][:2]
+    if inp["theta"] is not None:
+        td = to_gpu_f32(inp["theta"])
+        if fused:
+            Y = gsa.affine_grid_sample_fused(td, Xd, inp["out_spatial"], mode, pad, ac)
+        else:
+            grid = gsa.affine_grid(td, (n, c) + tuple(inp["out_spatial"]), ac)
+            Y = gsa.grid_sample(Xd, grid, mode, pad, ac)
+    else:
+        Y = gsa.grid_sample(Xd, to_gpu_f32(inp["grid"]), mode, pad, ac)
+    return Y, Xin
+
+
+def oracle_grid(inp, ac):
+    if inp["theta"] is not None:
+        n, c = inp["x_shape"][:2]
+        return oracle.affine_grid(inp["theta"], (n, c) + tuple(inp["out_spatial"]), ac)
+    return inp["grid"]
+
+
+def cases(reduced: bool):
+    out = []
+    for name, w in W.WORKLOADS.items():
+        for kind in w.dtypes:
+            for mode, pad in mode_list(w):
+                acs = (0, 1) if name == "stn2d_tiny" else (w.align_corners,)
+                for ac in acs:
+                    fused_opts = (False, True) if w.grid_kind.startswith("affine") else (False,)
+                    for fused in fused_opts:
+                        out.append(pytest.param(name, kind, mode, pad, ac, fused,
+                                                id="%s-%s-%s-%s-ac%d%s" % (
+                                                    name, kind, mode, pad, ac,
+                                                    "-fused" if fused else "")))
+    return out
+
+
+@pytest.mark.parametrize("name,kind,mode,pad,ac,fused", cases(True))
+def test_workload_reduced_all_elements(gsa, name, kind, mode, pad, ac, fused):
+    w = W.WORKLOADS[name]
+    x_shape, out_sp = REDUCED[name]
+    note("reduced %s %s %s/%s ac=%d fused=%s x=%s out=%s" % (name, kind, mode, pad, ac, fused,
+                                                             x_shape, out_sp))
+    inp = W.make_inputs(w, x_shape, out_sp)
+    Y, Xin = run_gpu(gsa, w, inp, kind, mode, pad, ac, fused)
+    ref = oracle.grid_sample(Xin, oracle_grid(inp, ac), mode, pad, ac)
+    check(from_gpu(Y), ref, mode, kind, np.abs(Xin).max(), name)
+
+
+def sample_indices(n, c, count, k, seed):
+    rng = np.random.default_rng(seed)
+    total = n * c * count
+    idx = [rng.integers(0, total, size=k)]
+    for b in range(n):
+        for ch in (0, c - 1):
+            base = (b * c + ch) * count
+            idx.append(base + np.arange(min(count, 64)))
+            idx.append(base + count - 1 - np.arange(min(count, 64)))
+    return np.unique(np.concatenate(idx))
+
+
+@pytest.mark.parametrize("name,kind,mode,pad,ac,fused",
+                         [p for p in cases(False) if "tiny" not in p.id])
+def test_workload_full_size_sampled(gsa, name, kind, mode, pad, ac, fused):
+    w = W.WORKLOADS[name]
+    note("full %s %s %s/%s ac=%d fused=%s x=%s" % (name, kind, mode, pad, ac, fused, w.x_shape))
+    inp = W.make_inputs(w)
+    Y, Xin = run_gpu(gsa, w, inp, kind, mode, pad, ac, fused)
+    n, c = w.x_shape[:2]
+    count = int(np.prod(w.out_spatial))
+    idx = sample_indices(n, c, count, 16384, w.seed)
+    torch = torch_mod()
+    got = Y.reshape(-1)[torch.from_numpy(idx).cuda()]
+    got = from_gpu(got)
+    del Y
+    ref = oracle.grid_sample_points(Xin, oracle_grid(inp, ac), idx, mode, pad, ac)
+    check(got, ref, mode, kind, np.abs(Xin).max(), "full " + name)
