@@ -67,11 +67,16 @@ int sample(int r, const void *theta, const void *X, int x_dtype, const int64_t *
     if (N == 0 || C == 0 || out_count == 0) return GS_OK;
     if (in_count == 0) return GS_ERR_SHAPE;
     if (!X || !Y || (!grid && !theta)) return GS_ERR_NULL;
-    const int64_t tiles = (out_count + kBlockThreads - 1) / kBlockThreads;
+    const Extents in = spatial3(x_shape + 2, r), out = spatial3(out_sp, r);
+    const int tw = r == 2 ? gs::TileShape<2>::w : gs::TileShape<3>::w;
+    const int th = r == 2 ? gs::TileShape<2>::h : gs::TileShape<3>::h;
+    const int td = r == 2 ? gs::TileShape<2>::d : gs::TileShape<3>::d;
+    const int64_t tiles_w = (out.w + tw - 1) / tw, tiles_h = (out.h + th - 1) / th,
+                  tiles_d = (out.d + td - 1) / td;
+    const int64_t tiles = tiles_w * tiles_h * tiles_d;
     if (tiles > kMaxBlocks || N * tiles > kMaxBlocks) return GS_ERR_TOO_LARGE;
 
     const int bytes = elem_bytes(x_dtype);
-    const Extents in = spatial3(x_shape + 2, r), out = spatial3(out_sp, r);
     gs::SampleParams p;
     p.X = X;
     p.Y = Y;
@@ -89,13 +94,11 @@ int sample(int r, const void *theta, const void *X, int x_dtype, const int64_t *
     p.in_plane_bytes = (uint32_t)(in_count * bytes);
     p.out_plane_bytes = (uint32_t)(out_count * bytes);
     p.align_corners = align_corners;
+    p.tiles_w = (int)tiles_w;
+    p.tiles_h = (int)tiles_h;
+    p.tiles_d = (int)tiles_d;
     p.tiles_per_n = (int)tiles;
     p.nblocks = (int)(N * tiles);
-    gs::FastDivHost dw = gs::make_fastdiv((uint32_t)out.w), dh = gs::make_fastdiv((uint32_t)out.h);
-    p.div_w_m = dw.m;
-    p.div_w_s = dw.s;
-    p.div_h_m = dh.m;
-    p.div_h_s = dh.s;
     return hip_status(gs::launch_grid_sample(p, r, theta != nullptr, mode, padding, x_dtype,
                                              (hipStream_t)stream));
 }

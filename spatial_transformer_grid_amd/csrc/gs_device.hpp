@@ -53,6 +53,9 @@ struct F32 {
     __device__ __forceinline__ static void store_raw(uint32_t v, rsrc_t r, uint32_t off) {
         __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
     }
+    __device__ __forceinline__ static float from_raw(uint32_t v) {
+        return __builtin_bit_cast(float, v);
+    }
 };
 
 struct Half16Base {
@@ -67,8 +70,11 @@ struct Half16Base {
 };
 
 struct F16 : Half16Base {
+    __device__ __forceinline__ static float from_raw(uint16_t v) {
+        return (float)__builtin_bit_cast(_Float16, v);
+    }
     __device__ __forceinline__ static float load(rsrc_t r, uint32_t off) {
-        return (float)__builtin_bit_cast(_Float16, load_raw(r, off));
+        return from_raw(load_raw(r, off));
     }
     // round to nearest even (v_cvt_f16_f32)
     __device__ __forceinline__ static void store(float v, rsrc_t r, uint32_t off) {
@@ -77,8 +83,11 @@ struct F16 : Half16Base {
 };
 
 struct BF16 : Half16Base {
+    __device__ __forceinline__ static float from_raw(uint16_t v) {
+        return __builtin_bit_cast(float, (uint32_t)v << 16);
+    }
     __device__ __forceinline__ static float load(rsrc_t r, uint32_t off) {
-        return __builtin_bit_cast(float, (uint32_t)load_raw(r, off) << 16);
+        return from_raw(load_raw(r, off));
     }
     // round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
     __device__ __forceinline__ static void store(float v, rsrc_t r, uint32_t off) {

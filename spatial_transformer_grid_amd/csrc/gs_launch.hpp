@@ -32,10 +32,21 @@ struct SampleParams {
     uint32_t in_plane_bytes;   // in_d * in_h * in_w * sizeof(T)   (<= 2^30)
     uint32_t out_plane_bytes;  // out_count * sizeof(T)            (<= 2^30)
     int align_corners;
-    int tiles_per_n;           // ceil(out_count / kBlock)
+    int tiles_w, tiles_h, tiles_d;  // output tiles per image along W, H, D
+    int tiles_per_n;           // tiles_w * tiles_h * tiles_d
     int nblocks;               // N * tiles_per_n
-    uint32_t div_w_m, div_w_s; // fast division by out_w
-    uint32_t div_h_m, div_h_s; // fast division by out_h
+};
+
+// Output tile of one 256-thread block: 16 x 16 (2D) or 8 x 8 x 4 (3D).
+template <int R>
+struct TileShape;
+template <>
+struct TileShape<2> {
+    static constexpr int w = 16, h = 16, d = 1;
+};
+template <>
+struct TileShape<3> {
+    static constexpr int w = 8, h = 8, d = 4;
 };
 
 struct AffineParams {

@@ -104,6 +104,28 @@ def test_grid_sample_matches_oracle(gsa, rank, mode, pad, ac, kind):
           "%dD %s/%s/%d/%s" % (rank, mode, pad, ac, kind))
 
 
+@pytest.mark.parametrize("kind", KINDS)
+@pytest.mark.parametrize("ac", [0, 1])
+@pytest.mark.parametrize("pad", PADS)
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("rank", [2, 3])
+def test_grid_sample_direct_gather_path(gsa, rank, mode, pad, ac, kind):
+    """Random locations over an image larger than any LDS staging box: every
+    block takes the direct-gather loop."""
+    note("direct path %dD %s/%s ac=%d %s" % (rank, mode, pad, ac, kind))
+    rng = np.random.default_rng(3000 + 1000 * rank + 17 * ac + 3 * MODES.index(mode) + PADS.index(pad))
+    if rank == 2:
+        X = rng.uniform(-1, 1, (2, 11, 70, 90)).astype(np.float32)
+        G = rng.uniform(-1.3, 1.3, (2, 19, 23, 2)).astype(np.float32)
+    else:
+        X = rng.uniform(-1, 1, (2, 5, 20, 24, 28)).astype(np.float32)
+        G = rng.uniform(-1.3, 1.3, (2, 5, 6, 11, 3)).astype(np.float32)
+    Xd, Xin = x_to_gpu(X, kind)
+    Y = from_gpu(gsa.grid_sample(Xd, to_gpu_f32(G), mode, pad, ac))
+    check(Y, oracle.grid_sample(Xin, G, mode, pad, ac), mode, kind, np.abs(Xin).max(),
+          "direct %dD %s/%s/%d/%s" % (rank, mode, pad, ac, kind))
+
+
 @pytest.mark.parametrize("mode,pad", list(itertools.product(MODES, PADS)))
 def test_grid_sample_many_tiles(gsa, mode, pad):
     """Several tiles per image, ragged tail, channel count with a remainder."""
