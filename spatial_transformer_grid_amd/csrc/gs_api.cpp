@@ -13,6 +13,17 @@ constexpr int64_t kPlaneLimit = int64_t(1) << 28;   // elements per input/output
 constexpr int64_t kMaxBlocks = int64_t(1) << 24;    // thread blocks per launch
 constexpr int64_t kInt32Max = 0x7fffffff;
 constexpr int kBlockThreads = 256;
+constexpr int64_t kTargetBlocks = 2048;
+
+void tile_geometry(int r, int mode, int *w, int *h, int *d, int *q) {
+    if (r == 2 && mode != GS_MODE_CUBIC) {
+        *w = gs::Geo<2, 0>::w, *h = gs::Geo<2, 0>::h, *d = gs::Geo<2, 0>::d, *q = gs::Geo<2, 0>::Q;
+    } else if (r == 2) {
+        *w = gs::Geo<2, 2>::w, *h = gs::Geo<2, 2>::h, *d = gs::Geo<2, 2>::d, *q = gs::Geo<2, 2>::Q;
+    } else {
+        *w = gs::Geo<3, 0>::w, *h = gs::Geo<3, 0>::h, *d = gs::Geo<3, 0>::d, *q = gs::Geo<3, 0>::Q;
+    }
+}
 
 int elem_bytes(int dtype) { return dtype == GS_F32 ? 4 : 2; }
 
@@ -68,15 +79,22 @@ int sample(int r, const void *theta, const void *X, int x_dtype, const int64_t *
     if (in_count == 0) return GS_ERR_SHAPE;
     if (!X || !Y || (!grid && !theta)) return GS_ERR_NULL;
     const Extents in = spatial3(x_shape + 2, r), out = spatial3(out_sp, r);
-    const int tw = r == 2 ? gs::TileShape<2>::w : gs::TileShape<3>::w;
-    const int th = r == 2 ? gs::TileShape<2>::h : gs::TileShape<3>::h;
-    const int td = r == 2 ? gs::TileShape<2>::d : gs::TileShape<3>::d;
+    int tw, th, td, q;
+    tile_geometry(r, mode, &tw, &th, &td, &q);
     const int64_t tiles_w = (out.w + tw - 1) / tw, tiles_h = (out.h + th - 1) / th,
                   tiles_d = (out.d + td - 1) / td;
     const int64_t tiles = tiles_w * tiles_h * tiles_d;
     if (tiles > kMaxBlocks || N * tiles > kMaxBlocks) return GS_ERR_TOO_LARGE;
+    // split the channels over several blocks when there are too few tiles to
+    // keep every CU busy (8 resident blocks on each of 256 CUs)
+    int64_t groups = (kTargetBlocks + N * tiles - 1) / (N * tiles);
+    if (groups > C) groups = C;
+    if (groups < 1) groups = 1;
+    const int64_t cpg = (C + groups - 1) / groups;
+    groups = (C + cpg - 1) / cpg;
 
     const int bytes = elem_bytes(x_dtype);
+    const bool vec_in = in.w % gs::stage_chunk_elems(bytes) == 0 && (uintptr_t)X % 16 == 0;
     gs::SampleParams p;
     p.X = X;
     p.Y = Y;
@@ -98,9 +116,12 @@ int sample(int r, const void *theta, const void *X, int x_dtype, const int64_t *
     p.tiles_h = (int)tiles_h;
     p.tiles_d = (int)tiles_d;
     p.tiles_per_n = (int)tiles;
-    p.nblocks = (int)(N * tiles);
+    p.cgroups = (int)groups;
+    p.cpg = (int)cpg;
+    p.nblocks = (int)(N * groups * tiles);
+    p.vec_out = q > 1 && out.w % q == 0 && (uintptr_t)Y % (uintptr_t)(q * bytes) == 0;
     return hip_status(gs::launch_grid_sample(p, r, theta != nullptr, mode, padding, x_dtype,
-                                             (hipStream_t)stream));
+                                             vec_in, (hipStream_t)stream));
 }
 
 int grid_sample_rank(int r, const void *X, int x_dtype, const int64_t *x_shape, const void *grid,

@@ -26,6 +26,8 @@
 
 #include <limits.h>
 
+#include <type_traits>
+
 namespace gs {
 
 // Flat output location -> (d, h, w) for the grid generator.
@@ -180,27 +182,9 @@ __device__ __forceinline__ int div_small(int f, int d, float inv_d) {
     return q;
 }
 
-// ---------------------------------------------------------- staging sizes
-
-// LDS staging: U channels per chunk, CAP elements per channel slot, the last
-// element of every slot holds 0 (the target of out-of-image taps).
-template <int R, int MODE, typename T>
-struct Staging {
-    static constexpr int U = R == 2 ? (MODE == MODE_CUBIC ? 4 : 8) : (MODE == MODE_CUBIC ? 2 : 4);
-    static constexpr int CAP = 16384 / (U * T::bytes);
-    static constexpr int ZERO = CAP - 1;
-    static constexpr int EMAX = (CAP + kBlock - 1) / kBlock;
-};
-
-// Channels per load group of the direct path.
-template <int R, int MODE>
-struct DirectGroup {
-    static constexpr int U = MODE == MODE_NEAREST ? 8
-                             : MODE == MODE_LINEAR ? (R == 2 ? 8 : 4)
-                                                   : (R == 2 ? 2 : 1);
-};
-
-// Interpolate one channel: taps fetched by `fetch(offset)` (raw element).
+// Interpolate one output of one channel from its precomputed taps; `fetch`
+// returns the raw element at a tap offset.  3D cubic is summed separably from
+// 16 (z, y) row offsets and 4 x offsets.
 template <int R, int MODE, typename T, typename Fetch>
 __device__ __forceinline__ float interpolate(const uint32_t *off, const float *w,
                                              const uint32_t (&row)[16], const uint32_t (&col)[4],
@@ -233,298 +217,400 @@ __device__ __forceinline__ float interpolate(const uint32_t *off, const float *w
     }
 }
 
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+// Store the Q outputs of one lane for one channel: one 16-byte (fp32) or
+// 8-byte (fp16/bf16) store when the row layout allows it, else Q stores.
+template <typename T, int Q>
+__device__ __forceinline__ void store_outputs(const typename T::raw_t (&v)[Q], rsrc_t yr,
+                                              const uint32_t (&yoff)[Q], bool vec) {
+    if constexpr (Q == 4) {
+        if (vec) {
+            if constexpr (T::bytes == 4) {
+                u32x4 pk = {(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
+                __builtin_amdgcn_raw_buffer_store_b128(pk, yr, (int)yoff[0], 0, 0);
+            } else {
+                u32x2 pk = {(uint32_t)v[0] | ((uint32_t)v[1] << 16),
+                            (uint32_t)v[2] | ((uint32_t)v[3] << 16)};
+                __builtin_amdgcn_raw_buffer_store_b64(pk, yr, (int)yoff[0], 0, 0);
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q) T::store_raw(v[q], yr, yoff[q]);
+}
+
+template <typename T>
+__device__ __forceinline__ typename T::raw_t to_raw(float v);
+template <>
+__device__ __forceinline__ uint32_t to_raw<F32>(float v) { return __builtin_bit_cast(uint32_t, v); }
+template <>
+__device__ __forceinline__ uint16_t to_raw<F16>(float v) {
+    return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+template <>
+__device__ __forceinline__ uint16_t to_raw<BF16>(float v) {
+    return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
 // --------------------------------------------------------------- sampler
 
-template <int R, int MODE, int PAD, typename T, bool FUSED>
+template <int R, int MODE, int PAD, typename T, bool FUSED, bool VEC>
 __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
-    using TS = TileShape<R>;
-    using ST = Staging<R, MODE, T>;
+    using G = Geo<R, MODE>;
     using raw_t = typename T::raw_t;
+    constexpr int Q = G::Q;
+    constexpr int LPR = G::w / Q;  // lanes per output row of the tile
     constexpr int K = AxisK<MODE>::K;
     constexpr int TAPS = TapOffsets<R, K>::TAPS;
     constexpr bool SEPARABLE = MODE == MODE_CUBIC && R == 3;
     constexpr int NT = SEPARABLE ? 1 : TAPS;  // precomputed tap offsets / weights
-    __shared__ raw_t lds[ST::U * ST::CAP];
+    // LDS staging: U channels of CAP elements; the last element of a slot is 0
+    constexpr int U = 2;
+    constexpr int CAP = 8192 / T::bytes;
+    constexpr int CH = VEC ? 16 / T::bytes : 1;  // elements per staging chunk
+    constexpr int EMAX = (CAP / CH + kBlock - 1) / kBlock;
+    constexpr int ZERO = CAP - 1;
+    constexpr int LIMIT = CAP - CH;  // staged elements end before the zero chunk
+    typedef typename std::conditional<VEC, u32x4, raw_t>::type chunk_t;
+    __shared__ __align__(16) raw_t lds[U * CAP];
     __shared__ int red[kBlock / 64][2 * R];
 
     const int lb = xcd_logical_block(p.nblocks);
     if (lb >= p.nblocks) return;
-    const int n = lb / p.tiles_per_n;
-    int tile = lb - n * p.tiles_per_n;
+    const int tile = lb % p.tiles_per_n;
+    const int ncg = lb / p.tiles_per_n;
+    const int cg = ncg % p.cgroups;
+    const int n = ncg / p.cgroups;
     const int tx = tile % p.tiles_w;
-    tile /= p.tiles_w;
-    const int ty = tile % p.tiles_h;
-    const int tz = tile / p.tiles_h;
+    const int ty = (tile / p.tiles_w) % p.tiles_h;
+    const int tz = tile / (p.tiles_w * p.tiles_h);
     const int t = threadIdx.x;
-    const int ox = tx * TS::w + t % TS::w;
-    const int oy = ty * TS::h + (t / TS::w) % TS::h;
-    const int oz = tz * TS::d + t / (TS::w * TS::h);
-    const bool live = ox < p.out_w && oy < p.out_h && oz < p.out_d;
-    const int cx = min(ox, p.out_w - 1), cy = min(oy, p.out_h - 1), cz = min(oz, p.out_d - 1);
-    const uint32_t l = ((uint32_t)cz * (uint32_t)p.out_h + (uint32_t)cy) * (uint32_t)p.out_w + cx;
+    const int ox0 = tx * G::w + (t % LPR) * Q;
+    const int oy = ty * G::h + (t / LPR) % G::h;
+    const int oz = tz * G::d + t / (LPR * G::h);
     const int ac = p.align_corners;
-
-    float g[R];
-    if constexpr (FUSED) {
-        affine_vector<R>(p.theta + (size_t)n * R * (R + 1), cz, cy, cx, p.out_d, p.out_h, p.out_w,
-                         ac, g);
-    } else {
-        const float *gp = p.grid + ((size_t)n * p.out_count + l) * R;
-#pragma unroll
-        for (int k = 0; k < R; ++k) g[k] = gp[k];
-    }
-
-    // per-axis taps; component k addresses axis k of (W, H, D)
     const int ext[3] = {p.in_w, p.in_h, p.in_d};
-    AxisTaps<K> ax[R];
-    bool any = true;
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-        float q = unnormalize(g[k], ext[k], ac);
-        bool fin = __builtin_isfinite(q);
-        float pc = fin ? clampf(q, -kCoordLimit, kCoordLimit) : 0.0f;
-        axis_taps<MODE, PAD>(pc, ext[k], ac, ax[k]);
-        bool axis_any = false;
-#pragma unroll
-        for (int j = 0; j < K; ++j) {
-            ax[k].ok[j] = ax[k].ok[j] && fin;
-            axis_any = axis_any || ax[k].ok[j];
-        }
-        any = any && axis_any;
-    }
-    // a non-finite location, or one with no in-image tap on some axis, reads
-    // nothing: clear every axis so all its taps are invalid
-#pragma unroll
-    for (int k = 0; k < R; ++k)
-#pragma unroll
-        for (int j = 0; j < K; ++j) ax[k].ok[j] = ax[k].ok[j] && any;
 
-    // bounding box of every valid tap of the block
+    // ---- per output: location, taps, weights
+    bool live[Q];
+    uint32_t yoff[Q];
+    AxisTaps<K> ax[Q][R];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int ox = ox0 + q;
+        live[q] = ox < p.out_w && oy < p.out_h && oz < p.out_d;
+        const int cx = min(ox, p.out_w - 1), cy = min(oy, p.out_h - 1), cz = min(oz, p.out_d - 1);
+        const uint32_t l =
+            ((uint32_t)cz * (uint32_t)p.out_h + (uint32_t)cy) * (uint32_t)p.out_w + cx;
+        yoff[q] = live[q] ? l * (uint32_t)T::bytes : GS_OOB;
+        float g[R];
+        if constexpr (FUSED) {
+            affine_vector<R>(p.theta + (size_t)n * R * (R + 1), cz, cy, cx, p.out_d, p.out_h,
+                             p.out_w, ac, g);
+        } else {
+            const float *gp = p.grid + ((size_t)n * p.out_count + l) * R;
+#pragma unroll
+            for (int k = 0; k < R; ++k) g[k] = gp[k];
+        }
+        bool any = true;
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            float u = unnormalize(g[k], ext[k], ac);
+            bool fin = __builtin_isfinite(u);
+            float pc = fin ? clampf(u, -kCoordLimit, kCoordLimit) : 0.0f;
+            axis_taps<MODE, PAD>(pc, ext[k], ac, ax[q][k]);
+            bool axis_any = false;
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                ax[q][k].ok[j] = ax[q][k].ok[j] && fin;
+                axis_any = axis_any || ax[q][k].ok[j];
+            }
+            any = any && axis_any;
+        }
+        // a location that is not finite, or has no in-image tap on some axis,
+        // reads nothing: every one of its taps becomes invalid
+#pragma unroll
+        for (int k = 0; k < R; ++k)
+#pragma unroll
+            for (int j = 0; j < K; ++j) ax[q][k].ok[j] = ax[q][k].ok[j] && any;
+    }
+
+    // ---- bounding box of every valid tap of the block
     int mm[2 * R];
 #pragma unroll
     for (int k = 0; k < R; ++k) {
         int lo = INT_MAX, nhi = INT_MAX;
 #pragma unroll
-        for (int j = 0; j < K; ++j)
-            if (ax[k].ok[j]) {
-                lo = min(lo, ax[k].idx[j]);
-                nhi = min(nhi, -ax[k].idx[j]);
-            }
+        for (int q = 0; q < Q; ++q)
+#pragma unroll
+            for (int j = 0; j < K; ++j)
+                if (ax[q][k].ok[j]) {
+                    lo = min(lo, ax[q][k].idx[j]);
+                    nhi = min(nhi, -ax[q][k].idx[j]);
+                }
         mm[2 * k] = lo;
         mm[2 * k + 1] = nhi;
     }
     block_min<2 * R>(mm, red);
     int lo[3] = {0, 0, 0}, span[3] = {1, 1, 1};
-    int area = 0;
-    if (mm[0] != INT_MAX) {
-        area = 1;
+    const bool tile_any = mm[0] != INT_MAX;
+    if (tile_any) {
 #pragma unroll
         for (int k = 0; k < R; ++k) {
             lo[k] = mm[2 * k];
             span[k] = -mm[2 * k + 1] - mm[2 * k] + 1;
-            area *= span[k];
         }
     }
+    // staging layout: rows of nx chunks starting at the chunk-aligned xa
+    const int xa = lo[0] & ~(CH - 1);
+    const int nx = (lo[0] + span[0] - xa + CH - 1) / CH;
+    const int S = nx * CH;
+    const int64_t rows = (int64_t)span[1] * span[2];
+    const bool staged = (int64_t)S * rows <= LIMIT;
 
-    const uint32_t ip = p.in_plane_bytes, op = p.out_plane_bytes;
-    const char *xn = (const char *)p.X + (size_t)n * p.C * ip;
-    char *yn = (char *)p.Y + (size_t)n * p.C * op;
-    const uint32_t yoff = live ? l * (uint32_t)T::bytes : GS_OOB;
-    const int C = p.C;
-
-    // tap weights (products over axes) and, for 3D cubic, per-axis weights
-    float w[NT];
-    float wz[4] = {0, 0, 0, 0}, wy[4] = {0, 0, 0, 0}, wx[4] = {0, 0, 0, 0};
-    if constexpr (SEPARABLE) {
+    // ---- tap weights
+    float w[Q][NT];
+    float wz[Q][4], wy[Q][4], wx[Q][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            wx[j] = ax[0].w[j];
-            wy[j] = ax[1].w[j];
-            wz[j] = ax[2].w[j];
-        }
-        w[0] = 0.0f;
-    } else {
-#pragma unroll
-        for (int tap = 0; tap < TAPS; ++tap) {
-            float ww = 1.0f;
-            int rem = tap;
-#pragma unroll
-            for (int k = 0; k < R; ++k) {
-                ww = ww * ax[k].w[rem % K];
-                rem /= K;
-            }
-            w[tap] = ww;
-        }
-    }
-
-    // tap offsets from per-axis parts (stride[k] per unit of axis k)
-    auto build_offsets = [&](const uint32_t (&stride)[3], uint32_t bad, uint32_t cap,
-                             uint32_t (&off)[NT], uint32_t (&row)[16], uint32_t (&col)[4]) {
-        uint32_t part[R][K];
-#pragma unroll
-        for (int k = 0; k < R; ++k)
-#pragma unroll
-            for (int j = 0; j < K; ++j)
-                part[k][j] = ax[k].ok[j] ? (uint32_t)(ax[k].idx[j] - lo[k]) * stride[k] : bad;
+    for (int q = 0; q < Q; ++q) {
         if constexpr (SEPARABLE) {
 #pragma unroll
-            for (int jz = 0; jz < 4; ++jz)
-#pragma unroll
-                for (int jy = 0; jy < 4; ++jy)
-                    row[jz * 4 + jy] = __builtin_elementwise_add_sat(part[2][jz], part[1][jy]);
-#pragma unroll
-            for (int jx = 0; jx < 4; ++jx) col[jx] = part[0][jx];
-            off[0] = 0;
+            for (int j = 0; j < 4; ++j) {
+                wx[q][j] = ax[q][0].w[j];
+                wy[q][j] = ax[q][1].w[j];
+                wz[q][j] = ax[q][2].w[j];
+            }
+            w[q][0] = 0.0f;
         } else {
 #pragma unroll
+            for (int j = 0; j < 4; ++j) wx[q][j] = wy[q][j] = wz[q][j] = 0.0f;
+#pragma unroll
             for (int tap = 0; tap < TAPS; ++tap) {
-                uint32_t o = 0;
+                float ww = 1.0f;
                 int rem = tap;
 #pragma unroll
                 for (int k = 0; k < R; ++k) {
-                    o = __builtin_elementwise_add_sat(o, part[k][rem % K]);
+                    ww = ww * ax[q][k].w[rem % K];
                     rem /= K;
                 }
-                off[tap] = min(o, cap);
+                w[q][tap] = ww;
             }
+        }
+    }
+
+    // tap offsets from per-axis parts; an invalid tap's part is `bad` and the
+    // sums saturate, so any invalid tap ends at or beyond `cap`
+    uint32_t off[Q][NT], row[Q][16], col[Q][4];
+    auto build_offsets = [&](const int (&base)[3], const uint32_t (&stride)[3], uint32_t bad,
+                             uint32_t cap) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) row[i] = 0;
+        for (int q = 0; q < Q; ++q) {
+            uint32_t part[R][K];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) col[i] = 0;
+            for (int k = 0; k < R; ++k)
+#pragma unroll
+                for (int j = 0; j < K; ++j)
+                    part[k][j] = ax[q][k].ok[j] ? (uint32_t)(ax[q][k].idx[j] - base[k]) * stride[k]
+                                                : bad;
+            if constexpr (SEPARABLE) {
+#pragma unroll
+                for (int jz = 0; jz < 4; ++jz)
+#pragma unroll
+                    for (int jy = 0; jy < 4; ++jy)
+                        row[q][jz * 4 + jy] = __builtin_elementwise_add_sat(part[2][jz], part[1][jy]);
+#pragma unroll
+                for (int jx = 0; jx < 4; ++jx) col[q][jx] = part[0][jx];
+                off[q][0] = 0;
+            } else {
+#pragma unroll
+                for (int tap = 0; tap < TAPS; ++tap) {
+                    uint32_t o = 0;
+                    int rem = tap;
+#pragma unroll
+                    for (int k = 0; k < R; ++k) {
+                        o = __builtin_elementwise_add_sat(o, part[k][rem % K]);
+                        rem /= K;
+                    }
+                    off[q][tap] = min(o, cap);
+                }
+#pragma unroll
+                for (int i = 0; i < 16; ++i) row[q][i] = 0;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) col[q][i] = 0;
+            }
         }
     };
 
-    uint32_t off[NT], row[16], col[4];
+    const uint32_t ip = p.in_plane_bytes, op = p.out_plane_bytes;
+    const int cbeg = cg * p.cpg;
+    const int cend = min(p.C, cbeg + p.cpg);
+    const char *xn = (const char *)p.X + ((size_t)n * p.C) * ip;
+    char *yn = (char *)p.Y + ((size_t)n * p.C) * op;
+    const bool vec_out = p.vec_out != 0;
 
-    if (area <= ST::CAP - 1) {
+    if (staged) {
         // ------------------------------------------------ staged in LDS
-        constexpr int U = ST::U, CAP = ST::CAP, ZERO = ST::ZERO, EMAX = ST::EMAX;
         {
-            const uint32_t stride[3] = {1u, (uint32_t)span[0], (uint32_t)(span[0] * span[1])};
-            build_offsets(stride, 0x40000000u, (uint32_t)ZERO, off, row, col);
+            const int base[3] = {xa, lo[1], lo[2]};
+            const uint32_t stride[3] = {1u, (uint32_t)S, (uint32_t)(S * span[1])};
+            build_offsets(base, stride, 0x40000000u, (uint32_t)ZERO);
         }
-        // this thread's share of the box: element f = t + e * 256.  Elements
-        // past the box load through the out-of-range offset (value 0) into the
-        // zero slot, so the staging code has no branches: a branch would make
+        // this thread's chunks of the box: chunk c = t + e * 256.  Chunks past
+        // the box load through the out-of-range offset (zeros) into the last
+        // chunk of the slot, so this code has no branches: a branch would make
         // the compiler wait for every load in flight before the next one.
-        const float inv_w = 1.0f / (float)span[0];
-        const float inv_wh = 1.0f / (float)(span[0] * span[1]);
+        const int nchunks = nx * (int)rows;
+        const float inv_nx = 1.0f / (float)nx;
+        const float inv_sy = 1.0f / (float)span[1];
         uint32_t goff[EMAX], loff[EMAX];
 #pragma unroll
         for (int e = 0; e < EMAX; ++e) {
-            const int f = t + e * kBlock;
-            int z = 0, rem = f;
+            const int c = t + e * kBlock;
+            const int rr = div_small(c, nx, inv_nx);
+            const int cx = c - rr * nx;
+            int z = 0, y = rr;
             if (R == 3) {
-                z = div_small(f, span[0] * span[1], inv_wh);
-                rem = f - z * span[0] * span[1];
+                z = div_small(rr, span[1], inv_sy);
+                y = rr - z * span[1];
             }
-            const int y = div_small(rem, span[0], inv_w);
-            const int x = rem - y * span[0];
-            const bool in_box = f < area;
-            goff[e] = in_box ? (uint32_t)((((lo[2] + z) * p.in_h + lo[1] + y) * p.in_w + lo[0] + x) *
+            const bool in_box = c < nchunks;
+            goff[e] = in_box ? (uint32_t)((((lo[2] + z) * p.in_h + lo[1] + y) * p.in_w + xa + cx * CH) *
                                           T::bytes)
                              : GS_OOB;
-            loff[e] = in_box ? (uint32_t)f : (uint32_t)ZERO;
+            loff[e] = (uint32_t)(in_box ? c * CH : LIMIT) * T::bytes;
         }
         if (t < U) lds[t * CAP + ZERO] = 0;
 
-        raw_t pre[U][EMAX];
+        auto load_chunk = [&](rsrc_t r, uint32_t o) -> chunk_t {
+            if constexpr (VEC) return __builtin_amdgcn_raw_buffer_load_b128(r, (int)o, 0, 0);
+            else return T::load_raw(r, o);
+        };
+        chunk_t pre[U][EMAX];
+        auto prefetch = [&](int c0) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const bool has = u < C;
-            const rsrc_t r = make_rsrc(xn + (size_t)(has ? u : 0) * ip, ip);
+            for (int u = 0; u < U; ++u) {
+                const int c = c0 + u;
+                const bool has = c < cend;
+                const rsrc_t r = make_rsrc(xn + (size_t)(has ? c : cbeg) * ip, ip);
 #pragma unroll
-            for (int e = 0; e < EMAX; ++e) pre[u][e] = T::load_raw(r, has ? goff[e] : GS_OOB);
-        }
-        for (int c0 = 0; c0 < C; c0 += U) {
+                for (int e = 0; e < EMAX; ++e) pre[u][e] = load_chunk(r, has ? goff[e] : GS_OOB);
+            }
+        };
+        prefetch(cbeg);
+        for (int c0 = cbeg; c0 < cend; c0 += U) {
             __syncthreads();  // the previous chunk's LDS reads are done
 #pragma unroll
             for (int u = 0; u < U; ++u)
 #pragma unroll
-                for (int e = 0; e < EMAX; ++e) lds[u * CAP + loff[e]] = pre[u][e];
+                for (int e = 0; e < EMAX; ++e)
+                    *(chunk_t *)((char *)(lds + u * CAP) + loff[e]) = pre[u][e];
             __syncthreads();  // this chunk is in LDS
-            if (c0 + U < C) {
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int c = c0 + U + u;
-                    const bool has = c < C;
-                    const rsrc_t r = make_rsrc(xn + (size_t)(has ? c : 0) * ip, ip);
-#pragma unroll
-                    for (int e = 0; e < EMAX; ++e) pre[u][e] = T::load_raw(r, has ? goff[e] : GS_OOB);
-                }
-            }
+            if (c0 + U < cend) prefetch(c0 + U);
 #pragma unroll
             for (int u = 0; u < U; ++u) {
                 const int c = c0 + u;
-                const bool has = c < C;
+                const bool has = c < cend;
                 const raw_t *s = lds + u * CAP;
-                const rsrc_t yr = make_rsrc(yn + (size_t)(has ? c : 0) * op, op);
-                const uint32_t yo = has ? yoff : GS_OOB;
-                if constexpr (MODE == MODE_NEAREST) {
-                    T::store_raw(s[off[0]], yr, yo);
+                const rsrc_t yr = make_rsrc(yn + (size_t)(has ? c : cbeg) * op, op);
+                raw_t v[Q];
+                uint32_t yo[Q];
+#pragma unroll
+                for (int q = 0; q < Q; ++q) yo[q] = has ? yoff[q] : GS_OOB;
+                if constexpr (SEPARABLE) {
+#pragma unroll
+                    for (int q = 0; q < Q; ++q)
+                        v[q] = to_raw<T>(interpolate<R, MODE, T>(
+                            off[q], w[q], row[q], col[q], wz[q], wy[q], wx[q], (uint32_t)ZERO,
+                            [&](uint32_t o) { return s[o]; }));
                 } else {
-                    float v = interpolate<R, MODE, T>(off, w, row, col, wz, wy, wx, (uint32_t)ZERO,
-                                                      [&](uint32_t o) { return s[o]; });
-                    T::store(v, yr, yo);
+                    // all LDS reads of the channel first, then the arithmetic
+                    raw_t tv[Q][TAPS];
+#pragma unroll
+                    for (int q = 0; q < Q; ++q)
+#pragma unroll
+                        for (int tap = 0; tap < TAPS; ++tap) tv[q][tap] = s[off[q][tap]];
+#pragma unroll
+                    for (int q = 0; q < Q; ++q) {
+                        if constexpr (MODE == MODE_NEAREST) {
+                            v[q] = tv[q][0];
+                        } else {
+                            float acc = w[q][0] * T::from_raw(tv[q][0]);
+#pragma unroll
+                            for (int tap = 1; tap < TAPS; ++tap)
+                                acc = fmaf(w[q][tap], T::from_raw(tv[q][tap]), acc);
+                            v[q] = to_raw<T>(acc);
+                        }
+                    }
                 }
+                store_outputs<T, Q>(v, yr, yo, vec_out);
             }
         }
     } else {
         // ------------------------------------------------- direct gather
         {
-            lo[0] = lo[1] = lo[2] = 0;
+            const int base[3] = {0, 0, 0};
             const uint32_t stride[3] = {(uint32_t)T::bytes, (uint32_t)(p.in_w * T::bytes),
                                         (uint32_t)(p.in_w * p.in_h * T::bytes)};
-            build_offsets(stride, GS_OOB, 0xFFFFFFFFu, off, row, col);
+            build_offsets(base, stride, GS_OOB, 0xFFFFFFFFu);
         }
-        constexpr int U = DirectGroup<R, MODE>::U;
-        int c = 0;
-        for (; c + U <= C; c += U) {
-            if constexpr (MODE == MODE_NEAREST) {
-                raw_t v[U];
+        constexpr int UD = SEPARABLE ? 1 : (MODE == MODE_NEAREST ? 8 : (TAPS * Q >= 16 ? 1 : 2));
+        int c = cbeg;
+        for (; c + UD <= cend; c += UD) {
+            if constexpr (SEPARABLE) {
+                const rsrc_t r = make_rsrc(xn + (size_t)c * ip, ip);
+                raw_t v[Q];
 #pragma unroll
-                for (int u = 0; u < U; ++u)
-                    v[u] = T::load_raw(make_rsrc(xn + (size_t)(c + u) * ip, ip), off[0]);
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-                    T::store_raw(v[u], make_rsrc(yn + (size_t)(c + u) * op, op), yoff);
-            } else if constexpr (SEPARABLE) {
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const rsrc_t r = make_rsrc(xn + (size_t)(c + u) * ip, ip);
-                    float v = interpolate<R, MODE, T>(
-                        off, w, row, col, wz, wy, wx, 0xFFFFFFFFu,
-                        [&](uint32_t o) { return T::load_raw(r, o); });
-                    T::store(v, make_rsrc(yn + (size_t)(c + u) * op, op), yoff);
-                }
+                for (int q = 0; q < Q; ++q)
+                    v[q] = to_raw<T>(interpolate<R, MODE, T>(
+                        off[q], w[q], row[q], col[q], wz[q], wy[q], wx[q], 0xFFFFFFFFu,
+                        [&](uint32_t o) { return T::load_raw(r, o); }));
+                store_outputs<T, Q>(v, make_rsrc(yn + (size_t)c * op, op), yoff, vec_out);
             } else {
-                raw_t v[U][TAPS];
+                raw_t g[UD][Q][TAPS];
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
+                for (int u = 0; u < UD; ++u) {
                     const rsrc_t r = make_rsrc(xn + (size_t)(c + u) * ip, ip);
 #pragma unroll
-                    for (int tap = 0; tap < TAPS; ++tap) v[u][tap] = T::load_raw(r, off[tap]);
+                    for (int q = 0; q < Q; ++q)
+#pragma unroll
+                        for (int tap = 0; tap < TAPS; ++tap) g[u][q][tap] = T::load_raw(r, off[q][tap]);
                 }
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    float acc = w[0] * T::from_raw(v[u][0]);
+                for (int u = 0; u < UD; ++u) {
+                    raw_t v[Q];
 #pragma unroll
-                    for (int tap = 1; tap < TAPS; ++tap)
-                        acc = fmaf(w[tap], T::from_raw(v[u][tap]), acc);
-                    T::store(acc, make_rsrc(yn + (size_t)(c + u) * op, op), yoff);
+                    for (int q = 0; q < Q; ++q) {
+                        if constexpr (MODE == MODE_NEAREST) {
+                            v[q] = g[u][q][0];
+                        } else {
+                            float acc = w[q][0] * T::from_raw(g[u][q][0]);
+#pragma unroll
+                            for (int tap = 1; tap < TAPS; ++tap)
+                                acc = fmaf(w[q][tap], T::from_raw(g[u][q][tap]), acc);
+                            v[q] = to_raw<T>(acc);
+                        }
+                    }
+                    store_outputs<T, Q>(v, make_rsrc(yn + (size_t)(c + u) * op, op), yoff, vec_out);
                 }
             }
         }
-        for (; c < C; ++c) {
+        for (; c < cend; ++c) {
             const rsrc_t r = make_rsrc(xn + (size_t)c * ip, ip);
-            const rsrc_t yr = make_rsrc(yn + (size_t)c * op, op);
-            if constexpr (MODE == MODE_NEAREST) {
-                T::store_raw(T::load_raw(r, off[0]), yr, yoff);
-            } else {
-                float v = interpolate<R, MODE, T>(off, w, row, col, wz, wy, wx, 0xFFFFFFFFu,
-                                                  [&](uint32_t o) { return T::load_raw(r, o); });
-                T::store(v, yr, yoff);
+            raw_t v[Q];
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                if constexpr (MODE == MODE_NEAREST) {
+                    v[q] = T::load_raw(r, off[q][0]);
+                } else {
+                    v[q] = to_raw<T>(interpolate<R, MODE, T>(
+                        off[q], w[q], row[q], col[q], wz[q], wy[q], wx[q], 0xFFFFFFFFu,
+                        [&](uint32_t o) { return T::load_raw(r, o); }));
+                }
             }
+            store_outputs<T, Q>(v, make_rsrc(yn + (size_t)c * op, op), yoff, vec_out);
         }
     }
 }
@@ -534,46 +620,51 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
 static dim3 launch_grid(int nblocks) { return dim3(8 * ((nblocks + 7) / 8)); }
 
 template <int R, bool FUSED, int MODE, int PAD, typename T>
-static int launch_one(const SampleParams &p, hipStream_t s) {
-    hipLaunchKernelGGL((grid_sample_kernel<R, MODE, PAD, T, FUSED>), launch_grid(p.nblocks),
-                       dim3(kBlock), 0, s, p);
+static int launch_one(const SampleParams &p, bool vec, hipStream_t s) {
+    if (vec)
+        hipLaunchKernelGGL((grid_sample_kernel<R, MODE, PAD, T, FUSED, true>),
+                           launch_grid(p.nblocks), dim3(kBlock), 0, s, p);
+    else
+        hipLaunchKernelGGL((grid_sample_kernel<R, MODE, PAD, T, FUSED, false>),
+                           launch_grid(p.nblocks), dim3(kBlock), 0, s, p);
     return (int)hipGetLastError();
 }
 
 template <int R, bool FUSED, int MODE, int PAD>
-static int by_dtype(const SampleParams &p, int dtype, hipStream_t s) {
+static int by_dtype(const SampleParams &p, int dtype, bool vec, hipStream_t s) {
     switch (dtype) {
-    case 0: return launch_one<R, FUSED, MODE, PAD, F32>(p, s);
-    case 1: return launch_one<R, FUSED, MODE, PAD, F16>(p, s);
-    default: return launch_one<R, FUSED, MODE, PAD, BF16>(p, s);
+    case 0: return launch_one<R, FUSED, MODE, PAD, F32>(p, vec, s);
+    case 1: return launch_one<R, FUSED, MODE, PAD, F16>(p, vec, s);
+    default: return launch_one<R, FUSED, MODE, PAD, BF16>(p, vec, s);
     }
 }
 
 template <int R, bool FUSED, int MODE>
-static int by_padding(const SampleParams &p, int padding, int dtype, hipStream_t s) {
+static int by_padding(const SampleParams &p, int padding, int dtype, bool vec, hipStream_t s) {
     switch (padding) {
-    case PAD_ZEROS: return by_dtype<R, FUSED, MODE, PAD_ZEROS>(p, dtype, s);
-    case PAD_BORDER: return by_dtype<R, FUSED, MODE, PAD_BORDER>(p, dtype, s);
-    default: return by_dtype<R, FUSED, MODE, PAD_REFLECTION>(p, dtype, s);
+    case PAD_ZEROS: return by_dtype<R, FUSED, MODE, PAD_ZEROS>(p, dtype, vec, s);
+    case PAD_BORDER: return by_dtype<R, FUSED, MODE, PAD_BORDER>(p, dtype, vec, s);
+    default: return by_dtype<R, FUSED, MODE, PAD_REFLECTION>(p, dtype, vec, s);
     }
 }
 
 template <int R, bool FUSED>
-static int by_mode(const SampleParams &p, int mode, int padding, int dtype, hipStream_t s) {
+static int by_mode(const SampleParams &p, int mode, int padding, int dtype, bool vec,
+                   hipStream_t s) {
     switch (mode) {
-    case MODE_LINEAR: return by_padding<R, FUSED, MODE_LINEAR>(p, padding, dtype, s);
-    case MODE_NEAREST: return by_padding<R, FUSED, MODE_NEAREST>(p, padding, dtype, s);
-    default: return by_padding<R, FUSED, MODE_CUBIC>(p, padding, dtype, s);
+    case MODE_LINEAR: return by_padding<R, FUSED, MODE_LINEAR>(p, padding, dtype, vec, s);
+    case MODE_NEAREST: return by_padding<R, FUSED, MODE_NEAREST>(p, padding, dtype, vec, s);
+    default: return by_padding<R, FUSED, MODE_CUBIC>(p, padding, dtype, vec, s);
     }
 }
 
 int launch_grid_sample(const SampleParams &p, int rank, bool fused, int mode, int padding,
-                       int dtype, hipStream_t stream) {
+                       int dtype, bool vec_in, hipStream_t stream) {
     if (rank == 2)
-        return fused ? by_mode<2, true>(p, mode, padding, dtype, stream)
-                     : by_mode<2, false>(p, mode, padding, dtype, stream);
-    return fused ? by_mode<3, true>(p, mode, padding, dtype, stream)
-                 : by_mode<3, false>(p, mode, padding, dtype, stream);
+        return fused ? by_mode<2, true>(p, mode, padding, dtype, vec_in, stream)
+                     : by_mode<2, false>(p, mode, padding, dtype, vec_in, stream);
+    return fused ? by_mode<3, true>(p, mode, padding, dtype, vec_in, stream)
+                 : by_mode<3, false>(p, mode, padding, dtype, vec_in, stream);
 }
 
 int launch_affine_grid(const AffineParams &p, int rank, hipStream_t stream) {

@@ -18,8 +18,8 @@ inline FastDivHost make_fastdiv(uint32_t d) {
     return FastDivHost{d, (uint32_t)m, s};
 }
 
-// One sampling launch: 1 (2D) or 3 (3D) spatial axes, extents listed
-// outermost first; for 2D the depth extents are 1.
+// One sampling launch: 2 or 3 spatial axes, extents listed outermost first;
+// for 2D the depth extents are 1.
 struct SampleParams {
     const void *X;
     void *Y;
@@ -34,20 +34,24 @@ struct SampleParams {
     int align_corners;
     int tiles_w, tiles_h, tiles_d;  // output tiles per image along W, H, D
     int tiles_per_n;           // tiles_w * tiles_h * tiles_d
-    int nblocks;               // N * tiles_per_n
+    int cgroups, cpg;          // channel groups per image, channels per group
+    int nblocks;               // N * cgroups * tiles_per_n
+    int vec_out;               // Y rows allow one vector store per lane
 };
 
-// Output tile of one 256-thread block: 16 x 16 (2D) or 8 x 8 x 4 (3D).
-template <int R>
-struct TileShape;
-template <>
-struct TileShape<2> {
-    static constexpr int w = 16, h = 16, d = 1;
+// Output tile of one 256-thread block and the number Q of consecutive
+// outputs (along W) each lane owns.  2D nearest / linear: 32 x 32 outputs,
+// 4 per lane; 2D cubic: 16 x 16, 1 per lane; 3D: 8 x 8 x 4, 1 per lane.
+template <int R, int MODE>
+struct Geo {
+    static constexpr int Q = (R == 2 && MODE != 2) ? 4 : 1;
+    static constexpr int w = R == 2 ? (Q == 4 ? 32 : 16) : 8;
+    static constexpr int h = R == 2 ? (Q == 4 ? 32 : 16) : 8;
+    static constexpr int d = R == 2 ? 1 : 4;
 };
-template <>
-struct TileShape<3> {
-    static constexpr int w = 8, h = 8, d = 4;
-};
+
+// Elements per 16-byte chunk of the LDS staging copy.
+inline int stage_chunk_elems(int elem_bytes) { return 16 / elem_bytes; }
 
 struct AffineParams {
     const float *theta;  // (N, R, R+1)
@@ -63,9 +67,10 @@ struct AffineParams {
 };
 
 // Launchers (gs_kernels.hip).  Return 0 on success or the hipError_t of the
-// launch.  `rank` is 2 or 3; `dtype` 0 f32, 1 f16, 2 bf16.
+// launch.  `rank` is 2 or 3; `dtype` 0 f32, 1 f16, 2 bf16; `vec_in` selects
+// 16-byte staging loads (input rows a whole number of 16-byte chunks).
 int launch_grid_sample(const SampleParams &p, int rank, bool fused, int mode, int padding,
-                       int dtype, hipStream_t stream);
+                       int dtype, bool vec_in, hipStream_t stream);
 int launch_affine_grid(const AffineParams &p, int rank, hipStream_t stream);
 
 }  // namespace gs
