@@ -187,7 +187,7 @@ __device__ __forceinline__ int div_small(int f, int d, float inv_d) {
 // 16 (z, y) row offsets and 4 x offsets.
 template <int R, int MODE, typename T, typename Fetch>
 __device__ __forceinline__ float interpolate(const uint32_t *off, const float *w,
-                                             const uint32_t (&row)[16], const uint32_t (&col)[4],
+                                             const int (&row)[16], const int (&col)[4],
                                              const float (&wz)[4], const float (&wy)[4],
                                              const float (&wx)[4], uint32_t cap, Fetch fetch) {
     if constexpr (MODE == MODE_CUBIC && R == 3) {
@@ -200,7 +200,7 @@ __device__ __forceinline__ float interpolate(const uint32_t *off, const float *w
                 float sy = 0.0f;
 #pragma unroll
                 for (int jx = 0; jx < 4; ++jx) {
-                    uint32_t o = min(__builtin_elementwise_add_sat(row[jz * 4 + jy], col[jx]), cap);
+                    uint32_t o = min((uint32_t)(row[jz * 4 + jy] + col[jx]), cap);
                     sy = fmaf(wx[jx], T::from_raw(fetch(o)), sy);
                 }
                 sz = fmaf(wy[jy], sy, sz);
@@ -275,10 +275,12 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
     constexpr int ZERO = CAP - 1;
     constexpr int LIMIT = CAP - CH;  // staged elements end before the zero chunk
     typedef typename std::conditional<VEC, u32x4, raw_t>::type chunk_t;
+    constexpr int MAXR = 128;  // input rows (z, y) a staged tile may span
     __shared__ __align__(16) raw_t lds[U * CAP];
     __shared__ int red[kBlock / 64][2 * R];
+    __shared__ int row_lo[MAXR], row_hi[MAXR], row_xs[MAXR], row_base[MAXR + 1];
 
-    const int lb = xcd_logical_block(p.nblocks);
+    const int lb = xcd_logical_block_runs(p.nblocks);
     if (lb >= p.nblocks) return;
     const int tile = lb % p.tiles_per_n;
     const int ncg = lb / p.tiles_per_n;
@@ -364,12 +366,66 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
             span[k] = -mm[2 * k + 1] - mm[2 * k] + 1;
         }
     }
-    // staging layout: rows of nx chunks starting at the chunk-aligned xa
-    const int xa = lo[0] & ~(CH - 1);
-    const int nx = (lo[0] + span[0] - xa + CH - 1) / CH;
-    const int S = nx * CH;
-    const int64_t rows = (int64_t)span[1] * span[2];
-    const bool staged = (int64_t)S * rows <= LIMIT;
+    // ---- staging plan: every input row (z, y) of the box gets the interval
+    // of 16-byte chunks that covers the x taps the block reads in that row;
+    // rows are packed one after another in the LDS slot.
+    const int64_t nrows = (int64_t)span[1] * span[2];
+    int total_chunks = INT_MAX;
+    if (tile_any && nrows <= MAXR) {
+        if (t < MAXR) {
+            row_lo[t] = INT_MAX;
+            row_hi[t] = INT_MIN;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            int xl = INT_MAX, xh = INT_MIN;
+#pragma unroll
+            for (int j = 0; j < K; ++j)
+                if (ax[q][0].ok[j]) {
+                    xl = min(xl, ax[q][0].idx[j]);
+                    xh = max(xh, ax[q][0].idx[j]);
+                }
+#pragma unroll
+            for (int jz = 0; jz < (R == 3 ? K : 1); ++jz)
+#pragma unroll
+                for (int jy = 0; jy < K; ++jy) {
+                    const bool ok = xl <= xh && ax[q][1].ok[jy] && (R == 2 || ax[q][R - 1].ok[jz]);
+                    if (ok) {
+                        const int r = (R == 3 ? (ax[q][R - 1].idx[jz] - lo[2]) * span[1] : 0) +
+                                      ax[q][1].idx[jy] - lo[1];
+                        atomicMin(&row_lo[r], xl);
+                        atomicMax(&row_hi[r], xh);
+                    }
+                }
+        }
+        __syncthreads();
+        if (t < 64) {
+            // chunks per row, two rows per lane, and a wave-wide prefix sum
+            const int r0 = 2 * t, r1 = 2 * t + 1;
+            const bool e0 = r0 < nrows && row_hi[r0] >= row_lo[r0];
+            const bool e1 = r1 < nrows && row_hi[r1] >= row_lo[r1];
+            const int xs0 = e0 ? (row_lo[r0] & ~(CH - 1)) : 0;
+            const int xs1 = e1 ? (row_lo[r1] & ~(CH - 1)) : 0;
+            const int c0 = e0 ? (row_hi[r0] - xs0 + CH) / CH : 0;
+            const int c1 = e1 ? (row_hi[r1] - xs1 + CH) / CH : 0;
+            int incl = c0 + c1;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int v = __shfl_up(incl, d, 64);
+                if (t >= d) incl += v;
+            }
+            const int excl = incl - c0 - c1;
+            row_base[r0] = excl;
+            row_base[r1] = excl + c0;
+            row_xs[r0] = xs0;
+            row_xs[r1] = xs1;
+            if (t == 63) row_base[MAXR] = incl;
+        }
+        __syncthreads();
+        total_chunks = __builtin_amdgcn_readfirstlane(row_base[MAXR]);
+    }
+    const bool staged = (int64_t)total_chunks * CH <= LIMIT;
 
     // ---- tap weights
     float w[Q][NT];
@@ -401,40 +457,41 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
         }
     }
 
-    // tap offsets from per-axis parts; an invalid tap's part is `bad` and the
-    // sums saturate, so any invalid tap ends at or beyond `cap`
-    uint32_t off[Q][NT], row[Q][16], col[Q][4];
-    auto build_offsets = [&](const int (&base)[3], const uint32_t (&stride)[3], uint32_t bad,
-                             uint32_t cap) {
+    // Tap offsets = row part (z, y) + column part (x).  row_part(q, jz, jy)
+    // returns the row part of a valid row; an invalid tap gets `cap`.  For 3D
+    // cubic the parts are kept apart (summed per channel): an invalid part is
+    // -2^30, which makes the sum negative, i.e. >= 2^31 as unsigned.
+    constexpr int BADPART = -(1 << 30);
+    uint32_t off[Q][NT];
+    int row[Q][16], col[Q][4];
+    auto build_offsets = [&](auto row_part, int xscale, uint32_t cap) {
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
-            uint32_t part[R][K];
+            int rp[R == 3 ? K : 1][K];
+            bool rok[R == 3 ? K : 1][K];
 #pragma unroll
-            for (int k = 0; k < R; ++k)
+            for (int jz = 0; jz < (R == 3 ? K : 1); ++jz)
 #pragma unroll
-                for (int j = 0; j < K; ++j)
-                    part[k][j] = ax[q][k].ok[j] ? (uint32_t)(ax[q][k].idx[j] - base[k]) * stride[k]
-                                                : bad;
+                for (int jy = 0; jy < K; ++jy) {
+                    rok[jz][jy] = ax[q][1].ok[jy] && (R == 2 || ax[q][R - 1].ok[jz]);
+                    rp[jz][jy] = rok[jz][jy] ? row_part(ax[q][R - 1].idx[jz], ax[q][1].idx[jy]) : 0;
+                }
             if constexpr (SEPARABLE) {
 #pragma unroll
                 for (int jz = 0; jz < 4; ++jz)
 #pragma unroll
                     for (int jy = 0; jy < 4; ++jy)
-                        row[q][jz * 4 + jy] = __builtin_elementwise_add_sat(part[2][jz], part[1][jy]);
+                        row[q][jz * 4 + jy] = rok[jz][jy] ? rp[jz][jy] : BADPART;
 #pragma unroll
-                for (int jx = 0; jx < 4; ++jx) col[q][jx] = part[0][jx];
+                for (int jx = 0; jx < 4; ++jx)
+                    col[q][jx] = ax[q][0].ok[jx] ? ax[q][0].idx[jx] * xscale : BADPART;
                 off[q][0] = 0;
             } else {
 #pragma unroll
                 for (int tap = 0; tap < TAPS; ++tap) {
-                    uint32_t o = 0;
-                    int rem = tap;
-#pragma unroll
-                    for (int k = 0; k < R; ++k) {
-                        o = __builtin_elementwise_add_sat(o, part[k][rem % K]);
-                        rem /= K;
-                    }
-                    off[q][tap] = min(o, cap);
+                    const int jx = tap % K, jy = (tap / K) % K, jz = R == 3 ? tap / (K * K) : 0;
+                    const bool ok = ax[q][0].ok[jx] && rok[jz][jy];
+                    off[q][tap] = ok ? (uint32_t)(rp[jz][jy] + ax[q][0].idx[jx] * xscale) : cap;
                 }
 #pragma unroll
                 for (int i = 0; i < 16; ++i) row[q][i] = 0;
@@ -453,34 +510,39 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
 
     if (staged) {
         // ------------------------------------------------ staged in LDS
-        {
-            const int base[3] = {xa, lo[1], lo[2]};
-            const uint32_t stride[3] = {1u, (uint32_t)S, (uint32_t)(S * span[1])};
-            build_offsets(base, stride, 0x40000000u, (uint32_t)ZERO);
-        }
-        // this thread's chunks of the box: chunk c = t + e * 256.  Chunks past
-        // the box load through the out-of-range offset (zeros) into the last
-        // chunk of the slot, so this code has no branches: a branch would make
-        // the compiler wait for every load in flight before the next one.
-        const int nchunks = nx * (int)rows;
-        const float inv_nx = 1.0f / (float)nx;
+        // LDS element offset of pixel x of row r: row_base[r] * CH - row_xs[r] + x
+        build_offsets(
+            [&](int iz, int iy) {
+                const int r = (R == 3 ? (iz - lo[2]) * span[1] : 0) + iy - lo[1];
+                return row_base[r] * CH - row_xs[r];
+            },
+            1, (uint32_t)ZERO);
+        // this thread's chunks: chunk c = t + e * 256, found in the row table by
+        // a branch-free binary search.  Chunks past the plan load through the
+        // out-of-range offset (zeros) into the last chunk of the slot, so the
+        // copy loop has no branches: a branch would make the compiler wait for
+        // every load in flight before the next one.
         const float inv_sy = 1.0f / (float)span[1];
         uint32_t goff[EMAX], loff[EMAX];
 #pragma unroll
         for (int e = 0; e < EMAX; ++e) {
             const int c = t + e * kBlock;
-            const int rr = div_small(c, nx, inv_nx);
-            const int cx = c - rr * nx;
-            int z = 0, y = rr;
+            int r = 0;
+#pragma unroll
+            for (int step = MAXR / 2; step > 0; step >>= 1)
+                if (row_base[r + step] <= c) r += step;
+            const int cx = c - row_base[r];
+            int z = 0, y = r;
             if (R == 3) {
-                z = div_small(rr, span[1], inv_sy);
-                y = rr - z * span[1];
+                z = div_small(r, span[1], inv_sy);
+                y = r - z * span[1];
             }
-            const bool in_box = c < nchunks;
-            goff[e] = in_box ? (uint32_t)((((lo[2] + z) * p.in_h + lo[1] + y) * p.in_w + xa + cx * CH) *
-                                          T::bytes)
-                             : GS_OOB;
-            loff[e] = (uint32_t)(in_box ? c * CH : LIMIT) * T::bytes;
+            const bool in_plan = c < total_chunks;
+            goff[e] = in_plan ? (uint32_t)((((lo[2] + z) * p.in_h + lo[1] + y) * p.in_w + row_xs[r] +
+                                            cx * CH) *
+                                           T::bytes)
+                              : GS_OOB;
+            loff[e] = (uint32_t)(in_plan ? c * CH : LIMIT) * T::bytes;
         }
         if (t < U) lds[t * CAP + ZERO] = 0;
 
@@ -550,12 +612,9 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
         }
     } else {
         // ------------------------------------------------- direct gather
-        {
-            const int base[3] = {0, 0, 0};
-            const uint32_t stride[3] = {(uint32_t)T::bytes, (uint32_t)(p.in_w * T::bytes),
-                                        (uint32_t)(p.in_w * p.in_h * T::bytes)};
-            build_offsets(base, stride, GS_OOB, 0xFFFFFFFFu);
-        }
+        build_offsets(
+            [&](int iz, int iy) { return ((R == 3 ? iz * p.in_h : 0) + iy) * p.in_w * T::bytes; },
+            T::bytes, GS_OOB);
         constexpr int UD = SEPARABLE ? 1 : (MODE == MODE_NEAREST ? 8 : (TAPS * Q >= 16 ? 1 : 2));
         int c = cbeg;
         for (; c + UD <= cend; c += UD) {
@@ -618,15 +677,18 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
 // --------------------------------------------------------------- dispatch
 
 static dim3 launch_grid(int nblocks) { return dim3(8 * ((nblocks + 7) / 8)); }
+static dim3 launch_grid_runs(int nblocks) {
+    return dim3(8 * kRun * ((nblocks + 8 * kRun - 1) / (8 * kRun)));
+}
 
 template <int R, bool FUSED, int MODE, int PAD, typename T>
 static int launch_one(const SampleParams &p, bool vec, hipStream_t s) {
     if (vec)
         hipLaunchKernelGGL((grid_sample_kernel<R, MODE, PAD, T, FUSED, true>),
-                           launch_grid(p.nblocks), dim3(kBlock), 0, s, p);
+                           launch_grid_runs(p.nblocks), dim3(kBlock), 0, s, p);
     else
         hipLaunchKernelGGL((grid_sample_kernel<R, MODE, PAD, T, FUSED, false>),
-                           launch_grid(p.nblocks), dim3(kBlock), 0, s, p);
+                           launch_grid_runs(p.nblocks), dim3(kBlock), 0, s, p);
     return (int)hipGetLastError();
 }
 
