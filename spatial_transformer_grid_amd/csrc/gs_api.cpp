@@ -15,16 +15,6 @@ constexpr int64_t kInt32Max = 0x7fffffff;
 constexpr int kBlockThreads = 256;
 constexpr int64_t kTargetBlocks = 2048;
 
-void tile_geometry(int r, int mode, int *w, int *h, int *d, int *q) {
-    if (r == 2 && mode != GS_MODE_CUBIC) {
-        *w = gs::Geo<2, 0>::w, *h = gs::Geo<2, 0>::h, *d = gs::Geo<2, 0>::d, *q = gs::Geo<2, 0>::Q;
-    } else if (r == 2) {
-        *w = gs::Geo<2, 2>::w, *h = gs::Geo<2, 2>::h, *d = gs::Geo<2, 2>::d, *q = gs::Geo<2, 2>::Q;
-    } else {
-        *w = gs::Geo<3, 0>::w, *h = gs::Geo<3, 0>::h, *d = gs::Geo<3, 0>::d, *q = gs::Geo<3, 0>::Q;
-    }
-}
-
 int elem_bytes(int dtype) { return dtype == GS_F32 ? 4 : 2; }
 
 bool valid_x_dtype(int d) { return d == GS_F32 || d == GS_F16 || d == GS_BF16; }
@@ -79,8 +69,9 @@ int sample(int r, const void *theta, const void *X, int x_dtype, const int64_t *
     if (in_count == 0) return GS_ERR_SHAPE;
     if (!X || !Y || (!grid && !theta)) return GS_ERR_NULL;
     const Extents in = spatial3(x_shape + 2, r), out = spatial3(out_sp, r);
-    int tw, th, td, q;
-    tile_geometry(r, mode, &tw, &th, &td, &q);
+    int tw, th, td;
+    gs::tile_shape(r, mode, out.w, &tw, &th, &td);
+    const int q = mode == GS_MODE_CUBIC ? 1 : (r == 2 ? 4 : 2);
     const int64_t tiles_w = (out.w + tw - 1) / tw, tiles_h = (out.h + th - 1) / th,
                   tiles_d = (out.d + td - 1) / td;
     const int64_t tiles = tiles_w * tiles_h * tiles_d;
@@ -112,6 +103,11 @@ int sample(int r, const void *theta, const void *X, int x_dtype, const int64_t *
     p.in_plane_bytes = (uint32_t)(in_count * bytes);
     p.out_plane_bytes = (uint32_t)(out_count * bytes);
     p.align_corners = align_corners;
+    p.tile_w = tw;
+    p.tile_h = th;
+    p.tile_d = td;
+    p.lanes_row_log2 = __builtin_ctz((unsigned)(tw / q));
+    p.tile_h_log2 = __builtin_ctz((unsigned)th);
     p.tiles_w = (int)tiles_w;
     p.tiles_h = (int)tiles_h;
     p.tiles_d = (int)tiles_d;
@@ -120,6 +116,7 @@ int sample(int r, const void *theta, const void *X, int x_dtype, const int64_t *
     p.cpg = (int)cpg;
     p.nblocks = (int)(N * groups * tiles);
     p.vec_out = q > 1 && out.w % q == 0 && (uintptr_t)Y % (uintptr_t)(q * bytes) == 0;
+    p.vec_grid = r == 2 && q == 4 && grid != nullptr && out.w % 4 == 0 && (uintptr_t)grid % 16 == 0;
     return hip_status(gs::launch_grid_sample(p, r, theta != nullptr, mode, padding, x_dtype,
                                              vec_in, (hipStream_t)stream));
 }

@@ -7,7 +7,9 @@
 // uses explicit fmaf where it wants one.
 //
 // Memory: X and Y are addressed through raw buffer resources, one per
-// (image, channel) plane, with num_records = plane bytes.  A tap whose
+// (image, channel) plane, with num_records = plane bytes.  Y is written once
+// and never read back, so its stores are non-temporal (they stream through L2
+// without displacing the input rows that neighbouring tiles still need).  A tap whose
 // location is outside the image gets the offset GS_OOB (>= any plane size),
 // which the buffer unit turns into a read of 0 (zeros padding) or a dropped
 // store, without touching memory.
@@ -25,6 +27,7 @@ constexpr int kBlock = 256;              // threads per block: 4 wave64s
 constexpr uint32_t GS_OOB = 0x80000000u; // buffer offset that is always out of range
 constexpr float kCoordLimit = 16777216.0f;  // |p| clamp before float->int (2^24)
 constexpr float kCubicA = -0.75f;        // cubic convolution coefficient
+constexpr int kStoreNT = 2;              // buffer cache-policy bit: non-temporal
 
 // Word 3 of a gfx9-family buffer resource: 32-bit data format, no swizzle.
 constexpr int kRsrcWord3 = 0x00020000;
@@ -48,10 +51,10 @@ struct F32 {
         return __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
     }
     __device__ __forceinline__ static void store(float v, rsrc_t r, uint32_t off) {
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)off, 0, kStoreNT);
     }
     __device__ __forceinline__ static void store_raw(uint32_t v, rsrc_t r, uint32_t off) {
-        __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, kStoreNT);
     }
     __device__ __forceinline__ static float from_raw(uint32_t v) {
         return __builtin_bit_cast(float, v);
@@ -65,7 +68,7 @@ struct Half16Base {
         return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
     }
     __device__ __forceinline__ static void store_raw(uint16_t v, rsrc_t r, uint32_t off) {
-        __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(v, r, (int)off, 0, kStoreNT);
     }
 };
 

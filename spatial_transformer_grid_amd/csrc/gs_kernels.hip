@@ -220,20 +220,32 @@ __device__ __forceinline__ float interpolate(const uint32_t *off, const float *w
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 
-// Store the Q outputs of one lane for one channel: one 16-byte (fp32) or
-// 8-byte (fp16/bf16) store when the row layout allows it, else Q stores.
+// Store the Q outputs of one lane for one channel: one vector store of
+// Q elements when the row layout allows it, else Q stores.
 template <typename T, int Q>
 __device__ __forceinline__ void store_outputs(const typename T::raw_t (&v)[Q], rsrc_t yr,
                                               const uint32_t (&yoff)[Q], bool vec) {
+    if constexpr (Q == 2) {
+        if (vec) {
+            if constexpr (T::bytes == 4) {
+                u32x2 pk = {(uint32_t)v[0], (uint32_t)v[1]};
+                __builtin_amdgcn_raw_buffer_store_b64(pk, yr, (int)yoff[0], 0, kStoreNT);
+            } else {
+                __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v[0] | ((uint32_t)v[1] << 16), yr,
+                                                      (int)yoff[0], 0, kStoreNT);
+            }
+            return;
+        }
+    }
     if constexpr (Q == 4) {
         if (vec) {
             if constexpr (T::bytes == 4) {
                 u32x4 pk = {(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
-                __builtin_amdgcn_raw_buffer_store_b128(pk, yr, (int)yoff[0], 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(pk, yr, (int)yoff[0], 0, kStoreNT);
             } else {
                 u32x2 pk = {(uint32_t)v[0] | ((uint32_t)v[1] << 16),
                             (uint32_t)v[2] | ((uint32_t)v[3] << 16)};
-                __builtin_amdgcn_raw_buffer_store_b64(pk, yr, (int)yoff[0], 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b64(pk, yr, (int)yoff[0], 0, kStoreNT);
             }
             return;
         }
@@ -262,21 +274,19 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
     using G = Geo<R, MODE>;
     using raw_t = typename T::raw_t;
     constexpr int Q = G::Q;
-    constexpr int LPR = G::w / Q;  // lanes per output row of the tile
     constexpr int K = AxisK<MODE>::K;
     constexpr int TAPS = TapOffsets<R, K>::TAPS;
     constexpr bool SEPARABLE = MODE == MODE_CUBIC && R == 3;
     constexpr int NT = SEPARABLE ? 1 : TAPS;  // precomputed tap offsets / weights
-    // LDS staging: U channels of CAP elements; the last element of a slot is 0
-    constexpr int U = 2;
-    constexpr int CAP = 8192 / T::bytes;
+    // LDS staging: up to UMAX channel slots of SS elements in BUDGET elements;
+    // the last chunk of every slot holds zeros (the target of invalid taps)
+    constexpr int BUDGET = G::stage_bytes / T::bytes;
+    constexpr int UMAX = 8;
     constexpr int CH = VEC ? 16 / T::bytes : 1;  // elements per staging chunk
-    constexpr int EMAX = (CAP / CH + kBlock - 1) / kBlock;
-    constexpr int ZERO = CAP - 1;
-    constexpr int LIMIT = CAP - CH;  // staged elements end before the zero chunk
+    constexpr int EMAX = (BUDGET / CH + kBlock - 1) / kBlock;  // chunks per thread
     typedef typename std::conditional<VEC, u32x4, raw_t>::type chunk_t;
-    constexpr int MAXR = 128;  // input rows (z, y) a staged tile may span
-    __shared__ __align__(16) raw_t lds[U * CAP];
+    constexpr int MAXR = 256;  // input rows (z, y) a staged tile may span
+    __shared__ __align__(16) raw_t lds[BUDGET];
     __shared__ int red[kBlock / 64][2 * R];
     __shared__ int row_lo[MAXR], row_hi[MAXR], row_xs[MAXR], row_base[MAXR + 1];
 
@@ -290,9 +300,10 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
     const int ty = (tile / p.tiles_w) % p.tiles_h;
     const int tz = tile / (p.tiles_w * p.tiles_h);
     const int t = threadIdx.x;
-    const int ox0 = tx * G::w + (t % LPR) * Q;
-    const int oy = ty * G::h + (t / LPR) % G::h;
-    const int oz = tz * G::d + t / (LPR * G::h);
+    const int lrl = p.lanes_row_log2, thl = p.tile_h_log2;
+    const int ox0 = tx * p.tile_w + (t & ((1 << lrl) - 1)) * Q;
+    const int oy = ty * p.tile_h + ((t >> lrl) & ((1 << thl) - 1));
+    const int oz = tz * p.tile_d + (t >> (lrl + thl));
     const int ac = p.align_corners;
     const int ext[3] = {p.in_w, p.in_h, p.in_d};
 
@@ -300,6 +311,28 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
     bool live[Q];
     uint32_t yoff[Q];
     AxisTaps<K> ax[Q][R];
+    float gq[Q][R];
+    if constexpr (!FUSED && R == 2 && Q == 4) {
+        if (p.vec_grid) {
+            // the lane's 4 grid vectors are 32 contiguous, 32-byte aligned bytes
+            const int cy = min(oy, p.out_h - 1);
+            const int bx = min(ox0, p.out_w - 4);
+            const float4 *g4 = reinterpret_cast<const float4 *>(
+                p.grid + ((size_t)n * p.out_count + (uint32_t)cy * (uint32_t)p.out_w + bx) * 2);
+            const float4 a = g4[0], b = g4[1];
+            gq[0][0] = a.x, gq[0][1] = a.y, gq[1][0] = a.z, gq[1][1] = a.w;
+            gq[2][0] = b.x, gq[2][1] = b.y, gq[3][0] = b.z, gq[3][1] = b.w;
+        } else {
+#pragma unroll
+            for (int q = 0; q < Q; ++q) {
+                const int cx = min(ox0 + q, p.out_w - 1), cy = min(oy, p.out_h - 1);
+                const float *gp =
+                    p.grid + ((size_t)n * p.out_count + (uint32_t)cy * (uint32_t)p.out_w + cx) * 2;
+                gq[q][0] = gp[0];
+                gq[q][1] = gp[1];
+            }
+        }
+    }
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         const int ox = ox0 + q;
@@ -312,6 +345,9 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
         if constexpr (FUSED) {
             affine_vector<R>(p.theta + (size_t)n * R * (R + 1), cz, cy, cx, p.out_d, p.out_h,
                              p.out_w, ac, g);
+        } else if constexpr (R == 2 && Q == 4) {
+            g[0] = gq[q][0];
+            g[1] = gq[q][1];
         } else {
             const float *gp = p.grid + ((size_t)n * p.out_count + l) * R;
 #pragma unroll
@@ -372,9 +408,9 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
     const int64_t nrows = (int64_t)span[1] * span[2];
     int total_chunks = INT_MAX;
     if (tile_any && nrows <= MAXR) {
-        if (t < MAXR) {
-            row_lo[t] = INT_MAX;
-            row_hi[t] = INT_MIN;
+        for (int r = t; r < MAXR; r += kBlock) {
+            row_lo[r] = INT_MAX;
+            row_hi[r] = INT_MIN;
         }
         __syncthreads();
 #pragma unroll
@@ -401,31 +437,45 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
         }
         __syncthreads();
         if (t < 64) {
-            // chunks per row, two rows per lane, and a wave-wide prefix sum
-            const int r0 = 2 * t, r1 = 2 * t + 1;
-            const bool e0 = r0 < nrows && row_hi[r0] >= row_lo[r0];
-            const bool e1 = r1 < nrows && row_hi[r1] >= row_lo[r1];
-            const int xs0 = e0 ? (row_lo[r0] & ~(CH - 1)) : 0;
-            const int xs1 = e1 ? (row_lo[r1] & ~(CH - 1)) : 0;
-            const int c0 = e0 ? (row_hi[r0] - xs0 + CH) / CH : 0;
-            const int c1 = e1 ? (row_hi[r1] - xs1 + CH) / CH : 0;
-            int incl = c0 + c1;
+            // chunks per row, MAXR / 64 consecutive rows per lane, and a
+            // wave-wide prefix sum
+            constexpr int RPL = MAXR / 64;
+            int cnt[RPL], xs[RPL], sum = 0;
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+                const int r = RPL * t + i;
+                const bool e = r < nrows && row_hi[r] >= row_lo[r];
+                xs[i] = e ? (row_lo[r] & ~(CH - 1)) : 0;
+                cnt[i] = e ? (row_hi[r] - xs[i] + CH) / CH : 0;
+                sum += cnt[i];
+            }
+            int incl = sum;
 #pragma unroll
             for (int d = 1; d < 64; d <<= 1) {
                 const int v = __shfl_up(incl, d, 64);
                 if (t >= d) incl += v;
             }
-            const int excl = incl - c0 - c1;
-            row_base[r0] = excl;
-            row_base[r1] = excl + c0;
-            row_xs[r0] = xs0;
-            row_xs[r1] = xs1;
+            int run = incl - sum;
+#pragma unroll
+            for (int i = 0; i < RPL; ++i) {
+                row_base[RPL * t + i] = run;
+                row_xs[RPL * t + i] = xs[i];
+                run += cnt[i];
+            }
             if (t == 63) row_base[MAXR] = incl;
         }
         __syncthreads();
         total_chunks = __builtin_amdgcn_readfirstlane(row_base[MAXR]);
     }
-    const bool staged = (int64_t)total_chunks * CH <= LIMIT;
+    // slot stride: the plan plus one zero chunk; as many channels per LDS fill
+    // as the budget holds (the next fill is in flight while one is read)
+    const int SS = total_chunks < BUDGET ? (total_chunks + 1) * CH : INT_MAX;
+    const bool staged = SS <= BUDGET;
+    int U = 1;
+    if (staged) {
+        U = min(UMAX, BUDGET / SS);
+        U = (int)min<int64_t>(U, (int64_t)0x7fffffff / p.in_plane_bytes);
+    }
 
     // ---- tap weights
     float w[Q][NT];
@@ -510,23 +560,29 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
 
     if (staged) {
         // ------------------------------------------------ staged in LDS
-        // LDS element offset of pixel x of row r: row_base[r] * CH - row_xs[r] + x
+        // LDS element offset of pixel x of row r within a slot:
+        // row_base[r] * CH - row_xs[r] + x; invalid taps read the zero chunk
         build_offsets(
             [&](int iz, int iy) {
                 const int r = (R == 3 ? (iz - lo[2]) * span[1] : 0) + iy - lo[1];
                 return row_base[r] * CH - row_xs[r];
             },
-            1, (uint32_t)ZERO);
-        // this thread's chunks: chunk c = t + e * 256, found in the row table by
-        // a branch-free binary search.  Chunks past the plan load through the
-        // out-of-range offset (zeros) into the last chunk of the slot, so the
-        // copy loop has no branches: a branch would make the compiler wait for
+            1, (uint32_t)(SS - 1));
+        // this thread's copy items: item i = t + e * 256 is chunk c of channel
+        // slot u, i = u * total_chunks + c; c is found in the row table by a
+        // branch-free binary search.  Items past the plan load through the
+        // out-of-range offset (zeros) into slot 0's zero chunk, so the copy
+        // loop has no branches: a branch would make the compiler wait for
         // every load in flight before the next one.
+        const int nitems = U * total_chunks;
+        const float inv_tc = 1.0f / (float)total_chunks;
         const float inv_sy = 1.0f / (float)span[1];
         uint32_t goff[EMAX], loff[EMAX];
 #pragma unroll
         for (int e = 0; e < EMAX; ++e) {
-            const int c = t + e * kBlock;
+            const int i = t + e * kBlock;
+            const int u = div_small(i, total_chunks, inv_tc);
+            const int c = i - u * total_chunks;
             int r = 0;
 #pragma unroll
             for (int step = MAXR / 2; step > 0; step >>= 1)
@@ -537,63 +593,61 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
                 z = div_small(r, span[1], inv_sy);
                 y = r - z * span[1];
             }
-            const bool in_plan = c < total_chunks;
-            goff[e] = in_plan ? (uint32_t)((((lo[2] + z) * p.in_h + lo[1] + y) * p.in_w + row_xs[r] +
-                                            cx * CH) *
-                                           T::bytes)
+            const bool in_plan = i < nitems;
+            goff[e] = in_plan ? (uint32_t)u * p.in_plane_bytes +
+                                    (uint32_t)((((lo[2] + z) * p.in_h + lo[1] + y) * p.in_w +
+                                                row_xs[r] + cx * CH) *
+                                               T::bytes)
                               : GS_OOB;
-            loff[e] = (uint32_t)(in_plan ? c * CH : LIMIT) * T::bytes;
+            loff[e] = (uint32_t)(in_plan ? u * SS + c * CH : SS - CH) * T::bytes;
         }
-        if (t < U) lds[t * CAP + ZERO] = 0;
+        // zero chunk at the end of every slot
+        if (t < U) {
+            if constexpr (VEC) {
+                *(chunk_t *)(lds + t * SS + SS - CH) = chunk_t{0u, 0u, 0u, 0u};
+            } else {
+                lds[t * SS + SS - CH] = 0;
+            }
+        }
 
         auto load_chunk = [&](rsrc_t r, uint32_t o) -> chunk_t {
             if constexpr (VEC) return __builtin_amdgcn_raw_buffer_load_b128(r, (int)o, 0, 0);
             else return T::load_raw(r, o);
         };
-        chunk_t pre[U][EMAX];
+        // one resource spans the fill's channels; items of channels past the
+        // group's end fall outside it and read zeros
+        chunk_t pre[EMAX];
         auto prefetch = [&](int c0) {
+            const rsrc_t r = make_rsrc(xn + (size_t)c0 * ip, (uint32_t)min(U, cend - c0) * ip);
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = c0 + u;
-                const bool has = c < cend;
-                const rsrc_t r = make_rsrc(xn + (size_t)(has ? c : cbeg) * ip, ip);
-#pragma unroll
-                for (int e = 0; e < EMAX; ++e) pre[u][e] = load_chunk(r, has ? goff[e] : GS_OOB);
-            }
+            for (int e = 0; e < EMAX; ++e) pre[e] = load_chunk(r, goff[e]);
         };
         prefetch(cbeg);
         for (int c0 = cbeg; c0 < cend; c0 += U) {
-            __syncthreads();  // the previous chunk's LDS reads are done
+            __syncthreads();  // the previous fill's LDS reads are done
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int e = 0; e < EMAX; ++e)
-                    *(chunk_t *)((char *)(lds + u * CAP) + loff[e]) = pre[u][e];
-            __syncthreads();  // this chunk is in LDS
+            for (int e = 0; e < EMAX; ++e) *(chunk_t *)((char *)lds + loff[e]) = pre[e];
+            __syncthreads();  // this fill is in LDS
             if (c0 + U < cend) prefetch(c0 + U);
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
+            const int nv = min(U, cend - c0);
+            for (int u = 0; u < nv; ++u) {
                 const int c = c0 + u;
-                const bool has = c < cend;
-                const raw_t *s = lds + u * CAP;
-                const rsrc_t yr = make_rsrc(yn + (size_t)(has ? c : cbeg) * op, op);
+                const raw_t *sl = lds + u * SS;
+                const rsrc_t yr = make_rsrc(yn + (size_t)c * op, op);
                 raw_t v[Q];
-                uint32_t yo[Q];
-#pragma unroll
-                for (int q = 0; q < Q; ++q) yo[q] = has ? yoff[q] : GS_OOB;
                 if constexpr (SEPARABLE) {
 #pragma unroll
                     for (int q = 0; q < Q; ++q)
                         v[q] = to_raw<T>(interpolate<R, MODE, T>(
-                            off[q], w[q], row[q], col[q], wz[q], wy[q], wx[q], (uint32_t)ZERO,
-                            [&](uint32_t o) { return s[o]; }));
+                            off[q], w[q], row[q], col[q], wz[q], wy[q], wx[q], (uint32_t)(SS - 1),
+                            [&](uint32_t o) { return sl[o]; }));
                 } else {
                     // all LDS reads of the channel first, then the arithmetic
                     raw_t tv[Q][TAPS];
 #pragma unroll
                     for (int q = 0; q < Q; ++q)
 #pragma unroll
-                        for (int tap = 0; tap < TAPS; ++tap) tv[q][tap] = s[off[q][tap]];
+                        for (int tap = 0; tap < TAPS; ++tap) tv[q][tap] = sl[off[q][tap]];
 #pragma unroll
                     for (int q = 0; q < Q; ++q) {
                         if constexpr (MODE == MODE_NEAREST) {
@@ -607,7 +661,7 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
                         }
                     }
                 }
-                store_outputs<T, Q>(v, yr, yo, vec_out);
+                store_outputs<T, Q>(v, yr, yoff, vec_out);
             }
         }
     } else {

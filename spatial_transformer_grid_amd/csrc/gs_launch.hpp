@@ -32,23 +32,43 @@ struct SampleParams {
     uint32_t in_plane_bytes;   // in_d * in_h * in_w * sizeof(T)   (<= 2^30)
     uint32_t out_plane_bytes;  // out_count * sizeof(T)            (<= 2^30)
     int align_corners;
+    int tile_w, tile_h, tile_d;     // output tile of one block (powers of two)
+    int lanes_row_log2;             // log2(tile_w / Q): lanes per tile row
+    int tile_h_log2;                // log2(tile_h)
     int tiles_w, tiles_h, tiles_d;  // output tiles per image along W, H, D
     int tiles_per_n;           // tiles_w * tiles_h * tiles_d
     int cgroups, cpg;          // channel groups per image, channels per group
     int nblocks;               // N * cgroups * tiles_per_n
     int vec_out;               // Y rows allow one vector store per lane
+    int vec_grid;              // 2D grid rows allow 16-byte loads of 4 vectors
 };
 
-// Output tile of one 256-thread block and the number Q of consecutive
-// outputs (along W) each lane owns.  2D nearest / linear: 32 x 32 outputs,
-// 4 per lane; 2D cubic: 16 x 16, 1 per lane; 3D: 8 x 8 x 4, 1 per lane.
+// Outputs per lane Q (consecutive along W) and the LDS bytes for staging.
+// Nearest / linear: 4 outputs per lane in 2D, 2 in 3D; cubic: 1.
 template <int R, int MODE>
 struct Geo {
-    static constexpr int Q = (R == 2 && MODE != 2) ? 4 : 1;
-    static constexpr int w = R == 2 ? (Q == 4 ? 32 : 16) : 8;
-    static constexpr int h = R == 2 ? (Q == 4 ? 32 : 16) : 8;
-    static constexpr int d = R == 2 ? 1 : 4;
+    static constexpr int Q = MODE == 2 ? 1 : (R == 2 ? 4 : 2);
+    static constexpr int stage_bytes = 16384;
 };
+
+// Output tile of a 256-thread block: 2D nearest / linear 128 x 8 when an
+// output row fits in 128 locations (no tile boundary crosses the rows the
+// block reads), else 64 x 16, and 32 x 32 for rows of at most 32; 2D cubic
+// 16 x 16; 3D nearest / linear 16 x 8 x 4; 3D cubic 8 x 8 x 4.  Chosen by
+// measurement on the workloads the library is tuned for.
+inline void tile_shape(int r, int mode, int out_w, int *w, int *h, int *d) {
+    if (r == 2 && mode != 2) {
+        *w = out_w > 128 ? 64 : (out_w > 64 ? 128 : (out_w > 32 ? 64 : 32));
+        *h = 1024 / *w;
+        *d = 1;
+    } else if (r == 2) {
+        *w = 16, *h = 16, *d = 1;
+    } else if (mode != 2) {
+        *w = 16, *h = 8, *d = 4;
+    } else {
+        *w = 8, *h = 8, *d = 4;
+    }
+}
 
 // Elements per 16-byte chunk of the LDS staging copy.
 inline int stage_chunk_elems(int elem_bytes) { return 16 / elem_bytes; }
