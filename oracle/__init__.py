@@ -1,14 +1,15 @@
-"""Plain CPU reference (oracle) for AffineGrid and GridSample.
+"""Plain CPU reference (oracle) for AffineGrid, GridSample and Resize.
 
 TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
 CPU-baseline leg may import this package.  The GPU library and its Python
 binding never import it, and it never imports them.
 
-The arithmetic lives in ``oracle.c`` (plain scalar C, built with gcc
-``-O2 -ffp-contract=off``); this module only builds it, loads it and marshals
-numpy arrays.  Attribute names and defaults follow the GridSample page
-(mode "linear", padding_mode "zeros"; align_corners 0, the value every example
-that omits it behaves as).
+The arithmetic lives in ``oracle.c`` (AffineGrid, GridSample) and
+``resize.c`` (Resize), plain scalar C built with gcc ``-O2 -ffp-contract=off``;
+this module only builds them, loads them and marshals numpy arrays.
+Attribute names and defaults follow the GridSample page (mode "linear",
+padding_mode "zeros"; align_corners 0, the value every example that omits it
+behaves as) and the Resize page.
 """
 
 from __future__ import annotations
@@ -22,10 +23,15 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
+_RESIZE_SRC = os.path.join(_HERE, "resize.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 MODES = {"linear": 0, "nearest": 1, "cubic": 2}
 PADDINGS = {"zeros": 0, "border": 1, "reflection": 2}
+RESIZE_MODES = {"nearest": 0, "linear": 1, "cubic": 2}
+COORD_MODES = {"half_pixel": 0, "pytorch_half_pixel": 1, "align_corners": 2, "asymmetric": 3}
+NEAREST_MODES = {"round_prefer_floor": 0, "round_prefer_ceil": 1, "floor": 2, "ceil": 3}
+ASPECT_POLICIES = {"stretch": 0, "not_larger": 1, "not_smaller": 2}
 
 _lock = threading.Lock()
 _default = None
@@ -34,13 +40,15 @@ _default = None
 # against another build of the oracle source (used by the mutation tests).
 
 
-def build(force: bool = True, src: str = _SRC, out: str = _LIB) -> str:
-    """Compile oracle.c (or another copy of it) into a shared library."""
+def build(force: bool = True, src: str = _SRC, out: str = _LIB,
+          resize_src: str = _RESIZE_SRC) -> str:
+    """Compile oracle.c and resize.c (or other copies of them) into one shared
+    library."""
     if not force and os.path.exists(out):
         return out
     tmp = out + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
-           "-Wall", "-Wextra", "-o", tmp, src, "-lm"]
+           "-Wall", "-Wextra", "-o", tmp, src, resize_src, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
@@ -61,6 +69,12 @@ def _bind(path: str):
                                               c_int, c_int, c_int, p_i64, i64, p_f64]
     lib.oracle_grid_sample_points.restype = c_int
     lib.oracle_abi_version.restype = c_int
+    lib.oracle_resize.argtypes = [p_f32, c_int, p_i64, p_i64, p_f32, c_int, c_int, c_int,
+                                  ctypes.c_double, c_int, p_f64]
+    lib.oracle_resize.restype = c_int
+    lib.oracle_resize_output_shape.argtypes = [c_int, p_i64, c_int, p_i64, p_f32, p_i64, c_int,
+                                               c_int, p_i64]
+    lib.oracle_resize_output_shape.restype = c_int
     return lib
 
 
@@ -154,4 +168,70 @@ def grid_sample_points(X: np.ndarray, grid: np.ndarray, flat_index: np.ndarray,
                                        _ptr(Y, ctypes.c_double))
     if rc:
         raise ValueError("oracle_grid_sample_points rejected its arguments")
+    return Y
+
+
+def _axes_list(rank, count, axes):
+    if axes is None:
+        if count != rank:
+            raise ValueError("%d values for a tensor of rank %d and no axes" % (count, rank))
+        return list(range(rank))
+    return [int(a) for a in axes]
+
+
+def resize_output_shape(in_shape, scales=None, sizes=None, axes=None,
+                        keep_aspect_ratio_policy: str = "stretch", lib=None):
+    """Output extents of Resize from scales or sizes (exactly one given)."""
+    lib = lib or _load()
+    if (scales is None) == (sizes is None):
+        raise ValueError("give exactly one of scales and sizes")
+    in_shape = np.asarray(in_shape, dtype=np.int64)
+    rank = in_shape.shape[0]
+    vals = scales if scales is not None else sizes
+    ax = np.asarray(_axes_list(rank, len(vals), axes), dtype=np.int64)
+    sc = np.asarray(scales if scales is not None else [0.0] * len(vals), dtype=np.float32)
+    sz = np.asarray(sizes if sizes is not None else [0] * len(vals), dtype=np.int64)
+    out = np.empty(rank, dtype=np.int64)
+    rc = lib.oracle_resize_output_shape(rank, _ptr(in_shape, ctypes.c_int64), len(vals),
+                                        _ptr(ax, ctypes.c_int64), _ptr(sc, ctypes.c_float),
+                                        _ptr(sz, ctypes.c_int64), int(sizes is not None),
+                                        ASPECT_POLICIES[keep_aspect_ratio_policy],
+                                        _ptr(out, ctypes.c_int64))
+    if rc:
+        raise ValueError("oracle_resize_output_shape rejected its arguments")
+    return tuple(int(v) for v in out)
+
+
+def resize(X: np.ndarray, out_shape, scales=None, mode: str = "nearest",
+           coordinate_transformation_mode: str = "half_pixel",
+           nearest_mode: str = "round_prefer_floor", cubic_coeff_a: float = -0.75,
+           exclude_outside: int = 0, lib=None) -> np.ndarray:
+    """Resize(X) -> Y as float64 (unrounded).
+
+    out_shape: extents of Y (one per axis of X).  scales: per-axis scale used
+    by the coordinate transformation (one per axis), or None when the output
+    came from sizes (then each axis uses output extent / input extent).
+    Attribute names and defaults follow the Resize page (version 18).
+    """
+    lib = lib or _load()
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    rank = X.ndim
+    in_sp = np.asarray(X.shape, dtype=np.int64)
+    out_sp = np.asarray([int(v) for v in out_shape], dtype=np.int64)
+    if out_sp.shape[0] != rank:
+        raise ValueError("out_shape %s does not match X %s" % (tuple(out_sp), X.shape))
+    sc = None
+    if scales is not None:
+        sc = np.ascontiguousarray(scales, dtype=np.float32)
+        if sc.shape != (rank,):
+            raise ValueError("need one scale per axis")
+    Y = np.empty(tuple(out_sp), dtype=np.float64)
+    rc = lib.oracle_resize(_ptr(X, ctypes.c_float), rank, _ptr(in_sp, ctypes.c_int64),
+                           _ptr(out_sp, ctypes.c_int64),
+                           _ptr(sc, ctypes.c_float) if sc is not None else None,
+                           RESIZE_MODES[mode], COORD_MODES[coordinate_transformation_mode],
+                           NEAREST_MODES[nearest_mode], float(cubic_coeff_a),
+                           int(exclude_outside), _ptr(Y, ctypes.c_double))
+    if rc:
+        raise ValueError("oracle_resize rejected its arguments")
     return Y

@@ -6,9 +6,8 @@ the build container) and writes, next to this script:
   affine_grid_examples.json  -- the four worked examples of the AffineGrid page
   grid_sample_examples.json  -- the eighteen worked examples of the
                                 "GridSample - version 20" page
-  resize_examples.json       -- the Resize (version 18) cubic and linear
-                                examples whose printed outputs are used as
-                                border-padded sampling cross-checks
+  resize_examples.json       -- the Resize (version 18) examples, all but
+                                the antialias and tf_crop_and_resize ones
 
 Only numbers the pages print are stored (inputs, attributes, printed outputs),
 each with the page title and example name it came from.  Nothing here computes
@@ -124,21 +123,10 @@ def grid_sample_examples(lines):
     return out
 
 
-# Resize examples used as cross-checks: the cubic and linear ones with the
-# default cubic coefficient, exclude_outside=0 and no roi.
-RESIZE_NAMES = [
-    "test_resize_upsample_scales_cubic",
-    "test_resize_upsample_scales_cubic_align_corners",
-    "test_resize_downsample_scales_cubic",
-    "test_resize_downsample_scales_cubic_align_corners",
-    "test_resize_upsample_sizes_cubic",
-    "test_resize_downsample_sizes_cubic",
-    "test_resize_upsample_scales_cubic_asymmetric",
-    "test_resize_upsample_scales_linear",
-    "test_resize_upsample_scales_linear_align_corners",
-    "test_resize_downsample_scales_linear",
-    "test_resize_downsample_scales_linear_align_corners",
-]
+# Resize examples: every one on the page except the antialias and
+# tf_crop_and_resize ones (other filters and a region of interest, outside
+# what the library implements).
+RESIZE_SKIP = ("antialias", "tf_crop_and_resize")
 
 
 def bracket_block(s: str, i: int):
@@ -153,27 +141,45 @@ def bracket_block(s: str, i: int):
     raise ValueError("unbalanced brackets")
 
 
+def nested_shape(txt: str):
+    """Shape of a printed nested list (rows may wrap)."""
+    depth = txt[:txt.index(next(c for c in txt if c.isdigit() or c == "-"))].count("[")
+    rows = re.findall(r"\[([^\[\]]+)\]", txt)
+    return [1] * (depth - 2) + [len(rows), len(numbers(rows[0]))]
+
+
 def resize_examples(lines):
     # The Resize version 18 section is collapsed onto one very long line.
     text = page_text(lines, "page 2 of 5", "page 3 of 5")
     line = max(text, key=len)
+    heads = [(m.start(), m.group(1)) for m in re.finditer(r"\*\*_(resize_\w+)\*\*", line)]
     out = []
-    for name in RESIZE_NAMES:
-        short = name[len("test"):]
-        head = line.index("**" + short + "**")
-        nxt = line.find("**_resize", head + 5)
-        block = line[head: nxt if nxt > 0 else len(line)]
-        if ('name="%s"' % name) not in block:
+    for k, (head, short) in enumerate(heads):
+        name = "test_" + short
+        if any(tag in name for tag in RESIZE_SKIP):
+            continue
+        end = heads[k + 1][0] if k + 1 < len(heads) else len(line)
+        block = line[head:end]
+        # Examples are keyed by their heading; the listing's own test name is
+        # kept too (on the page the not_smaller upsample listing repeats the
+        # not_larger name).
+        listed = re.findall(r'name="(test_resize_\w+)"', block)
+        if len(listed) != 1:
             raise ValueError("example %s not delimited as expected" % name)
-        mode = re.search(r'mode="(\w+)"', block).group(1)
-        ctm = re.search(r'coordinate_transformation_mode="(\w+)"', block)
-        ctm = ctm.group(1) if ctm else "half_pixel"
+        node = block[block.index("make_node("):block.index("data = np.array(")]
+        attr = {}
+        for key in ("mode", "coordinate_transformation_mode", "nearest_mode"):
+            m = re.search(r'\b%s="(\w+)"' % key, node)
+            attr[key] = m.group(1) if m else None
+        m = re.search(r"cubic_coeff_a=(-?[\d.]+)", node)
+        attr["cubic_coeff_a"] = float(m.group(1)) if m else None
+        attr["exclude_outside"] = 1 if re.search(r"exclude_outside=(True|1)", node) else 0
+        m = re.search(r"axes = \[([^\]]*)\]", block)
+        attr["axes"] = [int(v) for v in numbers(m.group(1))] if m else None
+        m = re.search(r'keep_aspect_ratio_policy = "(\w+)"', block)
+        attr["keep_aspect_ratio_policy"] = m.group(1) if m else None
         d0 = block.index("data = np.array(") + len("data = np.array(")
         data_txt, _ = bracket_block(block, block.index("[", d0))
-        data = numbers(data_txt)
-        depth = data_txt[:data_txt.index(next(c for c in data_txt if c.isdigit()))].count("[")
-        rows = re.findall(r"\[([^\[\]]+)\]", data_txt)
-        data_shape = [1] * (depth - 2) + [len(rows), len(numbers(rows[0]))]
         scales = sizes = None
         m = re.search(r"scales = np\.array\(\[([^\]]*)\]", block)
         if m:
@@ -184,15 +190,19 @@ def resize_examples(lines):
         # the printed expected output is the commented block before "output ="
         c0 = block.index("# [[[[")
         c1 = block.index("output =", c0)
-        expected = numbers(block[c0:c1].replace("#", " "))
+        printed = block[c0:c1].replace("#", " ")
+        exp_txt, _ = bracket_block(printed, printed.index("["))
+        # the aspect-ratio examples also state the output extents in words
+        m = re.search(r"# Results in (\d+)x(\d+)", block)
+        attr["results_in"] = [int(m.group(1)), int(m.group(2))] if m else None
         out.append({
             "name": name,
             "citation": "Resize page (mlprodict, version 18), Examples: " + name,
-            "mode": mode,
-            "coordinate_transformation_mode": ctm,
-            "data_shape": data_shape, "data": data,
+            "listing_name": listed[0],
+            **attr,
+            "data_shape": nested_shape(data_txt), "data": numbers(data_txt),
             "scales": scales, "sizes": sizes,
-            "expected": expected,
+            "expected_shape": nested_shape(exp_txt), "expected": numbers(exp_txt),
         })
     return out
 

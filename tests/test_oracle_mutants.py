@@ -17,7 +17,7 @@ import pytest
 
 from conftest import ROOT, load_golden
 from test_oracle_bruteforce import brute_force
-from test_oracle_pages import resize_as_sampling_grid
+from test_oracle_pages import RESIZE_SAMPLING, resize_as_sampling_grid
 
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 
@@ -70,7 +70,7 @@ def pin_battery(om, lib):
         ref = np.array(ex["Y"]).reshape(ex["Y_shape"])
         if (np.abs(Y - ref) / np.maximum(1, np.abs(ref))).max() > 2e-6:
             return ex["name"]
-    for ex in load_golden("resize_examples.json"):
+    for ex in RESIZE_SAMPLING:
         data, G = resize_as_sampling_grid(ex)
         Y = om.grid_sample(data, G, ex["mode"], "border", 0, lib=lib)
         ref = np.array(ex["expected"]).reshape(Y.shape)
