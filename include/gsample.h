@@ -8,7 +8,9 @@
  *   (version 22 adds bfloat16)
  * plus their composition as the grid generator and sampler of a spatial
  * transformer (GridSample page, Summary), fused into one pass that never
- * writes the grid: gs_affine_grid_sample_fused.
+ * writes the grid: gs_affine_grid_sample_fused; and the axis-aligned special
+ * case of the sampler, the "Resize" operator (version 18): gs_resize and
+ * gs_resize_output_shape.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -146,6 +148,108 @@ int gs_grid_sample_3d(const void *X, int x_dtype, const int64_t *x_shape, const 
 int gs_affine_grid_sample_fused(const void *theta, int theta_dtype, const void *X, int x_dtype,
                                 const int64_t *x_shape, int x_rank, const int64_t *out_spatial,
                                 int mode, int padding, int align_corners, void *Y, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Resize (Resize page, version 18), without antialias and without
+ * tf_crop_and_resize (no region of interest).
+ * --------------------------------------------------------------------- */
+
+/* Attributes, mode: nearest (the default), linear (N-linear), cubic (N-cubic). */
+typedef enum { GS_RESIZE_NEAREST = 0, GS_RESIZE_LINEAR = 1, GS_RESIZE_CUBIC = 2 } gs_resize_mode;
+
+/* Attributes, coordinate_transformation_mode (half_pixel is the default):
+ * the location x_original of output index x along an axis with input extent
+ * n, scale s and length_resized L:
+ *   half_pixel          (x + 0.5) / s - 0.5
+ *   pytorch_half_pixel  L > 1 ? (x + 0.5) / s - 0.5 : 0
+ *   align_corners       L > 1 ? x * (n - 1) / (L - 1) : 0
+ *   asymmetric          x / s
+ * computed in fp32, one rounded operation at a time, left to right. */
+typedef enum {
+    GS_CT_HALF_PIXEL = 0,
+    GS_CT_PYTORCH_HALF_PIXEL = 1,
+    GS_CT_ALIGN_CORNERS = 2,
+    GS_CT_ASYMMETRIC = 3
+} gs_coord_mode;
+
+/* Attributes, nearest_mode (round_prefer_floor is the default): halfway
+ * locations go down, halfway locations go up, floor, ceil.  The index is
+ * then clamped into [0, n-1]. */
+typedef enum {
+    GS_NEAREST_ROUND_PREFER_FLOOR = 0,
+    GS_NEAREST_ROUND_PREFER_CEIL = 1,
+    GS_NEAREST_FLOOR = 2,
+    GS_NEAREST_CEIL = 3
+} gs_nearest_mode;
+
+/* Attributes, keep_aspect_ratio_policy (stretch is the default). */
+typedef enum {
+    GS_ASPECT_STRETCH = 0,
+    GS_ASPECT_NOT_LARGER = 1,
+    GS_ASPECT_NOT_SMALLER = 2
+} gs_aspect_policy;
+
+/*
+ * Output extents of Resize (Resize page, Summary; Inputs scales / sizes;
+ * Attributes axes and keep_aspect_ratio_policy).  Host only, launches nothing.
+ *
+ *   x_shape, rank  host, the input extents (1 <= rank <= 8).
+ *   axes, count    host, the axes that scales / sizes refer to (count
+ *                  entries, negative values count from the back, no
+ *                  repeats); axes NULL means all axes in order (count ==
+ *                  rank).  Other axes keep their extent.
+ *   scales         host, count scales (> 0), or NULL.  Extent =
+ *                  floor(extent * scale), evaluated in double precision.
+ *   sizes          host, count sizes (>= 0), or NULL.  With policy stretch
+ *                  the extents are the sizes; not_larger / not_smaller take
+ *                  one scale, the min / max over the listed axes of
+ *                  size / extent, and give round-half-up(scale * extent).
+ *   y_shape        host, rank entries, written on success.
+ *
+ * Exactly one of scales and sizes is given.  Errors: GS_ERR_NULL (x_shape or
+ * y_shape NULL, or neither scales nor sizes), GS_ERR_SHAPE (rank or count out
+ * of range, bad or repeated axis, negative extent or size), GS_ERR_ATTR (both
+ * scales and sizes, a scale not finite and > 0, policy out of range).
+ */
+int gs_resize_output_shape(const int64_t *x_shape, int rank, const int64_t *axes, int count,
+                           const float *scales, const int64_t *sizes, int keep_aspect_ratio_policy,
+                           int64_t *y_shape);
+
+/*
+ * Resize (Resize page, Summary: every output element is a weighted average
+ * of sampling locations of the input; Attributes as the enums above).
+ *
+ *   X            device, the input, rank axes with extents x_shape, element
+ *                type x_dtype (GS_F32, GS_F16, GS_BF16).
+ *   x_shape, rank  host, 1 <= rank <= 8.
+ *   y_shape      host, rank entries: the output extents (for instance from
+ *                gs_resize_output_shape).  Only the last three axes may be
+ *                resized; every other axis must keep its extent (and scale 1).
+ *   scales       host, rank per-axis scales (finite, > 0) when the extents
+ *                came from scales, or NULL when they came from sizes.  With
+ *                scales, axis a uses s = scales[a] and L = x_shape[a] * s
+ *                (fp32, unfloored); without, s = y/x extent (fp32) and L = y
+ *                extent.
+ *   mode, coordinate_transformation_mode, nearest_mode   the enums above.
+ *   cubic_coeff_a  the cubic convolution coefficient a (finite; the page's
+ *                default is -0.75).
+ *   exclude_outside  0: locations beyond the input take the edge element;
+ *                1: their weight is 0 and the remaining weights along that
+ *                axis are renormalised to sum 1.
+ *   Y            device, extents y_shape, element type x_dtype, written whole.
+ *
+ * Linear and cubic accumulate in fp32 axis by axis (x innermost); nearest
+ * copies the selected element bit for bit.  Errors: GS_ERR_NULL, GS_ERR_SHAPE
+ * (rank out of range, negative extent, a resized axis before the last three,
+ * a zero input extent with a non-empty output), GS_ERR_DTYPE, GS_ERR_ATTR (an
+ * enum out of range, exclude_outside not 0/1, cubic_coeff_a or a scale not
+ * finite, a scale <= 0), GS_ERR_TOO_LARGE (the product of the leading axes
+ * above 2^31-1, an input or output plane of the resized axes above 2^28
+ * elements, more than 2^24 thread blocks), GS_ERR_HIP.
+ */
+int gs_resize(const void *X, int x_dtype, const int64_t *x_shape, int rank, const int64_t *y_shape,
+              const float *scales, int mode, int coordinate_transformation_mode, int nearest_mode,
+              float cubic_coeff_a, int exclude_outside, void *Y, void *stream);
 
 #ifdef __cplusplus
 }

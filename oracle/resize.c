@@ -60,6 +60,12 @@
 
 #define RZ_MAX_RANK 8
 
+/* Magnitude beyond which a location is clamped before any float->int
+ * conversion (only reachable with extreme scales; every such location lies
+ * far outside any supported extent, so the clamped tap index is the same).
+ * A memory-safety reading; the page says nothing about it. */
+#define RZ_COORD_LIMIT 16777216.0f
+
 /* Output extents from scales or sizes (Summary; keep_aspect_ratio_policy).
  * `axes` lists the axes that `values` refer to (count entries); other axes
  * keep their extent.  use_sizes=0: values are scales (float), extent =
@@ -161,6 +167,7 @@ static int64_t clamp_index(int64_t i, int64_t n)
 static void axis_taps(float p, int64_t n, int mode, int nearest_mode, double a,
                       int exclude_outside, rz_taps *t)
 {
+    p = p < -RZ_COORD_LIMIT ? -RZ_COORD_LIMIT : (p > RZ_COORD_LIMIT ? RZ_COORD_LIMIT : p);
     if (mode == RZ_MODE_NEAREST) {
         float q;
         switch (nearest_mode) {

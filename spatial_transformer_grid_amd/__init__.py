@@ -1,9 +1,9 @@
 """spatial_transformer_grid_amd -- MI355X-native spatial-transformer sampler.
 
 Python face of libgsample (include/gsample.h): the grid generator
-(AffineGrid), the 2D/3D sampler (GridSample) and their fused composition, all
-computed by hand-written HIP kernels for gfx950.  Tensors are torch GPU
-tensors; torch supplies device memory and streams only.
+(AffineGrid), the 2D/3D sampler (GridSample), their fused composition and
+Resize, all computed by hand-written HIP kernels for gfx950.  Tensors are
+torch GPU tensors; torch supplies device memory and streams only.
 
     from spatial_transformer_grid_amd import affine_grid, grid_sample
     grid = affine_grid(theta, (N, C, H, W), align_corners=0)
@@ -22,6 +22,10 @@ from ._binding import (  # noqa: F401
     affine_grid_sample_fused,
     grid_sample,
     lib,
+    resize,
+    resize_output_shape,
+    resize_to,
 )
 
-__all__ = ["affine_grid", "grid_sample", "affine_grid_sample_fused", "GSError", "lib"]
+__all__ = ["affine_grid", "grid_sample", "affine_grid_sample_fused", "resize",
+           "resize_output_shape", "resize_to", "GSError", "lib"]

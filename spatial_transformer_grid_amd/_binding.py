@@ -19,11 +19,16 @@ GS_OK, GS_ERR_NULL, GS_ERR_SHAPE, GS_ERR_DTYPE, GS_ERR_ATTR, GS_ERR_TOO_LARGE, G
 GS_F32, GS_F16, GS_BF16 = 0, 1, 2
 MODES = {"linear": 0, "bilinear": 0, "nearest": 1, "cubic": 2, "bicubic": 2}
 PADDINGS = {"zeros": 0, "border": 1, "reflection": 2}
+RESIZE_MODES = {"nearest": 0, "linear": 1, "cubic": 2}
+COORD_MODES = {"half_pixel": 0, "pytorch_half_pixel": 1, "align_corners": 2, "asymmetric": 3}
+NEAREST_MODES = {"round_prefer_floor": 0, "round_prefer_ceil": 1, "floor": 2, "ceil": 3}
+ASPECT_POLICIES = {"stretch": 0, "not_larger": 1, "not_smaller": 2}
 
 # C entry points and their argument types (mirrors include/gsample.h)
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _PI64 = ctypes.POINTER(ctypes.c_int64)
+_PF32 = ctypes.POINTER(ctypes.c_float)
 SIGNATURES = {
     "gs_abi_version": ([], _I),
     "gs_status_string": ([_I], ctypes.c_char_p),
@@ -31,6 +36,8 @@ SIGNATURES = {
     "gs_grid_sample_2d": ([_P, _I, _PI64, _P, _I, _PI64, _I, _I, _I, _P, _P], _I),
     "gs_grid_sample_3d": ([_P, _I, _PI64, _P, _I, _PI64, _I, _I, _I, _P, _P], _I),
     "gs_affine_grid_sample_fused": ([_P, _I, _P, _I, _PI64, _I, _PI64, _I, _I, _I, _P, _P], _I),
+    "gs_resize_output_shape": ([_PI64, _I, _PI64, _I, _PF32, _PI64, _I, _PI64], _I),
+    "gs_resize": ([_P, _I, _PI64, _I, _PI64, _PF32, _I, _I, _I, ctypes.c_float, _I, _P, _P], _I),
 }
 
 _lock = threading.Lock()
@@ -168,4 +175,70 @@ def affine_grid_sample_fused(theta, X, out_spatial, mode: str = "linear",
         MODES[mode], PADDINGS[padding_mode], int(align_corners),
         ctypes.c_void_p(Y.data_ptr()), _stream(stream, X.device))
     _check(st, "gs_affine_grid_sample_fused")
+    return Y
+
+
+def resize_output_shape(x_shape, scales=None, sizes=None, axes=None,
+                        keep_aspect_ratio_policy: str = "stretch"):
+    """Output extents of Resize from scales or sizes (gs_resize_output_shape)."""
+    x_shape = [int(v) for v in x_shape]
+    vals = scales if scales is not None else sizes
+    if vals is None:
+        raise ValueError("give scales or sizes")
+    count = len(vals)
+    ax = int64_array(axes) if axes is not None else None
+    sc = (ctypes.c_float * max(1, count))(*[float(v) for v in scales]) if scales is not None else None
+    sz = int64_array(sizes) if sizes is not None else None
+    out = (ctypes.c_int64 * len(x_shape))()
+    st = lib().gs_resize_output_shape(int64_array(x_shape), len(x_shape), ax, count, sc, sz,
+                                      ASPECT_POLICIES[keep_aspect_ratio_policy], out)
+    _check(st, "gs_resize_output_shape")
+    return tuple(int(v) for v in out)
+
+
+def resize(X, scales=None, sizes=None, axes=None, mode: str = "nearest",
+           coordinate_transformation_mode: str = "half_pixel",
+           nearest_mode: str = "round_prefer_floor", cubic_coeff_a: float = -0.75,
+           exclude_outside: int = 0, keep_aspect_ratio_policy: str = "stretch", out=None,
+           stream=None):
+    """Resize(X, scales | sizes) -> Y on the GPU (gs_resize).
+
+    Attribute names and defaults follow the Resize page (version 18); scales
+    or sizes refer to `axes` (all axes when None)."""
+    X = _device_tensor(X, "X")
+    rank = X.dim()
+    shape = resize_output_shape(X.shape, scales, sizes, axes, keep_aspect_ratio_policy)
+    full = None
+    if scales is not None:
+        per_axis = [1.0] * rank
+        for i, v in enumerate(scales):
+            a = int(axes[i]) if axes is not None else i
+            per_axis[a % rank] = float(v)
+        full = (ctypes.c_float * rank)(*per_axis)
+    Y = _out_tensor(out, shape, X)
+    st = lib().gs_resize(ctypes.c_void_p(X.data_ptr()), dtype_code(X), int64_array(X.shape), rank,
+                         int64_array(shape), full, RESIZE_MODES[mode],
+                         COORD_MODES[coordinate_transformation_mode], NEAREST_MODES[nearest_mode],
+                         float(cubic_coeff_a), int(exclude_outside),
+                         ctypes.c_void_p(Y.data_ptr()), _stream(stream, X.device))
+    _check(st, "gs_resize")
+    return Y
+
+
+def resize_to(X, y_shape, scales=None, mode: str = "nearest",
+              coordinate_transformation_mode: str = "half_pixel",
+              nearest_mode: str = "round_prefer_floor", cubic_coeff_a: float = -0.75,
+              exclude_outside: int = 0, out=None, stream=None):
+    """gs_resize with explicit output extents and per-axis scales (or None)."""
+    X = _device_tensor(X, "X")
+    rank = X.dim()
+    y_shape = [int(v) for v in y_shape]
+    full = (ctypes.c_float * rank)(*[float(v) for v in scales]) if scales is not None else None
+    Y = _out_tensor(out, y_shape, X)
+    st = lib().gs_resize(ctypes.c_void_p(X.data_ptr()), dtype_code(X), int64_array(X.shape), rank,
+                         int64_array(y_shape), full, RESIZE_MODES[mode],
+                         COORD_MODES[coordinate_transformation_mode], NEAREST_MODES[nearest_mode],
+                         float(cubic_coeff_a), int(exclude_outside),
+                         ctypes.c_void_p(Y.data_ptr()), _stream(stream, X.device))
+    _check(st, "gs_resize")
     return Y

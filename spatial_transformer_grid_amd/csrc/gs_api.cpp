@@ -5,6 +5,7 @@
 #include "gsample.h"
 #include "gs_launch.hpp"
 
+#include <math.h>
 #include <stdint.h>
 
 namespace {
@@ -135,6 +136,12 @@ int grid_sample_rank(int r, const void *X, int x_dtype, const int64_t *x_shape, 
                   align_corners, Y, stream);
 }
 
+// Axis index from a possibly negative `axes` entry; -1 when out of range.
+int norm_axis(int64_t a, int rank) {
+    if (a < 0) a += rank;
+    return a >= 0 && a < rank ? (int)a : -1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -217,6 +224,150 @@ int gs_affine_grid_sample_fused(const void *theta, int theta_dtype, const void *
     // a NULL theta with work to do is reported by sample() as GS_ERR_NULL
     return sample(r, theta, X, x_dtype, x_shape, nullptr, out_spatial, mode, padding,
                   align_corners, Y, stream);
+}
+
+int gs_resize_output_shape(const int64_t *x_shape, int rank, const int64_t *axes, int count,
+                           const float *scales, const int64_t *sizes, int keep_aspect_ratio_policy,
+                           int64_t *y_shape) {
+    if (!x_shape || !y_shape) return GS_ERR_NULL;
+    if (scales && sizes) return GS_ERR_ATTR;
+    if (!scales && !sizes) return GS_ERR_NULL;
+    if (rank < 1 || rank > 8 || count < 0 || count > rank || (!axes && count != rank))
+        return GS_ERR_SHAPE;
+    if (keep_aspect_ratio_policy < GS_ASPECT_STRETCH ||
+        keep_aspect_ratio_policy > GS_ASPECT_NOT_SMALLER)
+        return GS_ERR_ATTR;
+    int dims[8];
+    bool seen[8] = {false, false, false, false, false, false, false, false};
+    for (int i = 0; i < count; ++i) {
+        const int d = axes ? norm_axis(axes[i], rank) : i;
+        if (d < 0 || seen[d]) return GS_ERR_SHAPE;
+        seen[d] = true;
+        dims[i] = d;
+    }
+    for (int a = 0; a < rank; ++a)
+        if (x_shape[a] < 0) return GS_ERR_SHAPE;
+    int64_t out[8];
+    for (int a = 0; a < rank; ++a) out[a] = x_shape[a];
+    if (scales) {
+        for (int i = 0; i < count; ++i) {
+            if (!(scales[i] > 0.0f) || !isfinite(scales[i])) return GS_ERR_ATTR;
+            // Summary: floor(input extent * scale)
+            out[dims[i]] = (int64_t)floor((double)x_shape[dims[i]] * (double)scales[i]);
+        }
+    } else if (keep_aspect_ratio_policy == GS_ASPECT_STRETCH) {
+        for (int i = 0; i < count; ++i) {
+            if (sizes[i] < 0) return GS_ERR_SHAPE;
+            out[dims[i]] = sizes[i];
+        }
+    } else {
+        // one scale for every listed axis: the smallest (not_larger) or the
+        // largest (not_smaller) size / extent ratio
+        double s = 0.0;
+        for (int i = 0; i < count; ++i) {
+            if (sizes[i] < 0 || x_shape[dims[i]] == 0) return GS_ERR_SHAPE;
+            const double r = (double)sizes[i] / (double)x_shape[dims[i]];
+            const bool take = keep_aspect_ratio_policy == GS_ASPECT_NOT_LARGER ? r < s : r > s;
+            if (i == 0 || take) s = r;
+        }
+        for (int i = 0; i < count; ++i)
+            out[dims[i]] = (int64_t)floor(s * (double)x_shape[dims[i]] + 0.5);  // halfway up
+    }
+    for (int a = 0; a < rank; ++a) y_shape[a] = out[a];
+    return GS_OK;
+}
+
+int gs_resize(const void *X, int x_dtype, const int64_t *x_shape, int rank, const int64_t *y_shape,
+              const float *scales, int mode, int coordinate_transformation_mode, int nearest_mode,
+              float cubic_coeff_a, int exclude_outside, void *Y, void *stream) {
+    if (!x_shape || !y_shape) return GS_ERR_NULL;
+    if (rank < 1 || rank > 8) return GS_ERR_SHAPE;
+    if (!valid_x_dtype(x_dtype)) return GS_ERR_DTYPE;
+    if (mode < GS_RESIZE_NEAREST || mode > GS_RESIZE_CUBIC) return GS_ERR_ATTR;
+    if (coordinate_transformation_mode < GS_CT_HALF_PIXEL ||
+        coordinate_transformation_mode > GS_CT_ASYMMETRIC)
+        return GS_ERR_ATTR;
+    if (nearest_mode < GS_NEAREST_ROUND_PREFER_FLOOR || nearest_mode > GS_NEAREST_CEIL)
+        return GS_ERR_ATTR;
+    if ((exclude_outside != 0 && exclude_outside != 1) || !isfinite(cubic_coeff_a))
+        return GS_ERR_ATTR;
+    for (int a = 0; a < rank; ++a) {
+        if (x_shape[a] < 0 || y_shape[a] < 0) return GS_ERR_SHAPE;
+        if (scales && (!(scales[a] > 0.0f) || !isfinite(scales[a]))) return GS_ERR_ATTR;
+    }
+    // the resized axes: from the outermost axis that changes to the last
+    int first = rank - 1;
+    for (int a = 0; a < rank; ++a)
+        if (y_shape[a] != x_shape[a] || (scales && scales[a] != 1.0f)) {
+            first = a;
+            break;
+        }
+    if (first < rank - 3) return GS_ERR_SHAPE;
+    const int s = rank - first;  // 1, 2 or 3 spatial axes
+    int64_t planes = 0, in_count = 0, out_count = 0;
+    if (!product_within(x_shape, first, kInt32Max, &planes)) return GS_ERR_TOO_LARGE;
+    if (!product_within(x_shape + first, s, kPlaneLimit, &in_count)) return GS_ERR_TOO_LARGE;
+    if (!product_within(y_shape + first, s, kPlaneLimit, &out_count)) return GS_ERR_TOO_LARGE;
+    if (planes == 0 || out_count == 0) return GS_OK;
+    if (in_count == 0) return GS_ERR_SHAPE;
+    if (!X || !Y) return GS_ERR_NULL;
+
+    gs::ResizeParams p;
+    p.X = X;
+    p.Y = Y;
+    p.P = (int)planes;
+    for (int k = 0; k < 3; ++k) {
+        // k = 0 is the last axis (W), 1 is H, 2 is D
+        gs::ResizeAxis &ax = p.ax[k];
+        const int a = rank - 1 - k;
+        if (k >= s) {
+            ax.n = ax.m = 1;
+            ax.scale = ax.lr = 1.0f;
+            continue;
+        }
+        ax.n = (int)x_shape[a];
+        ax.m = (int)y_shape[a];
+        if (scales) {
+            ax.scale = scales[a];
+            ax.lr = (float)ax.n * ax.scale;
+        } else {
+            ax.scale = (float)ax.m / (float)ax.n;
+            ax.lr = (float)ax.m;
+        }
+    }
+    p.ct = coordinate_transformation_mode;
+    p.nearest_mode = nearest_mode;
+    p.exclude_outside = exclude_outside;
+    p.cubic_a = cubic_coeff_a;
+    const int bytes = elem_bytes(x_dtype);
+    p.in_plane_bytes = (uint32_t)(in_count * bytes);
+    p.out_plane_bytes = (uint32_t)(out_count * bytes);
+    const bool d3 = s == 3;
+    // the kernel's mode numbering is the enum's
+    const int q = d3 ? (mode == GS_RESIZE_CUBIC ? 1 : 2) : 4;
+    int tw, th;
+    gs::resize_tile_shape(q, p.ax[0].m, p.ax[1].m, &tw, &th);
+    p.tile_w = tw;
+    p.tile_h = th;
+    p.lanes_row_log2 = __builtin_ctz((unsigned)(tw / q));
+    const int64_t tiles_w = (p.ax[0].m + tw - 1) / tw, tiles_h = (p.ax[1].m + th - 1) / th;
+    const int64_t tiles = tiles_w * tiles_h * p.ax[2].m;
+    if (tiles > kMaxBlocks) return GS_ERR_TOO_LARGE;
+    int64_t groups = (kTargetBlocks + tiles - 1) / tiles;
+    if (groups > planes) groups = planes;
+    if (groups < 1) groups = 1;
+    const int64_t ppg = (planes + groups - 1) / groups;
+    groups = (planes + ppg - 1) / ppg;
+    if (groups * tiles > kMaxBlocks) return GS_ERR_TOO_LARGE;
+    p.tiles_w = (int)tiles_w;
+    p.tiles_h = (int)tiles_h;
+    p.tiles_per_plane = (int)tiles;
+    p.pgroups = (int)groups;
+    p.ppg = (int)ppg;
+    p.nblocks = (int)(groups * tiles);
+    p.vec_out = q > 1 && p.ax[0].m % q == 0 && (uintptr_t)Y % (uintptr_t)(q * bytes) == 0;
+    const bool vec_in = p.ax[0].n % gs::stage_chunk_elems(bytes) == 0 && (uintptr_t)X % 16 == 0;
+    return hip_status(gs::launch_resize(p, d3, mode, x_dtype, vec_in, (hipStream_t)stream));
 }
 
 }  // extern "C"

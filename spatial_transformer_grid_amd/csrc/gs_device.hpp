@@ -221,4 +221,85 @@ __device__ __forceinline__ int xcd_logical_block_runs(int nblocks) {
     return grp * (8 * kRun) + (r & 7) * kRun + (r >> 3);
 }
 
+
+// ------------------------------------------------------- block reduction
+
+template <int NV>
+__device__ __forceinline__ void block_min(int (&v)[NV], int (*red)[NV]) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) v[i] = min(v[i], __shfl_xor(v[i], off, 64));
+    const int wave = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0)
+#pragma unroll
+        for (int i = 0; i < NV; ++i) red[wave][i] = v[i];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        int m = red[0][i];
+#pragma unroll
+        for (int wv = 1; wv < kBlock / 64; ++wv) m = min(m, red[wv][i]);
+        v[i] = __builtin_amdgcn_readfirstlane(m);
+    }
+}
+
+// q = f / d for 0 <= f < 2^16, 1 <= d: fp32 estimate, then one correction.
+__device__ __forceinline__ int div_small(int f, int d, float inv_d) {
+    int q = (int)((float)f * inv_d);
+    int r = f - q * d;
+    q += (r < 0) ? -1 : (r >= d ? 1 : 0);
+    return q;
+}
+
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+// Store the Q outputs of one lane for one channel: one vector store of
+// Q elements when the row layout allows it, else Q stores.
+template <typename T, int Q>
+__device__ __forceinline__ void store_outputs(const typename T::raw_t (&v)[Q], rsrc_t yr,
+                                              const uint32_t (&yoff)[Q], bool vec) {
+    if constexpr (Q == 2) {
+        if (vec) {
+            if constexpr (T::bytes == 4) {
+                u32x2 pk = {(uint32_t)v[0], (uint32_t)v[1]};
+                __builtin_amdgcn_raw_buffer_store_b64(pk, yr, (int)yoff[0], 0, kStoreNT);
+            } else {
+                __builtin_amdgcn_raw_buffer_store_b32((uint32_t)v[0] | ((uint32_t)v[1] << 16), yr,
+                                                      (int)yoff[0], 0, kStoreNT);
+            }
+            return;
+        }
+    }
+    if constexpr (Q == 4) {
+        if (vec) {
+            if constexpr (T::bytes == 4) {
+                u32x4 pk = {(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
+                __builtin_amdgcn_raw_buffer_store_b128(pk, yr, (int)yoff[0], 0, kStoreNT);
+            } else {
+                u32x2 pk = {(uint32_t)v[0] | ((uint32_t)v[1] << 16),
+                            (uint32_t)v[2] | ((uint32_t)v[3] << 16)};
+                __builtin_amdgcn_raw_buffer_store_b64(pk, yr, (int)yoff[0], 0, kStoreNT);
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < Q; ++q) T::store_raw(v[q], yr, yoff[q]);
+}
+
+template <typename T>
+__device__ __forceinline__ typename T::raw_t to_raw(float v);
+template <>
+__device__ __forceinline__ uint32_t to_raw<F32>(float v) { return __builtin_bit_cast(uint32_t, v); }
+template <>
+__device__ __forceinline__ uint16_t to_raw<F16>(float v) {
+    return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+template <>
+__device__ __forceinline__ uint16_t to_raw<BF16>(float v) {
+    return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
 }  // namespace gs

@@ -86,11 +86,66 @@ struct AffineParams {
     uint32_t div_h_m, div_h_s;
 };
 
-// Launchers (gs_kernels.hip).  Return 0 on success or the hipError_t of the
+// One resized axis: input and output extent, the scale of the coordinate
+// transformation and length_resized (scale * input extent, or the output
+// extent when the extents came from sizes).
+struct ResizeAxis {
+    int n, m;
+    float scale, lr;
+};
+
+// One Resize launch over P planes of up to 3 resized trailing axes.
+struct ResizeParams {
+    const void *X;
+    void *Y;
+    int P;                     // planes: product of the leading (unresized) axes
+    ResizeAxis ax[3];          // W, H, D (extent 1 when absent)
+    int ct;                    // coordinate_transformation_mode 0..3
+    int nearest_mode;          // 0..3
+    int exclude_outside;       // 0 / 1
+    float cubic_a;
+    uint32_t in_plane_bytes, out_plane_bytes;  // each <= 2^30
+    int tile_w, tile_h;        // output tile of one block (tile_w / Q lanes per row)
+    int lanes_row_log2;
+    int tiles_w, tiles_h, tiles_per_plane;     // tiles_per_plane = tiles_w * tiles_h * D_out
+    int pgroups, ppg;          // plane groups, planes per group
+    int nblocks;               // pgroups * tiles_per_plane
+    int vec_out;               // Y rows allow one vector store per lane
+};
+
+// Outputs per lane and LDS staging bytes of the Resize kernel: 4 outputs per
+// lane when at most H and W are resized, 2 (nearest, linear) or 1 (cubic)
+// when D is resized too.
+template <int MODE, bool D3>
+struct RzGeo {
+    static constexpr int Q = D3 ? (MODE == 2 ? 1 : 2) : 4;
+    static constexpr int stage_bytes = 16384;
+};
+
+// Resize tile: 16 lanes per row (64 outputs at Q = 4), 32 for rows of 65..128
+// outputs, fewer for narrow rows; when the output has few rows the tile is
+// widened instead (a 1-D resize uses up to 256 lanes per row).
+inline void resize_tile_shape(int q, int out_w, int out_h, int *tw, int *th) {
+    int lanes = (q == 4 && out_w > 64 && out_w <= 128) ? 32 : 16;
+    while (lanes > 4 && (lanes / 2) * q >= out_w) lanes /= 2;
+    int h = 256 / lanes;
+    while (h > 1 && h / 2 >= out_h && lanes < 256) {
+        h /= 2;
+        lanes *= 2;
+    }
+    *tw = lanes * q;
+    *th = h;
+}
+
+// Launchers (gs_kernels.hip, gs_resize.hip).  Return 0 on success or the hipError_t of the
 // launch.  `rank` is 2 or 3; `dtype` 0 f32, 1 f16, 2 bf16; `vec_in` selects
 // 16-byte staging loads (input rows a whole number of 16-byte chunks).
 int launch_grid_sample(const SampleParams &p, int rank, bool fused, int mode, int padding,
                        int dtype, bool vec_in, hipStream_t stream);
 int launch_affine_grid(const AffineParams &p, int rank, hipStream_t stream);
+// `d3`: the third axis from the end is resized; `mode` 0 nearest, 1 linear,
+// 2 cubic.
+int launch_resize(const ResizeParams &p, bool d3, int mode, int dtype, bool vec_in,
+                  hipStream_t stream);
 
 }  // namespace gs

@@ -6,6 +6,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from conftest import ROOT
@@ -33,7 +34,7 @@ def declared_functions():
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "gs_abi_version", "gs_status_string", "gs_affine_grid", "gs_grid_sample_2d",
-        "gs_grid_sample_3d", "gs_affine_grid_sample_fused"])
+        "gs_grid_sample_3d", "gs_affine_grid_sample_fused", "gs_resize", "gs_resize_output_shape"])
 
 
 def test_library_exports_every_declared_symbol(gs):
@@ -144,3 +145,89 @@ def test_binding_refuses_host_tensors(gs):
 
     with pytest.raises(ValueError):
         grid_sample(torch.zeros(1, 1, 2, 2), torch.zeros(1, 2, 2, 2))
+
+
+def resize_call(gs, x_shape, y_shape, scales=None, X=FAKE, Y=FAKE, dt=0, mode=0, ct=0, nm=0,
+                a=-0.75, ex=0, rank=None):
+    lib = gs.lib()
+    sc = (ctypes.c_float * len(scales))(*scales) if scales is not None else None
+    return lib.gs_resize(X, dt, gs.int64_array(x_shape), len(x_shape) if rank is None else rank,
+                         gs.int64_array(y_shape), sc, mode, ct, nm, a, ex, Y, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dt=5), 3),
+    (dict(mode=3), 4),
+    (dict(ct=4), 4),
+    (dict(ct=-1), 4),
+    (dict(nm=4), 4),
+    (dict(ex=2), 4),
+    (dict(a=float("nan")), 4),
+    (dict(scales=[1.0, 1.0, 0.0, 2.0]), 4),
+    (dict(scales=[1.0, 1.0, float("inf"), 2.0]), 4),
+    (dict(rank=0), 2),
+    (dict(rank=9), 2),
+    (dict(X=None), 1),
+    (dict(Y=None), 1),
+])
+def test_resize_rejects(gs, kw, status):
+    assert resize_call(gs, [2, 3, 4, 5], [2, 3, 8, 10], **kw) == status
+
+
+def test_resize_shape_rules(gs):
+    # only the last three axes may change
+    assert resize_call(gs, [2, 3, 4, 5, 6], [4, 3, 4, 5, 6]) == 2
+    assert resize_call(gs, [2, 3, 4, 5, 6], [2, 3, 4, 5, 6], scales=[1.5, 1, 1, 1, 1]) == 2
+    assert resize_call(gs, [2, 3, -4, 5], [2, 3, 8, 10]) == 2
+    assert resize_call(gs, [2, 3, 0, 5], [2, 3, 8, 10]) == 2        # empty input, output not
+    assert resize_call(gs, [2, 3, 4, 5], [2, 3, 0, 10], X=None, Y=None) == 0
+    assert resize_call(gs, [0, 3, 4, 5], [0, 3, 8, 10], X=None, Y=None) == 0
+    assert resize_call(gs, [1, 1, 1 << 15, 1 << 14], [1, 1, 2, 2]) == 5
+
+
+def test_resize_output_shape_matches_oracle(gs, oracle_mod):
+    """The library's host shape rule (Summary, keep_aspect_ratio_policy)
+    agrees with the oracle's on the page examples and on random cases."""
+    from conftest import load_golden
+    from spatial_transformer_grid_amd import resize_output_shape
+
+    cases = []
+    for ex in load_golden("resize_examples.json"):
+        cases.append((ex["data_shape"], ex["scales"], ex["sizes"], ex["axes"],
+                      ex["keep_aspect_ratio_policy"] or "stretch"))
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        rank = int(rng.integers(1, 6))
+        shape = [int(v) for v in rng.integers(1, 40, rank)]
+        count = int(rng.integers(1, rank + 1))
+        axes = [int(a) for a in rng.permutation(rank)[:count]]
+        axes = [a - rank if rng.random() < 0.3 else a for a in axes]
+        if rng.random() < 0.5:
+            scales = [float(np.float32(v)) for v in rng.uniform(0.05, 4.0, count)]
+            cases.append((shape, scales, None, axes, "stretch"))
+        else:
+            sizes = [int(v) for v in rng.integers(0, 60, count)]
+            pol = ["stretch", "not_larger", "not_smaller"][int(rng.integers(0, 3))]
+            cases.append((shape, None, sizes, axes, pol))
+    for shape, sc, sz, axes, pol in cases:
+        ref = oracle_mod.resize_output_shape(shape, scales=sc, sizes=sz, axes=axes,
+                                             keep_aspect_ratio_policy=pol)
+        got = resize_output_shape(shape, sc, sz, axes, pol)
+        assert got == ref, (shape, sc, sz, axes, pol)
+
+
+def test_resize_output_shape_rejects(gs):
+    lib = gs.lib()
+    f = lambda xs, axes, sc=None, sz=None, pol=0, n=None: lib.gs_resize_output_shape(
+        gs.int64_array(xs), len(xs), gs.int64_array(axes) if axes is not None else None,
+        len(axes) if n is None and axes is not None else (n if n is not None else len(xs)),
+        (ctypes.c_float * 4)(*sc) if sc is not None else None,
+        gs.int64_array(sz) if sz is not None else None, pol, (ctypes.c_int64 * 8)())
+    assert f([2, 3], [0, 0], sc=[1, 1]) == 2          # repeated axis
+    assert f([2, 3], [0, 2], sc=[1, 1]) == 2          # axis out of range
+    assert f([2, 3], [0, 1], sc=[1, 1], sz=[1, 1]) == 4
+    assert f([2, 3], [0, 1]) == 1
+    assert f([2, 3], [0, 1], sc=[1, -1]) == 4
+    assert f([2, 3], [0, 1], sz=[1, -1]) == 2
+    assert f([2, 3], [0, 1], sz=[1, 1], pol=3) == 4
+    assert f([2, 3], None, sc=[1, 1], n=1) == 2       # no axes: one value per axis
