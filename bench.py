@@ -13,7 +13,8 @@ and Y) divided by its mean duration, measured with events on the launch stream
 inside the timed region.  `traffic` is the HBM byte count from rocprofv3
 counters (profiles/sampler_traffic.json) when those were taken on the current
 kernel source, else null.  `cpu_baseline` times the plain CPU oracle on the
-same workload.  `paths` reports the other workload shapes (kernel time only).
+same workload.  `paths` reports the other workload shapes, Resize included
+(kernel time only).
 """
 
 from __future__ import annotations
@@ -258,6 +259,24 @@ def run_paths(torch, gsa, flush_buf):
         us, _ = time_kernel(torch, lambda: gsa.grid_sample(X, G, "linear", "zeros", 0, out=Y), 20)
         record("flow2d_half/%s-linear-zeros" % kind, w.name, "gs_grid_sample_2d", us, w.outputs,
                X.numel() * 2, fp, G.numel() * 4 + w.outputs * 2)
+        del X, Y
+
+    # Resize workloads (fp32): at their scales every input element has a
+    # non-zero weight, so all of X is compulsory
+    for name, rw in W.RESIZE_WORKLOADS.items():
+        X = torch.from_numpy(W.make_resize_input(rw)).cuda()
+        rank = X.dim()
+        axes = list(range(rank - len(rw.scales), rank))
+        shape = gsa.resize_output_shape(X.shape, list(rw.scales), None, axes)
+        Y = torch.empty(shape, device="cuda")
+        scales = rw.full_scales()
+        fn = lambda: gsa.resize_to(X, shape, scales, rw.mode, rw.coordinate_transformation_mode,
+                                   out=Y)
+        fn()
+        us, _ = time_kernel(torch, fn, 20, flush)
+        warm, _ = time_kernel(torch, fn, 20)
+        record(name, name, "gs_resize", us, Y.numel(), X.numel() * 4, X.numel() * 4,
+               Y.numel() * 4, warm)
         del X, Y
     return out
 

@@ -75,6 +75,9 @@ def _bind(path: str):
     lib.oracle_resize_output_shape.argtypes = [c_int, p_i64, c_int, p_i64, p_f32, p_i64, c_int,
                                                c_int, p_i64]
     lib.oracle_resize_output_shape.restype = c_int
+    lib.oracle_resize_points.argtypes = [p_f32, c_int, p_i64, p_i64, p_f32, c_int, c_int, c_int,
+                                         ctypes.c_double, c_int, p_i64, i64, p_f64]
+    lib.oracle_resize_points.restype = c_int
     return lib
 
 
@@ -234,4 +237,29 @@ def resize(X: np.ndarray, out_shape, scales=None, mode: str = "nearest",
                            int(exclude_outside), _ptr(Y, ctypes.c_double))
     if rc:
         raise ValueError("oracle_resize rejected its arguments")
+    return Y
+
+
+def resize_points(X: np.ndarray, out_shape, flat_index: np.ndarray, scales=None,
+                  mode: str = "nearest", coordinate_transformation_mode: str = "half_pixel",
+                  nearest_mode: str = "round_prefer_floor", cubic_coeff_a: float = -0.75,
+                  exclude_outside: int = 0, lib=None) -> np.ndarray:
+    """Resize evaluated only at the listed flat indices of Y (float64)."""
+    lib = lib or _load()
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    rank = X.ndim
+    in_sp = np.asarray(X.shape, dtype=np.int64)
+    out_sp = np.asarray([int(v) for v in out_shape], dtype=np.int64)
+    sc = None if scales is None else np.ascontiguousarray(scales, dtype=np.float32)
+    idx = np.ascontiguousarray(flat_index, dtype=np.int64)
+    Y = np.empty(idx.shape[0], dtype=np.float64)
+    rc = lib.oracle_resize_points(_ptr(X, ctypes.c_float), rank, _ptr(in_sp, ctypes.c_int64),
+                                  _ptr(out_sp, ctypes.c_int64),
+                                  _ptr(sc, ctypes.c_float) if sc is not None else None,
+                                  RESIZE_MODES[mode], COORD_MODES[coordinate_transformation_mode],
+                                  NEAREST_MODES[nearest_mode], float(cubic_coeff_a),
+                                  int(exclude_outside), _ptr(idx, ctypes.c_int64), idx.shape[0],
+                                  _ptr(Y, ctypes.c_double))
+    if rc:
+        raise ValueError("oracle_resize_points rejected its arguments")
     return Y

@@ -220,6 +220,90 @@ static void axis_taps(float p, int64_t n, int mode, int nearest_mode, double a,
     }
 }
 
+typedef struct {
+    const float *X;
+    int rank;
+    const int64_t *in_shape, *out_shape;
+    float scale[RZ_MAX_RANK], length_resized[RZ_MAX_RANK];
+    int mode, ct, nearest_mode, exclude_outside;
+    double cubic_a;
+    int64_t out_count;
+} rz_problem;
+
+static int rz_setup(rz_problem *P, const float *X, int rank, const int64_t *in_shape,
+                    const int64_t *out_shape, const float *scales, int mode, int ct,
+                    int nearest_mode, double cubic_a, int exclude_outside)
+{
+    if (rank < 1 || rank > RZ_MAX_RANK || mode < 0 || mode > 2 || ct < 0 || ct > 3 ||
+        nearest_mode < 0 || nearest_mode > 3)
+        return -1;
+    P->X = X;
+    P->rank = rank;
+    P->in_shape = in_shape;
+    P->out_shape = out_shape;
+    P->mode = mode;
+    P->ct = ct;
+    P->nearest_mode = nearest_mode;
+    P->exclude_outside = exclude_outside;
+    P->cubic_a = cubic_a;
+    P->out_count = 1;
+    for (int a = 0; a < rank; ++a) {
+        if (in_shape[a] < 0 || out_shape[a] < 0 || (in_shape[a] == 0 && out_shape[a] > 0))
+            return -1;
+        P->out_count *= out_shape[a];
+        if (scales) {
+            P->scale[a] = scales[a];
+            P->length_resized[a] = (float)in_shape[a] * P->scale[a];
+        } else {
+            P->scale[a] = in_shape[a] > 0 ? (float)out_shape[a] / (float)in_shape[a] : 1.0f;
+            P->length_resized[a] = (float)out_shape[a];
+        }
+        if (!(P->scale[a] > 0.0f) || !isfinite(P->scale[a]))
+            return -1;
+    }
+    return 0;
+}
+
+/* Output element o (flat, row-major): the sum over the product of the
+ * per-axis taps of weight * X[taps]. */
+static double rz_value(const rz_problem *P, int64_t o)
+{
+    rz_taps taps[RZ_MAX_RANK];
+    int64_t o_idx[RZ_MAX_RANK];
+    int64_t rest = o;
+    for (int a = P->rank - 1; a >= 0; --a) { /* last axis fastest */
+        o_idx[a] = rest % P->out_shape[a];
+        rest /= P->out_shape[a];
+    }
+    for (int a = 0; a < P->rank; ++a) {
+        float p = original_coordinate(o_idx[a], P->scale[a], P->length_resized[a],
+                                      P->in_shape[a], P->ct);
+        axis_taps(p, P->in_shape[a], P->mode, P->nearest_mode, P->cubic_a, P->exclude_outside,
+                  &taps[a]);
+    }
+    int sel[RZ_MAX_RANK] = {0};
+    double acc = 0.0;
+    for (;;) {
+        double w = 1.0;
+        int64_t off = 0;
+        for (int a = 0; a < P->rank; ++a) {
+            w *= taps[a].weight[sel[a]];
+            off = off * P->in_shape[a] + taps[a].index[sel[a]];
+        }
+        acc += w * (double)P->X[off];
+        int a = P->rank - 1;
+        while (a >= 0) {
+            if (++sel[a] < taps[a].count)
+                break;
+            sel[a] = 0;
+            --a;
+        }
+        if (a < 0)
+            break;
+    }
+    return acc;
+}
+
 /*
  * Y = Resize(X): X has `rank` axes with extents in_shape, Y extents
  * out_shape (row-major, float64 output, every element written).
@@ -235,60 +319,31 @@ int oracle_resize(const float *X, int rank, const int64_t *in_shape, const int64
                   const float *scales, int mode, int ct, int nearest_mode, double cubic_a,
                   int exclude_outside, double *Y)
 {
-    if (rank < 1 || rank > RZ_MAX_RANK || mode < 0 || mode > 2 || ct < 0 || ct > 3 ||
-        nearest_mode < 0 || nearest_mode > 3)
+    rz_problem P;
+    if (rz_setup(&P, X, rank, in_shape, out_shape, scales, mode, ct, nearest_mode, cubic_a,
+                 exclude_outside))
         return -1;
-    int64_t out_count = 1;
-    float scale[RZ_MAX_RANK], length_resized[RZ_MAX_RANK];
-    for (int a = 0; a < rank; ++a) {
-        if (in_shape[a] < 0 || out_shape[a] < 0 || (in_shape[a] == 0 && out_shape[a] > 0))
+    for (int64_t o = 0; o < P.out_count; ++o)
+        Y[o] = rz_value(&P, o);
+    return 0;
+}
+
+/* As oracle_resize, only for the `count` outputs whose flat indices are listed
+ * in `flat`; the values go to Y[0..count).  Returns 0, or -1 on a bad argument
+ * or index. */
+int oracle_resize_points(const float *X, int rank, const int64_t *in_shape,
+                         const int64_t *out_shape, const float *scales, int mode, int ct,
+                         int nearest_mode, double cubic_a, int exclude_outside,
+                         const int64_t *flat, int64_t count, double *Y)
+{
+    rz_problem P;
+    if (rz_setup(&P, X, rank, in_shape, out_shape, scales, mode, ct, nearest_mode, cubic_a,
+                 exclude_outside))
+        return -1;
+    for (int64_t i = 0; i < count; ++i) {
+        if (flat[i] < 0 || flat[i] >= P.out_count)
             return -1;
-        out_count *= out_shape[a];
-        if (scales) {
-            scale[a] = scales[a];
-            length_resized[a] = (float)in_shape[a] * scale[a];
-        } else {
-            scale[a] = in_shape[a] > 0 ? (float)out_shape[a] / (float)in_shape[a] : 1.0f;
-            length_resized[a] = (float)out_shape[a];
-        }
-        if (!(scale[a] > 0.0f) || !isfinite(scale[a]))
-            return -1;
-    }
-    rz_taps taps[RZ_MAX_RANK];
-    int64_t o_idx[RZ_MAX_RANK];
-    for (int64_t o = 0; o < out_count; ++o) {
-        /* output multi-index, last axis fastest */
-        int64_t rest = o;
-        for (int a = rank - 1; a >= 0; --a) {
-            o_idx[a] = rest % out_shape[a];
-            rest /= out_shape[a];
-        }
-        for (int a = 0; a < rank; ++a) {
-            float p = original_coordinate(o_idx[a], scale[a], length_resized[a], in_shape[a], ct);
-            axis_taps(p, in_shape[a], mode, nearest_mode, cubic_a, exclude_outside, &taps[a]);
-        }
-        /* sum over the product of the per-axis taps */
-        int sel[RZ_MAX_RANK] = {0};
-        double acc = 0.0;
-        for (;;) {
-            double w = 1.0;
-            int64_t off = 0;
-            for (int a = 0; a < rank; ++a) {
-                w *= taps[a].weight[sel[a]];
-                off = off * in_shape[a] + taps[a].index[sel[a]];
-            }
-            acc += w * (double)X[off];
-            int a = rank - 1;
-            while (a >= 0) {
-                if (++sel[a] < taps[a].count)
-                    break;
-                sel[a] = 0;
-                --a;
-            }
-            if (a < 0)
-                break;
-        }
-        Y[o] = acc;
+        Y[i] = rz_value(&P, flat[i]);
     }
     return 0;
 }

@@ -46,3 +46,22 @@ def test_bench_refuses_more_than_one_gpu():
                        text=True)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+@pytest.mark.parametrize("name", list(__import__("workloads").RESIZE_WORKLOADS))
+def test_resize_workloads_read_every_input_element(oracle_mod, name):
+    """The benchmark counts all of X as compulsory for the Resize workloads:
+    at their scales every input element gets a non-zero weight (checked with
+    one-hot inputs on a reduced extent with the same scales)."""
+    import workloads as W
+
+    w = W.RESIZE_WORKLOADS[name]
+    r = len(w.scales)
+    ext = (6,) * r if r == 3 else (10, 12)
+    count = int(np.prod(ext))
+    X = np.eye(count, dtype=np.float32).reshape((count,) + ext)
+    shape = oracle_mod.resize_output_shape((count,) + ext, scales=list(w.scales),
+                                           axes=list(range(1, r + 1)))
+    Y = oracle_mod.resize(X, shape, [1.0] + list(w.scales), w.mode,
+                          w.coordinate_transformation_mode)
+    assert (np.abs(Y).reshape(count, -1).max(1) > 0).all()

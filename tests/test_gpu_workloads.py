@@ -1,4 +1,5 @@
-"""The five synthetic workloads on the GPU against the oracle.
+"""The synthetic workloads (five sampler, five Resize) on the GPU against the
+oracle.
 
 * reduced shapes (same distributions, several tiles, ragged tails): every
   output element is compared;
@@ -119,3 +120,51 @@ def test_workload_full_size_sampled(gsa, name, kind, mode, pad, ac, fused):
     del Y
     ref = oracle.grid_sample_points(Xin, oracle_grid(inp, ac), idx, mode, pad, ac)
     check(got, ref, mode, kind, np.abs(Xin).max(), "full " + name)
+
+
+# ------------------------------------------------------------------ Resize
+
+RESIZE_REDUCED = {
+    "resize2d_up2_linear": (3, 5, 37, 45),
+    "resize2d_up2_nearest": (3, 5, 37, 45),
+    "resize2d_up2_cubic": (3, 5, 37, 45),
+    "resize2d_down2_linear": (3, 5, 74, 90),
+    "resize3d_up2_linear": (2, 3, 9, 10, 11),
+}
+
+
+def resize_gpu(gsa, w, X):
+    """The call the benchmark makes (scales on the trailing axes)."""
+    rank = X.ndim
+    axes = list(range(rank - len(w.scales), rank))
+    return gsa.resize(x_to_gpu(X, "f32")[0], scales=list(w.scales), axes=axes, mode=w.mode,
+                      coordinate_transformation_mode=w.coordinate_transformation_mode)
+
+
+@pytest.mark.parametrize("name", list(W.RESIZE_WORKLOADS))
+def test_resize_workload_reduced_all_elements(gsa, name):
+    w = W.RESIZE_WORKLOADS[name]
+    X = W.make_resize_input(w, RESIZE_REDUCED[name])
+    note("reduced %s x=%s" % (name, X.shape))
+    Y = resize_gpu(gsa, w, X)
+    ref = oracle.resize(X, tuple(Y.shape), w.full_scales(), w.mode,
+                        w.coordinate_transformation_mode)
+    check(from_gpu(Y), ref, w.mode, "f32", np.abs(X).max(), name)
+
+
+@pytest.mark.parametrize("name", list(W.RESIZE_WORKLOADS))
+def test_resize_workload_full_size_sampled(gsa, name):
+    w = W.RESIZE_WORKLOADS[name]
+    note("full %s x=%s" % (name, w.x_shape))
+    X = W.make_resize_input(w)
+    Y = resize_gpu(gsa, w, X)
+    shape = tuple(Y.shape)
+    planes = int(np.prod(shape[:len(shape) - len(w.scales)]))
+    count = int(np.prod(shape[len(shape) - len(w.scales):]))
+    idx = sample_indices(planes, 1, count, 16384, w.seed)
+    torch = torch_mod()
+    got = from_gpu(Y.reshape(-1)[torch.from_numpy(idx).cuda()])
+    del Y
+    ref = oracle.resize_points(X, shape, idx, w.full_scales(), w.mode,
+                               w.coordinate_transformation_mode)
+    check(got, ref, w.mode, "f32", np.abs(X).max(), "full " + name)

@@ -286,8 +286,8 @@ RESIZE_MUTANTS = [
     ("align_corners divides by length_resized",
      "xf * (float)(n - 1) / (length_resized - 1.0f)", "xf * (float)(n - 1) / length_resized"),
     ("asymmetric multiplies by the scale", "return xf / scale;", "return xf * scale;"),
-    ("length_resized floored", "length_resized[a] = (float)in_shape[a] * scale[a];",
-     "length_resized[a] = floorf((float)in_shape[a] * scale[a]);"),
+    ("length_resized floored", "P->length_resized[a] = (float)in_shape[a] * P->scale[a];",
+     "P->length_resized[a] = floorf((float)in_shape[a] * P->scale[a]);"),
     ("scale from sizes inverted",
      "scale[a] = in_shape[a] > 0 ? (float)out_shape[a] / (float)in_shape[a] : 1.0f;",
      "scale[a] = out_shape[a] > 0 ? (float)in_shape[a] / (float)out_shape[a] : 1.0f;"),

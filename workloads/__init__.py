@@ -14,7 +14,8 @@ numpy has no bfloat16 type; :func:`half_bits_to_f32` widens them exactly.
 The five named workloads mirror the shapes and value distributions of the
 spatial-transformer use the GridSample page describes (an STN-style batch of
 near-identity affine transforms, a random flow field, a volumetric transform
-and a large smooth-flow half-precision batch).  The pages print no benchmark
+and a large smooth-flow half-precision batch).  The Resize workloads are
+feature-map sized up- and downsampling batches.  The pages print no benchmark
 and name no dataset; these synthetic inputs stand in for real images.
 """
 
@@ -38,6 +39,9 @@ __all__ = [
     "to_half_bits",
     "half_bits_to_f32",
     "make_inputs",
+    "ResizeWorkload",
+    "RESIZE_WORKLOADS",
+    "make_resize_input",
 ]
 
 
@@ -220,3 +224,42 @@ def make_inputs(w: Workload, x_shape=None, out_spatial=None):
             out["X_bits"][kind] = bits
             out["X_half_as_f32"][kind] = half_bits_to_f32(bits, kind)
     return out
+
+
+@dataclass(frozen=True)
+class ResizeWorkload:
+    """One named Resize input recipe: X ~ U(-1, 1) and per-axis scales of the
+    resized trailing axes (the output extents follow from them)."""
+
+    name: str
+    seed: int
+    x_shape: tuple
+    scales: tuple                # one per trailing resized axis
+    mode: str                    # "nearest" | "linear" | "cubic"
+    coordinate_transformation_mode: str = "half_pixel"
+
+    def full_scales(self):
+        lead = len(self.x_shape) - len(self.scales)
+        return [1.0] * lead + [float(v) for v in self.scales]
+
+
+RESIZE_WORKLOADS = {
+    # 2x upsampling of a batch of 64-channel 128x128 feature maps
+    "resize2d_up2_linear": ResizeWorkload("resize2d_up2_linear", 21, (32, 64, 128, 128),
+                                          (2.0, 2.0), "linear"),
+    "resize2d_up2_nearest": ResizeWorkload("resize2d_up2_nearest", 22, (32, 64, 128, 128),
+                                           (2.0, 2.0), "nearest"),
+    "resize2d_up2_cubic": ResizeWorkload("resize2d_up2_cubic", 23, (32, 64, 128, 128),
+                                         (2.0, 2.0), "cubic"),
+    # 2x downsampling of 256x256 maps
+    "resize2d_down2_linear": ResizeWorkload("resize2d_down2_linear", 24, (32, 64, 256, 256),
+                                            (0.5, 0.5), "linear"),
+    # 2x trilinear upsampling of 64^3 volumes
+    "resize3d_up2_linear": ResizeWorkload("resize3d_up2_linear", 25, (2, 16, 64, 64, 64),
+                                          (2.0, 2.0, 2.0), "linear"),
+}
+
+
+def make_resize_input(w: ResizeWorkload, x_shape=None) -> np.ndarray:
+    """X of a Resize workload (optionally at a reduced shape), fp32 U(-1, 1)."""
+    return uniform(rng(w.seed), tuple(x_shape or w.x_shape), -1.0, 1.0)
