@@ -344,7 +344,7 @@ int gs_resize(const void *X, int x_dtype, const int64_t *x_shape, int rank, cons
     p.out_plane_bytes = (uint32_t)(out_count * bytes);
     const bool d3 = s == 3;
     // the kernel's mode numbering is the enum's
-    const int q = d3 ? (mode == GS_RESIZE_CUBIC ? 1 : 2) : 4;
+    const int q = gs::resize_outputs_per_lane(d3, mode);
     int tw, th;
     gs::resize_tile_shape(q, p.ax[0].m, p.ax[1].m, &tw, &th);
     p.tile_w = tw;

@@ -113,12 +113,18 @@ struct ResizeParams {
     int vec_out;               // Y rows allow one vector store per lane
 };
 
-// Outputs per lane and LDS staging bytes of the Resize kernel: 4 outputs per
-// lane when at most H and W are resized, 2 (nearest, linear) or 1 (cubic)
-// when D is resized too.
+// Outputs per lane of the Resize kernel (mode 0 nearest, 1 linear, 2 cubic):
+// 4 (cubic 2) when at most H and W are resized, 2 (cubic 1) when D is resized
+// too.  Cubic holds 16 or 64 taps per output; fewer outputs per lane keep its
+// registers, and so its occupancy, in line (measured).
+constexpr int resize_outputs_per_lane(bool d3, int mode) {
+    return d3 ? (mode == 2 ? 1 : 2) : (mode == 2 ? 2 : 4);
+}
+
+// Outputs per lane and LDS staging bytes of the Resize kernel.
 template <int MODE, bool D3>
 struct RzGeo {
-    static constexpr int Q = D3 ? (MODE == 2 ? 1 : 2) : 4;
+    static constexpr int Q = resize_outputs_per_lane(D3, MODE);
     static constexpr int stage_bytes = 16384;
 };
 
