@@ -69,6 +69,13 @@ def _bind(path: str):
                                               c_int, c_int, c_int, p_i64, i64, p_f64]
     lib.oracle_grid_sample_points.restype = c_int
     lib.oracle_abi_version.restype = c_int
+    lib.oracle_grid_sample_ex.argtypes = [p_f32, p_f64, c_int, i64, i64, p_i64, p_f32, p_f64,
+                                          p_i64, c_int, c_int, c_int, p_f64]
+    lib.oracle_grid_sample_ex.restype = c_int
+    lib.oracle_grid_sample_points_ex.argtypes = [p_f32, p_f64, c_int, i64, i64, p_i64, p_f32,
+                                                 p_f64, p_i64, c_int, c_int, c_int, p_i64, i64,
+                                                 p_f64]
+    lib.oracle_grid_sample_points_ex.restype = c_int
     lib.oracle_resize.argtypes = [p_f32, c_int, p_i64, p_i64, p_f32, c_int, c_int, c_int,
                                   ctypes.c_double, c_int, p_f64]
     lib.oracle_resize.restype = c_int
@@ -122,20 +129,43 @@ def affine_grid(theta: np.ndarray, size, align_corners: int = 0, lib=None) -> np
 
 
 def _check_sample_args(X, grid):
-    X = np.ascontiguousarray(X, dtype=np.float32)
-    grid = np.ascontiguousarray(grid, dtype=np.float32)
+    """X as fp32 (fp32 and half inputs widened exactly) or float64 (double and
+    integer inputs); the grid as fp32 (fp32, fp16) or float64 (double)."""
+    X = np.asarray(X)
+    grid = np.asarray(grid)
+    if X.dtype in (np.float32, np.float16):
+        X = np.ascontiguousarray(X, dtype=np.float32)
+    else:
+        X = np.ascontiguousarray(X, dtype=np.float64)
+    if grid.dtype == np.float64:
+        grid = np.ascontiguousarray(grid)
+    elif grid.dtype in (np.float32, np.float16):
+        grid = np.ascontiguousarray(grid, dtype=np.float32)
+    else:
+        raise TypeError("grid must be a float tensor, got %s" % grid.dtype)
     r = X.ndim - 2
     if r < 1 or grid.ndim != r + 2 or grid.shape[0] != X.shape[0] or grid.shape[-1] != r:
         raise ValueError("X %s and grid %s do not match" % (X.shape, grid.shape))
     return X, grid, r
 
 
+def _xg_ptrs(X, grid):
+    xf = _ptr(X, ctypes.c_float) if X.dtype == np.float32 else None
+    xd = _ptr(X, ctypes.c_double) if X.dtype == np.float64 else None
+    gf = _ptr(grid, ctypes.c_float) if grid.dtype == np.float32 else None
+    gd = _ptr(grid, ctypes.c_double) if grid.dtype == np.float64 else None
+    return xf, xd, gf, gd
+
+
 def grid_sample(X: np.ndarray, grid: np.ndarray, mode: str = "linear",
                 padding_mode: str = "zeros", align_corners: int = 0, lib=None) -> np.ndarray:
     """GridSample(X, grid) -> Y as float64 (unrounded).
 
-    X: (N, C, *in_spatial) fp32 (half inputs are passed widened exactly).
-    grid: (N, *out_spatial, r) fp32.  Returns (N, C, *out_spatial) float64.
+    X: (N, C, *in_spatial), any rank r >= 1: fp32 (half inputs are passed
+    widened exactly), float64, or an integer type (converted to float64).
+    grid: (N, *out_spatial, r) fp32 or fp16 (coordinates in fp32) or float64
+    (coordinates in float64).  Returns (N, C, *out_spatial) float64; integer
+    outputs are to_integer() of it.
     """
     lib = lib or _load()
     X, grid, r = _check_sample_args(X, grid)
@@ -143,10 +173,11 @@ def grid_sample(X: np.ndarray, grid: np.ndarray, mode: str = "linear",
     in_sp = np.asarray(X.shape[2:], dtype=np.int64)
     out_sp = np.asarray(grid.shape[1:-1], dtype=np.int64)
     Y = np.empty((n, c, *grid.shape[1:-1]), dtype=np.float64)
-    rc = lib.oracle_grid_sample(_ptr(X, ctypes.c_float), r, n, c, _ptr(in_sp, ctypes.c_int64),
-                                _ptr(grid, ctypes.c_float), _ptr(out_sp, ctypes.c_int64),
-                                MODES[mode], PADDINGS[padding_mode], int(align_corners),
-                                _ptr(Y, ctypes.c_double))
+    xf, xd, gf, gd = _xg_ptrs(X, grid)
+    rc = lib.oracle_grid_sample_ex(xf, xd, r, n, c, _ptr(in_sp, ctypes.c_int64), gf, gd,
+                                   _ptr(out_sp, ctypes.c_int64), MODES[mode],
+                                   PADDINGS[padding_mode], int(align_corners),
+                                   _ptr(Y, ctypes.c_double))
     if rc:
         raise ValueError("oracle_grid_sample rejected its arguments")
     return Y
@@ -163,12 +194,12 @@ def grid_sample_points(X: np.ndarray, grid: np.ndarray, flat_index: np.ndarray,
     out_sp = np.asarray(grid.shape[1:-1], dtype=np.int64)
     idx = np.ascontiguousarray(flat_index, dtype=np.int64)
     Y = np.empty(idx.shape[0], dtype=np.float64)
-    rc = lib.oracle_grid_sample_points(_ptr(X, ctypes.c_float), r, n, c,
-                                       _ptr(in_sp, ctypes.c_int64), _ptr(grid, ctypes.c_float),
-                                       _ptr(out_sp, ctypes.c_int64), MODES[mode],
-                                       PADDINGS[padding_mode], int(align_corners),
-                                       _ptr(idx, ctypes.c_int64), idx.shape[0],
-                                       _ptr(Y, ctypes.c_double))
+    xf, xd, gf, gd = _xg_ptrs(X, grid)
+    rc = lib.oracle_grid_sample_points_ex(xf, xd, r, n, c, _ptr(in_sp, ctypes.c_int64), gf, gd,
+                                          _ptr(out_sp, ctypes.c_int64), MODES[mode],
+                                          PADDINGS[padding_mode], int(align_corners),
+                                          _ptr(idx, ctypes.c_int64), idx.shape[0],
+                                          _ptr(Y, ctypes.c_double))
     if rc:
         raise ValueError("oracle_grid_sample_points rejected its arguments")
     return Y
@@ -263,3 +294,19 @@ def resize_points(X: np.ndarray, out_shape, flat_index: np.ndarray, scales=None,
     if rc:
         raise ValueError("oracle_resize_points rejected its arguments")
     return Y
+
+
+def to_integer(values: np.ndarray, dtype) -> np.ndarray:
+    """The final cast of integer inputs (GridSample page, Outputs: computed as
+    floating point and cast to integer at the end).  Reading: truncation
+    toward zero, as a C conversion does, saturated to the range of the type
+    (cubic weights can overshoot it); a NaN becomes 0."""
+    dtype = np.dtype(dtype)
+    info = np.iinfo(dtype)
+    v = np.nan_to_num(np.asarray(values, dtype=np.float64), nan=0.0)
+    v = np.trunc(v)
+    lo, hi = float(info.min), float(info.max)
+    out = np.where(v <= lo, info.min, np.where(v >= hi, info.max, 0)).astype(dtype)
+    inside = (v > lo) & (v < hi)
+    out[inside] = v[inside].astype(dtype)
+    return out

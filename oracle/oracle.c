@@ -20,13 +20,17 @@
  *
  * Precision (the readings behind these choices are listed with the design
  * notes of the repository):
- *   - Grid generation and un-normalisation are carried out in fp32, the
- *     element type of every grid on the pages, one rounded operation at a
- *     time, in the order written below (build with -ffp-contract=off).  These
- *     steps decide integer tap indices, so they are done in the grid's own
- *     precision.
+ *   - Grid generation and un-normalisation are carried out in the grid's own
+ *     element type, one rounded operation at a time, in the order written
+ *     below (build with -ffp-contract=off): fp32 for fp32 grids (the type of
+ *     every grid on the pages; fp16 / bf16 grids are widened exactly to fp32
+ *     first), float64 for double grids.  These steps decide integer tap
+ *     indices.
  *   - Interpolation weights and the weighted sum are carried out in float64
- *     and returned unrounded.
+ *     and returned unrounded; X may be given as fp32 or as float64 (double X,
+ *     and integer X converted to float64: the GridSample page computes
+ *     integer inputs in floating point and casts at the end, a cast the
+ *     Python side of the oracle applies).
  *
  * What pins it (tests/test_oracle_*.py): the worked examples printed on the
  * AffineGrid and GridSample pages, the Resize cubic and linear examples
@@ -61,6 +65,16 @@
 #define OR_COORD_LIMIT 16777216.0f
 
 int oracle_abi_version(void) { return 1; }
+
+int oracle_grid_sample_ex(const float *X, const double *Xd, int r, int64_t N, int64_t C,
+                          const int64_t *in_spatial, const float *grid, const double *gridd,
+                          const int64_t *out_spatial, int mode, int padding, int align_corners,
+                          double *Y);
+int oracle_grid_sample_points_ex(const float *X, const double *Xd, int r, int64_t N, int64_t C,
+                                 const int64_t *in_spatial, const float *grid,
+                                 const double *gridd, const int64_t *out_spatial, int mode,
+                                 int padding, int align_corners, const int64_t *flat,
+                                 int64_t count, double *Y);
 
 /* ---------------------------------------------------------------------- */
 /* AffineGrid                                                              */
@@ -217,6 +231,60 @@ static double keys_kernel(double s, double a)
 
 #define OR_CUBIC_A (-0.75)
 
+/* The same coordinate steps for a double grid, in float64 (one rounded
+ * operation at a time, same order and bounds as the fp32 functions above). */
+static double unnormalize_d(double g, int64_t n, int align_corners)
+{
+    if (align_corners) {
+        double u = (g + 1.0) / 2.0;
+        return u * (double)(n - 1);
+    }
+    double v = (g + 1.0) * (double)n;
+    return (v - 1.0) / 2.0;
+}
+
+static double reflect_d(double p, double lo, double hi)
+{
+    double span = hi - lo;
+    if (span <= 0.0)
+        return 0.0;
+    double d = fabs(p - lo);
+    double f = floor(d / span);
+    double fs = f * span;
+    double e = d - fs;
+    double half = floor(f * 0.5);
+    int odd = (f - 2.0 * half) != 0.0;
+    return odd ? hi - e : lo + e;
+}
+
+static double clamp_d(double v, double lo, double hi)
+{
+    return v < lo ? lo : (v > hi ? hi : v);
+}
+
+static void reflect_bounds_d(int64_t n, int align_corners, double *lo, double *hi)
+{
+    if (align_corners) {
+        *lo = 0.0;
+        *hi = (double)(n - 1);
+    } else {
+        *lo = -0.5;
+        *hi = (double)n - 0.5;
+    }
+}
+
+static double pad_coordinate_d(double p, int64_t n, int padding, int align_corners)
+{
+    if (padding == OR_PAD_BORDER)
+        return clamp_d(p, 0.0, (double)(n - 1));
+    if (padding == OR_PAD_REFLECTION) {
+        double lo, hi;
+        reflect_bounds_d(n, align_corners, &lo, &hi);
+        return clamp_d(reflect_d(p, lo, hi), 0.0, (double)(n - 1));
+    }
+    return p;
+}
+
 /* Per-axis taps of one location: up to 4 (index, weight, valid) triples. */
 typedef struct {
     int count;
@@ -288,12 +356,76 @@ static int make_axis_taps(float g, int64_t n, int mode, int padding, int align_c
     return 1;
 }
 
+/* make_axis_taps for a location of a double grid: the coordinate steps in
+ * float64, the taps and weights as above. */
+static int make_axis_taps_d(double g, int64_t n, int mode, int padding, int align_corners,
+                            axis_taps *t)
+{
+    double p = unnormalize_d(g, n, align_corners);
+    if (!isfinite(p))
+        return 0;
+    p = clamp_d(p, -(double)OR_COORD_LIMIT, (double)OR_COORD_LIMIT);
+
+    if (mode == OR_MODE_NEAREST) {
+        double q = pad_coordinate_d(p, n, padding, align_corners);
+        int64_t i = (int64_t)rint(q); /* ties to even */
+        t->count = 1;
+        t->index[0] = i;
+        t->weight[0] = 1.0;
+        t->valid[0] = (i >= 0 && i < n);
+        return 1;
+    }
+
+    if (mode == OR_MODE_LINEAR) {
+        double q = pad_coordinate_d(p, n, padding, align_corners);
+        double fl = floor(q);
+        double frac = q - fl; /* exact */
+        int64_t i0 = (int64_t)fl;
+        t->count = 2;
+        t->index[0] = i0;
+        t->index[1] = i0 + 1;
+        t->weight[0] = 1.0 - frac;
+        t->weight[1] = frac;
+        for (int j = 0; j < 2; ++j)
+            t->valid[j] = (t->index[j] >= 0 && t->index[j] < n);
+        return 1;
+    }
+
+    double fl = floor(p);
+    double frac = p - fl;
+    int64_t i0 = (int64_t)fl;
+    t->count = 4;
+    t->weight[0] = keys_kernel(frac + 1.0, OR_CUBIC_A);
+    t->weight[1] = keys_kernel(frac, OR_CUBIC_A);
+    t->weight[2] = keys_kernel(1.0 - frac, OR_CUBIC_A);
+    t->weight[3] = keys_kernel(2.0 - frac, OR_CUBIC_A);
+    for (int j = 0; j < 4; ++j) {
+        int64_t i = i0 - 1 + j;
+        if (padding == OR_PAD_ZEROS) {
+            t->index[j] = i;
+            t->valid[j] = (i >= 0 && i < n);
+        } else if (padding == OR_PAD_BORDER) {
+            t->index[j] = i < 0 ? 0 : (i > n - 1 ? n - 1 : i);
+            t->valid[j] = 1;
+        } else {
+            double lo, hi;
+            reflect_bounds_d(n, align_corners, &lo, &hi);
+            double q = clamp_d(reflect_d((double)i, lo, hi), 0.0, (double)(n - 1));
+            t->index[j] = (int64_t)q;
+            t->valid[j] = 1;
+        }
+    }
+    return 1;
+}
+
 typedef struct {
-    const float *X;
+    const float *X;   /* fp32 X, or */
+    const double *Xd; /* float64 X (exactly one of the two is set) */
     int r;
     int64_t N, C;
     const int64_t *in_sp;
-    const float *grid;
+    const float *grid;   /* fp32 grid, or */
+    const double *gridd; /* float64 grid */
     const int64_t *out_sp;
     int mode, padding, align_corners;
     int64_t in_count, out_count;
@@ -303,11 +435,14 @@ typedef struct {
  * contributes nothing (non-finite coordinate). */
 static int location_taps(const sample_problem *P, int64_t n, int64_t o, axis_taps *taps)
 {
-    const float *g = P->grid + (n * P->out_count + o) * P->r;
     for (int a = 0; a < P->r; ++a) {
         /* component k of the location vector refers to axis r-1-k */
-        float ga = g[P->r - 1 - a];
-        if (!make_axis_taps(ga, P->in_sp[a], P->mode, P->padding, P->align_corners, &taps[a]))
+        int64_t at = (n * P->out_count + o) * P->r + (P->r - 1 - a);
+        int ok = P->gridd ? make_axis_taps_d(P->gridd[at], P->in_sp[a], P->mode, P->padding,
+                                             P->align_corners, &taps[a])
+                          : make_axis_taps(P->grid[at], P->in_sp[a], P->mode, P->padding,
+                                           P->align_corners, &taps[a]);
+        if (!ok)
             return 0;
     }
     return 1;
@@ -317,7 +452,7 @@ static int location_taps(const sample_problem *P, int64_t n, int64_t o, axis_tap
  *   prod_a weight_a * (all taps in range ? X[n, c, index...] : 0). */
 static double sample_value(const sample_problem *P, const axis_taps *taps, int64_t n, int64_t c)
 {
-    const float *plane = P->X + (n * P->C + c) * P->in_count;
+    const int64_t base = (n * P->C + c) * P->in_count;
     int sel[OR_MAX_RANK];
     for (int a = 0; a < P->r; ++a)
         sel[a] = 0;
@@ -333,7 +468,7 @@ static double sample_value(const sample_problem *P, const axis_taps *taps, int64
             off = off * P->in_sp[a] + t->index[sel[a]];
         }
         if (valid)
-            acc += w * (double)plane[off];
+            acc += w * (P->Xd ? P->Xd[base + off] : (double)P->X[base + off]);
         /* advance the odometer, innermost axis fastest */
         int a = P->r - 1;
         while (a >= 0) {
@@ -348,20 +483,24 @@ static double sample_value(const sample_problem *P, const axis_taps *taps, int64
     return acc;
 }
 
-static int setup_problem(sample_problem *P, const float *X, int r, int64_t N, int64_t C,
-                         const int64_t *in_sp, const float *grid, const int64_t *out_sp,
-                         int mode, int padding, int align_corners)
+static int setup_problem(sample_problem *P, const float *X, const double *Xd, int r, int64_t N,
+                         int64_t C, const int64_t *in_sp, const float *grid, const double *gridd,
+                         const int64_t *out_sp, int mode, int padding, int align_corners)
 {
     if (r < 1 || r > OR_MAX_RANK || N < 0 || C < 0)
         return -1;
     if (mode < 0 || mode > 2 || padding < 0 || padding > 2 || (align_corners != 0 && align_corners != 1))
         return -1;
+    if (!X == !Xd || !grid == !gridd)
+        return -1;
     P->X = X;
+    P->Xd = Xd;
     P->r = r;
     P->N = N;
     P->C = C;
     P->in_sp = in_sp;
     P->grid = grid;
+    P->gridd = gridd;
     P->out_sp = out_sp;
     P->mode = mode;
     P->padding = padding;
@@ -387,8 +526,23 @@ int oracle_grid_sample(const float *X, int r, int64_t N, int64_t C, const int64_
                        const float *grid, const int64_t *out_spatial, int mode, int padding,
                        int align_corners, double *Y)
 {
+    return oracle_grid_sample_ex(X, NULL, r, N, C, in_spatial, grid, NULL, out_spatial, mode,
+                                 padding, align_corners, Y);
+}
+
+/*
+ * General form: X given either as fp32 (X) or as float64 (Xd), the grid
+ * either as fp32 (grid) or as float64 (gridd); exactly one of each pair is
+ * non-NULL.  A float64 grid takes the coordinate steps in float64.
+ */
+int oracle_grid_sample_ex(const float *X, const double *Xd, int r, int64_t N, int64_t C,
+                          const int64_t *in_spatial, const float *grid, const double *gridd,
+                          const int64_t *out_spatial, int mode, int padding, int align_corners,
+                          double *Y)
+{
     sample_problem P;
-    if (setup_problem(&P, X, r, N, C, in_spatial, grid, out_spatial, mode, padding, align_corners))
+    if (setup_problem(&P, X, Xd, r, N, C, in_spatial, grid, gridd, out_spatial, mode, padding,
+                      align_corners))
         return -1;
     axis_taps taps[OR_MAX_RANK];
     for (int64_t n = 0; n < N; ++n) {
@@ -413,8 +567,20 @@ int oracle_grid_sample_points(const float *X, int r, int64_t N, int64_t C,
                               const int64_t *out_spatial, int mode, int padding, int align_corners,
                               const int64_t *flat, int64_t count, double *Y)
 {
+    return oracle_grid_sample_points_ex(X, NULL, r, N, C, in_spatial, grid, NULL, out_spatial,
+                                        mode, padding, align_corners, flat, count, Y);
+}
+
+/* General form of oracle_grid_sample_points (see oracle_grid_sample_ex). */
+int oracle_grid_sample_points_ex(const float *X, const double *Xd, int r, int64_t N, int64_t C,
+                                 const int64_t *in_spatial, const float *grid,
+                                 const double *gridd, const int64_t *out_spatial, int mode,
+                                 int padding, int align_corners, const int64_t *flat,
+                                 int64_t count, double *Y)
+{
     sample_problem P;
-    if (setup_problem(&P, X, r, N, C, in_spatial, grid, out_spatial, mode, padding, align_corners))
+    if (setup_problem(&P, X, Xd, r, N, C, in_spatial, grid, gridd, out_spatial, mode, padding,
+                      align_corners))
         return -1;
     axis_taps taps[OR_MAX_RANK];
     for (int64_t i = 0; i < count; ++i) {

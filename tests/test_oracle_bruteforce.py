@@ -18,7 +18,8 @@ the GridSample page and the Resize cubic examples).
 Sampling positions p are computed in fp32 from the normalised location, as
 the un-normalisation fixed by the printed examples; this keeps nearest
 comparisons exact.  Every mode x padding x align_corners combination runs in
-2D and 3D, on extents 1..5 including extent-1 axes.
+1-D to 4-D, with fp32 and float64 grids, on extents 1..5 including extent-1
+axes.
 """
 
 import itertools
@@ -46,12 +47,15 @@ def nearest_kernel(s, j):
     return np.where(a < 0.5, 1.0, np.where((a == 0.5) & (j % 2 == 0), 1.0, 0.0))
 
 
-def pixel_position(g, n, ac):
-    g = np.float32(g)
-    one = np.float32(1)
+def pixel_position(g, n, ac, double=False):
+    """Un-normalisation in the grid's precision (fp32, or float64 for a
+    double grid)."""
+    f = np.float64 if double else np.float32
+    g = f(g)
+    one = f(1)
     if ac:
-        return ((g + one) / np.float32(2)) * np.float32(n - 1)
-    return ((g + one) * np.float32(n) - one) / np.float32(2)
+        return ((g + one) / f(2)) * f(n - 1)
+    return ((g + one) * f(n) - one) / f(2)
 
 
 def pad_mode(padding, ac):
@@ -65,6 +69,7 @@ def pad_mode(padding, ac):
 def brute_force(X, grid, mode, padding, ac):
     N, C = X.shape[:2]
     in_sp = X.shape[2:]
+    double = grid.dtype == np.float64
     r = len(in_sp)
     out_sp = grid.shape[1:-1]
     # lattice large enough to hold every tap of every location in the tests
@@ -77,7 +82,7 @@ def brute_force(X, grid, mode, padding, ac):
             weights = []
             for a in range(r):
                 # component k of the location vector addresses axis r-1-k
-                p = float(pixel_position(g[r - 1 - a], in_sp[a], ac))
+                p = float(pixel_position(g[r - 1 - a], in_sp[a], ac, double))
                 j = np.arange(-L, in_sp[a] + L)
                 s = p - j
                 if mode == "nearest":
@@ -99,16 +104,21 @@ COMBOS = list(itertools.product(["nearest", "linear", "cubic"], ["zeros", "borde
 
 
 @pytest.mark.parametrize("mode,padding,ac", COMBOS)
-@pytest.mark.parametrize("rank", [2, 3])
-def test_oracle_matches_dense_lattice(oracle_mod, mode, padding, ac, rank):
+@pytest.mark.parametrize("rank", [1, 2, 3, 4])
+@pytest.mark.parametrize("precision", ["f32", "f64"])
+def test_oracle_matches_dense_lattice(oracle_mod, mode, padding, ac, rank, precision):
+    """Every rank the page defines in general (1-D, 2-D, 3-D, 4-D here), with
+    fp32 grids and X, and with float64 grids and X (coordinates in float64)."""
     rng = np.random.default_rng(100 + 7 * rank + 31 * ac)
-    for trial in range(4):
-        in_sp = tuple(int(v) for v in rng.integers(1, 6, size=rank))
+    dt = np.float32 if precision == "f32" else np.float64
+    for trial in range(4 if rank < 4 else 2):
+        hi = 6 if rank < 4 else 4
+        in_sp = tuple(int(v) for v in rng.integers(1, hi, size=rank))
         if trial == 0:
             in_sp = (1,) * rank                       # all extents 1
-        out_sp = tuple(int(v) for v in rng.integers(1, 4, size=rank))
-        X = rng.uniform(-1, 1, size=(2, 2) + in_sp).astype(np.float32)
-        G = rng.uniform(-1.7, 1.7, size=(2,) + out_sp + (rank,)).astype(np.float32)
+        out_sp = tuple(int(v) for v in rng.integers(1, 4 if rank < 4 else 3, size=rank))
+        X = rng.uniform(-1, 1, size=(2, 2) + in_sp).astype(dt)
+        G = rng.uniform(-1.7, 1.7, size=(2,) + out_sp + (rank,)).astype(dt)
         Y = oracle_mod.grid_sample(X, G, mode, padding, ac)
         B = brute_force(X, G, mode, padding, ac)
         if mode == "nearest":

@@ -2,7 +2,10 @@
 
 Each mutant is a one-line edit of oracle/oracle.c (an index off by one, a
 dropped term, a swapped sign or operand, a wrong constant or rounding rule),
-compiled on the CPU into a temporary library.  The pin battery below — the
+compiled on the CPU into a temporary library.  Where the same line appears in
+the fp32-coordinate and the float64-coordinate paths, the first one (fp32) is
+mutated; the DOUBLE_MUTANTS hit the float64 path, which the battery also
+exercises with double grids.  The pin battery below — the
 pages' printed examples, the Resize cross-checks, the dense-lattice brute
 force and the reflection symmetry — must reject every mutant while accepting
 the unmodified oracle.  Mutants are chosen so that none reads outside its
@@ -46,11 +49,28 @@ MUTANTS = [
      "t->valid[j] = (i > 0 && i < n);"),
     ("cubic border clamps to n-2", "t->index[j] = i < 0 ? 0 : (i > n - 1 ? n - 1 : i);",
      "t->index[j] = i < 0 ? 0 : (i > n - 2 ? (n > 1 ? n - 2 : 0) : i);"),
-    ("location vector read outermost first", "float ga = g[P->r - 1 - a];", "float ga = g[a];"),
+    ("location vector read outermost first", "(n * P->out_count + o) * P->r + (P->r - 1 - a);",
+     "(n * P->out_count + o) * P->r + a;"),
     ("reflection result not clamped back into the image",
      "return clampf(reflect(p, lo, hi), 0.0f, (float)(n - 1));", "return reflect(p, lo, hi);"),
     ("border clamp at n instead of n-1", "return clampf(p, 0.0f, (float)(n - 1));",
      "return clampf(p, 0.0f, (float)n - 0.5f);"),
+]
+
+
+DOUBLE_MUTANTS = [
+    ("double grid: align_corners=0 shift with the wrong sign", "return (v - 1.0) / 2.0;",
+     "return (v + 1.0) / 2.0;"),
+    ("double grid: reflection bound at the pixel centre", "*lo = -0.5;", "*lo = 0.0;"),
+    ("double grid: nearest rounds half away from zero", "int64_t i = (int64_t)rint(q);",
+     "int64_t i = (int64_t)round(q);"),
+    ("double grid: linear second tap repeats the first", "t->index[1] = i0 + 1;",
+     "t->index[1] = i0;"),
+    ("double grid: cubic outer weight at the wrong distance",
+     "t->weight[3] = keys_kernel(2.0 - frac, OR_CUBIC_A);",
+     "t->weight[3] = keys_kernel(1.0 + frac, OR_CUBIC_A);"),
+    ("double grid: border clamp at n", "return clamp_d(p, 0.0, (double)(n - 1));",
+     "return clamp_d(p, 0.0, (double)n - 0.5);"),
 ]
 
 
@@ -76,17 +96,29 @@ def pin_battery(om, lib):
         ref = np.array(ex["expected"]).reshape(Y.shape)
         if (np.abs(Y - ref) / np.maximum(1, np.abs(ref))).max() > 2e-6:
             return ex["name"]
+    for ex in load_golden("grid_sample_examples.json"):
+        X = np.array(ex["X"], np.float64).reshape(ex["X_shape"])
+        G = np.array(ex["grid"], np.float64).reshape(ex["grid_shape"])
+        Y = om.grid_sample(X, G, ex["mode"] or "linear", ex["padding_mode"] or "zeros",
+                           ex["align_corners"] or 0, lib=lib)
+        ref = np.array(ex["Y"]).reshape(ex["Y_shape"])
+        if (np.abs(Y - ref) / np.maximum(1, np.abs(ref))).max() > 2e-6:
+            return ex["name"] + " (double)"
     rng = np.random.default_rng(2024)
     for mode, pad, ac in itertools.product(["nearest", "linear", "cubic"],
                                            ["zeros", "border", "reflection"], [0, 1]):
-        for rank in (2, 3):
+        for rank, dt in ((2, np.float32), (3, np.float32), (1, np.float64), (2, np.float64)):
             in_sp = tuple(int(v) for v in rng.integers(1, 6, size=rank))
             out_sp = (3,) * rank
-            X = rng.uniform(-1, 1, (1, 2) + in_sp).astype(np.float32)
-            G = rng.uniform(-1.7, 1.7, (1,) + out_sp + (rank,)).astype(np.float32)
+            X = rng.uniform(-1, 1, (1, 2) + in_sp).astype(dt)
+            G = rng.uniform(-1.7, 1.7, (1,) + out_sp + (rank,)).astype(dt)
+            if dt == np.float64 and mode == "nearest":
+                # exact ties, so the rounding rule matters on the float64 path too
+                G[..., 0] = rng.integers(-6, 7, size=G.shape[:-1]) / 4.0
             Y = om.grid_sample(X, G, mode, pad, ac, lib=lib)
             if np.abs(Y - brute_force(X, G, mode, pad, ac)).max() > 1e-12:
-                return "brute force %s/%s/%d/%dD %s" % (mode, pad, ac, rank, in_sp)
+                return "brute force %s/%s/%d/%dD %s %s" % (mode, pad, ac, rank, in_sp,
+                                                          np.dtype(dt).name)
     for mode, ac in itertools.product(["linear", "cubic"], [0, 1]):
         X = rng.uniform(-1, 1, (1, 1, 5, 7)).astype(np.float32)
         G = (rng.integers(-3072, 3072, (1, 6, 6, 2)) / 1024.0).astype(np.float32)
@@ -101,12 +133,20 @@ def test_unmodified_oracle_passes_battery(oracle_mod):
     assert pin_battery(oracle_mod, None) is None
 
 
-@pytest.mark.parametrize("desc,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_planted_mistake_is_caught(oracle_mod, tmp_path, desc, old, new):
+def mutate(src, old, new, last):
+    """Replace the first (fp32 path) or the last (float64 path) occurrence."""
+    i = src.rfind(old) if last else src.find(old)
+    assert i >= 0, "mutation site not found: " + old
+    return src[:i] + new + src[i + len(old):]
+
+
+@pytest.mark.parametrize("desc,old,new,last",
+                         [m + (False,) for m in MUTANTS] + [m + (True,) for m in DOUBLE_MUTANTS],
+                         ids=[m[0] for m in MUTANTS + DOUBLE_MUTANTS])
+def test_planted_mistake_is_caught(oracle_mod, tmp_path, desc, old, new, last):
     src = open(SRC).read()
-    assert src.count(old) == 1, "mutation site not found: " + desc
     mutant = tmp_path / "mutant.c"
-    mutant.write_text(src.replace(old, new))
+    mutant.write_text(mutate(src, old, new, last))
     so = oracle_mod.build(src=str(mutant), out=str(tmp_path / "libmutant.so"))
     lib = oracle_mod.load_library(so)
     caught = pin_battery(oracle_mod, lib)
