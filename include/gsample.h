@@ -54,8 +54,23 @@ typedef enum {
     GS_ERR_HIP = 6        /* the HIP runtime reported an error at launch */
 } gs_status;
 
-/* Element types (GridSample page, Type Constraints; bfloat16 from version 22). */
-typedef enum { GS_F32 = 0, GS_F16 = 1, GS_BF16 = 2 } gs_dtype;
+/* Element types (GridSample page, Type Constraints; bfloat16 from version 22):
+ * X / Y of GridSample may be any of them; grids are GS_F32, GS_F16, GS_BF16
+ * or GS_F64; Resize takes GS_F32, GS_F16 and GS_BF16; theta is GS_F32. */
+typedef enum {
+    GS_F32 = 0,
+    GS_F16 = 1,
+    GS_BF16 = 2,
+    GS_F64 = 3,
+    GS_I8 = 4,
+    GS_U8 = 5,
+    GS_I16 = 6,
+    GS_U16 = 7,
+    GS_I32 = 8,
+    GS_U32 = 9,
+    GS_I64 = 10,
+    GS_U64 = 11
+} gs_dtype;
 
 /* GridSample page, Attributes, mode: linear (the default; bilinear in 2D,
  * trilinear in 3D), nearest (ties to the even index), cubic (bicubic /
@@ -109,11 +124,14 @@ int gs_affine_grid(const void *theta, int theta_dtype, const int64_t *size, int 
  *   Y            device, (N, C, H_out, W_out), same element type as X,
  *                written whole.
  *
+ * Element types: see gs_grid_sample below (any gs_dtype for X; GS_F32,
+ * GS_F16, GS_BF16 or GS_F64 grids).
+ *
  * Errors: GS_ERR_NULL, GS_ERR_SHAPE (batch mismatch, last grid dim not 2,
- * negative extent, zero input extent with non-empty output), GS_ERR_DTYPE
- * (x_dtype not GS_F32/GS_F16/GS_BF16, grid_dtype not GS_F32), GS_ERR_ATTR,
- * GS_ERR_TOO_LARGE (an input plane H_in*W_in or an output plane H_out*W_out
- * of more than 2^28 elements, or more than 2^24 thread blocks), GS_ERR_HIP.
+ * negative extent, zero input extent with non-empty output), GS_ERR_DTYPE,
+ * GS_ERR_ATTR, GS_ERR_TOO_LARGE (an input plane H_in*W_in or an output plane
+ * H_out*W_out of more than 2^28 elements or 2^30 bytes, or more than 2^24
+ * thread blocks), GS_ERR_HIP.
  */
 int gs_grid_sample_2d(const void *X, int x_dtype, const int64_t *x_shape, const void *grid,
                       int grid_dtype, const int64_t *grid_shape, int mode, int padding,
@@ -130,6 +148,36 @@ int gs_grid_sample_3d(const void *X, int x_dtype, const int64_t *x_shape, const 
                       int align_corners, void *Y, void *stream);
 
 /*
+ * GridSample of any rank (GridSample page, Summary: X of rank r+2 with shape
+ * (N, C, D1, ..., Dr), grid (N, D1_out, ..., Dr_out, r), Y (N, C, D1_out, ...,
+ * Dr_out); the location vector lists the innermost axis first) and any
+ * numeric element type (Type Constraints).
+ *
+ *   X, x_dtype   device, any gs_dtype.  Integer X is interpolated in
+ *                floating point and cast at the end (Outputs): truncated
+ *                toward zero and saturated to the type's range.
+ *   x_shape, x_rank   host, x_rank = r + 2 entries, 1 <= r <= 6.
+ *   grid, grid_dtype  device, GS_F32, GS_F16, GS_BF16 (coordinates computed
+ *                in fp32 from the exactly widened values) or GS_F64
+ *                (coordinates in double).
+ *   grid_shape   host, x_rank entries; grid_shape[0] == x_shape[0],
+ *                grid_shape[x_rank - 1] == r.
+ *   mode, padding, align_corners   as for gs_grid_sample_2d.
+ *   Y            device, (N, C, grid_shape[1 .. r]), element type x_dtype.
+ *
+ * fp32 / fp16 / bf16 X with an fp32 grid in 2 or 3 spatial dimensions run
+ * the tuned kernels of gs_grid_sample_2d / _3d (fp32 accumulation).  Every
+ * other combination runs a direct-gather kernel that sums in double in the
+ * order of the definition (weights as products over the axes, outermost
+ * first; taps innermost axis fastest).
+ *
+ * Errors: as gs_grid_sample_2d; GS_ERR_SHAPE also for x_rank outside 3..8.
+ */
+int gs_grid_sample(const void *X, int x_dtype, const int64_t *x_shape, int x_rank, const void *grid,
+                   int grid_dtype, const int64_t *grid_shape, int mode, int padding,
+                   int align_corners, void *Y, void *stream);
+
+/*
  * AffineGrid followed by GridSample in one pass (the grid generator and
  * sampler of a spatial transformer).  Each output location computes its grid
  * vector from theta in registers exactly as gs_affine_grid does (same bits)
@@ -138,7 +186,7 @@ int gs_grid_sample_3d(const void *X, int x_dtype, const int64_t *x_shape, const 
  * same align_corners.
  *
  *   theta        device, (N, 2, 3) (x_rank 4) or (N, 3, 4) (x_rank 5), GS_F32.
- *   X, x_dtype   device input as for gs_grid_sample_2d/_3d.
+ *   X, x_dtype   device input, GS_F32, GS_F16 or GS_BF16.
  *   x_shape, x_rank   host, x_rank (4 or 5) entries.
  *   out_spatial  host, (H_out, W_out) or (D_out, H_out, W_out).
  *   Y            device, (N, C, *out_spatial), element type x_dtype.

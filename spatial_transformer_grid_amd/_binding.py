@@ -16,7 +16,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgsample.so")
 
 GS_OK, GS_ERR_NULL, GS_ERR_SHAPE, GS_ERR_DTYPE, GS_ERR_ATTR, GS_ERR_TOO_LARGE, GS_ERR_HIP = range(7)
-GS_F32, GS_F16, GS_BF16 = 0, 1, 2
+(GS_F32, GS_F16, GS_BF16, GS_F64, GS_I8, GS_U8, GS_I16, GS_U16, GS_I32, GS_U32, GS_I64,
+ GS_U64) = range(12)
 MODES = {"linear": 0, "bilinear": 0, "nearest": 1, "cubic": 2, "bicubic": 2}
 PADDINGS = {"zeros": 0, "border": 1, "reflection": 2}
 RESIZE_MODES = {"nearest": 0, "linear": 1, "cubic": 2}
@@ -36,6 +37,7 @@ SIGNATURES = {
     "gs_grid_sample_2d": ([_P, _I, _PI64, _P, _I, _PI64, _I, _I, _I, _P, _P], _I),
     "gs_grid_sample_3d": ([_P, _I, _PI64, _P, _I, _PI64, _I, _I, _I, _P, _P], _I),
     "gs_affine_grid_sample_fused": ([_P, _I, _P, _I, _PI64, _I, _PI64, _I, _I, _I, _P, _P], _I),
+    "gs_grid_sample": ([_P, _I, _PI64, _I, _P, _I, _PI64, _I, _I, _I, _P, _P], _I),
     "gs_resize_output_shape": ([_PI64, _I, _PI64, _I, _PF32, _PI64, _I, _PI64], _I),
     "gs_resize": ([_P, _I, _PI64, _I, _PI64, _PF32, _I, _I, _I, ctypes.c_float, _I, _P, _P], _I),
 }
@@ -81,7 +83,12 @@ def _torch():
 
 def dtype_code(t) -> int:
     torch = _torch()
-    codes = {torch.float32: GS_F32, torch.float16: GS_F16, torch.bfloat16: GS_BF16}
+    codes = {torch.float32: GS_F32, torch.float16: GS_F16, torch.bfloat16: GS_BF16,
+             torch.float64: GS_F64, torch.int8: GS_I8, torch.uint8: GS_U8, torch.int16: GS_I16,
+             torch.int32: GS_I32, torch.int64: GS_I64}
+    for name, code in (("uint16", GS_U16), ("uint32", GS_U32), ("uint64", GS_U64)):
+        if hasattr(torch, name):
+            codes[getattr(torch, name)] = code
     if t.dtype not in codes:
         raise TypeError("unsupported element type %s" % t.dtype)
     return codes[t.dtype]
@@ -136,22 +143,26 @@ def _out_tensor(out, shape, like):
 
 def grid_sample(X, grid, mode: str = "linear", padding_mode: str = "zeros",
                 align_corners: int = 0, out=None, stream=None):
-    """GridSample(X, grid) -> Y on the GPU (gs_grid_sample_2d / _3d)."""
+    """GridSample(X, grid) -> Y on the GPU: gs_grid_sample_2d / _3d for 2 and
+    3 spatial dimensions, gs_grid_sample for 1 to 6."""
     X = _device_tensor(X, "X")
     grid = _device_tensor(grid, "grid")
     r = X.dim() - 2
-    if r not in (2, 3):
-        raise ValueError("X must have 2 or 3 spatial dimensions")
     if grid.dim() != r + 2:
         raise ValueError("grid must have rank %d" % (r + 2))
     shape = (X.shape[0], X.shape[1], *grid.shape[1:-1])
     Y = _out_tensor(out, shape, X)
-    fn = lib().gs_grid_sample_2d if r == 2 else lib().gs_grid_sample_3d
-    st = fn(ctypes.c_void_p(X.data_ptr()), dtype_code(X), int64_array(X.shape),
-            ctypes.c_void_p(grid.data_ptr()), dtype_code(grid), int64_array(grid.shape),
+    args = (ctypes.c_void_p(X.data_ptr()), dtype_code(X), int64_array(X.shape))
+    rest = (ctypes.c_void_p(grid.data_ptr()), dtype_code(grid), int64_array(grid.shape),
             MODES[mode], PADDINGS[padding_mode], int(align_corners),
             ctypes.c_void_p(Y.data_ptr()), _stream(stream, X.device))
-    _check(st, "gs_grid_sample_%dd" % r)
+    if r in (2, 3):
+        name = "gs_grid_sample_%dd" % r
+        st = getattr(lib(), name)(*args, *rest)
+    else:
+        name = "gs_grid_sample"
+        st = lib().gs_grid_sample(*args, X.dim(), *rest)
+    _check(st, name)
     return Y
 
 

@@ -16,9 +16,20 @@ constexpr int64_t kInt32Max = 0x7fffffff;
 constexpr int kBlockThreads = 256;
 constexpr int64_t kTargetBlocks = 2048;
 
-int elem_bytes(int dtype) { return dtype == GS_F32 ? 4 : 2; }
+int elem_bytes(int dtype) {
+    switch (dtype) {
+    case GS_F16: case GS_BF16: case GS_I16: case GS_U16: return 2;
+    case GS_F64: case GS_I64: case GS_U64: return 8;
+    case GS_I8: case GS_U8: return 1;
+    default: return 4;
+    }
+}
 
+// element types of the tuned sampler and of Resize
 bool valid_x_dtype(int d) { return d == GS_F32 || d == GS_F16 || d == GS_BF16; }
+// every numeric type GridSample accepts for X
+bool valid_any_dtype(int d) { return d >= GS_F32 && d <= GS_U64; }
+bool valid_grid_dtype(int d) { return d == GS_F32 || d == GS_F16 || d == GS_BF16 || d == GS_F64; }
 
 int check_attrs(int mode, int padding, int align_corners) {
     if (mode < GS_MODE_LINEAR || mode > GS_MODE_CUBIC) return GS_ERR_ATTR;
@@ -122,18 +133,70 @@ int sample(int r, const void *theta, const void *X, int x_dtype, const int64_t *
                                              vec_in, (hipStream_t)stream));
 }
 
+// Validation and launch of the any-rank, any-type sampler.
+int sample_nd(int r, const void *X, int x_dtype, const int64_t *x_shape, const void *grid,
+              int grid_dtype, const int64_t *out_sp, int mode, int padding, int align_corners,
+              void *Y, void *stream) {
+    for (int i = 0; i < r + 2; ++i)
+        if (x_shape[i] < 0) return GS_ERR_SHAPE;
+    const int64_t N = x_shape[0], C = x_shape[1];
+    const int bytes = elem_bytes(x_dtype);
+    int64_t in_count = 0, out_count = 0;
+    if (N > kInt32Max || C > kInt32Max) return GS_ERR_TOO_LARGE;
+    if (!product_within(x_shape + 2, r, kPlaneLimit, &in_count)) return GS_ERR_TOO_LARGE;
+    if (!product_within(out_sp, r, kPlaneLimit, &out_count)) return GS_ERR_TOO_LARGE;
+    if (in_count * bytes > (int64_t(1) << 30) || out_count * bytes > (int64_t(1) << 30))
+        return GS_ERR_TOO_LARGE;
+    if (N == 0 || C == 0 || out_count == 0) return GS_OK;
+    if (in_count == 0) return GS_ERR_SHAPE;
+    if (!X || !Y || !grid) return GS_ERR_NULL;
+    const int64_t tiles = (out_count + kBlockThreads - 1) / kBlockThreads;
+    if (N * tiles > kMaxBlocks) return GS_ERR_TOO_LARGE;
+    int64_t groups = (kTargetBlocks + N * tiles - 1) / (N * tiles);
+    if (groups > C) groups = C;
+    if (groups < 1) groups = 1;
+    const int64_t cpg = (C + groups - 1) / groups;
+    groups = (C + cpg - 1) / cpg;
+    if (N * groups * tiles > kMaxBlocks) return GS_ERR_TOO_LARGE;
+    gs::NdParams p;
+    p.X = X;
+    p.Y = Y;
+    p.grid = grid;
+    p.x_dtype = x_dtype;
+    p.grid_dtype = grid_dtype;
+    p.N = (int)N;
+    p.C = (int)C;
+    for (int a = 0; a < 6; ++a) p.in_ext[a] = a < r ? (int)x_shape[2 + a] : 1;
+    p.out_count = (uint32_t)out_count;
+    p.in_plane_bytes = (uint32_t)(in_count * bytes);
+    p.out_plane_bytes = (uint32_t)(out_count * bytes);
+    p.padding = padding;
+    p.align_corners = align_corners;
+    p.tiles = (int)tiles;
+    p.cgroups = (int)groups;
+    p.cpg = (int)cpg;
+    p.nblocks = (int)(N * groups * tiles);
+    return hip_status(gs::launch_grid_sample_nd(p, r, mode, grid_dtype == GS_F64,
+                                                (hipStream_t)stream));
+}
+
+// GridSample with r spatial axes: the tuned kernels for fp32 / fp16 / bf16 X
+// with an fp32 grid in 2D and 3D, the any-rank kernel otherwise.
 int grid_sample_rank(int r, const void *X, int x_dtype, const int64_t *x_shape, const void *grid,
                      int grid_dtype, const int64_t *grid_shape, int mode, int padding,
                      int align_corners, void *Y, void *stream) {
     if (!x_shape || !grid_shape) return GS_ERR_NULL;
-    if (!valid_x_dtype(x_dtype) || grid_dtype != GS_F32) return GS_ERR_DTYPE;
+    if (!valid_any_dtype(x_dtype) || !valid_grid_dtype(grid_dtype)) return GS_ERR_DTYPE;
     int rc = check_attrs(mode, padding, align_corners);
     if (rc) return rc;
     for (int i = 0; i < r + 2; ++i)
         if (grid_shape[i] < 0) return GS_ERR_SHAPE;
     if (grid_shape[0] != x_shape[0] || grid_shape[r + 1] != r) return GS_ERR_SHAPE;
-    return sample(r, nullptr, X, x_dtype, x_shape, grid, grid_shape + 1, mode, padding,
-                  align_corners, Y, stream);
+    if ((r == 2 || r == 3) && valid_x_dtype(x_dtype) && grid_dtype == GS_F32)
+        return sample(r, nullptr, X, x_dtype, x_shape, grid, grid_shape + 1, mode, padding,
+                      align_corners, Y, stream);
+    return sample_nd(r, X, x_dtype, x_shape, grid, grid_dtype, grid_shape + 1, mode, padding,
+                     align_corners, Y, stream);
 }
 
 // Axis index from a possibly negative `axes` entry; -1 when out of range.
@@ -210,6 +273,14 @@ int gs_grid_sample_3d(const void *X, int x_dtype, const int64_t *x_shape, const 
                       int align_corners, void *Y, void *stream) {
     return grid_sample_rank(3, X, x_dtype, x_shape, grid, grid_dtype, grid_shape, mode, padding,
                             align_corners, Y, stream);
+}
+
+int gs_grid_sample(const void *X, int x_dtype, const int64_t *x_shape, int x_rank, const void *grid,
+                   int grid_dtype, const int64_t *grid_shape, int mode, int padding,
+                   int align_corners, void *Y, void *stream) {
+    if (x_rank < 3 || x_rank > 8) return GS_ERR_SHAPE;
+    return grid_sample_rank(x_rank - 2, X, x_dtype, x_shape, grid, grid_dtype, grid_shape, mode,
+                            padding, align_corners, Y, stream);
 }
 
 int gs_affine_grid_sample_fused(const void *theta, int theta_dtype, const void *X, int x_dtype,

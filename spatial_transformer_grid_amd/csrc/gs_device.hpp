@@ -122,53 +122,70 @@ __device__ __forceinline__ float base_position(int i, int m, int align_corners) 
     return (float)(2 * i + 1) / (float)m - 1.0f;
 }
 
+// The coordinate steps below are written once for the grid's coordinate
+// type F: float (fp32, fp16 and bf16 grids) or double (double grids).
+template <typename F>
+__device__ __forceinline__ F floor_t(F v) {
+    if constexpr (sizeof(F) == 4) return floorf(v);
+    else return floor(v);
+}
+template <typename F>
+__device__ __forceinline__ F fabs_t(F v) {
+    if constexpr (sizeof(F) == 4) return fabsf(v);
+    else return fabs(v);
+}
+
 // Normalised location -> pixel coordinate along an axis of n pixels
 // (GridSample page, Attributes: align_corners).  (g+1)/2 is computed as
 // (g+1)*0.5, which rounds identically.
-__device__ __forceinline__ float unnormalize(float g, int n, int align_corners) {
+template <typename F>
+__device__ __forceinline__ F unnormalize(F g, int n, int align_corners) {
     if (align_corners) {
-        float u = (g + 1.0f) * 0.5f;
-        return u * (float)(n - 1);
+        F u = (g + F(1)) * F(0.5);
+        return u * (F)(n - 1);
     }
-    float v = (g + 1.0f) * (float)n;
-    return (v - 1.0f) * 0.5f;
+    F v = (g + F(1)) * (F)n;
+    return (v - F(1)) * F(0.5);
 }
 
-__device__ __forceinline__ float clampf(float v, float lo, float hi) {
+template <typename F>
+__device__ __forceinline__ F clampf(F v, F lo, F hi) {
     return v < lo ? lo : (v > hi ? hi : v);
 }
 
 // Fold p into [lo, hi] by repeated reflection (GridSample page, padding_mode).
-__device__ __forceinline__ float reflect(float p, float lo, float hi) {
-    float span = hi - lo;
-    if (span <= 0.0f) return 0.0f;
-    float d = fabsf(p - lo);
-    float f = floorf(d / span);
-    float fs = f * span;
-    float e = d - fs;
-    float half = floorf(f * 0.5f);
-    bool odd = (f - 2.0f * half) != 0.0f;
+template <typename F>
+__device__ __forceinline__ F reflect(F p, F lo, F hi) {
+    F span = hi - lo;
+    if (span <= F(0)) return F(0);
+    F d = fabs_t(p - lo);
+    F f = floor_t(d / span);
+    F fs = f * span;
+    F e = d - fs;
+    F half = floor_t(f * F(0.5));
+    bool odd = (f - F(2) * half) != F(0);
     return odd ? hi - e : lo + e;
 }
 
-__device__ __forceinline__ void reflect_bounds(int n, int align_corners, float &lo, float &hi) {
+template <typename F>
+__device__ __forceinline__ void reflect_bounds(int n, int align_corners, F &lo, F &hi) {
     if (align_corners) {
-        lo = 0.0f;
-        hi = (float)(n - 1);
+        lo = F(0);
+        hi = (F)(n - 1);
     } else {
-        lo = -0.5f;
-        hi = (float)n - 0.5f;
+        lo = F(-0.5);
+        hi = (F)n - F(0.5);
     }
 }
 
 // Location padding of nearest and linear modes.
-template <int PAD>
-__device__ __forceinline__ float pad_coordinate(float p, int n, int align_corners) {
-    if (PAD == PAD_BORDER) return clampf(p, 0.0f, (float)(n - 1));
+template <int PAD, typename F>
+__device__ __forceinline__ F pad_coordinate(F p, int n, int align_corners) {
+    if (PAD == PAD_BORDER) return clampf(p, F(0), (F)(n - 1));
     if (PAD == PAD_REFLECTION) {
-        float lo, hi;
+        F lo, hi;
         reflect_bounds(n, align_corners, lo, hi);
-        return clampf(reflect(p, lo, hi), 0.0f, (float)(n - 1));
+        return clampf(reflect(p, lo, hi), F(0), (F)(n - 1));
     }
     return p;
 }
@@ -187,13 +204,14 @@ __device__ __forceinline__ void cubic_weights(float t, float w[4]) {
     w[3] = fmaf(fmaf(fmaf(a, x3, -5.0f * a), x3, 8.0f * a), x3, -4.0f * a);
 }
 
-// Tap index of cubic mode after per-tap padding (border / reflection).
-template <int PAD>
+// Tap index of cubic mode after per-tap padding (border / reflection), the
+// reflection folded in the coordinate type F.
+template <int PAD, typename F = float>
 __device__ __forceinline__ int pad_tap(int i, int n, int align_corners) {
     if (PAD == PAD_BORDER) return i < 0 ? 0 : (i > n - 1 ? n - 1 : i);
-    float lo, hi;
+    F lo, hi;
     reflect_bounds(n, align_corners, lo, hi);
-    return (int)clampf(reflect((float)i, lo, hi), 0.0f, (float)(n - 1));
+    return (int)clampf(reflect((F)i, lo, hi), F(0), (F)(n - 1));
 }
 
 // ----------------------------------------------------------- block order

@@ -143,12 +143,33 @@ inline void resize_tile_shape(int q, int out_w, int out_h, int *tw, int *th) {
     *th = h;
 }
 
-// Launchers (gs_kernels.hip, gs_resize.hip).  Return 0 on success or the hipError_t of the
+// One launch of the any-rank, any-type sampler (gs_nd.hip).
+struct NdParams {
+    const void *X;
+    void *Y;
+    const void *grid;
+    int x_dtype;               // 0 f32, 1 f16, 2 bf16, 3 f64, 4 i8, 5 u8, 6 i16, 7 u16,
+                               // 8 i32, 9 u32, 10 i64, 11 u64
+    int grid_dtype;            // 0 f32, 1 f16, 2 bf16, 3 f64
+    int N, C;
+    int in_ext[6];             // spatial input extents, outermost first
+    uint32_t out_count;        // output locations per image (<= 2^28)
+    uint32_t in_plane_bytes, out_plane_bytes;  // each <= 2^30
+    int padding, align_corners;
+    int tiles;                 // ceil(out_count / 256)
+    int cgroups, cpg, nblocks; // channel groups, channels per group, blocks
+};
+
+// Launchers (gs_kernels.hip, gs_resize.hip, gs_nd.hip).  Return 0 on success or the hipError_t of the
 // launch.  `rank` is 2 or 3; `dtype` 0 f32, 1 f16, 2 bf16; `vec_in` selects
 // 16-byte staging loads (input rows a whole number of 16-byte chunks).
 int launch_grid_sample(const SampleParams &p, int rank, bool fused, int mode, int padding,
                        int dtype, bool vec_in, hipStream_t stream);
 int launch_affine_grid(const AffineParams &p, int rank, hipStream_t stream);
+// `rank` 1..6 spatial axes; `double_grid`: the grid is double (coordinates in
+// double), else fp32 / fp16 / bf16 (coordinates in fp32).
+int launch_grid_sample_nd(const NdParams &p, int rank, int mode, bool double_grid,
+                          hipStream_t stream);
 // `d3`: the third axis from the end is resized; `mode` 0 nearest, 1 linear,
 // 2 cubic.
 int launch_resize(const ResizeParams &p, bool d3, int mode, int dtype, bool vec_in,

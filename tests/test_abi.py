@@ -34,7 +34,8 @@ def declared_functions():
 def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "gs_abi_version", "gs_status_string", "gs_affine_grid", "gs_grid_sample_2d",
-        "gs_grid_sample_3d", "gs_affine_grid_sample_fused", "gs_resize", "gs_resize_output_shape"])
+        "gs_grid_sample_3d", "gs_affine_grid_sample_fused", "gs_resize", "gs_resize_output_shape",
+        "gs_grid_sample"])
 
 
 def test_library_exports_every_declared_symbol(gs):
@@ -66,8 +67,10 @@ def sample2d(gs, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(x_dtype=7), 3),
-    (dict(grid_dtype=1), 3),
+    (dict(x_dtype=12), 3),
+    (dict(x_dtype=-1), 3),
+    (dict(grid_dtype=4), 3),
+    (dict(grid_dtype=5), 3),
     (dict(mode=3), 4),
     (dict(mode=-1), 4),
     (dict(padding=3), 4),
@@ -231,3 +234,30 @@ def test_resize_output_shape_rejects(gs):
     assert f([2, 3], [0, 1], sz=[1, -1]) == 2
     assert f([2, 3], [0, 1], sz=[1, 1], pol=3) == 4
     assert f([2, 3], None, sc=[1, 1], n=1) == 2       # no axes: one value per axis
+
+
+def test_grid_sample_any_rank_rejects(gs):
+    lib = gs.lib()
+
+    def f(xs, gsh, rank=None, xdt=0, gdt=0, X=FAKE, Y=FAKE, grid=FAKE):
+        return lib.gs_grid_sample(X, xdt, gs.int64_array(xs), len(xs) if rank is None else rank,
+                                  grid, gdt, gs.int64_array(gsh), 0, 0, 0, Y, None)
+
+    assert f([1, 2, 3], [1, 4, 1], rank=2) == 2              # x_rank below 3
+    assert f([1] * 9, [1] * 8 + [7], rank=9) == 2             # more than 6 spatial axes
+    assert f([1, 2, 3], [1, 4, 2]) == 2                       # last grid dim must be r
+    assert f([1, 2, 3], [2, 4, 1]) == 2                       # batch mismatch
+    assert f([1, 2, 3], [1, 4, 1], xdt=13) == 3
+    assert f([1, 2, 3], [1, 4, 1], gdt=4) == 3                # integer grids are not allowed
+    assert f([1, 2, 3], [1, 4, 1], grid=None) == 1
+    assert f([1, 2, 3], [1, 0, 1], X=None, Y=None, grid=None) == 0
+    assert f([1, 2, 1 << 28], [1, 4, 1], xdt=3) == 5          # 2^28 doubles: above 2^30 bytes
+
+
+def test_binding_dtype_codes(gs):
+    torch = pytest.importorskip("torch")
+    assert gs.dtype_code(torch.zeros(1, dtype=torch.uint8)) == gs.GS_U8
+    assert gs.dtype_code(torch.zeros(1, dtype=torch.float64)) == gs.GS_F64
+    assert gs.dtype_code(torch.zeros(1, dtype=torch.int64)) == gs.GS_I64
+    with pytest.raises(TypeError):
+        gs.dtype_code(torch.zeros(1, dtype=torch.bool))

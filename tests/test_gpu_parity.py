@@ -243,7 +243,7 @@ def test_errors_raise_through_binding(gsa):
     with pytest.raises(gsa.GSError):
         gsa.grid_sample(X, torch.zeros(3, 5, 5, 2, device="cuda"))      # batch mismatch
     with pytest.raises(gsa.GSError):
-        gsa.grid_sample(X, torch.zeros(2, 5, 5, 2, device="cuda", dtype=torch.float16))
+        gsa.grid_sample(X, torch.zeros(2, 5, 5, 2, device="cuda", dtype=torch.int32))  # integer grid
     with pytest.raises(gsa.GSError):
         gsa.grid_sample(X, torch.zeros(2, 5, 5, 2, device="cuda"), align_corners=3)
     with pytest.raises(gsa.GSError):
