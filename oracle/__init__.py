@@ -62,6 +62,8 @@ def _bind(path: str):
     i64, c_int = ctypes.c_int64, ctypes.c_int
     lib.oracle_affine_grid.argtypes = [p_f32, c_int, i64, p_i64, c_int, p_f32]
     lib.oracle_affine_grid.restype = c_int
+    lib.oracle_affine_grid_d.argtypes = [p_f64, c_int, i64, p_i64, c_int, p_f64]
+    lib.oracle_affine_grid_d.restype = c_int
     lib.oracle_grid_sample.argtypes = [p_f32, c_int, i64, i64, p_i64, p_f32, p_i64,
                                        c_int, c_int, c_int, p_f64]
     lib.oracle_grid_sample.restype = c_int
@@ -108,12 +110,16 @@ def _ptr(a: np.ndarray, ctype):
 
 
 def affine_grid(theta: np.ndarray, size, align_corners: int = 0, lib=None) -> np.ndarray:
-    """AffineGrid(theta, size) -> grid (fp32).
+    """AffineGrid(theta, size) -> grid.
 
-    theta: (N, r, r+1) fp32.  size: (N, C, *spatial) as on the page (C unused).
-    Returns (N, *spatial, r) fp32.
+    theta: (N, r, r+1) fp32 (fp16 and bf16 theta are passed widened exactly;
+    the caller rounds the fp32 grid to the half type) or float64 (then the
+    steps run in float64 and the grid is float64).  size: (N, C, *spatial) as
+    on the page (C unused).  Returns (N, *spatial, r).
     """
     lib = lib or _load()
+    if np.asarray(theta).dtype == np.float64:
+        return _affine_grid_d(np.ascontiguousarray(theta), size, align_corners, lib)
     theta = np.ascontiguousarray(theta, dtype=np.float32)
     size = [int(s) for s in size]
     n, r = theta.shape[0], theta.shape[1]
@@ -125,6 +131,21 @@ def affine_grid(theta: np.ndarray, size, align_corners: int = 0, lib=None) -> np
                                 int(align_corners), _ptr(out, ctypes.c_float))
     if rc:
         raise ValueError("oracle_affine_grid rejected its arguments")
+    return out
+
+
+def _affine_grid_d(theta, size, align_corners, lib):
+    size = [int(s) for s in size]
+    n, r = theta.shape[0], theta.shape[1]
+    if theta.shape != (n, r, r + 1) or len(size) != r + 2 or size[0] != n:
+        raise ValueError("theta %s does not match size %s" % (theta.shape, size))
+    spatial = np.asarray(size[2:], dtype=np.int64)
+    out = np.empty((n, *size[2:], r), dtype=np.float64)
+    rc = lib.oracle_affine_grid_d(_ptr(theta, ctypes.c_double), r, n,
+                                  _ptr(spatial, ctypes.c_int64), int(align_corners),
+                                  _ptr(out, ctypes.c_double))
+    if rc:
+        raise ValueError("oracle_affine_grid_d rejected its arguments")
     return out
 
 

@@ -147,6 +147,59 @@ int oracle_affine_grid(const float *theta, int r, int64_t N, const int64_t *out_
     return 0;
 }
 
+/* AffineGrid with a double theta: the same steps in float64 (the grid is
+ * double too; AffineGrid page, Type Constraints: theta and grid share T1). */
+static double base_position_d(int64_t i, int64_t m, int align_corners)
+{
+    if (align_corners) {
+        if (m == 1)
+            return 0.0;
+        return (double)(2 * i) / (double)(m - 1) - 1.0;
+    }
+    return (double)(2 * i + 1) / (double)m - 1.0;
+}
+
+int oracle_affine_grid_d(const double *theta, int r, int64_t N, const int64_t *out_spatial,
+                         int align_corners, double *grid)
+{
+    if (r < 1 || r > OR_MAX_RANK || N < 0)
+        return -1;
+    int64_t count = 1;
+    for (int a = 0; a < r; ++a) {
+        if (out_spatial[a] < 0)
+            return -1;
+        count *= out_spatial[a];
+    }
+    for (int64_t n = 0; n < N; ++n) {
+        const double *th = theta + n * r * (r + 1);
+        for (int64_t flat = 0; flat < count; ++flat) {
+            int64_t idx[OR_MAX_RANK];
+            int64_t rem = flat;
+            for (int a = r - 1; a >= 0; --a) {
+                idx[a] = rem % out_spatial[a];
+                rem /= out_spatial[a];
+            }
+            double b[OR_MAX_RANK]; /* innermost first */
+            for (int j = 0; j < r; ++j) {
+                int a = r - 1 - j;
+                b[j] = base_position_d(idx[a], out_spatial[a], align_corners);
+            }
+            double *out = grid + (n * count + flat) * r;
+            for (int k = 0; k < r; ++k) {
+                const double *row = th + k * (r + 1);
+                double s = row[0] * b[0];
+                for (int j = 1; j < r; ++j) {
+                    double prod = row[j] * b[j];
+                    s = s + prod;
+                }
+                s = s + row[r];
+                out[k] = s;
+            }
+        }
+    }
+    return 0;
+}
+
 /* ---------------------------------------------------------------------- */
 /* GridSample                                                              */
 /* ---------------------------------------------------------------------- */

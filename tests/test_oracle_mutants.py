@@ -59,6 +59,9 @@ MUTANTS = [
 
 
 DOUBLE_MUTANTS = [
+    ("double theta: pixel-centre position off by half a pixel",
+     "return (double)(2 * i + 1) / (double)m - 1.0;", "return (double)(2 * i) / (double)m - 1.0;"),
+    ("double theta: translation column dropped", "s = s + row[r];", "s = s + 0.0 * row[r];"),
     ("double grid: align_corners=0 shift with the wrong sign", "return (v - 1.0) / 2.0;",
      "return (v + 1.0) / 2.0;"),
     ("double grid: reflection bound at the pixel centre", "*lo = -0.5;", "*lo = 0.0;"),
@@ -96,6 +99,12 @@ def pin_battery(om, lib):
         ref = np.array(ex["expected"]).reshape(Y.shape)
         if (np.abs(Y - ref) / np.maximum(1, np.abs(ref))).max() > 2e-6:
             return ex["name"]
+    for ex in load_golden("affine_grid_examples.json"):
+        th = np.array(ex["theta"], np.float64).reshape(ex["theta_shape"])
+        g = om.affine_grid(th, ex["size"], ex["align_corners"], lib=lib)
+        ref = np.array(ex["grid"]).reshape(ex["grid_shape"])
+        if (np.abs(g - ref) / np.maximum(1, np.abs(ref))).max() > 2e-6:
+            return ex["name"] + " (double)"
     for ex in load_golden("grid_sample_examples.json"):
         X = np.array(ex["X"], np.float64).reshape(ex["X_shape"])
         G = np.array(ex["grid"], np.float64).reshape(ex["grid_shape"])

@@ -79,3 +79,35 @@ def test_nearest_copies_large_integers(oracle_mod):
     Y = oracle_mod.grid_sample(X, G, "nearest", "zeros", 1)
     assert oracle_mod.to_integer(Y, np.int32).reshape(-1).tolist() == [2**31 - 1, -2**31,
                                                                       123456789]
+
+
+AFFINE = load_golden("affine_grid_examples.json")
+
+
+@pytest.mark.parametrize("ex", AFFINE, ids=[e["name"] for e in AFFINE])
+def test_affine_grid_examples_in_double(oracle_mod, ex):
+    theta = np.array(ex["theta"], np.float64).reshape(ex["theta_shape"])
+    g = oracle_mod.affine_grid(theta, ex["size"], ex["align_corners"])
+    assert g.dtype == np.float64
+    ref = np.array(ex["grid"]).reshape(ex["grid_shape"])
+    assert (np.abs(g - ref) / np.maximum(1, np.abs(ref))).max() <= PRINT_TOL
+
+
+@pytest.mark.parametrize("ac", [0, 1])
+def test_affine_grid_double_is_a_linear_map_of_linspace(oracle_mod, ac):
+    """Closed form in float64: positions are numpy.linspace over [-1, 1]
+    (corner centres, ac=1) or its pixel centres (ac=0), mapped by theta."""
+    rng = np.random.default_rng(9)
+    theta = rng.normal(0, 1, (2, 3, 4))
+    D, H, W = 3, 4, 5
+    g = oracle_mod.affine_grid(theta, (2, 1, D, H, W), ac)
+
+    def pos(m):
+        if ac:
+            return np.linspace(-1, 1, m) if m > 1 else np.zeros(1)
+        return (2 * np.arange(m) + 1) / m - 1
+
+    z, y, x = np.meshgrid(pos(D), pos(H), pos(W), indexing="ij")
+    hom = np.stack([x, y, z, np.ones_like(x)], -1)
+    ref = np.einsum("dhwj,nkj->ndhwk", hom, theta)
+    assert np.abs(g - ref).max() <= 1e-14
