@@ -94,17 +94,21 @@ const char *gs_status_string(int status);
  * AffineGrid (AffineGrid page, Summary; Inputs theta and size; Output grid).
  *
  *   theta        device, (N, 2, 3) for size_len 4 or (N, 3, 4) for size_len 5,
- *                element type theta_dtype (GS_F32 only).  Row k maps the
- *                homogeneous position (x, y[, z], 1) to component k.
+ *                element type theta_dtype: GS_F32, GS_F16, GS_BF16 or GS_F64
+ *                (Type Constraints: theta and grid share one type).  Row k
+ *                maps the homogeneous position (x, y[, z], 1) to component k.
+ *                Half types compute in fp32 and round the grid once; GS_F64
+ *                computes in double.
  *   size, size_len  host, the output size (N, C, H, W) or (N, C, D, H, W);
  *                C is not used.  All entries >= 0.
  *   align_corners   1: -1 and 1 are the centres of the corner pixels;
  *                0: they are the outer edges of the corner pixels.
- *   grid         device, (N, H, W, 2) or (N, D, H, W, 3) fp32, written whole.
+ *   grid         device, (N, H, W, 2) or (N, D, H, W, 3), element type
+ *                theta_dtype, written whole.
  *                Component 0 is x (along W), 1 is y (along H), 2 is z (along D).
  *
  * Errors: GS_ERR_NULL (theta or grid NULL with N*spatial > 0), GS_ERR_SHAPE
- * (size_len not 4 or 5, negative extent), GS_ERR_DTYPE (theta not GS_F32),
+ * (size_len not 4 or 5, negative extent), GS_ERR_DTYPE (theta not a float type),
  * GS_ERR_ATTR (align_corners not 0/1), GS_ERR_TOO_LARGE (H*W or D*H*W above
  * 2^31-1, or more than 2^24 thread blocks), GS_ERR_HIP.
  */

@@ -113,7 +113,8 @@ def _check(status: int, where: str):
 
 
 def affine_grid(theta, size, align_corners: int = 0, out=None, stream=None):
-    """AffineGrid(theta, size) -> grid on the GPU (gs_affine_grid)."""
+    """AffineGrid(theta, size) -> grid on the GPU (gs_affine_grid); the grid
+    has theta's element type."""
     torch = _torch()
     theta = _device_tensor(theta, "theta")
     size = [int(s) for s in size]
@@ -122,9 +123,9 @@ def affine_grid(theta, size, align_corners: int = 0, out=None, stream=None):
         raise ValueError("theta %s does not match size %s" % (tuple(theta.shape), size))
     shape = (size[0], *size[2:], r)
     if out is None:
-        out = torch.empty(shape, dtype=torch.float32, device=theta.device)
-    elif tuple(out.shape) != shape or not out.is_contiguous() or out.dtype != torch.float32:
-        raise ValueError("out must be a contiguous fp32 tensor of shape %s" % (shape,))
+        out = torch.empty(shape, dtype=theta.dtype, device=theta.device)
+    elif tuple(out.shape) != shape or not out.is_contiguous() or out.dtype != theta.dtype:
+        raise ValueError("out must be a contiguous %s tensor of shape %s" % (theta.dtype, shape))
     st = lib().gs_affine_grid(ctypes.c_void_p(theta.data_ptr()), dtype_code(theta), int64_array(size),
                               len(size), int(align_corners), ctypes.c_void_p(out.data_ptr()),
                               _stream(stream, theta.device))

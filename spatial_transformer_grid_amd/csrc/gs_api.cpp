@@ -228,7 +228,7 @@ int gs_affine_grid(const void *theta, int theta_dtype, const int64_t *size, int 
                    int align_corners, void *grid, void *stream) {
     if (!size) return GS_ERR_NULL;
     if (size_len != 4 && size_len != 5) return GS_ERR_SHAPE;
-    if (theta_dtype != GS_F32) return GS_ERR_DTYPE;
+    if (!valid_grid_dtype(theta_dtype)) return GS_ERR_DTYPE;
     if (align_corners != 0 && align_corners != 1) return GS_ERR_ATTR;
     for (int i = 0; i < size_len; ++i)
         if (size[i] < 0) return GS_ERR_SHAPE;
@@ -243,8 +243,9 @@ int gs_affine_grid(const void *theta, int theta_dtype, const int64_t *size, int 
     if (tiles > kMaxBlocks || N * tiles > kMaxBlocks) return GS_ERR_TOO_LARGE;
     const Extents out = spatial3(size + 2, r);
     gs::AffineParams p;
-    p.theta = (const float *)theta;
-    p.grid = (float *)grid;
+    p.theta = theta;
+    p.grid = grid;
+    p.theta_dtype = theta_dtype;
     p.N = (int)N;
     p.out_d = out.d;
     p.out_h = out.h;

@@ -113,13 +113,15 @@ __device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
 // ------------------------------------------------------------ coordinates
 
 // Position of sample i of m evenly spaced samples over [-1, 1]
-// (AffineGrid page, Summary; align_corners as described there).
-__device__ __forceinline__ float base_position(int i, int m, int align_corners) {
+// (AffineGrid page, Summary; align_corners as described there), in the
+// computation type F of the grid (float, or double for a double theta).
+template <typename F = float>
+__device__ __forceinline__ F base_position(int i, int m, int align_corners) {
     if (align_corners) {
-        if (m == 1) return 0.0f;
-        return (float)(2 * i) / (float)(m - 1) - 1.0f;
+        if (m == 1) return F(0);
+        return (F)(2 * i) / (F)(m - 1) - F(1);
     }
-    return (float)(2 * i + 1) / (float)m - 1.0f;
+    return (F)(2 * i + 1) / (F)m - F(1);
 }
 
 // The coordinate steps below are written once for the grid's coordinate

@@ -51,20 +51,21 @@ __device__ __forceinline__ void decompose(uint32_t l, int out_w, int out_h, uint
 // base position.  Products and sums are rounded one at a time, summed left
 // to right with the translation last; gs_affine_grid and the fused sampler
 // both use this function, so they produce the same bits.
-template <int R>
-__device__ __forceinline__ void affine_vector(const float *th, int d, int h, int w, int out_d,
-                                              int out_h, int out_w, int ac, float g[R]) {
-    float b[3];
-    b[0] = base_position(w, out_w, ac);
-    b[1] = base_position(h, out_h, ac);
-    b[2] = R == 3 ? base_position(d, out_d, ac) : 0.0f;
+// The computation type F is float (fp32, fp16 and bf16 theta) or double.
+template <int R, typename F>
+__device__ __forceinline__ void affine_vector(const F *th, int d, int h, int w, int out_d,
+                                              int out_h, int out_w, int ac, F g[R]) {
+    F b[3];
+    b[0] = base_position<F>(w, out_w, ac);
+    b[1] = base_position<F>(h, out_h, ac);
+    b[2] = R == 3 ? base_position<F>(d, out_d, ac) : F(0);
 #pragma unroll
     for (int k = 0; k < R; ++k) {
-        const float *row = th + k * (R + 1);
-        float s = row[0] * b[0];
+        const F *row = th + k * (R + 1);
+        F s = row[0] * b[0];
 #pragma unroll
         for (int j = 1; j < R; ++j) {
-            float prod = row[j] * b[j];
+            F prod = row[j] * b[j];
             s = s + prod;
         }
         s = s + row[R];
@@ -72,8 +73,26 @@ __device__ __forceinline__ void affine_vector(const float *th, int d, int h, int
     }
 }
 
-template <int R>
+// Element type TT of theta and the grid (AffineGrid page, Type Constraints):
+// float, double, _Float16, or __bf16; half types compute in fp32 and round the
+// grid to nearest even once, at the store.
+template <typename TT>
+struct GridElem {
+    typedef float F;
+    __device__ static F widen(TT v) { return (F)v; }
+    __device__ static TT narrow(F v) { return (TT)v; }
+};
+template <>
+struct GridElem<double> {
+    typedef double F;
+    __device__ static double widen(double v) { return v; }
+    __device__ static double narrow(double v) { return v; }
+};
+
+template <int R, typename TT>
 __global__ __launch_bounds__(kBlock) void affine_grid_kernel(AffineParams p) {
+    using E = GridElem<TT>;
+    using F = typename E::F;
     const int lb = xcd_logical_block(p.nblocks);
     if (lb >= p.nblocks) return;
     const int n = lb / p.tiles_per_n;
@@ -82,12 +101,15 @@ __global__ __launch_bounds__(kBlock) void affine_grid_kernel(AffineParams p) {
     if (l >= p.out_count) return;
     int d, h, w;
     decompose<R>(l, p.out_w, p.out_h, p.div_w_m, p.div_w_s, p.div_h_m, p.div_h_s, d, h, w);
-    float g[R];
-    affine_vector<R>(p.theta + (size_t)n * R * (R + 1), d, h, w, p.out_d, p.out_h, p.out_w,
-                     p.align_corners, g);
-    float *out = p.grid + ((size_t)n * p.out_count + l) * R;
+    const TT *tp = (const TT *)p.theta + (size_t)n * R * (R + 1);
+    F th[R * (R + 1)];
 #pragma unroll
-    for (int k = 0; k < R; ++k) out[k] = g[k];
+    for (int i = 0; i < R * (R + 1); ++i) th[i] = E::widen(tp[i]);
+    F g[R];
+    affine_vector<R, F>(th, d, h, w, p.out_d, p.out_h, p.out_w, p.align_corners, g);
+    TT *out = (TT *)p.grid + ((size_t)n * p.out_count + l) * R;
+#pragma unroll
+    for (int k = 0; k < R; ++k) out[k] = E::narrow(g[k]);
 }
 
 // ------------------------------------------------------------------ taps
@@ -703,12 +725,24 @@ int launch_grid_sample(const SampleParams &p, int rank, bool fused, int mode, in
                  : by_mode<3, false>(p, mode, padding, dtype, vec_in, stream);
 }
 
-int launch_affine_grid(const AffineParams &p, int rank, hipStream_t stream) {
+template <typename TT>
+static int affine_launch(const AffineParams &p, int rank, hipStream_t stream) {
     if (rank == 2)
-        hipLaunchKernelGGL(affine_grid_kernel<2>, launch_grid(p.nblocks), dim3(kBlock), 0, stream, p);
+        hipLaunchKernelGGL((affine_grid_kernel<2, TT>), launch_grid(p.nblocks), dim3(kBlock), 0,
+                           stream, p);
     else
-        hipLaunchKernelGGL(affine_grid_kernel<3>, launch_grid(p.nblocks), dim3(kBlock), 0, stream, p);
+        hipLaunchKernelGGL((affine_grid_kernel<3, TT>), launch_grid(p.nblocks), dim3(kBlock), 0,
+                           stream, p);
     return (int)hipGetLastError();
+}
+
+int launch_affine_grid(const AffineParams &p, int rank, hipStream_t stream) {
+    switch (p.theta_dtype) {
+    case 1: return affine_launch<_Float16>(p, rank, stream);
+    case 2: return affine_launch<__bf16>(p, rank, stream);
+    case 3: return affine_launch<double>(p, rank, stream);
+    default: return affine_launch<float>(p, rank, stream);
+    }
 }
 
 }  // namespace gs

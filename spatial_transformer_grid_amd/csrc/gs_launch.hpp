@@ -74,8 +74,9 @@ inline void tile_shape(int r, int mode, int out_w, int *w, int *h, int *d) {
 inline int stage_chunk_elems(int elem_bytes) { return 16 / elem_bytes; }
 
 struct AffineParams {
-    const float *theta;  // (N, R, R+1)
-    float *grid;         // (N, out..., R)
+    const void *theta;   // (N, R, R+1), element type theta_dtype
+    void *grid;          // (N, out..., R), element type theta_dtype
+    int theta_dtype;     // 0 f32, 1 f16, 2 bf16, 3 f64
     int N;
     int out_d, out_h, out_w;
     uint32_t out_count;

@@ -115,7 +115,8 @@ def test_affine_grid_rejects(gs):
     f = lambda size, n=None, dt=0, ac=0, theta=FAKE, grid=FAKE: lib.gs_affine_grid(
         theta, dt, gs.int64_array(size), len(size) if n is None else n, ac, grid, None)
     assert f([2, 3, 4, 5], n=3) == 2
-    assert f([2, 3, 4, 5], dt=1) == 3
+    assert f([2, 3, 4, 5], dt=4) == 3          # integer theta
+    assert f([2, 3, 4, 5], dt=12) == 3
     assert f([2, 3, 4, 5], ac=-1) == 4
     assert f([2, 3, -4, 5]) == 2
     assert f([2, 3, 4, 5], theta=None) == 1

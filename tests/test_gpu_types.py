@@ -200,3 +200,31 @@ def test_non_finite_locations(gsa):
         run(gsa, X, G, mode, pad, 0, "f32", what="non-finite 1-D")
     Xi = rng.integers(-100, 100, (1, 3, 40)).astype(np.int16)
     run(gsa, Xi, G, "linear", "zeros", 1, "int16", what="non-finite int16")
+
+
+
+
+@pytest.mark.parametrize("kind,rank,ac", list(itertools.product(["f64", "f16", "bf16"], [2, 3],
+                                                                [0, 1])))
+def test_affine_grid_types(gsa, kind, rank, ac):
+    """AffineGrid with a double theta matches the float64 oracle bit for bit;
+    with fp16 / bf16 theta, the fp32 oracle on the widened theta rounded once
+    to the half type."""
+    torch = torch_mod()
+    note("affine_grid %s rank %d ac=%d" % (kind, rank, ac))
+    rng = np.random.default_rng(70 + rank)
+    theta = rng.normal(0, 1, (3, rank, rank + 1))
+    size = (3, 2) + ((37, 45) if rank == 2 else (9, 10, 11))
+    if kind == "f64":
+        g = gsa.affine_grid(tgpu(theta), size, ac)
+        got = g.cpu().numpy()
+        ref = oracle.affine_grid(theta, size, ac)
+        assert got.dtype == np.float64 and np.array_equal(got, ref)
+        return
+    bits = W.to_half_bits(theta.astype(np.float32), kind)
+    tdt = torch.float16 if kind == "f16" else torch.bfloat16
+    g = gsa.affine_grid(tgpu(bits.view(np.int16), tdt), size, ac)
+    assert g.dtype == tdt
+    got = g.view(torch.int16).cpu().numpy().view(np.uint16)
+    ref32 = oracle.affine_grid(W.half_bits_to_f32(bits, kind), size, ac)
+    assert np.array_equal(got, W.to_half_bits(ref32, kind))
