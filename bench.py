@@ -177,7 +177,7 @@ def run_paths(torch, gsa, flush_buf):
     sink = torch.empty((), device="cuda")
 
     def flush():
-        torch.sum(flush_buf, out=sink)
+        torch.sum(flush_buf, dim=0, out=sink)
 
     def record(name, workload, kernel, us, outputs, x_bytes_full, x_bytes_fp, other_bytes, warm_us=None):
         comp = x_bytes_fp + other_bytes
@@ -264,6 +264,29 @@ def run_paths(torch, gsa, flush_buf):
         record("flow2d_half/%s-linear-zeros" % kind, w.name, "gs_grid_sample_2d", us, w.outputs,
                X.numel() * 2, fp, G.numel() * 4 + w.outputs * 2)
         del X, Y
+
+    # other ranks and element types (the any-rank kernel)
+    for name, tw in W.TYPE_WORKLOADS.items():
+        inp = W.make_type_inputs(tw)
+        n, c = tw.x_shape[:2]
+        X = torch.from_numpy(inp["X"]).cuda()
+        if inp["theta"] is not None:
+            th = torch.from_numpy(inp["theta"]).cuda()
+            G = gsa.affine_grid(th, (n, c) + tw.out_spatial, tw.align_corners)
+        else:
+            G = torch.from_numpy(inp["grid"]).cuda()
+        Y = torch.empty((n, c) + tw.out_spatial, dtype=X.dtype, device="cuda")
+        es = X.element_size()
+        fp = footprint_elements(G.cpu().numpy(), tw.x_shape[2:], tw.mode, tw.padding,
+                                tw.align_corners) * c * es
+        fn = lambda: gsa.grid_sample(X, G, tw.mode, tw.padding, tw.align_corners, out=Y)
+        fn()
+        us, _ = time_kernel(torch, fn, 20, flush)
+        warm, _ = time_kernel(torch, fn, 20)
+        record("%s/%s-%s" % (name, tw.mode, tw.padding), name, "gs_grid_sample (any-rank kernel)",
+               us, tw.outputs, X.numel() * es, fp, G.numel() * G.element_size() + tw.outputs * es,
+               warm)
+        del X, Y, G, inp
 
     # Resize workloads (fp32): at their scales every input element has a
     # non-zero weight, so all of X is compulsory

@@ -1,5 +1,5 @@
-"""The synthetic workloads (five sampler, five Resize) on the GPU against the
-oracle.
+"""The synthetic workloads (five sampler, five Resize, three of other ranks
+and element types) on the GPU against the oracle.
 
 * reduced shapes (same distributions, several tiles, ragged tails): every
   output element is compared;
@@ -168,3 +168,68 @@ def test_resize_workload_full_size_sampled(gsa, name):
     ref = oracle.resize_points(X, shape, idx, w.full_scales(), w.mode,
                                w.coordinate_transformation_mode)
     check(got, ref, w.mode, "f32", np.abs(X).max(), "full " + name)
+
+
+# ----------------------------------------------- other ranks and element types
+
+TYPE_REDUCED = {
+    "stn2d_u8": ((3, 3, 45, 53), (41, 47)),
+    "signal1d_f32": ((3, 5, 300), (257,)),
+    "vol3d_f64": ((2, 3, 9, 10, 11), (7, 8, 9)),
+}
+
+
+def type_expected(ref, x):
+    """The oracle's float64 value after the output conversion of X's type
+    (the any-rank kernel matches it bit for bit)."""
+    if x.dtype == np.uint8:
+        return oracle.to_integer(ref, np.uint8)
+    if x.dtype == np.float32:
+        return ref.astype(np.float32)
+    return ref
+
+
+def type_gpu(gsa, w, inp):
+    torch = torch_mod()
+    n, c = inp["x_shape"][:2]
+    X = torch.from_numpy(inp["X"]).cuda()
+    if inp["theta"] is not None:
+        grid = gsa.affine_grid(torch.from_numpy(inp["theta"]).cuda(),
+                               (n, c) + tuple(inp["out_spatial"]), w.align_corners)
+        g_ref = oracle.affine_grid(inp["theta"], (n, c) + tuple(inp["out_spatial"]),
+                                   w.align_corners)
+    else:
+        grid = torch.from_numpy(inp["grid"]).cuda()
+        g_ref = inp["grid"]
+    return gsa.grid_sample(X, grid, w.mode, w.padding, w.align_corners), g_ref
+
+
+@pytest.mark.parametrize("name", list(W.TYPE_WORKLOADS))
+def test_type_workload_reduced_all_elements(gsa, name):
+    w = W.TYPE_WORKLOADS[name]
+    x_shape, out_sp = TYPE_REDUCED[name]
+    note("reduced %s x=%s out=%s" % (name, x_shape, out_sp))
+    inp = W.make_type_inputs(w, x_shape, out_sp)
+    Y, g_ref = type_gpu(gsa, w, inp)
+    torch_mod().cuda.synchronize()
+    got = Y.cpu().numpy()
+    ref = type_expected(oracle.grid_sample(inp["X"], g_ref, w.mode, w.padding, w.align_corners),
+                        inp["X"])
+    assert np.array_equal(got, ref), name
+
+
+@pytest.mark.parametrize("name", list(W.TYPE_WORKLOADS))
+def test_type_workload_full_size_sampled(gsa, name):
+    w = W.TYPE_WORKLOADS[name]
+    note("full %s x=%s" % (name, w.x_shape))
+    inp = W.make_type_inputs(w)
+    Y, g_ref = type_gpu(gsa, w, inp)
+    n, c = w.x_shape[:2]
+    count = int(np.prod(w.out_spatial))
+    idx = sample_indices(n, c, count, 16384, w.seed)
+    torch = torch_mod()
+    got = Y.reshape(-1)[torch.from_numpy(idx).cuda()].cpu().numpy()
+    del Y
+    ref = type_expected(oracle.grid_sample_points(inp["X"], g_ref, idx, w.mode, w.padding,
+                                                  w.align_corners), inp["X"])
+    assert np.array_equal(got, ref), name

@@ -42,6 +42,10 @@ __all__ = [
     "ResizeWorkload",
     "RESIZE_WORKLOADS",
     "make_resize_input",
+    "TypeWorkload",
+    "TYPE_WORKLOADS",
+    "make_type_inputs",
+    "smooth_warp_1d",
 ]
 
 
@@ -263,3 +267,83 @@ RESIZE_WORKLOADS = {
 def make_resize_input(w: ResizeWorkload, x_shape=None) -> np.ndarray:
     """X of a Resize workload (optionally at a reduced shape), fp32 U(-1, 1)."""
     return uniform(rng(w.seed), tuple(x_shape or w.x_shape), -1.0, 1.0)
+
+
+def smooth_warp_1d(g: np.random.Generator, n: int, wo: int, n_waves: int = 4,
+                   amp: float = 0.01) -> np.ndarray:
+    """(n, wo, 1) fp32 field: the pixel-centre positions of a wo-sample line
+    over [-1, 1] plus a sum of ``n_waves`` sinusoids of amplitude ``amp`` with
+    wave numbers u ~ U(-4, 4) and phases phi ~ U(0, 2*pi).  float64, rounded
+    once to fp32."""
+    xs = -1.0 + (2.0 * np.arange(wo) + 1.0) / wo
+    out = np.empty((n, wo, 1), dtype=np.float32)
+    for b in range(n):
+        u = g.uniform(-4.0, 4.0, n_waves)
+        phi = g.uniform(0.0, 2.0 * math.pi, n_waves)
+        flow = np.zeros(wo)
+        for j in range(n_waves):
+            flow += amp * np.sin(2.0 * math.pi * u[j] * xs + phi[j])
+        out[b, :, 0] = (xs + flow).astype(np.float32)
+    return out
+
+
+@dataclass(frozen=True)
+class TypeWorkload:
+    """A GridSample workload of another rank or element type."""
+
+    name: str
+    seed: int
+    x_shape: tuple
+    out_spatial: tuple
+    mode: str
+    padding: str
+    align_corners: int
+    x_kind: str                  # "uint8" | "f32" | "f64"
+    grid_kind: str               # "affine_near_identity" | "smooth_warp_1d"
+    precision: str = "f32"       # theta / grid element type: "f32" | "f64"
+
+    @property
+    def outputs(self) -> int:
+        return int(self.x_shape[0] * self.x_shape[1] * np.prod(self.out_spatial))
+
+
+TYPE_WORKLOADS = {
+    # an STN batch of 8-bit RGB images warped by near-identity affine maps
+    "stn2d_u8": TypeWorkload("stn2d_u8", 31, (64, 3, 512, 512), (512, 512), "linear", "zeros", 0,
+                             "uint8", "affine_near_identity"),
+    # 1-D resampling of long fp32 signals along smooth monotone warps
+    "signal1d_f32": TypeWorkload("signal1d_f32", 32, (64, 128, 8192), (8192,), "linear", "zeros",
+                                 0, "f32", "smooth_warp_1d"),
+    # the volumetric transform in double precision (theta, grid and X)
+    "vol3d_f64": TypeWorkload("vol3d_f64", 33, (2, 16, 64, 64, 64), (64, 64, 64), "linear",
+                              "border", 0, "f64", "affine_near_identity", "f64"),
+}
+
+
+def make_type_inputs(w: TypeWorkload, x_shape=None, out_spatial=None):
+    """Draw a TypeWorkload's inputs: theta (affine kinds, w.precision) or the
+    grid, then X in its element type (uint8 uniform over 0..255, fp32
+    U(-1, 1), double N(0, 1))."""
+    x_shape = tuple(x_shape or w.x_shape)
+    out_spatial = tuple(out_spatial or w.out_spatial)
+    n = x_shape[0]
+    r = len(out_spatial)
+    g = rng(w.seed)
+    theta = grid = None
+    if w.grid_kind == "affine_near_identity":
+        theta = near_identity_theta(g, n, r, 0.1)
+        if w.precision == "f64":
+            eye = np.zeros((r, r + 1))
+            eye[:r, :r] = np.eye(r)
+            theta = eye[None] + 0.1 * g.standard_normal((n, r, r + 1))
+    elif w.grid_kind == "smooth_warp_1d":
+        grid = smooth_warp_1d(g, n, out_spatial[0])
+    else:
+        raise ValueError(w.grid_kind)
+    if w.x_kind == "uint8":
+        X = g.integers(0, 256, x_shape, dtype=np.uint8)
+    elif w.x_kind == "f64":
+        X = g.standard_normal(x_shape)
+    else:
+        X = uniform(g, x_shape, -1.0, 1.0)
+    return {"X": X, "theta": theta, "grid": grid, "x_shape": x_shape, "out_spatial": out_spatial}
