@@ -1,11 +1,13 @@
-"""Plain CPU reference (oracle) for AffineGrid, GridSample and Resize.
+"""Plain CPU reference (oracle) for AffineGrid, GridSample, Resize and
+DeformConv.
 
 TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
 CPU-baseline leg may import this package.  The GPU library and its Python
 binding never import it, and it never imports them.
 
-The arithmetic lives in ``oracle.c`` (AffineGrid, GridSample) and
-``resize.c`` (Resize), plain scalar C built with gcc ``-O2 -ffp-contract=off``;
+The arithmetic lives in ``oracle.c`` (AffineGrid, GridSample), ``resize.c``
+(Resize) and ``deform_conv.c`` (DeformConv), plain scalar C built with gcc
+``-O2 -ffp-contract=off``;
 this module only builds them, loads them and marshals numpy arrays.
 Attribute names and defaults follow the GridSample page (mode "linear",
 padding_mode "zeros"; align_corners 0, the value every example that omits it
@@ -24,6 +26,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _RESIZE_SRC = os.path.join(_HERE, "resize.c")
+_DEFORM_SRC = os.path.join(_HERE, "deform_conv.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 MODES = {"linear": 0, "nearest": 1, "cubic": 2}
@@ -41,14 +44,14 @@ _default = None
 
 
 def build(force: bool = True, src: str = _SRC, out: str = _LIB,
-          resize_src: str = _RESIZE_SRC) -> str:
-    """Compile oracle.c and resize.c (or other copies of them) into one shared
-    library."""
+          resize_src: str = _RESIZE_SRC, deform_src: str = _DEFORM_SRC) -> str:
+    """Compile oracle.c, resize.c and deform_conv.c (or other copies of them)
+    into one shared library."""
     if not force and os.path.exists(out):
         return out
     tmp = out + ".tmp%d" % os.getpid()
     cmd = ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
-           "-Wall", "-Wextra", "-o", tmp, src, resize_src, "-lm"]
+           "-Wall", "-Wextra", "-o", tmp, src, resize_src, deform_src, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
@@ -87,6 +90,10 @@ def _bind(path: str):
     lib.oracle_resize_points.argtypes = [p_f32, c_int, p_i64, p_i64, p_f32, c_int, c_int, c_int,
                                          ctypes.c_double, c_int, p_i64, i64, p_f64]
     lib.oracle_resize_points.restype = c_int
+    lib.oracle_deform_conv.argtypes = [p_f64, c_int, i64, i64, p_i64, p_f64, i64, p_i64, p_f64,
+                                       p_f64, p_f64, p_i64, p_i64, p_i64, p_i64, i64, i64, c_int,
+                                       p_f64]
+    lib.oracle_deform_conv.restype = c_int
     return lib
 
 
@@ -331,3 +338,52 @@ def to_integer(values: np.ndarray, dtype) -> np.ndarray:
     inside = (v > lo) & (v < hi)
     out[inside] = v[inside].astype(dtype)
     return out
+
+
+def deform_conv_output_shape(in_sp, ksz, strides, pads, dilations):
+    """(in + pad_begin + pad_end - (dilation * (k - 1) + 1)) // stride + 1."""
+    r = len(in_sp)
+    return tuple((in_sp[a] + pads[a] + pads[r + a] - (dilations[a] * (ksz[a] - 1) + 1))
+                 // strides[a] + 1 for a in range(r))
+
+
+def deform_conv(X, W, offset, B=None, mask=None, strides=None, pads=None, dilations=None,
+                group: int = 1, offset_group: int = 1, lib=None) -> np.ndarray:
+    """DeformConv(X, W, offset, B, mask) -> Y as float64 (unrounded).
+
+    Arrays are fp32 (half data widened exactly: locations in fp32) or float64
+    (locations in float64); attribute names and defaults follow the
+    convolution operators (strides and dilations 1, pads 0, group and
+    offset_group 1)."""
+    lib = lib or _load()
+    X = np.asarray(X)
+    coord_f32 = 0 if X.dtype == np.float64 else 1
+    X = np.ascontiguousarray(X, dtype=np.float64)
+    W = np.ascontiguousarray(W, dtype=np.float64)
+    offset = np.ascontiguousarray(offset, dtype=np.float64)
+    n, c = X.shape[:2]
+    r = X.ndim - 2
+    in_sp = X.shape[2:]
+    ksz = W.shape[2:]
+    strides = [1] * r if strides is None else list(strides)
+    dilations = [1] * r if dilations is None else list(dilations)
+    pads = [0] * (2 * r) if pads is None else list(pads)
+    out_sp = deform_conv_output_shape(in_sp, ksz, strides, pads, dilations)
+    oc = W.shape[0]
+    Y = np.empty((n, oc) + out_sp, dtype=np.float64)
+    b = None if B is None else np.ascontiguousarray(B, dtype=np.float64)
+    m = None if mask is None else np.ascontiguousarray(mask, dtype=np.float64)
+    arr = lambda v: np.asarray(v, dtype=np.int64)
+    in_a, k_a, o_a, s_a, p_a, d_a = (arr(in_sp), arr(ksz), arr(out_sp), arr(strides), arr(pads),
+                                     arr(dilations))
+    rc = lib.oracle_deform_conv(_ptr(X, ctypes.c_double), r, n, c, _ptr(in_a, ctypes.c_int64),
+                                _ptr(W, ctypes.c_double), oc, _ptr(k_a, ctypes.c_int64),
+                                _ptr(offset, ctypes.c_double),
+                                _ptr(b, ctypes.c_double) if b is not None else None,
+                                _ptr(m, ctypes.c_double) if m is not None else None,
+                                _ptr(o_a, ctypes.c_int64), _ptr(s_a, ctypes.c_int64),
+                                _ptr(p_a, ctypes.c_int64), _ptr(d_a, ctypes.c_int64), int(group),
+                                int(offset_group), coord_f32, _ptr(Y, ctypes.c_double))
+    if rc:
+        raise ValueError("oracle_deform_conv rejected its arguments")
+    return Y

@@ -1,0 +1,166 @@
+/*
+ * deform_conv.c -- plain, slow, CPU reference of DeformConv (version 22).
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this library.  It shares no code, header,
+ * table or constant with the GPU library, and the GPU library never calls it.
+ *
+ * What it follows ("DeformConv" page, since version 22):
+ *   - Inputs: X (N, C, D1..Dn); W (oC, C/group, k1..kn); offset
+ *     (N, offset_group * k1*..*kn * n, o1..on), one displacement per kernel
+ *     position and spatial axis; optional B (oC); optional mask
+ *     (N, offset_group * k1*..*kn, o1..on), default ones.
+ *   - Each kernel position samples X at its regular convolution position
+ *     plus its offset, by linear interpolation; locations outside the
+ *     (padded) input read zero.  The sample is multiplied by the mask, then
+ *     by the weight, summed over input channels and kernel positions, plus
+ *     the bias.
+ *
+ * Readings (the page prints no attribute list; its four examples use
+ * kernel_shape, pads and offset_group, and fix the rest of the layout):
+ *   - offset holds, for kernel position k (row-major over k1..kn) of offset
+ *     group g, the n displacements of channels g*K*n + k*n + a, axis a
+ *     outermost first (the examples: channel 0 moves tap (0,0) along H,
+ *     channel 5 moves tap (1,0) along W);
+ *   - input channel c belongs to offset group c / (C / offset_group); the
+ *     mask channel of (g, k) is g*K + k;
+ *   - strides, dilations, pads (begin values for every axis, then end
+ *     values) and group have their convolution meaning: the regular position
+ *     of output o and kernel position k along axis a is
+ *     o_a * stride_a - pad_begin_a + k_a * dilation_a, and output channel oc
+ *     of group G = oc / (oC / group) reads input channels
+ *     G*(C/group) .. (G+1)*(C/group)-1 (not exemplified on the page);
+ *   - interpolation is linear along every axis with X taken as zero outside
+ *     the image (the padded region is zero as well);
+ *   - the sampling location (regular position + offset) is computed in the
+ *     offset's element type: fp32 for fp32, fp16 and bf16 data (the caller
+ *     passes half data widened exactly), float64 for double.  It decides the
+ *     taps, so it is computed in that precision; the weights and the sums are
+ *     float64.
+ */
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define DC_MAX_RANK 3
+
+/* Linear interpolation of one plane of X (float64, spatial extents in_sp) at
+ * the location whose per-axis floor is base and fractional part frac, X zero
+ * outside the image: the sum over the 2^r corners, innermost axis fastest, of
+ * the product of the per-axis weights (outermost first) times X. */
+static double sample_linear(const double *plane, int r, const int64_t *in_sp,
+                            const double *frac, const int64_t *base)
+{
+    double acc = 0.0;
+    for (int t = 0; t < (1 << r); ++t) {
+        double w = 1.0;
+        int valid = 1;
+        int64_t off = 0;
+        for (int a = 0; a < r; ++a) {
+            int bit = (t >> (r - 1 - a)) & 1; /* innermost axis fastest */
+            int64_t i = base[a] + bit;
+            w *= bit ? frac[a] : 1.0 - frac[a];
+            valid = valid && i >= 0 && i < in_sp[a];
+            off = off * in_sp[a] + i;
+        }
+        if (valid)
+            acc += w * plane[off];
+    }
+    return acc;
+}
+
+/*
+ * Y = DeformConv(X, W, offset, B, mask), r spatial axes (1 .. 3).
+ *   X      (N, C, in_sp...)            float64
+ *   Wt     (OC, C/group, ksz...)       float64
+ *   offset (N, og*K*r, out_sp...)      float64 (values of the offset type)
+ *   B      (OC) or NULL;  mask (N, og*K, out_sp...) or NULL
+ *   strides, dilations: r entries; pads: 2r entries (begins, then ends)
+ *   coord_f32: 1 -> locations computed in fp32, 0 -> in float64
+ *   Y      (N, OC, out_sp...)          float64, every element written
+ * The output extents out_sp are given and must equal
+ * (in + pad_begin + pad_end - (dilation * (k - 1) + 1)) / stride + 1.
+ * Returns 0, or -1 on a bad argument.
+ */
+int oracle_deform_conv(const double *X, int r, int64_t N, int64_t C, const int64_t *in_sp,
+                       const double *Wt, int64_t OC, const int64_t *ksz, const double *offset,
+                       const double *B, const double *mask, const int64_t *out_sp,
+                       const int64_t *strides, const int64_t *pads, const int64_t *dilations,
+                       int64_t group, int64_t offset_group, int coord_f32, double *Y)
+{
+    if (r < 1 || r > DC_MAX_RANK || N < 0 || C < 1 || OC < 1 || group < 1 || offset_group < 1)
+        return -1;
+    if (C % group || OC % group || C % offset_group)
+        return -1;
+    int64_t in_count = 1, out_count = 1, K = 1;
+    for (int a = 0; a < r; ++a) {
+        if (in_sp[a] < 1 || ksz[a] < 1 || strides[a] < 1 || dilations[a] < 1 || out_sp[a] < 0)
+            return -1;
+        int64_t span = dilations[a] * (ksz[a] - 1) + 1;
+        int64_t expect = (in_sp[a] + pads[a] + pads[r + a] - span) / strides[a] + 1;
+        if (out_sp[a] != expect)
+            return -1;
+        in_count *= in_sp[a];
+        out_count *= out_sp[a];
+        K *= ksz[a];
+    }
+    const int64_t Cg = C / group, OCg = OC / group, Cog = C / offset_group;
+
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t oc = 0; oc < OC; ++oc) {
+            const int64_t G = oc / OCg;
+            for (int64_t o = 0; o < out_count; ++o) {
+                int64_t oi[DC_MAX_RANK];
+                int64_t rest = o;
+                for (int a = r - 1; a >= 0; --a) {
+                    oi[a] = rest % out_sp[a];
+                    rest /= out_sp[a];
+                }
+                double acc = 0.0;
+                for (int64_t cl = 0; cl < Cg; ++cl) {
+                    const int64_t c = G * Cg + cl;
+                    const int64_t g = c / Cog;
+                    const double *plane = X + (n * C + c) * in_count;
+                    for (int64_t k = 0; k < K; ++k) {
+                        int64_t ki[DC_MAX_RANK];
+                        int64_t kr = k;
+                        for (int a = r - 1; a >= 0; --a) {
+                            ki[a] = kr % ksz[a];
+                            kr /= ksz[a];
+                        }
+                        double frac[DC_MAX_RANK];
+                        int64_t base[DC_MAX_RANK];
+                        int finite = 1;
+                        for (int a = 0; a < r && finite; ++a) {
+                            int64_t regular = oi[a] * strides[a] - pads[a] + ki[a] * dilations[a];
+                            double d = offset[((n * offset_group + g) * K * r + k * r + a) *
+                                                  out_count + o];
+                            double loc = coord_f32 ? (double)((float)regular + (float)d)
+                                                   : (double)regular + d;
+                            /* a location beyond any image reads zero (and is
+                             * kept away from the integer conversion) */
+                            if (!isfinite(loc) || fabs(loc) > 16777216.0) {
+                                finite = 0;
+                                break;
+                            }
+                            double fl = floor(loc); /* exact for an fp32 value too */
+                            base[a] = (int64_t)fl;
+                            frac[a] = loc - fl;     /* exact */
+                        }
+                        if (!finite)
+                            continue;
+                        double v = sample_linear(plane, r, in_sp, frac, base);
+                        if (mask)
+                            v *= mask[((n * offset_group + g) * K + k) * out_count + o];
+                        acc += Wt[(oc * Cg + cl) * K + k] * v;
+                    }
+                }
+                if (B)
+                    acc += B[oc];
+                Y[(n * OC + oc) * out_count + o] = acc;
+            }
+        }
+    }
+    return 0;
+}

@@ -8,6 +8,7 @@ the build container) and writes, next to this script:
                                 "GridSample - version 20" page
   resize_examples.json       -- the Resize (version 18) examples, all but
                                 the antialias and tf_crop_and_resize ones
+  deform_conv_examples.json  -- the four DeformConv (version 22) examples
 
 Only numbers the pages print are stored (inputs, attributes, printed outputs),
 each with the page title and example name it came from.  Nothing here computes
@@ -207,6 +208,83 @@ def resize_examples(lines):
     return out
 
 
+def bracket_values(block: str, label: str):
+    """Shape and printed text of the tensor after 'label: shape=(...)'."""
+    m = re.search(re.escape(label) + r": shape=\(([^)]*)\), dtype=(\w+)", block)
+    if not m:
+        return None
+    rest = block[m.end():]
+    txt, _ = bracket_block(rest, rest.index("["))
+    return parse_shape(m.group(1)), m.group(2), txt
+
+
+def deform_conv_examples(lines):
+    # The DeformConv page is collapsed onto one long line; one example's
+    # offset tensor is printed with numpy's summarisation ("...") over its
+    # channel axis: the channels it prints are kept, the elided ones are
+    # listed under "elided_channels" and stored as zeros (a reading: the
+    # printed output is reproduced with them zero).
+    text = page_text(lines, "page 4 of 5", "page 5 of 5")
+    line = max(text, key=len)
+    heads = [(m.start(), m.group(1)) for m in re.finditer(r"\*\*(test_cc_\w+)\*\*", line)]
+    out = []
+    for k, (pos, name) in enumerate(heads):
+        end = heads[k + 1][0] if k + 1 < len(heads) else line.index("Differences with previous")
+        block = line[pos:end]
+        attrs = block[block.index("Attributes:"):block.index("Inputs:")]
+        ex = {"name": name,
+              "citation": "DeformConv page (onnx-light, since version 22), Examples: " + name}
+        for key in ("kernel_shape", "pads", "strides", "dilations"):
+            m = re.search(key + r" = \[([^\]]*)\]", attrs)
+            ex[key] = [int(v) for v in numbers(m.group(1))] if m else None
+        for key in ("offset_group", "group"):
+            m = re.search(r"\b" + key + r" = (\d+)", attrs)
+            ex[key] = int(m.group(1)) if m else None
+        for label in ("X", "W", "offset", "B", "mask", "Y"):
+            got = bracket_values(block, label)
+            if got is None:
+                ex[label] = None
+                continue
+            shape, dtype, txt = got
+            elided = []
+            if "..." in txt:
+                # channel blocks of the (1, C, h, w) tensor around the ellipsis
+                # strip the batch bracket and the n = 0 bracket
+                inner = txt[txt.index("[") + 1:txt.rindex("]")]
+                nblock, _ = bracket_block(inner, inner.index("["))
+                inner = nblock[1:-1]
+                parts = []
+                i = 0
+                while i < len(inner):
+                    if inner[i] == "[":
+                        b, i = bracket_block(inner, i)
+                        parts.append(b)
+                    elif inner.startswith("...", i):
+                        parts.append("...")
+                        i += 3
+                    else:
+                        i += 1
+                head = parts[:parts.index("...")]
+                tail = parts[parts.index("...") + 1:]
+                per = prod(shape[2:])
+                elided = list(range(len(head), shape[1] - len(tail)))
+                vals = []
+                for b in head:
+                    vals += numbers(b)
+                vals += [0.0] * (per * len(elided))
+                for b in tail:
+                    vals += numbers(b)
+            else:
+                vals = numbers(txt)
+            if len(vals) != prod(shape):
+                raise ValueError("%s %s: %d values for %s" % (name, label, len(vals), shape))
+            ex[label] = {"shape": shape, "dtype": dtype, "values": vals}
+            if elided:
+                ex[label]["elided_channels"] = elided
+        out.append(ex)
+    return out
+
+
 def main():
     if not os.path.exists(PAGES):
         sys.exit("page text not found at " + PAGES)
@@ -214,7 +292,8 @@ def main():
         lines = f.read().split("\n")
     for fname, items in (("affine_grid_examples.json", affine_grid_examples(lines)),
                          ("grid_sample_examples.json", grid_sample_examples(lines)),
-                         ("resize_examples.json", resize_examples(lines))):
+                         ("resize_examples.json", resize_examples(lines)),
+                         ("deform_conv_examples.json", deform_conv_examples(lines))):
         with open(os.path.join(HERE, fname), "w") as f:
             json.dump(items, f, indent=0)
             f.write("\n")
