@@ -10,7 +10,9 @@
  * transformer (GridSample page, Summary), fused into one pass that never
  * writes the grid: gs_affine_grid_sample_fused; and the axis-aligned special
  * case of the sampler, the "Resize" operator (version 18): gs_resize and
- * gs_resize_output_shape.
+ * gs_resize_output_shape; and DeformConv (version 22), whose offset-tap
+ * sampling is the same zero-padded linear gather feeding a convolution:
+ * gs_deform_conv.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -302,6 +304,54 @@ int gs_resize_output_shape(const int64_t *x_shape, int rank, const int64_t *axes
 int gs_resize(const void *X, int x_dtype, const int64_t *x_shape, int rank, const int64_t *y_shape,
               const float *scales, int mode, int coordinate_transformation_mode, int nearest_mode,
               float cubic_coeff_a, int exclude_outside, void *Y, void *stream);
+
+/* ------------------------------------------------------------------------
+ * DeformConv (DeformConv page, since version 22)
+ * --------------------------------------------------------------------- */
+
+/*
+ * Y = DeformConv(X, W, offset, B, mask): each kernel position samples X at its
+ * regular convolution position plus its offset by linear interpolation (X is
+ * zero outside the image), times the mask, times the weight, summed over the
+ * input channels of the output channel's group and the kernel positions, plus
+ * the bias (Inputs X, W, offset, B, mask; Outputs Y).
+ *
+ *   X, dtype     device, (N, C, D1 .. Dr), r = x_rank - 2 in 1..3; dtype
+ *                GS_F32, GS_F16, GS_BF16 or GS_F64.  W, offset, B, mask and Y
+ *                share dtype.
+ *   W, w_shape   device (oC, C / group, k1 .. kr); host shape, x_rank entries.
+ *   offset       device (N, offset_group * k1*..*kr * r, o1 .. or): for kernel
+ *                position k (row-major) of offset group g, channel
+ *                g*K*r + k*r + a holds the displacement along axis a, outermost
+ *                axis first (the page's examples fix this order).
+ *   B            device (oC) or NULL (zeros).
+ *   mask         device (N, offset_group * k1*..*kr, o1 .. or) or NULL (ones).
+ *   strides, pads, dilations   host, r, 2r (begins then ends) and r entries,
+ *                or NULL for 1, 0 and 1 (the page lists no attributes; these
+ *                are read with their convolution meaning).
+ *   group        input channels split into `group` groups, output channel oc
+ *                reading group oc / (oC / group).
+ *   offset_group input channel c uses offset group c / (C / offset_group).
+ *   Y            device (N, oC, o1 .. or), o_a = (D_a + pad_begin + pad_end -
+ *                (dilation * (k_a - 1) + 1)) / stride + 1.
+ *
+ * The sampling location (regular position + offset) is computed in fp32 for
+ * fp32 / fp16 / bf16 data and in double for double data.  2-D fp32, fp16 and
+ * bf16 run on the matrix cores (MFMA, fp32 accumulation; the sampled values
+ * are rounded to the data type before the product); other cases accumulate
+ * in double.
+ *
+ * Errors: GS_ERR_NULL, GS_ERR_SHAPE (x_rank not 3..5, C or oC not divisible
+ * by group, C not divisible by offset_group, w_shape[1] != C / group, an
+ * empty or too small padded input), GS_ERR_DTYPE, GS_ERR_ATTR (stride or
+ * dilation < 1, negative pad, group or offset_group < 1), GS_ERR_TOO_LARGE
+ * (an image of X, of Y or all of W above 2^31 - 1 bytes, extents of 2^24 or
+ * more, too many thread blocks), GS_ERR_HIP.
+ */
+int gs_deform_conv(const void *X, int dtype, const int64_t *x_shape, int x_rank, const void *W,
+                   const int64_t *w_shape, const void *offset, const void *B, const void *mask,
+                   const int64_t *strides, const int64_t *pads, const int64_t *dilations,
+                   int group, int offset_group, void *Y, void *stream);
 
 #ifdef __cplusplus
 }

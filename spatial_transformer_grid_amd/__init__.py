@@ -1,8 +1,9 @@
 """spatial_transformer_grid_amd -- MI355X-native spatial-transformer sampler.
 
 Python face of libgsample (include/gsample.h): the grid generator
-(AffineGrid), the 2D/3D sampler (GridSample), their fused composition and
-Resize, all computed by hand-written HIP kernels for gfx950.  Tensors are
+(AffineGrid), the sampler (GridSample) of any rank and type, their fused
+composition, Resize and DeformConv, all computed by hand-written HIP kernels
+for gfx950.  Tensors are
 torch GPU tensors; torch supplies device memory and streams only.
 
     from spatial_transformer_grid_amd import affine_grid, grid_sample
@@ -20,6 +21,8 @@ from ._binding import (  # noqa: F401
     PADDINGS,
     affine_grid,
     affine_grid_sample_fused,
+    deform_conv,
+    deform_conv_output_shape,
     grid_sample,
     lib,
     resize,
@@ -28,4 +31,5 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = ["affine_grid", "grid_sample", "affine_grid_sample_fused", "resize",
-           "resize_output_shape", "resize_to", "GSError", "lib"]
+           "resize_output_shape", "resize_to", "deform_conv", "deform_conv_output_shape",
+           "GSError", "lib"]

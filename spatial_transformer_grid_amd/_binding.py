@@ -38,6 +38,8 @@ SIGNATURES = {
     "gs_grid_sample_3d": ([_P, _I, _PI64, _P, _I, _PI64, _I, _I, _I, _P, _P], _I),
     "gs_affine_grid_sample_fused": ([_P, _I, _P, _I, _PI64, _I, _PI64, _I, _I, _I, _P, _P], _I),
     "gs_grid_sample": ([_P, _I, _PI64, _I, _P, _I, _PI64, _I, _I, _I, _P, _P], _I),
+    "gs_deform_conv": ([_P, _I, _PI64, _I, _P, _PI64, _P, _P, _P, _PI64, _PI64, _PI64, _I, _I,
+                        _P, _P], _I),
     "gs_resize_output_shape": ([_PI64, _I, _PI64, _I, _PF32, _PI64, _I, _PI64], _I),
     "gs_resize": ([_P, _I, _PI64, _I, _PI64, _PF32, _I, _I, _I, ctypes.c_float, _I, _P, _P], _I),
 }
@@ -253,4 +255,55 @@ def resize_to(X, y_shape, scales=None, mode: str = "nearest",
                          float(cubic_coeff_a), int(exclude_outside),
                          ctypes.c_void_p(Y.data_ptr()), _stream(stream, X.device))
     _check(st, "gs_resize")
+    return Y
+
+
+def deform_conv_output_shape(x_shape, w_shape, strides=None, pads=None, dilations=None):
+    r = len(x_shape) - 2
+    strides = [1] * r if strides is None else list(strides)
+    dilations = [1] * r if dilations is None else list(dilations)
+    pads = [0] * (2 * r) if pads is None else list(pads)
+    out = [(x_shape[2 + a] + pads[a] + pads[r + a] - (dilations[a] * (w_shape[2 + a] - 1) + 1))
+           // strides[a] + 1 for a in range(r)]
+    return (x_shape[0], w_shape[0], *out)
+
+
+def deform_conv(X, W, offset, B=None, mask=None, strides=None, pads=None, dilations=None,
+                group: int = 1, offset_group: int = 1, out=None, stream=None):
+    """DeformConv(X, W, offset, B, mask) -> Y on the GPU (gs_deform_conv).
+
+    Attribute names follow the convolution operators (strides, pads as begins
+    then ends, dilations, group, offset_group)."""
+    X = _device_tensor(X, "X")
+    W = _device_tensor(W, "W")
+    offset = _device_tensor(offset, "offset")
+    B = _device_tensor(B, "B") if B is not None else None
+    mask = _device_tensor(mask, "mask") if mask is not None else None
+    for name, t in (("W", W), ("offset", offset), ("B", B), ("mask", mask)):
+        if t is not None and t.dtype != X.dtype:
+            raise TypeError("%s must have X's element type" % name)
+    shape = deform_conv_output_shape(tuple(X.shape), tuple(W.shape), strides, pads, dilations)
+    r = X.dim() - 2
+    npos = 1
+    for v in shape[2:]:
+        npos *= v
+    K = 1
+    for v in W.shape[2:]:
+        K *= v
+    if tuple(offset.shape) != (X.shape[0], offset_group * K * r, *shape[2:]):
+        raise ValueError("offset must have shape %s" % ((X.shape[0], offset_group * K * r,
+                                                         *shape[2:]),))
+    if mask is not None and tuple(mask.shape) != (X.shape[0], offset_group * K, *shape[2:]):
+        raise ValueError("mask must have shape %s" % ((X.shape[0], offset_group * K,
+                                                       *shape[2:]),))
+    if B is not None and tuple(B.shape) != (W.shape[0],):
+        raise ValueError("B must have shape (%d,)" % W.shape[0])
+    Y = _out_tensor(out, shape, X)
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    arr = lambda v: int64_array(v) if v is not None else None
+    st = lib().gs_deform_conv(ptr(X), dtype_code(X), int64_array(X.shape), X.dim(), ptr(W),
+                              int64_array(W.shape), ptr(offset), ptr(B), ptr(mask), arr(strides),
+                              arr(pads), arr(dilations), int(group), int(offset_group), ptr(Y),
+                              _stream(stream, X.device))
+    _check(st, "gs_deform_conv")
     return Y

@@ -442,4 +442,113 @@ int gs_resize(const void *X, int x_dtype, const int64_t *x_shape, int rank, cons
     return hip_status(gs::launch_resize(p, d3, mode, x_dtype, vec_in, (hipStream_t)stream));
 }
 
+int gs_deform_conv(const void *X, int dtype, const int64_t *x_shape, int x_rank, const void *W,
+                   const int64_t *w_shape, const void *offset, const void *B, const void *mask,
+                   const int64_t *strides, const int64_t *pads, const int64_t *dilations,
+                   int group, int offset_group, void *Y, void *stream) {
+    if (!x_shape || !w_shape) return GS_ERR_NULL;
+    if (x_rank < 3 || x_rank > 5) return GS_ERR_SHAPE;
+    if (dtype != GS_F32 && dtype != GS_F16 && dtype != GS_BF16 && dtype != GS_F64)
+        return GS_ERR_DTYPE;
+    const int r = x_rank - 2;
+    for (int i = 0; i < x_rank; ++i)
+        if (x_shape[i] < 0 || w_shape[i] < 0) return GS_ERR_SHAPE;
+    const int64_t N = x_shape[0], C = x_shape[1], OC = w_shape[0];
+    if (group < 1 || offset_group < 1) return GS_ERR_ATTR;
+    if (C < 1 || OC < 1 || C % group || OC % group || C % offset_group ||
+        w_shape[1] != C / group)
+        return GS_ERR_SHAPE;
+    int64_t st[3], pb[3], pe[3], dl[3], ext[3], ks[3], out[3];
+    int64_t npos = 1, plane = 1, K = 1;
+    for (int a = 0; a < r; ++a) {
+        st[a] = strides ? strides[a] : 1;
+        dl[a] = dilations ? dilations[a] : 1;
+        pb[a] = pads ? pads[a] : 0;
+        pe[a] = pads ? pads[r + a] : 0;
+        if (st[a] < 1 || dl[a] < 1 || pb[a] < 0 || pe[a] < 0) return GS_ERR_ATTR;
+        ext[a] = x_shape[2 + a];
+        ks[a] = w_shape[2 + a];
+        if (ext[a] < 1 || ks[a] < 1) return GS_ERR_SHAPE;
+        // the sampling arithmetic clamps locations beyond 2^24
+        if (ext[a] >= (int64_t(1) << 24) || ks[a] * dl[a] >= (int64_t(1) << 24) ||
+            pb[a] >= (int64_t(1) << 24) || pe[a] >= (int64_t(1) << 24) || st[a] >= (int64_t(1) << 24))
+            return GS_ERR_TOO_LARGE;
+        const int64_t span = dl[a] * (ks[a] - 1) + 1;
+        const int64_t room = ext[a] + pb[a] + pe[a] - span;
+        if (room < 0) return GS_ERR_SHAPE;
+        out[a] = room / st[a] + 1;
+        npos *= out[a];
+        plane *= ext[a];
+        K *= ks[a];
+    }
+    const int bytes = elem_bytes(dtype);
+    const int64_t Cg = C / group, OCg = OC / group;
+    if (C * plane * bytes > kInt32Max || OC * npos * bytes > kInt32Max ||
+        OC * Cg * K * bytes > kInt32Max || N > kInt32Max)
+        return GS_ERR_TOO_LARGE;
+    if (N == 0) return GS_OK;
+    if (!X || !W || !offset || !Y) return GS_ERR_NULL;
+
+    gs::DeformParams p;
+    p.X = X;
+    p.Wt = W;
+    p.offset = offset;
+    p.mask = mask;
+    p.B = B;
+    p.Y = Y;
+    p.N = (int)N;
+    p.C = (int)C;
+    p.OC = (int)OC;
+    for (int a = 0; a < 3; ++a) {
+        p.in_ext[a] = a < r ? (int)ext[a] : 1;
+        p.out_ext[a] = a < r ? (int)out[a] : 1;
+        p.k_ext[a] = a < r ? (int)ks[a] : 1;
+        p.stride[a] = a < r ? (int)st[a] : 1;
+        p.pad[a] = a < r ? (int)pb[a] : 0;
+        p.dil[a] = a < r ? (int)dl[a] : 1;
+    }
+    p.H = p.in_ext[0];
+    p.W = r >= 2 ? p.in_ext[1] : 1;
+    p.KH = p.k_ext[0];
+    p.KW = r >= 2 ? p.k_ext[1] : 1;
+    p.OH = p.out_ext[0];
+    p.OW = r >= 2 ? p.out_ext[1] : 1;
+    p.sh = p.stride[0];
+    p.sw = p.stride[1];
+    p.pt = p.pad[0];
+    p.pl = p.pad[1];
+    p.dh = p.dil[0];
+    p.dw = p.dil[1];
+    p.group = group;
+    p.og = offset_group;
+    p.Cg = (int)Cg;
+    p.OCg = (int)OCg;
+    p.Cog = (int)(C / offset_group);
+    p.Ktot = (int)(Cg * K);
+    int span = 1;
+    for (int64_t G = 0; G < group; ++G) {
+        const int64_t first = (G * Cg) / p.Cog, last = ((G + 1) * Cg - 1) / p.Cog;
+        if (last - first + 1 > span) span = (int)(last - first + 1);
+    }
+    p.og_span = span;
+    p.x_plane_bytes = (uint32_t)(plane * bytes);
+    p.w_bytes = (uint32_t)(OC * Cg * K * bytes);
+    p.npos = (uint32_t)npos;
+    const bool mfma = r == 2 && dtype != GS_F64;
+    if (mfma) {
+        const int64_t tm = OCg > 128 ? 256 : 128;
+        const int64_t m_tiles = (OCg + tm - 1) / tm, n_tiles = (npos + 63) / 64;
+        const int64_t nblocks = N * group * m_tiles * n_tiles;
+        if (nblocks > kMaxBlocks) return GS_ERR_TOO_LARGE;
+        p.m_tiles = (int)m_tiles;
+        p.n_tiles = (int)n_tiles;
+        p.nblocks = (int)nblocks;
+    } else {
+        const int64_t total = N * OC * npos;
+        if ((total + kBlockThreads - 1) / kBlockThreads > kInt32Max) return GS_ERR_TOO_LARGE;
+        p.m_tiles = p.n_tiles = p.nblocks = 0;
+    }
+    return hip_status(gs::launch_deform_conv(p, r, dtype, mfma, (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -1,0 +1,450 @@
+// gs_deform.hip -- DeformConv (version 22) for gfx950.
+//
+// Y[n, oc, o] = B[oc] + sum over the input channels c of oc's group and the
+// kernel positions k of W[oc, c, k] * mask[n, g(c), k, o] *
+// linear_sample(X[n, c], regular(o, k) + offset[n, g(c), k, o])
+// (DeformConv page: Inputs X, W, offset, B, mask; Summary).  Per image and
+// group this is a matrix product of W (oC/group x K, K = C/group * kernel
+// size) with the sampled "columns" (K x output positions).
+//
+// 2-D fp32 / fp16 / bf16 run an implicit GEMM on the matrix cores: a block
+// owns TM output channels x 64 output positions of one image and group and
+// walks K in chunks of 32.  Per chunk it stages the W tile in LDS and samples
+// the 32 x 64 column tile straight into LDS (the columns never reach HBM),
+// then each wave multiplies its 32-row blocks with MFMA 32x32 instructions
+// (fp32: 32x32x2; fp16 / bf16: 32x32x16, fp32 accumulation).  The sampling of
+// a (kernel position, output position) pair is the same for every channel of
+// an offset group, so the block first computes, for its 64 positions, every
+// such pair's four corner offsets and mask-folded weights into an LDS table.
+// Everything else (double data, 1-D and 3-D) runs a direct kernel: one lane
+// per output, summed in double.
+#include "gs_device.hpp"
+#include "gs_launch.hpp"
+
+#include <stdint.h>
+
+namespace gs {
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+
+constexpr int DC_TN = 64;   // output positions per block
+constexpr int DC_TK = 32;   // K per chunk
+constexpr int DC_TABLE = 16;  // kernel positions x offset groups the LDS table holds
+
+// ------------------------------------------------------------ sampling
+
+// Corner element offsets (-1 = outside the image) and weights of the linear
+// sample of an H x W plane at (lh, lw), the mask folded into the weights.
+struct Corners {
+    int off[4];
+    float w[4];
+};
+
+__device__ __forceinline__ Corners corners_of(float lh, float lw, float m, int H, int W) {
+    Corners c;
+    if (!__builtin_isfinite(lh) || !__builtin_isfinite(lw) || fabsf(lh) > kCoordLimit ||
+        fabsf(lw) > kCoordLimit) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            c.off[q] = -1;
+            c.w[q] = 0.0f;
+        }
+        return c;
+    }
+    const float fh0 = floorf(lh), fw0 = floorf(lw);
+    const float fh = lh - fh0, fw = lw - fw0;  // exact
+    const int h0 = (int)fh0, w0 = (int)fw0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int dy = q >> 1, dx = q & 1;
+        const int h = h0 + dy, w = w0 + dx;
+        const bool ok = h >= 0 && h < H && w >= 0 && w < W;
+        c.off[q] = ok ? h * W + w : -1;
+        c.w[q] = (dy ? fh : 1.0f - fh) * (dx ? fw : 1.0f - fw) * m;
+    }
+    return c;
+}
+
+// Element (index i) of a DeformConv operand of type T, widened to float.
+template <typename T>
+__device__ __forceinline__ float ld(const void *p, size_t i) {
+    if constexpr (T::bytes == 4) return ((const float *)p)[i];
+    else return T::from_raw(((const uint16_t *)p)[i]);
+}
+
+// --------------------------------------------------------- implicit GEMM
+
+// MB: 32-row blocks of output channels per wave (TM = 4 waves * 32 * MB).
+template <typename T, int MB, bool TABLE>
+__global__ __launch_bounds__(kBlock) void deform_conv2d_mfma(DeformParams p) {
+    using raw_t = typename T::raw_t;
+    constexpr int TM = 4 * 32 * MB;
+    constexpr int PAD = 16 / T::bytes;      // row padding against LDS bank conflicts
+    constexpr int LK = DC_TK + PAD;         // LDS row pitch (elements)
+    constexpr int TE = DC_TABLE * DC_TN;    // table entries
+    __shared__ __align__(16) raw_t As[TM * LK];      // W tile, [m][k]
+    __shared__ __align__(16) raw_t Bs[DC_TN * LK];   // column tile, [position][k]
+    __shared__ int tb_off[TABLE ? 4 * TE : 1];
+    __shared__ float tb_w[TABLE ? 4 * TE : 1];
+
+    const int lb = xcd_logical_block_runs(p.nblocks);
+    if (lb >= p.nblocks) return;
+    const int nt = lb % p.n_tiles;
+    int rest = lb / p.n_tiles;
+    const int mt = rest % p.m_tiles;
+    rest /= p.m_tiles;
+    const int G = rest % p.group;
+    const int n = rest / p.group;
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    const int npos = p.OH * p.OW;
+    const int KK = p.KH * p.KW;
+    const int g_first = (G * p.Cg) / p.Cog;
+
+    // this thread's output position in the column tile
+    const int pos = t & (DC_TN - 1);
+    const int o = nt * DC_TN + pos;
+    const bool o_ok = o < npos;
+    const int oh = o_ok ? o / p.OW : 0, ow = o_ok ? o - (o / p.OW) * p.OW : 0;
+
+    const size_t off_img = (size_t)n * p.og * KK * 2 * npos;   // offset of image n
+    const size_t msk_img = (size_t)n * p.og * KK * npos;       // mask of image n
+    // no offset or mask is read for a position past the end of the plane or
+    // an offset group past the last one (a conv group may span fewer groups
+    // than the widest one the table is sized for)
+    auto sample_of = [&](int g, int tap) -> Corners {
+        Corners none;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            none.off[q] = -1;
+            none.w[q] = 0.0f;
+        }
+        if (!o_ok || g >= p.og) return none;
+        const int i = tap / p.KW, j = tap - (tap / p.KW) * p.KW;
+        const size_t oc2 = off_img + ((size_t)(g * KK + tap) * 2) * npos + o;
+        const float dy = ld<T>(p.offset, oc2), dx = ld<T>(p.offset, oc2 + npos);
+        const float m = p.mask ? ld<T>(p.mask, msk_img + (size_t)(g * KK + tap) * npos + o) : 1.0f;
+        // regular position + offset, in fp32
+        const float lh = (float)(oh * p.sh - p.pt + i * p.dh) + dy;
+        const float lw = (float)(ow * p.sw - p.pl + j * p.dw) + dx;
+        return corners_of(lh, lw, m, p.H, p.W);
+    };
+
+    if constexpr (TABLE) {
+        const int entries = p.og_span * KK * DC_TN;
+        for (int e = t; e < entries; e += kBlock) {
+            // e = (gi * KK + tap) * 64 + pos, and pos == t & 63 here
+            const int gt = e / DC_TN;
+            const int gi = gt / KK, tap = gt - gi * KK;
+            const Corners c = sample_of(g_first + gi, tap);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                tb_off[q * TE + e] = c.off[q];
+                tb_w[q * TE + e] = c.w[q];
+            }
+        }
+    }
+
+    // X of image n: one buffer resource; channel c's plane starts at
+    // c * plane_bytes (every offset stays below 2^31)
+    const rsrc_t xr = make_rsrc((const char *)p.X + (size_t)n * p.C * p.x_plane_bytes,
+                                (uint32_t)p.C * p.x_plane_bytes);
+    // W rows of this block: output channels G*OCg + mt*TM + m
+    const int oc0 = G * p.OCg + mt * TM;
+    const int m_valid = min(TM, p.OCg - mt * TM);
+    const rsrc_t wr = make_rsrc(p.Wt, p.w_bytes);
+
+    floatx16 acc[MB][2];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
+
+    for (int k0 = 0; k0 < p.Ktot; k0 += DC_TK) {
+        __syncthreads();  // the previous chunk's LDS reads (and the table) are done
+        // ---- W tile: TM x 32
+        for (int e = t; e < TM * DC_TK; e += kBlock) {
+            const int m = e / DC_TK, kk = e - m * DC_TK;
+            const int k = k0 + kk;
+            const bool ok = m < m_valid && k < p.Ktot;
+            const uint32_t wo = ok ? (uint32_t)(((size_t)(oc0 + m) * p.Ktot + k) * T::bytes) : GS_OOB;
+            As[m * LK + kk] = T::load_raw(wr, wo);
+        }
+        // ---- column tile: 32 x 64, this thread's position, 8 of the K slots
+#pragma unroll
+        for (int s = 0; s < DC_TK / (kBlock / DC_TN); ++s) {
+            const int kk = (t >> 6) + (kBlock / DC_TN) * s;
+            const int k = k0 + kk;
+            float v = 0.0f;
+            if (k < p.Ktot) {
+                const int cl = k / KK, tap = k - (k / KK) * KK;
+                const int c = G * p.Cg + cl;
+                const int g = c / p.Cog;
+                Corners cr;
+                if constexpr (TABLE) {
+                    const int e = ((g - g_first) * KK + tap) * DC_TN + pos;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        cr.off[q] = tb_off[q * TE + e];
+                        cr.w[q] = tb_w[q * TE + e];
+                    }
+                } else {
+                    cr = sample_of(g, tap);
+                }
+                const uint32_t pb = (uint32_t)c * p.x_plane_bytes;
+                float x[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    x[q] = T::load(xr, cr.off[q] >= 0 ? pb + (uint32_t)cr.off[q] * T::bytes : GS_OOB);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) v = cr.off[q] >= 0 ? fmaf(cr.w[q], x[q], v) : v;
+            }
+            Bs[pos * LK + kk] = to_raw<T>(v);
+        }
+        __syncthreads();
+        // ---- MFMA: wave `wave` owns rows [wave * 32 * MB, +32 * MB), all 64 positions
+        if constexpr (T::bytes == 4) {
+#pragma unroll
+            for (int ks = 0; ks < DC_TK / 2; ++ks) {
+                const int kk = 2 * ks + (lane >> 5);
+                float b[2];
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    b[nb] = __builtin_bit_cast(float, (uint32_t)Bs[(32 * nb + (lane & 31)) * LK + kk]);
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const int m = (wave * MB + mb) * 32 + (lane & 31);
+                    const float a = __builtin_bit_cast(float, (uint32_t)As[m * LK + kk]);
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb)
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b[nb], acc[mb][nb], 0, 0, 0);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < DC_TK / 16; ++ks) {
+                const int kk = 16 * ks + 8 * (lane >> 5);
+                u32x4 bv[2];
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    bv[nb] = *(const u32x4 *)&Bs[(32 * nb + (lane & 31)) * LK + kk];
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const int m = (wave * MB + mb) * 32 + (lane & 31);
+                    const u32x4 av = *(const u32x4 *)&As[m * LK + kk];
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb) {
+                        if constexpr (__is_same(T, BF16))
+                            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv[nb]),
+                                acc[mb][nb], 0, 0, 0);
+                        else
+                            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                                __builtin_bit_cast(halfx8, av), __builtin_bit_cast(halfx8, bv[nb]),
+                                acc[mb][nb], 0, 0, 0);
+                    }
+                }
+            }
+        }
+    }
+
+    // ---- epilogue: lane holds column (lane & 31) + 32 nb and rows
+    // 8 (r / 4) + 4 (lane / 32) + (r % 4) of each 32 x 32 block
+    const rsrc_t yr = make_rsrc((char *)p.Y + (size_t)n * p.OC * npos * T::bytes,
+                                (uint32_t)((size_t)p.OC * npos * T::bytes));
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int m = (wave * MB + mb) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const bool mok = m < m_valid;
+            const float bias = (mok && p.B) ? ld<T>(p.B, oc0 + m) : 0.0f;
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                const int oo = nt * DC_TN + 32 * nb + (lane & 31);
+                const bool ok = mok && oo < npos;
+                const uint32_t yo =
+                    ok ? (uint32_t)(((size_t)(oc0 + m) * npos + oo) * T::bytes) : GS_OOB;
+                T::store(acc[mb][nb][r] + bias, yr, yo);
+            }
+        }
+}
+
+// ----------------------------------------------------------- direct kernel
+
+// Linear sample of one plane (r axes) at the location with per-axis floor
+// `base` and fraction `frac`, zero outside, in double: corners innermost
+// axis fastest, weights as products over the axes (outermost first).
+template <int R, typename T>
+__device__ __forceinline__ double sample_direct(rsrc_t xr, uint32_t plane_byte, const int *ext,
+                                                const int *base, const double *frac) {
+    double acc = 0.0;
+#pragma unroll
+    for (int tcorner = 0; tcorner < (1 << R); ++tcorner) {
+        double w = 1.0;
+        bool valid = true;
+        uint32_t off = 0;
+#pragma unroll
+        for (int a = 0; a < R; ++a) {
+            const int bit = (tcorner >> (R - 1 - a)) & 1;
+            const int i = base[a] + bit;
+            w = w * (bit ? frac[a] : 1.0 - frac[a]);
+            valid = valid && i >= 0 && i < ext[a];
+            off = off * (uint32_t)ext[a] + (uint32_t)i;
+        }
+        const double x = T::load(xr, valid ? plane_byte + off * (uint32_t)T::bytes : GS_OOB);
+        acc = valid ? acc + w * x : acc;
+    }
+    return acc;
+}
+
+// Element types of the direct kernel: loads widen to double, stores round.
+struct DcF32 {
+    static constexpr int bytes = 4;
+    __device__ static double load(rsrc_t r, uint32_t o) { return (double)F32::load(r, o); }
+    __device__ static double at(const void *p, size_t i) { return ((const float *)p)[i]; }
+    __device__ static void store(double v, rsrc_t r, uint32_t o) { F32::store((float)v, r, o); }
+};
+struct DcF16 {
+    static constexpr int bytes = 2;
+    __device__ static double load(rsrc_t r, uint32_t o) { return (double)F16::load(r, o); }
+    __device__ static double at(const void *p, size_t i) {
+        return (double)F16::from_raw(((const uint16_t *)p)[i]);
+    }
+    __device__ static void store(double v, rsrc_t r, uint32_t o) { F16::store((float)v, r, o); }
+};
+struct DcBF16 {
+    static constexpr int bytes = 2;
+    __device__ static double load(rsrc_t r, uint32_t o) { return (double)BF16::load(r, o); }
+    __device__ static double at(const void *p, size_t i) {
+        return (double)BF16::from_raw(((const uint16_t *)p)[i]);
+    }
+    __device__ static void store(double v, rsrc_t r, uint32_t o) { BF16::store((float)v, r, o); }
+};
+struct DcF64 {
+    static constexpr int bytes = 8;
+    __device__ static double load(rsrc_t r, uint32_t o) {
+        return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(r, (int)o, 0, 0));
+    }
+    __device__ static double at(const void *p, size_t i) { return ((const double *)p)[i]; }
+    __device__ static void store(double v, rsrc_t r, uint32_t o) {
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)o, 0, kStoreNT);
+    }
+};
+
+// One lane per output (n, oc, o); locations in fp32 (double for double data).
+template <int R, typename T>
+__global__ __launch_bounds__(kBlock) void deform_conv_direct(DeformParams p) {
+    const size_t idx = (size_t)blockIdx.x * kBlock + threadIdx.x;
+    const size_t npos = p.npos;
+    const size_t total = (size_t)p.N * p.OC * npos;
+    if (idx >= total) return;
+    const size_t o = idx % npos;
+    const int oc = (int)((idx / npos) % p.OC);
+    const int n = (int)(idx / (npos * p.OC));
+    const int G = oc / p.OCg;
+    int oi[3];
+    size_t rem = o;
+#pragma unroll
+    for (int a = R - 1; a >= 0; --a) {
+        oi[a] = (int)(rem % (size_t)p.out_ext[a]);
+        rem /= (size_t)p.out_ext[a];
+    }
+    const rsrc_t xr = make_rsrc((const char *)p.X + (size_t)n * p.C * p.x_plane_bytes,
+                                (uint32_t)p.C * p.x_plane_bytes);
+    const int K = p.Ktot / p.Cg;
+    double acc = 0.0;
+    for (int cl = 0; cl < p.Cg; ++cl) {
+        const int c = G * p.Cg + cl;
+        const int g = c / p.Cog;
+        for (int k = 0; k < K; ++k) {
+            int ki[3];
+            int kr = k;
+#pragma unroll
+            for (int a = R - 1; a >= 0; --a) {
+                ki[a] = kr % p.k_ext[a];
+                kr /= p.k_ext[a];
+            }
+            int base[3];
+            double frac[3];
+            bool finite = true;
+#pragma unroll
+            for (int a = 0; a < R; ++a) {
+                const int regular = oi[a] * p.stride[a] - p.pad[a] + ki[a] * p.dil[a];
+                const double d =
+                    T::at(p.offset, (((size_t)n * p.og + g) * K * R + (size_t)k * R + a) * npos + o);
+                double loc;
+                if constexpr (T::bytes == 8) loc = (double)regular + d;
+                else loc = (double)((float)regular + (float)d);
+                if (!__builtin_isfinite(loc) || fabs(loc) > (double)kCoordLimit) finite = false;
+                const double fl = finite ? floor(loc) : 0.0;
+                base[a] = (int)fl;
+                frac[a] = finite ? loc - fl : 0.0;
+            }
+            if (!finite) continue;
+            double v = sample_direct<R, T>(xr, (uint32_t)c * p.x_plane_bytes, p.in_ext, base, frac);
+            if (p.mask) v = v * T::at(p.mask, (((size_t)n * p.og + g) * K + k) * npos + o);
+            acc = acc + T::at(p.Wt, ((size_t)oc * p.Cg + cl) * K + k) * v;
+        }
+    }
+    if (p.B) acc = acc + T::at(p.B, oc);
+    const rsrc_t yr = make_rsrc((char *)p.Y + (size_t)n * p.OC * npos * T::bytes,
+                                (uint32_t)((size_t)p.OC * npos * T::bytes));
+    T::store(acc, yr, (uint32_t)(((size_t)oc * npos + o) * T::bytes));
+}
+
+// --------------------------------------------------------------- dispatch
+
+template <typename T>
+static int mfma_launch(const DeformParams &p, hipStream_t s) {
+    const dim3 grid(8 * kRun * ((p.nblocks + 8 * kRun - 1) / (8 * kRun)));
+    const bool table = p.og_span * p.KH * p.KW <= DC_TABLE;
+    const bool wide = p.OCg > 128;
+    if (wide) {
+        if (table) hipLaunchKernelGGL((deform_conv2d_mfma<T, 2, true>), grid, dim3(kBlock), 0, s, p);
+        else hipLaunchKernelGGL((deform_conv2d_mfma<T, 2, false>), grid, dim3(kBlock), 0, s, p);
+    } else {
+        if (table) hipLaunchKernelGGL((deform_conv2d_mfma<T, 1, true>), grid, dim3(kBlock), 0, s, p);
+        else hipLaunchKernelGGL((deform_conv2d_mfma<T, 1, false>), grid, dim3(kBlock), 0, s, p);
+    }
+    return (int)hipGetLastError();
+}
+
+template <int R, typename T>
+static int direct_launch(const DeformParams &p, hipStream_t s) {
+    const size_t total = (size_t)p.N * p.OC * p.npos;
+    const dim3 grid((unsigned)((total + kBlock - 1) / kBlock));
+    hipLaunchKernelGGL((deform_conv_direct<R, T>), grid, dim3(kBlock), 0, s, p);
+    return (int)hipGetLastError();
+}
+
+template <typename T>
+static int direct_by_rank(const DeformParams &p, int rank, hipStream_t s) {
+    switch (rank) {
+    case 1: return direct_launch<1, T>(p, s);
+    case 2: return direct_launch<2, T>(p, s);
+    default: return direct_launch<3, T>(p, s);
+    }
+}
+
+int launch_deform_conv(const DeformParams &p, int rank, int dtype, bool mfma, hipStream_t s) {
+    if (mfma) {
+        switch (dtype) {
+        case 0: return mfma_launch<F32>(p, s);
+        case 1: return mfma_launch<F16>(p, s);
+        default: return mfma_launch<BF16>(p, s);
+        }
+    }
+    switch (dtype) {
+    case 0: return direct_by_rank<DcF32>(p, rank, s);
+    case 1: return direct_by_rank<DcF16>(p, rank, s);
+    case 2: return direct_by_rank<DcBF16>(p, rank, s);
+    default: return direct_by_rank<DcF64>(p, rank, s);
+    }
+}
+
+}  // namespace gs

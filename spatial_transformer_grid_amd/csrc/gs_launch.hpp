@@ -161,7 +161,24 @@ struct NdParams {
     int cgroups, cpg, nblocks; // channel groups, channels per group, blocks
 };
 
-// Launchers (gs_kernels.hip, gs_resize.hip, gs_nd.hip).  Return 0 on success or the hipError_t of the
+// One DeformConv launch (gs_deform.hip).  2-D uses the H / W / sh ... fields,
+// the direct kernel the per-axis arrays (r <= 3 axes, outermost first).
+struct DeformParams {
+    const void *X, *Wt, *offset, *mask, *B;  // mask and B may be NULL
+    void *Y;
+    int N, C, OC;
+    int H, W, KH, KW, OH, OW;                // 2-D extents
+    int sh, sw, pt, pl, dh, dw;              // 2-D strides, pad begins, dilations
+    int in_ext[3], out_ext[3], k_ext[3], stride[3], pad[3], dil[3];
+    int group, og, Cg, OCg, Cog, Ktot;       // Ktot = Cg * kernel size
+    int og_span;                             // offset groups one conv group spans
+    int m_tiles, n_tiles, nblocks;
+    uint32_t x_plane_bytes;                  // one input plane; C planes < 2^31 bytes
+    uint32_t w_bytes;                        // all of W (< 2^31)
+    uint32_t npos;                           // output positions per plane
+};
+
+// Launchers (gs_kernels.hip, gs_resize.hip, gs_nd.hip, gs_deform.hip).  Return 0 on success or the hipError_t of the
 // launch.  `rank` is 2 or 3; `dtype` 0 f32, 1 f16, 2 bf16; `vec_in` selects
 // 16-byte staging loads (input rows a whole number of 16-byte chunks).
 int launch_grid_sample(const SampleParams &p, int rank, bool fused, int mode, int padding,
@@ -171,6 +188,9 @@ int launch_affine_grid(const AffineParams &p, int rank, hipStream_t stream);
 // double), else fp32 / fp16 / bf16 (coordinates in fp32).
 int launch_grid_sample_nd(const NdParams &p, int rank, int mode, bool double_grid,
                           hipStream_t stream);
+// `mfma`: the 2-D matrix-core kernel (dtype 0 f32, 1 f16, 2 bf16); else the
+// direct kernel (rank 1..3, dtype 0..3 with 3 = f64).
+int launch_deform_conv(const DeformParams &p, int rank, int dtype, bool mfma, hipStream_t stream);
 // `d3`: the third axis from the end is resized; `mode` 0 nearest, 1 linear,
 // 2 cubic.
 int launch_resize(const ResizeParams &p, bool d3, int mode, int dtype, bool vec_in,

@@ -35,7 +35,7 @@ def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "gs_abi_version", "gs_status_string", "gs_affine_grid", "gs_grid_sample_2d",
         "gs_grid_sample_3d", "gs_affine_grid_sample_fused", "gs_resize", "gs_resize_output_shape",
-        "gs_grid_sample"])
+        "gs_grid_sample", "gs_deform_conv"])
 
 
 def test_library_exports_every_declared_symbol(gs):
@@ -262,3 +262,28 @@ def test_binding_dtype_codes(gs):
     assert gs.dtype_code(torch.zeros(1, dtype=torch.int64)) == gs.GS_I64
     with pytest.raises(TypeError):
         gs.dtype_code(torch.zeros(1, dtype=torch.bool))
+
+
+def test_deform_conv_rejects(gs):
+    lib = gs.lib()
+
+    def f(xs, ws, dt=0, X=FAKE, W=FAKE, off=FAKE, Y=FAKE, st=None, pd=None, dl=None, grp=1,
+          og=1, rank=None):
+        a = lambda v: gs.int64_array(v) if v is not None else None
+        return lib.gs_deform_conv(X, dt, gs.int64_array(xs), len(xs) if rank is None else rank, W,
+                                  gs.int64_array(ws), off, None, None, a(st), a(pd), a(dl), grp,
+                                  og, Y, None)
+
+    assert f([1, 4, 8, 8], [6, 4, 3, 3], dt=5) == 3              # integer data
+    assert f([1, 4, 8, 8], [6, 4, 3, 3], rank=6) == 2
+    assert f([1, 4, 8, 8], [6, 3, 3, 3]) == 2                     # W's C/group
+    assert f([1, 4, 8, 8], [5, 2, 3, 3], grp=2) == 2              # oC % group
+    assert f([1, 4, 8, 8], [6, 4, 3, 3], og=3) == 2               # C % offset_group
+    assert f([1, 4, 8, 8], [6, 4, 3, 3], grp=0) == 4
+    assert f([1, 4, 8, 8], [6, 4, 3, 3], st=[0, 1]) == 4
+    assert f([1, 4, 8, 8], [6, 4, 3, 3], pd=[0, -1, 0, 0]) == 4
+    assert f([1, 4, 2, 8], [6, 4, 3, 3]) == 2                     # padded input too small
+    assert f([1, 4, 8, 8], [6, 4, 3, 3], X=None) == 1
+    assert f([1, 4, 8, 8], [6, 4, 3, 3], off=None) == 1
+    assert f([0, 4, 8, 8], [6, 4, 3, 3], X=None, W=None, off=None, Y=None) == 0
+    assert f([1, 4, 1 << 24, 2], [6, 4, 3, 1]) == 5
