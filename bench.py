@@ -288,6 +288,32 @@ def run_paths(torch, gsa, flush_buf):
                warm)
         del X, Y, G, inp
 
+    # DeformConv layers: matrix-core throughput (flops of the convolution)
+    for name, dw in W.DEFORM_WORKLOADS.items():
+        inp = W.make_deform_inputs(dw)
+        for kind in dw.dtypes:
+            tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[kind]
+            d = {k: torch.from_numpy(v).cuda().to(tdt) for k, v in inp.items()}
+            Y = torch.empty(dw.out_shape(), dtype=tdt, device="cuda")
+            fn = lambda: gsa.deform_conv(d["X"], d["W"], d["offset"], d["B"], d["mask"],
+                                         pads=list(dw.pads), group=dw.group,
+                                         offset_group=dw.offset_group, out=Y)
+            fn()
+            us, _ = time_kernel(torch, fn, 20, flush)
+            peak = 157.3 if kind == "f32" else 2500.0
+            tflops = dw.flops / (us * 1e-6) / 1e12
+            es = 4 if kind == "f32" else 2
+            io = (inp["X"].size + inp["W"].size + inp["offset"].size + inp["mask"].size
+                  + inp["B"].size + Y.numel()) * es
+            out.append({"path": "%s/%s" % (name, kind), "workload": name,
+                        "kernel": "gs_deform_conv (implicit GEMM, MFMA)", "kernel_us": round(us, 2),
+                        "bound": "mfma", "TFLOPs": tflops, "peak_TFLOPs": peak,
+                        "frac_mfma_peak": tflops / peak, "flops": dw.flops, "io_bytes": io,
+                        "GBps_io": io / (us * 1e-6) / 1e9})
+            log("%-28s %8.1f us  %7.1f TFLOP/s  %.3f of the %s MFMA peak" % (
+                "%s/%s" % (name, kind), us, tflops, tflops / peak, kind))
+            del d, Y
+
     # Resize workloads (fp32): at their scales every input element has a
     # non-zero weight, so all of X is compulsory
     for name, rw in W.RESIZE_WORKLOADS.items():

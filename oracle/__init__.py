@@ -94,6 +94,9 @@ def _bind(path: str):
                                        p_f64, p_f64, p_i64, p_i64, p_i64, p_i64, i64, i64, c_int,
                                        p_f64]
     lib.oracle_deform_conv.restype = c_int
+    lib.oracle_deform_conv_points.argtypes = lib.oracle_deform_conv.argtypes[:-1] + [p_i64, i64,
+                                                                                   p_f64]
+    lib.oracle_deform_conv_points.restype = c_int
     return lib
 
 
@@ -348,13 +351,14 @@ def deform_conv_output_shape(in_sp, ksz, strides, pads, dilations):
 
 
 def deform_conv(X, W, offset, B=None, mask=None, strides=None, pads=None, dilations=None,
-                group: int = 1, offset_group: int = 1, lib=None) -> np.ndarray:
+                group: int = 1, offset_group: int = 1, lib=None, flat_index=None) -> np.ndarray:
     """DeformConv(X, W, offset, B, mask) -> Y as float64 (unrounded).
 
     Arrays are fp32 (half data widened exactly: locations in fp32) or float64
     (locations in float64); attribute names and defaults follow the
     convolution operators (strides and dilations 1, pads 0, group and
-    offset_group 1)."""
+    offset_group 1).  With flat_index, only those flat outputs of Y are
+    computed (a 1-D array)."""
     lib = lib or _load()
     X = np.asarray(X)
     coord_f32 = 0 if X.dtype == np.float64 else 1
@@ -370,20 +374,27 @@ def deform_conv(X, W, offset, B=None, mask=None, strides=None, pads=None, dilati
     pads = [0] * (2 * r) if pads is None else list(pads)
     out_sp = deform_conv_output_shape(in_sp, ksz, strides, pads, dilations)
     oc = W.shape[0]
-    Y = np.empty((n, oc) + out_sp, dtype=np.float64)
+    if flat_index is not None:
+        idx = np.ascontiguousarray(flat_index, dtype=np.int64)
+        Y = np.empty(idx.shape[0], dtype=np.float64)
+    else:
+        Y = np.empty((n, oc) + out_sp, dtype=np.float64)
     b = None if B is None else np.ascontiguousarray(B, dtype=np.float64)
     m = None if mask is None else np.ascontiguousarray(mask, dtype=np.float64)
     arr = lambda v: np.asarray(v, dtype=np.int64)
     in_a, k_a, o_a, s_a, p_a, d_a = (arr(in_sp), arr(ksz), arr(out_sp), arr(strides), arr(pads),
                                      arr(dilations))
-    rc = lib.oracle_deform_conv(_ptr(X, ctypes.c_double), r, n, c, _ptr(in_a, ctypes.c_int64),
-                                _ptr(W, ctypes.c_double), oc, _ptr(k_a, ctypes.c_int64),
-                                _ptr(offset, ctypes.c_double),
-                                _ptr(b, ctypes.c_double) if b is not None else None,
-                                _ptr(m, ctypes.c_double) if m is not None else None,
-                                _ptr(o_a, ctypes.c_int64), _ptr(s_a, ctypes.c_int64),
-                                _ptr(p_a, ctypes.c_int64), _ptr(d_a, ctypes.c_int64), int(group),
-                                int(offset_group), coord_f32, _ptr(Y, ctypes.c_double))
+    args = [_ptr(X, ctypes.c_double), r, n, c, _ptr(in_a, ctypes.c_int64),
+            _ptr(W, ctypes.c_double), oc, _ptr(k_a, ctypes.c_int64), _ptr(offset, ctypes.c_double),
+            _ptr(b, ctypes.c_double) if b is not None else None,
+            _ptr(m, ctypes.c_double) if m is not None else None, _ptr(o_a, ctypes.c_int64),
+            _ptr(s_a, ctypes.c_int64), _ptr(p_a, ctypes.c_int64), _ptr(d_a, ctypes.c_int64),
+            int(group), int(offset_group), coord_f32]
+    if flat_index is not None:
+        rc = lib.oracle_deform_conv_points(*args, _ptr(idx, ctypes.c_int64), idx.shape[0],
+                                           _ptr(Y, ctypes.c_double))
+    else:
+        rc = lib.oracle_deform_conv(*args, _ptr(Y, ctypes.c_double))
     if rc:
         raise ValueError("oracle_deform_conv rejected its arguments")
     return Y

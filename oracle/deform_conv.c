@@ -70,6 +70,118 @@ static double sample_linear(const double *plane, int r, const int64_t *in_sp,
     return acc;
 }
 
+typedef struct {
+    const double *X, *Wt, *offset, *B, *mask;
+    int r;
+    int64_t N, C, OC, og;
+    const int64_t *in_sp, *ksz, *out_sp, *strides, *pads, *dilations;
+    int64_t Cg, OCg, Cog, K, in_count, out_count;
+    int coord_f32;
+} dc_problem;
+
+static int dc_setup(dc_problem *P, const double *X, int r, int64_t N, int64_t C,
+                    const int64_t *in_sp, const double *Wt, int64_t OC, const int64_t *ksz,
+                    const double *offset, const double *B, const double *mask,
+                    const int64_t *out_sp, const int64_t *strides, const int64_t *pads,
+                    const int64_t *dilations, int64_t group, int64_t offset_group, int coord_f32)
+{
+    if (r < 1 || r > DC_MAX_RANK || N < 0 || C < 1 || OC < 1 || group < 1 || offset_group < 1)
+        return -1;
+    if (C % group || OC % group || C % offset_group)
+        return -1;
+    P->in_count = 1;
+    P->out_count = 1;
+    P->K = 1;
+    for (int a = 0; a < r; ++a) {
+        if (in_sp[a] < 1 || ksz[a] < 1 || strides[a] < 1 || dilations[a] < 1 || out_sp[a] < 0)
+            return -1;
+        int64_t span = dilations[a] * (ksz[a] - 1) + 1;
+        int64_t expect = (in_sp[a] + pads[a] + pads[r + a] - span) / strides[a] + 1;
+        if (out_sp[a] != expect)
+            return -1;
+        P->in_count *= in_sp[a];
+        P->out_count *= out_sp[a];
+        P->K *= ksz[a];
+    }
+    P->X = X;
+    P->Wt = Wt;
+    P->offset = offset;
+    P->B = B;
+    P->mask = mask;
+    P->r = r;
+    P->N = N;
+    P->C = C;
+    P->OC = OC;
+    P->og = offset_group;
+    P->in_sp = in_sp;
+    P->ksz = ksz;
+    P->out_sp = out_sp;
+    P->strides = strides;
+    P->pads = pads;
+    P->dilations = dilations;
+    P->Cg = C / group;
+    P->OCg = OC / group;
+    P->Cog = C / offset_group;
+    P->coord_f32 = coord_f32;
+    return 0;
+}
+
+/* Output element (n, oc, o): bias + sum over the channels of oc's group and
+ * the kernel positions of W * mask * linear sample. */
+static double dc_value(const dc_problem *P, int64_t n, int64_t oc, int64_t o)
+{
+    const int r = P->r;
+    const int64_t K = P->K, out_count = P->out_count;
+    const int64_t G = oc / P->OCg;
+    int64_t oi[DC_MAX_RANK];
+    int64_t rest = o;
+    for (int a = r - 1; a >= 0; --a) {
+        oi[a] = rest % P->out_sp[a];
+        rest /= P->out_sp[a];
+    }
+    double acc = 0.0;
+    for (int64_t cl = 0; cl < P->Cg; ++cl) {
+        const int64_t c = G * P->Cg + cl;
+        const int64_t g = c / P->Cog;
+        const double *plane = P->X + (n * P->C + c) * P->in_count;
+        for (int64_t k = 0; k < K; ++k) {
+            int64_t ki[DC_MAX_RANK];
+            int64_t kr = k;
+            for (int a = r - 1; a >= 0; --a) {
+                ki[a] = kr % P->ksz[a];
+                kr /= P->ksz[a];
+            }
+            double frac[DC_MAX_RANK];
+            int64_t base[DC_MAX_RANK];
+            int finite = 1;
+            for (int a = 0; a < r && finite; ++a) {
+                int64_t regular = oi[a] * P->strides[a] - P->pads[a] + ki[a] * P->dilations[a];
+                double d = P->offset[((n * P->og + g) * K * r + k * r + a) * out_count + o];
+                double loc = P->coord_f32 ? (double)((float)regular + (float)d)
+                                          : (double)regular + d;
+                /* a location beyond any image reads zero (and is kept away
+                 * from the integer conversion) */
+                if (!isfinite(loc) || fabs(loc) > 16777216.0) {
+                    finite = 0;
+                    break;
+                }
+                double fl = floor(loc); /* exact for an fp32 value too */
+                base[a] = (int64_t)fl;
+                frac[a] = loc - fl;     /* exact */
+            }
+            if (!finite)
+                continue;
+            double v = sample_linear(plane, r, P->in_sp, frac, base);
+            if (P->mask)
+                v *= P->mask[((n * P->og + g) * K + k) * out_count + o];
+            acc += P->Wt[(oc * P->Cg + cl) * K + k] * v;
+        }
+    }
+    if (P->B)
+        acc += P->B[oc];
+    return acc;
+}
+
 /*
  * Y = DeformConv(X, W, offset, B, mask), r spatial axes (1 .. 3).
  *   X      (N, C, in_sp...)            float64
@@ -89,78 +201,40 @@ int oracle_deform_conv(const double *X, int r, int64_t N, int64_t C, const int64
                        const int64_t *strides, const int64_t *pads, const int64_t *dilations,
                        int64_t group, int64_t offset_group, int coord_f32, double *Y)
 {
-    if (r < 1 || r > DC_MAX_RANK || N < 0 || C < 1 || OC < 1 || group < 1 || offset_group < 1)
+    dc_problem P;
+    if (dc_setup(&P, X, r, N, C, in_sp, Wt, OC, ksz, offset, B, mask, out_sp, strides, pads,
+                 dilations, group, offset_group, coord_f32))
         return -1;
-    if (C % group || OC % group || C % offset_group)
-        return -1;
-    int64_t in_count = 1, out_count = 1, K = 1;
-    for (int a = 0; a < r; ++a) {
-        if (in_sp[a] < 1 || ksz[a] < 1 || strides[a] < 1 || dilations[a] < 1 || out_sp[a] < 0)
-            return -1;
-        int64_t span = dilations[a] * (ksz[a] - 1) + 1;
-        int64_t expect = (in_sp[a] + pads[a] + pads[r + a] - span) / strides[a] + 1;
-        if (out_sp[a] != expect)
-            return -1;
-        in_count *= in_sp[a];
-        out_count *= out_sp[a];
-        K *= ksz[a];
-    }
-    const int64_t Cg = C / group, OCg = OC / group, Cog = C / offset_group;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t oc = 0; oc < OC; ++oc)
+            for (int64_t o = 0; o < P.out_count; ++o)
+                Y[(n * OC + oc) * P.out_count + o] = dc_value(&P, n, oc, o);
+    return 0;
+}
 
-    for (int64_t n = 0; n < N; ++n) {
-        for (int64_t oc = 0; oc < OC; ++oc) {
-            const int64_t G = oc / OCg;
-            for (int64_t o = 0; o < out_count; ++o) {
-                int64_t oi[DC_MAX_RANK];
-                int64_t rest = o;
-                for (int a = r - 1; a >= 0; --a) {
-                    oi[a] = rest % out_sp[a];
-                    rest /= out_sp[a];
-                }
-                double acc = 0.0;
-                for (int64_t cl = 0; cl < Cg; ++cl) {
-                    const int64_t c = G * Cg + cl;
-                    const int64_t g = c / Cog;
-                    const double *plane = X + (n * C + c) * in_count;
-                    for (int64_t k = 0; k < K; ++k) {
-                        int64_t ki[DC_MAX_RANK];
-                        int64_t kr = k;
-                        for (int a = r - 1; a >= 0; --a) {
-                            ki[a] = kr % ksz[a];
-                            kr /= ksz[a];
-                        }
-                        double frac[DC_MAX_RANK];
-                        int64_t base[DC_MAX_RANK];
-                        int finite = 1;
-                        for (int a = 0; a < r && finite; ++a) {
-                            int64_t regular = oi[a] * strides[a] - pads[a] + ki[a] * dilations[a];
-                            double d = offset[((n * offset_group + g) * K * r + k * r + a) *
-                                                  out_count + o];
-                            double loc = coord_f32 ? (double)((float)regular + (float)d)
-                                                   : (double)regular + d;
-                            /* a location beyond any image reads zero (and is
-                             * kept away from the integer conversion) */
-                            if (!isfinite(loc) || fabs(loc) > 16777216.0) {
-                                finite = 0;
-                                break;
-                            }
-                            double fl = floor(loc); /* exact for an fp32 value too */
-                            base[a] = (int64_t)fl;
-                            frac[a] = loc - fl;     /* exact */
-                        }
-                        if (!finite)
-                            continue;
-                        double v = sample_linear(plane, r, in_sp, frac, base);
-                        if (mask)
-                            v *= mask[((n * offset_group + g) * K + k) * out_count + o];
-                        acc += Wt[(oc * Cg + cl) * K + k] * v;
-                    }
-                }
-                if (B)
-                    acc += B[oc];
-                Y[(n * OC + oc) * out_count + o] = acc;
-            }
-        }
+/* As oracle_deform_conv, only for the `count` outputs whose flat indices into
+ * Y are listed in `flat`; the values go to Y[0..count).  Returns 0, or -1 on
+ * a bad argument or index. */
+int oracle_deform_conv_points(const double *X, int r, int64_t N, int64_t C,
+                              const int64_t *in_sp, const double *Wt, int64_t OC,
+                              const int64_t *ksz, const double *offset, const double *B,
+                              const double *mask, const int64_t *out_sp, const int64_t *strides,
+                              const int64_t *pads, const int64_t *dilations, int64_t group,
+                              int64_t offset_group, int coord_f32, const int64_t *flat,
+                              int64_t count, double *Y)
+{
+    dc_problem P;
+    if (dc_setup(&P, X, r, N, C, in_sp, Wt, OC, ksz, offset, B, mask, out_sp, strides, pads,
+                 dilations, group, offset_group, coord_f32))
+        return -1;
+    for (int64_t i = 0; i < count; ++i) {
+        const int64_t f = flat[i];
+        if (f < 0 || f >= N * OC * P.out_count)
+            return -1;
+        const int64_t o = f % P.out_count;
+        const int64_t oc = (f / P.out_count) % OC;
+        const int64_t n = f / (P.out_count * OC);
+        Y[i] = dc_value(&P, n, oc, o);
     }
     return 0;
 }

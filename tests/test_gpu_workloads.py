@@ -1,5 +1,5 @@
 """The synthetic workloads (five sampler, five Resize, three of other ranks
-and element types) on the GPU against the oracle.
+and element types, a DeformConv layer) on the GPU against the oracle.
 
 * reduced shapes (same distributions, several tiles, ragged tails): every
   output element is compared;
@@ -233,3 +233,65 @@ def test_type_workload_full_size_sampled(gsa, name):
     ref = type_expected(oracle.grid_sample_points(inp["X"], g_ref, idx, w.mode, w.padding,
                                                   w.align_corners), inp["X"])
     assert np.array_equal(got, ref), name
+
+
+# ------------------------------------------------------------------ DeformConv
+
+def deform_dev(inp, kind):
+    torch = torch_mod()
+    out, exact = {}, {}
+    for k, a in inp.items():
+        if kind == "f32":
+            out[k], exact[k] = torch.from_numpy(a).cuda(), a
+        else:
+            bits = W.to_half_bits(a, kind)
+            out[k] = torch.from_numpy(bits.view(np.int16)).cuda().view(
+                torch.float16 if kind == "f16" else torch.bfloat16)
+            exact[k] = W.half_bits_to_f32(bits, kind)
+    return out, exact
+
+
+def deform_check(got, ref, S, kind, what):
+    rel = {"f32": 2e-5, "f16": 2e-3, "bf16": 1e-2}[kind]
+    ulp = {"f32": 0.0, "f16": 2.0 ** -10, "bf16": 2.0 ** -7}[kind]
+    tol = rel * S + ulp * np.abs(ref) + 1e-30
+    err = np.abs(got - ref)
+    assert (err <= tol).all(), "%s: max err/tol %.3g" % (what, (err / tol).max())
+
+
+@pytest.mark.parametrize("name,kind", [(n, k) for n, w in W.DEFORM_WORKLOADS.items()
+                                       for k in w.dtypes])
+def test_deform_workload_reduced_all_elements(gsa, name, kind):
+    w = W.DEFORM_WORKLOADS[name]
+    xs = (2, 24, 19, 21)
+    ws = (40, 24) + tuple(w.w_shape[2:])
+    note("reduced %s %s x=%s w=%s" % (name, kind, xs, ws))
+    d, e = deform_dev(W.make_deform_inputs(w, xs, ws), kind)
+    Y = gsa.deform_conv(d["X"], d["W"], d["offset"], d["B"], d["mask"], pads=list(w.pads),
+                        group=w.group, offset_group=w.offset_group)
+    got = Y.double().cpu().numpy()
+    args = dict(pads=list(w.pads), group=w.group, offset_group=w.offset_group)
+    ref = oracle.deform_conv(e["X"], e["W"], e["offset"], e["B"], e["mask"], **args)
+    S = oracle.deform_conv(np.abs(e["X"]), np.abs(e["W"]), e["offset"], None, np.abs(e["mask"]),
+                           **args) + np.abs(e["B"]).reshape(1, -1, 1, 1)
+    deform_check(got, ref, S, kind, name)
+
+
+@pytest.mark.parametrize("name,kind", [(n, k) for n, w in W.DEFORM_WORKLOADS.items()
+                                       for k in w.dtypes])
+def test_deform_workload_full_size_sampled(gsa, name, kind):
+    w = W.DEFORM_WORKLOADS[name]
+    note("full %s %s x=%s" % (name, kind, w.x_shape))
+    d, e = deform_dev(W.make_deform_inputs(w), kind)
+    Y = gsa.deform_conv(d["X"], d["W"], d["offset"], d["B"], d["mask"], pads=list(w.pads),
+                        group=w.group, offset_group=w.offset_group)
+    n, oc, oh, ow = w.out_shape()
+    idx = sample_indices(n, oc, oh * ow, 4096, w.seed)
+    torch = torch_mod()
+    got = Y.reshape(-1)[torch.from_numpy(idx).cuda()].double().cpu().numpy()
+    del Y
+    args = dict(pads=list(w.pads), group=w.group, offset_group=w.offset_group, flat_index=idx)
+    ref = oracle.deform_conv(e["X"], e["W"], e["offset"], e["B"], e["mask"], **args)
+    S = oracle.deform_conv(np.abs(e["X"]), np.abs(e["W"]), e["offset"], None, np.abs(e["mask"]),
+                           **args) + np.abs(e["B"])[(idx // (oh * ow)) % oc]
+    deform_check(got, ref, S, kind, "full " + name)

@@ -235,22 +235,23 @@ def battery(om, lib):
 
 
 MUTANTS = [
-    ("offset components swapped", "offset[((n * offset_group + g) * K * r + k * r + a) *",
-     "offset[((n * offset_group + g) * K * r + k * r + (r - 1 - a)) *"),
-    ("regular position without the pad", "oi[a] * strides[a] - pads[a] + ki[a] * dilations[a]",
-     "oi[a] * strides[a] + ki[a] * dilations[a]"),
-    ("dilation ignored", "oi[a] * strides[a] - pads[a] + ki[a] * dilations[a]",
-     "oi[a] * strides[a] - pads[a] + ki[a]"),
+    ("offset components swapped", "P->offset[((n * P->og + g) * K * r + k * r + a)",
+     "P->offset[((n * P->og + g) * K * r + k * r + (r - 1 - a))"),
+    ("regular position without the pad",
+     "oi[a] * P->strides[a] - P->pads[a] + ki[a] * P->dilations[a]",
+     "oi[a] * P->strides[a] + ki[a] * P->dilations[a]"),
+    ("dilation ignored", "oi[a] * P->strides[a] - P->pads[a] + ki[a] * P->dilations[a]",
+     "oi[a] * P->strides[a] - P->pads[a] + ki[a]"),
     ("linear weights swapped", "w *= bit ? frac[a] : 1.0 - frac[a];",
      "w *= bit ? 1.0 - frac[a] : frac[a];"),
     ("zero extension replaced by a clamp", "valid = valid && i >= 0 && i < in_sp[a];",
      "i = i < 0 ? 0 : (i >= in_sp[a] ? in_sp[a] - 1 : i);"),
-    ("mask channel of the wrong group", "v *= mask[((n * offset_group + g) * K + k) * out_count + o];",
-     "v *= mask[((n * offset_group + 0) * K + k) * out_count + o];"),
-    ("offset group by modulo", "const int64_t g = c / Cog;", "const int64_t g = c % offset_group;"),
-    ("weights of the wrong group", "acc += Wt[(oc * Cg + cl) * K + k] * v;",
-     "acc += Wt[(oc * Cg + cl) * K + (K - 1 - k)] * v;"),
-    ("bias dropped", "acc += B[oc];", "acc += 0.0 * B[oc];"),
+    ("mask channel of the wrong group", "v *= P->mask[((n * P->og + g) * K + k) * out_count + o];",
+     "v *= P->mask[((n * P->og + 0) * K + k) * out_count + o];"),
+    ("offset group by modulo", "const int64_t g = c / P->Cog;", "const int64_t g = c % P->og;"),
+    ("weights of the wrong kernel position", "acc += P->Wt[(oc * P->Cg + cl) * K + k] * v;",
+     "acc += P->Wt[(oc * P->Cg + cl) * K + (K - 1 - k)] * v;"),
+    ("bias dropped", "acc += P->B[oc];", "acc += 0.0 * P->B[oc];"),
 ]
 
 

@@ -46,6 +46,9 @@ __all__ = [
     "TYPE_WORKLOADS",
     "make_type_inputs",
     "smooth_warp_1d",
+    "DeformWorkload",
+    "DEFORM_WORKLOADS",
+    "make_deform_inputs",
 ]
 
 
@@ -347,3 +350,56 @@ def make_type_inputs(w: TypeWorkload, x_shape=None, out_spatial=None):
     else:
         X = uniform(g, x_shape, -1.0, 1.0)
     return {"X": X, "theta": theta, "grid": grid, "x_shape": x_shape, "out_spatial": out_spatial}
+
+
+@dataclass(frozen=True)
+class DeformWorkload:
+    """A DeformConv layer: X ~ U(-1, 1), W ~ U(-w, w) with w = 1/sqrt(fan-in),
+    pixel offsets ~ N(0, offset_std^2), mask ~ U(0, 1), B ~ U(-0.1, 0.1)."""
+
+    name: str
+    seed: int
+    x_shape: tuple               # (N, C, H, W)
+    w_shape: tuple               # (oC, C / group, kH, kW)
+    pads: tuple
+    group: int = 1
+    offset_group: int = 1
+    offset_std: float = 1.0
+    dtypes: tuple = ("bf16", "f32")
+
+    def out_shape(self):
+        n, _, h, w = self.x_shape
+        oc, _, kh, kw = self.w_shape
+        return (n, oc, h + self.pads[0] + self.pads[2] - kh + 1,
+                w + self.pads[1] + self.pads[3] - kw + 1)
+
+    @property
+    def flops(self) -> int:
+        n, oc, oh, ow = self.out_shape()
+        k = self.w_shape[1] * self.w_shape[2] * self.w_shape[3]
+        return 2 * n * oc * oh * ow * k
+
+
+DEFORM_WORKLOADS = {
+    # a modulated deformable 3x3 layer of a ResNet stage at 64x64 (DCNv2-style)
+    "dcn2d_resnet": DeformWorkload("dcn2d_resnet", 41, (8, 256, 64, 64), (256, 256, 3, 3),
+                                   (1, 1, 1, 1)),
+}
+
+
+def make_deform_inputs(w: DeformWorkload, x_shape=None, w_shape=None):
+    """X, W, offset, mask, B of a DeformWorkload (fp32; optionally reduced)."""
+    x_shape = tuple(x_shape or w.x_shape)
+    w_shape = tuple(w_shape or w.w_shape)
+    g = rng(w.seed)
+    n, _, h, wd = x_shape
+    kh, kw = w_shape[2:]
+    oh = h + w.pads[0] + w.pads[2] - kh + 1
+    ow = wd + w.pads[1] + w.pads[3] - kw + 1
+    fan_in = w_shape[1] * kh * kw
+    X = uniform(g, x_shape, -1.0, 1.0)
+    Wt = uniform(g, w_shape, -1.0 / math.sqrt(fan_in), 1.0 / math.sqrt(fan_in))
+    off = normal(g, (n, w.offset_group * kh * kw * 2, oh, ow), w.offset_std)
+    mask = uniform(g, (n, w.offset_group * kh * kw, oh, ow), 0.0, 1.0)
+    B = uniform(g, (w_shape[0],), -0.1, 0.1)
+    return {"X": X, "W": Wt, "offset": off, "mask": mask, "B": B}
