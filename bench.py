@@ -295,9 +295,12 @@ def run_paths(torch, gsa, flush_buf):
             tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[kind]
             d = {k: torch.from_numpy(v).cuda().to(tdt) for k, v in inp.items()}
             Y = torch.empty(dw.out_shape(), dtype=tdt, device="cuda")
+            ws = torch.empty(gsa.deform_conv_workspace_size(
+                dw.x_shape, dw.w_shape, gsa.dtype_code(d["X"]), None, list(dw.pads), None,
+                dw.group, dw.offset_group), dtype=torch.uint8, device="cuda")
             fn = lambda: gsa.deform_conv(d["X"], d["W"], d["offset"], d["B"], d["mask"],
                                          pads=list(dw.pads), group=dw.group,
-                                         offset_group=dw.offset_group, out=Y)
+                                         offset_group=dw.offset_group, out=Y, workspace=ws)
             fn()
             us, _ = time_kernel(torch, fn, 20, flush)
             peak = 157.3 if kind == "f32" else 2500.0

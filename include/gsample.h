@@ -20,8 +20,9 @@
  *   tensors owned by the caller.  Shape arrays are HOST memory, read only
  *   during the call.
  * - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
- *   The library allocates no memory, keeps no state between calls and never
- *   synchronises; a call returns once its kernel is enqueued.
+ *   The library allocates no memory (scratch space comes from the caller),
+ *   keeps no state between calls and never synchronises; a call returns once
+ *   its kernels are enqueued.
  * - The output must not overlap any input.
  * - Every argument is validated before anything is launched.  On any error
  *   nothing is launched or written and the status says why.  A tensor with a
@@ -335,6 +336,16 @@ int gs_resize(const void *X, int x_dtype, const int64_t *x_shape, int rank, cons
  *   Y            device (N, oC, o1 .. or), o_a = (D_a + pad_begin + pad_end -
  *                (dilation * (k_a - 1) + 1)) / stride + 1.
  *
+ *   workspace, workspace_bytes   device scratch owned by the caller, or NULL
+ *                and 0.  With at least gs_deform_conv_workspace_size() bytes
+ *                (256-byte aligned), 2-D fp32 / fp16 / bf16 data whose conv
+ *                groups and offset groups hold multiples of 8 channels run on
+ *                a channels-last copy of X made there (8 channels per load);
+ *                otherwise they gather from X's planes.  Both sum the same
+ *                terms in fp32; only the rounding order differs.  The
+ *                workspace is overwritten; it must not be shared by calls
+ *                that may run at the same time.
+ *
  * The sampling location (regular position + offset) is computed in fp32 for
  * fp32 / fp16 / bf16 data and in double for double data.  2-D fp32, fp16 and
  * bf16 run on the matrix cores (MFMA, fp32 accumulation; the sampled values
@@ -346,12 +357,25 @@ int gs_resize(const void *X, int x_dtype, const int64_t *x_shape, int rank, cons
  * empty or too small padded input), GS_ERR_DTYPE, GS_ERR_ATTR (stride or
  * dilation < 1, negative pad, group or offset_group < 1), GS_ERR_TOO_LARGE
  * (an image of X, of Y or all of W above 2^31 - 1 bytes, extents of 2^24 or
- * more, too many thread blocks), GS_ERR_HIP.
+ * more, too many thread blocks), GS_ERR_ATTR for a negative workspace_bytes,
+ * GS_ERR_HIP.
  */
 int gs_deform_conv(const void *X, int dtype, const int64_t *x_shape, int x_rank, const void *W,
                    const int64_t *w_shape, const void *offset, const void *B, const void *mask,
                    const int64_t *strides, const int64_t *pads, const int64_t *dilations,
-                   int group, int offset_group, void *Y, void *stream);
+                   int group, int offset_group, void *Y, void *workspace,
+                   int64_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of workspace gs_deform_conv uses for these shapes and attributes (the
+ * same arguments, same validation and errors), 0 when no workspace helps:
+ * N*C*D1*..*Dr elements for X, plus oC * k1*..*kr * (C/group rounded up to
+ * 32) for W, each part rounded up to 256 bytes.  Written to *bytes (host).
+ */
+int gs_deform_conv_workspace_size(int dtype, const int64_t *x_shape, int x_rank,
+                                  const int64_t *w_shape, const int64_t *strides,
+                                  const int64_t *pads, const int64_t *dilations, int group,
+                                  int offset_group, int64_t *bytes);
 
 #ifdef __cplusplus
 }

@@ -23,6 +23,8 @@ from ._binding import (  # noqa: F401
     affine_grid_sample_fused,
     deform_conv,
     deform_conv_output_shape,
+    deform_conv_workspace_size,
+    dtype_code,
     grid_sample,
     lib,
     resize,
@@ -32,4 +34,5 @@ from ._binding import (  # noqa: F401
 
 __all__ = ["affine_grid", "grid_sample", "affine_grid_sample_fused", "resize",
            "resize_output_shape", "resize_to", "deform_conv", "deform_conv_output_shape",
+           "deform_conv_workspace_size", "dtype_code",
            "GSError", "lib"]

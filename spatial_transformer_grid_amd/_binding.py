@@ -39,7 +39,9 @@ SIGNATURES = {
     "gs_affine_grid_sample_fused": ([_P, _I, _P, _I, _PI64, _I, _PI64, _I, _I, _I, _P, _P], _I),
     "gs_grid_sample": ([_P, _I, _PI64, _I, _P, _I, _PI64, _I, _I, _I, _P, _P], _I),
     "gs_deform_conv": ([_P, _I, _PI64, _I, _P, _PI64, _P, _P, _P, _PI64, _PI64, _PI64, _I, _I,
-                        _P, _P], _I),
+                        _P, _P, ctypes.c_int64, _P], _I),
+    "gs_deform_conv_workspace_size": ([_I, _PI64, _I, _PI64, _PI64, _PI64, _PI64, _I, _I, _PI64],
+                                      _I),
     "gs_resize_output_shape": ([_PI64, _I, _PI64, _I, _PF32, _PI64, _I, _PI64], _I),
     "gs_resize": ([_P, _I, _PI64, _I, _PI64, _PF32, _I, _I, _I, ctypes.c_float, _I, _P, _P], _I),
 }
@@ -269,11 +271,13 @@ def deform_conv_output_shape(x_shape, w_shape, strides=None, pads=None, dilation
 
 
 def deform_conv(X, W, offset, B=None, mask=None, strides=None, pads=None, dilations=None,
-                group: int = 1, offset_group: int = 1, out=None, stream=None):
+                group: int = 1, offset_group: int = 1, out=None, stream=None, workspace=None):
     """DeformConv(X, W, offset, B, mask) -> Y on the GPU (gs_deform_conv).
 
     Attribute names follow the convolution operators (strides, pads as begins
-    then ends, dilations, group, offset_group)."""
+    then ends, dilations, group, offset_group).  `workspace`: a device tensor
+    of scratch bytes; None takes one of the size the library asks for from
+    torch's allocator, and an empty tensor runs without one."""
     X = _device_tensor(X, "X")
     W = _device_tensor(W, "W")
     offset = _device_tensor(offset, "offset")
@@ -301,9 +305,30 @@ def deform_conv(X, W, offset, B=None, mask=None, strides=None, pads=None, dilati
     Y = _out_tensor(out, shape, X)
     ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
     arr = lambda v: int64_array(v) if v is not None else None
+    need = ctypes.c_int64(0)
+    _check(lib().gs_deform_conv_workspace_size(
+        dtype_code(X), int64_array(X.shape), X.dim(), int64_array(W.shape), arr(strides),
+        arr(pads), arr(dilations), int(group), int(offset_group), ctypes.byref(need)),
+        "gs_deform_conv_workspace_size")
+    if workspace is None and need.value > 0:
+        workspace = _torch().empty(need.value, dtype=_torch().uint8, device=X.device)
+    ws_ptr = ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib().gs_deform_conv(ptr(X), dtype_code(X), int64_array(X.shape), X.dim(), ptr(W),
                               int64_array(W.shape), ptr(offset), ptr(B), ptr(mask), arr(strides),
                               arr(pads), arr(dilations), int(group), int(offset_group), ptr(Y),
-                              _stream(stream, X.device))
+                              ws_ptr, ws_bytes, _stream(stream, X.device))
     _check(st, "gs_deform_conv")
     return Y
+
+
+def deform_conv_workspace_size(X_shape, W_shape, dtype, strides=None, pads=None, dilations=None,
+                               group: int = 1, offset_group: int = 1) -> int:
+    """Bytes of workspace deform_conv uses (gs_deform_conv_workspace_size)."""
+    arr = lambda v: int64_array(v) if v is not None else None
+    need = ctypes.c_int64(0)
+    _check(lib().gs_deform_conv_workspace_size(
+        dtype, int64_array(X_shape), len(X_shape), int64_array(W_shape), arr(strides), arr(pads),
+        arr(dilations), int(group), int(offset_group), ctypes.byref(need)),
+        "gs_deform_conv_workspace_size")
+    return need.value

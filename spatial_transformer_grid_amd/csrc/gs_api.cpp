@@ -1,7 +1,8 @@
 // gs_api.cpp -- C ABI of libgsample: argument validation and kernel dispatch.
 //
 // Every check runs before any launch; a rejected call leaves all memory
-// untouched.  The library holds no state and allocates nothing.
+// untouched.  The library holds no state and allocates nothing: scratch
+// memory (DeformConv's channels-last copies) comes from the caller.
 #include "gsample.h"
 #include "gs_launch.hpp"
 
@@ -442,10 +443,26 @@ int gs_resize(const void *X, int x_dtype, const int64_t *x_shape, int rank, cons
     return hip_status(gs::launch_resize(p, d3, mode, x_dtype, vec_in, (hipStream_t)stream));
 }
 
-int gs_deform_conv(const void *X, int dtype, const int64_t *x_shape, int x_rank, const void *W,
-                   const int64_t *w_shape, const void *offset, const void *B, const void *mask,
-                   const int64_t *strides, const int64_t *pads, const int64_t *dilations,
-                   int group, int offset_group, void *Y, void *stream) {
+namespace {
+
+// Bytes of the channels-last workspace (a copy of X as (N, H, W, C), then W
+// as (OC, KH*KW, Cgp)); 0 when that kernel does not apply: it needs 2-D
+// fp32 / fp16 / bf16 data and conv and offset groups of a multiple of 8
+// channels.
+constexpr int64_t kWsAlign = 256;
+int64_t round_ws(int64_t b) { return (b + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+bool cl_applies(int r, int dtype, int64_t Cg, int64_t Cog) {
+    return r == 2 && dtype != GS_F64 && Cg % 8 == 0 && Cog % 8 == 0;
+}
+
+int64_t cl_w2_elems(int64_t OC, int64_t Cg, int64_t K) { return OC * K * ((Cg + 31) / 32 * 32); }
+
+// Shared validation of gs_deform_conv and gs_deform_conv_workspace_size:
+// fills p (pointers aside), the rank, and the output count.
+int deform_setup(int dtype, const int64_t *x_shape, int x_rank, const int64_t *w_shape,
+                 const int64_t *strides, const int64_t *pads, const int64_t *dilations, int group,
+                 int offset_group, gs::DeformParams &p, int &r_out, int64_t &N_out) {
     if (!x_shape || !w_shape) return GS_ERR_NULL;
     if (x_rank < 3 || x_rank > 5) return GS_ERR_SHAPE;
     if (dtype != GS_F32 && dtype != GS_F16 && dtype != GS_BF16 && dtype != GS_F64)
@@ -486,16 +503,7 @@ int gs_deform_conv(const void *X, int dtype, const int64_t *x_shape, int x_rank,
     if (C * plane * bytes > kInt32Max || OC * npos * bytes > kInt32Max ||
         OC * Cg * K * bytes > kInt32Max || N > kInt32Max)
         return GS_ERR_TOO_LARGE;
-    if (N == 0) return GS_OK;
-    if (!X || !W || !offset || !Y) return GS_ERR_NULL;
-
-    gs::DeformParams p;
-    p.X = X;
-    p.Wt = W;
-    p.offset = offset;
-    p.mask = mask;
-    p.B = B;
-    p.Y = Y;
+    p = gs::DeformParams{};
     p.N = (int)N;
     p.C = (int)C;
     p.OC = (int)OC;
@@ -534,21 +542,82 @@ int gs_deform_conv(const void *X, int dtype, const int64_t *x_shape, int x_rank,
     p.x_plane_bytes = (uint32_t)(plane * bytes);
     p.w_bytes = (uint32_t)(OC * Cg * K * bytes);
     p.npos = (uint32_t)npos;
-    const bool mfma = r == 2 && dtype != GS_F64;
-    if (mfma) {
-        const int64_t tm = OCg > 128 ? 256 : 128;
-        const int64_t m_tiles = (OCg + tm - 1) / tm, n_tiles = (npos + 63) / 64;
+    p.Cgp = (int)((Cg + 31) / 32 * 32);
+    p.K2 = (int)(K * p.Cgp);
+    p.x_img_bytes = (uint32_t)(C * plane * bytes);
+    const int64_t w2 = cl_w2_elems(OC, Cg, K) * bytes;
+    p.w2_bytes = w2 <= kInt32Max ? (uint32_t)w2 : 0;
+    r_out = r;
+    N_out = N;
+    return GS_OK;
+}
+
+int64_t cl_workspace_bytes(const gs::DeformParams &p, int r, int dtype) {
+    if (!cl_applies(r, dtype, p.Cg, p.Cog) || p.w2_bytes == 0) return 0;
+    return round_ws((int64_t)p.N * p.x_img_bytes) + round_ws(p.w2_bytes);
+}
+
+}  // namespace
+
+int gs_deform_conv_workspace_size(int dtype, const int64_t *x_shape, int x_rank,
+                                  const int64_t *w_shape, const int64_t *strides,
+                                  const int64_t *pads, const int64_t *dilations, int group,
+                                  int offset_group, int64_t *bytes) {
+    if (!bytes) return GS_ERR_NULL;
+    gs::DeformParams p;
+    int r;
+    int64_t N;
+    const int rc = deform_setup(dtype, x_shape, x_rank, w_shape, strides, pads, dilations, group,
+                                offset_group, p, r, N);
+    if (rc != GS_OK) return rc;
+    *bytes = cl_workspace_bytes(p, r, dtype);
+    return GS_OK;
+}
+
+int gs_deform_conv(const void *X, int dtype, const int64_t *x_shape, int x_rank, const void *W,
+                   const int64_t *w_shape, const void *offset, const void *B, const void *mask,
+                   const int64_t *strides, const int64_t *pads, const int64_t *dilations,
+                   int group, int offset_group, void *Y, void *workspace, int64_t workspace_bytes,
+                   void *stream) {
+    gs::DeformParams p;
+    int r;
+    int64_t N;
+    const int rc = deform_setup(dtype, x_shape, x_rank, w_shape, strides, pads, dilations, group,
+                                offset_group, p, r, N);
+    if (rc != GS_OK) return rc;
+    if (workspace_bytes < 0) return GS_ERR_ATTR;
+    if (N == 0) return GS_OK;
+    if (!X || !W || !offset || !Y) return GS_ERR_NULL;
+    p.X = X;
+    p.Wt = W;
+    p.offset = offset;
+    p.mask = mask;
+    p.B = B;
+    p.Y = Y;
+    p.w_vec = (p.Ktot * elem_bytes(dtype)) % 16 == 0 && (uintptr_t)W % 16 == 0;
+    const int64_t need = cl_workspace_bytes(p, r, dtype);
+    int path = gs::DC_PATH_DIRECT;
+    if (need > 0 && workspace && workspace_bytes >= need && (uintptr_t)workspace % kWsAlign == 0) {
+        path = gs::DC_PATH_CL;
+        p.Xt = workspace;
+        p.W2 = (char *)workspace + round_ws((int64_t)p.N * p.x_img_bytes);
+    } else if (r == 2 && dtype != GS_F64) {
+        path = gs::DC_PATH_GATHER;
+    }
+    if (path != gs::DC_PATH_DIRECT) {
+        const int64_t tm = p.OCg > 128 ? 256 : 128;
+        const int64_t m_tiles = (p.OCg + tm - 1) / tm, n_tiles = ((int64_t)p.npos + 63) / 64;
         const int64_t nblocks = N * group * m_tiles * n_tiles;
         if (nblocks > kMaxBlocks) return GS_ERR_TOO_LARGE;
         p.m_tiles = (int)m_tiles;
         p.n_tiles = (int)n_tiles;
         p.nblocks = (int)nblocks;
     } else {
-        const int64_t total = N * OC * npos;
+        const int64_t total = N * p.OC * (int64_t)p.npos;
         if ((total + kBlockThreads - 1) / kBlockThreads > kInt32Max) return GS_ERR_TOO_LARGE;
         p.m_tiles = p.n_tiles = p.nblocks = 0;
     }
-    return hip_status(gs::launch_deform_conv(p, r, dtype, mfma, (hipStream_t)stream));
+    return hip_status(gs::launch_deform_conv(p, r, dtype, path, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -36,7 +36,9 @@ constexpr int DC_TABLE = 16;  // kernel positions x offset groups the LDS table 
 // ------------------------------------------------------------ sampling
 
 // Corner element offsets (-1 = outside the image) and weights of the linear
-// sample of an H x W plane at (lh, lw), the mask folded into the weights.
+// sample of an H x W plane at (lh, lw), the mask folded into the weights; a
+// corner outside the image has weight 0 and is read through the out-of-range
+// offset (so it loads 0 and adds exactly 0).
 struct Corners {
     int off[4];
     float w[4];
@@ -62,7 +64,7 @@ __device__ __forceinline__ Corners corners_of(float lh, float lw, float m, int H
         const int h = h0 + dy, w = w0 + dx;
         const bool ok = h >= 0 && h < H && w >= 0 && w < W;
         c.off[q] = ok ? h * W + w : -1;
-        c.w[q] = (dy ? fh : 1.0f - fh) * (dx ? fw : 1.0f - fw) * m;
+        c.w[q] = ok ? (dy ? fh : 1.0f - fh) * (dx ? fw : 1.0f - fw) * m : 0.0f;
     }
     return c;
 }
@@ -74,7 +76,111 @@ __device__ __forceinline__ float ld(const void *p, size_t i) {
     else return T::from_raw(((const uint16_t *)p)[i]);
 }
 
+// Corners of the sample that kernel position `tap` of offset group g takes
+// for output position o = (oh, ow) of image n.  No offset or mask is read for
+// a position past the end of the plane or an offset group past the last one
+// (a conv group may span fewer offset groups than the widest one).
+template <typename T>
+__device__ __forceinline__ Corners sample_corners(const DeformParams &p, int n, int o, bool o_ok,
+                                                  int oh, int ow, int g, int tap) {
+    Corners none;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        none.off[q] = -1;
+        none.w[q] = 0.0f;
+    }
+    if (!o_ok || g >= p.og) return none;
+    const int npos = p.OH * p.OW, KK = p.KH * p.KW;
+    const int i = tap / p.KW, j = tap - (tap / p.KW) * p.KW;
+    const size_t oc2 = (size_t)n * p.og * KK * 2 * npos + ((size_t)(g * KK + tap) * 2) * npos + o;
+    const float dy = ld<T>(p.offset, oc2), dx = ld<T>(p.offset, oc2 + npos);
+    const float m =
+        p.mask ? ld<T>(p.mask, (size_t)n * p.og * KK * npos + (size_t)(g * KK + tap) * npos + o) : 1.0f;
+    // regular position + offset, in fp32
+    const float lh = (float)(oh * p.sh - p.pt + i * p.dh) + dy;
+    const float lw = (float)(ow * p.sw - p.pl + j * p.dw) + dx;
+    return corners_of(lh, lw, m, p.H, p.W);
+}
+
 // --------------------------------------------------------- implicit GEMM
+
+// MFMA over one K chunk held in LDS: wave `wave` owns rows
+// [wave * 32 * MB, +32 * MB) of the W tile As ([m][k], pitch LK) and all 64
+// positions of the column tile Bs ([position][k], pitch LK).
+template <typename T, int MB, int LK>
+__device__ __forceinline__ void mfma_chunk(const typename T::raw_t *As, const typename T::raw_t *Bs,
+                                           floatx16 (&acc)[MB][2], int wave, int lane) {
+    if constexpr (T::bytes == 4) {
+#pragma unroll
+        for (int ks = 0; ks < DC_TK / 2; ++ks) {
+            const int kk = 2 * ks + (lane >> 5);
+            float b[2];
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+                b[nb] = __builtin_bit_cast(float, (uint32_t)Bs[(32 * nb + (lane & 31)) * LK + kk]);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int m = (wave * MB + mb) * 32 + (lane & 31);
+                const float a = __builtin_bit_cast(float, (uint32_t)As[m * LK + kk]);
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb)
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b[nb], acc[mb][nb], 0, 0, 0);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < DC_TK / 16; ++ks) {
+            const int kk = 16 * ks + 8 * (lane >> 5);
+            u32x4 bv[2];
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+                bv[nb] = *(const u32x4 *)&Bs[(32 * nb + (lane & 31)) * LK + kk];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const int m = (wave * MB + mb) * 32 + (lane & 31);
+                const u32x4 av = *(const u32x4 *)&As[m * LK + kk];
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
+                    if constexpr (__is_same(T, BF16))
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv[nb]),
+                            acc[mb][nb], 0, 0, 0);
+                    else
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            __builtin_bit_cast(halfx8, av), __builtin_bit_cast(halfx8, bv[nb]),
+                            acc[mb][nb], 0, 0, 0);
+                }
+            }
+        }
+    }
+}
+
+// Bias and store of a block's TM x 64 tile of Y (image n, output channels
+// oc0.., positions nt * 64..): lane holds column (lane & 31) + 32 nb and rows
+// 8 (r / 4) + 4 (lane / 32) + (r % 4) of each 32 x 32 block.
+template <typename T, int MB>
+__device__ __forceinline__ void store_tile(const DeformParams &p, const floatx16 (&acc)[MB][2], int n,
+                                           int oc0, int m_valid, int nt, int wave, int lane) {
+    const int npos = p.OH * p.OW;
+    const rsrc_t yr = make_rsrc((char *)p.Y + (size_t)n * p.OC * npos * T::bytes,
+                                (uint32_t)((size_t)p.OC * npos * T::bytes));
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int m = (wave * MB + mb) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            const bool mok = m < m_valid;
+            const float bias = (mok && p.B) ? ld<T>(p.B, oc0 + m) : 0.0f;
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+                const int oo = nt * DC_TN + 32 * nb + (lane & 31);
+                const bool ok = mok && oo < npos;
+                const uint32_t yo =
+                    ok ? (uint32_t)(((size_t)(oc0 + m) * npos + oo) * T::bytes) : GS_OOB;
+                T::store(acc[mb][nb][r] + bias, yr, yo);
+            }
+        }
+}
 
 // MB: 32-row blocks of output channels per wave (TM = 4 waves * 32 * MB).
 template <typename T, int MB, bool TABLE>
@@ -109,27 +215,8 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_mfma(DeformParams p) {
     const bool o_ok = o < npos;
     const int oh = o_ok ? o / p.OW : 0, ow = o_ok ? o - (o / p.OW) * p.OW : 0;
 
-    const size_t off_img = (size_t)n * p.og * KK * 2 * npos;   // offset of image n
-    const size_t msk_img = (size_t)n * p.og * KK * npos;       // mask of image n
-    // no offset or mask is read for a position past the end of the plane or
-    // an offset group past the last one (a conv group may span fewer groups
-    // than the widest one the table is sized for)
     auto sample_of = [&](int g, int tap) -> Corners {
-        Corners none;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            none.off[q] = -1;
-            none.w[q] = 0.0f;
-        }
-        if (!o_ok || g >= p.og) return none;
-        const int i = tap / p.KW, j = tap - (tap / p.KW) * p.KW;
-        const size_t oc2 = off_img + ((size_t)(g * KK + tap) * 2) * npos + o;
-        const float dy = ld<T>(p.offset, oc2), dx = ld<T>(p.offset, oc2 + npos);
-        const float m = p.mask ? ld<T>(p.mask, msk_img + (size_t)(g * KK + tap) * npos + o) : 1.0f;
-        // regular position + offset, in fp32
-        const float lh = (float)(oh * p.sh - p.pt + i * p.dh) + dy;
-        const float lw = (float)(ow * p.sw - p.pl + j * p.dw) + dx;
-        return corners_of(lh, lw, m, p.H, p.W);
+        return sample_corners<T>(p, n, o, o_ok, oh, ow, g, tap);
     };
 
     if constexpr (TABLE) {
@@ -164,114 +251,350 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_mfma(DeformParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
 
-    for (int k0 = 0; k0 < p.Ktot; k0 += DC_TK) {
-        __syncthreads();  // the previous chunk's LDS reads (and the table) are done
-        // ---- W tile: TM x 32
-        for (int e = t; e < TM * DC_TK; e += kBlock) {
-            const int m = e / DC_TK, kk = e - m * DC_TK;
-            const int k = k0 + kk;
-            const bool ok = m < m_valid && k < p.Ktot;
-            const uint32_t wo = ok ? (uint32_t)(((size_t)(oc0 + m) * p.Ktot + k) * T::bytes) : GS_OOB;
-            As[m * LK + kk] = T::load_raw(wr, wo);
-        }
-        // ---- column tile: 32 x 64, this thread's position, 8 of the K slots
+    // Software pipeline: the next chunk's W tile (16-byte loads when the rows
+    // allow) and column gathers are in flight while the current chunk runs on
+    // the matrix cores.  Items past K or past the block's rows load through
+    // the out-of-range offset (zeros), so the loads carry no branch.
+    constexpr int CPR = DC_TK * T::bytes / 16;      // 16-byte parts per W row
+    constexpr int WV = TM * CPR / kBlock;           // vector W parts per thread
+    constexpr int NS = DC_TK / (kBlock / DC_TN);    // column slots per thread
+    const bool wvec = p.w_vec != 0;
+    u32x4 wpre[WV];
+    float xpre[NS][4];
+    float cw[NS][4];  // corner weights of the non-table path
+    auto prefetch = [&](int k0) {
+        if (wvec) {
 #pragma unroll
-        for (int s = 0; s < DC_TK / (kBlock / DC_TN); ++s) {
-            const int kk = (t >> 6) + (kBlock / DC_TN) * s;
-            const int k = k0 + kk;
-            float v = 0.0f;
-            if (k < p.Ktot) {
-                const int cl = k / KK, tap = k - (k / KK) * KK;
-                const int c = G * p.Cg + cl;
-                const int g = c / p.Cog;
-                Corners cr;
-                if constexpr (TABLE) {
-                    const int e = ((g - g_first) * KK + tap) * DC_TN + pos;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        cr.off[q] = tb_off[q * TE + e];
-                        cr.w[q] = tb_w[q * TE + e];
-                    }
-                } else {
-                    cr = sample_of(g, tap);
-                }
-                const uint32_t pb = (uint32_t)c * p.x_plane_bytes;
-                float x[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    x[q] = T::load(xr, cr.off[q] >= 0 ? pb + (uint32_t)cr.off[q] * T::bytes : GS_OOB);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) v = cr.off[q] >= 0 ? fmaf(cr.w[q], x[q], v) : v;
+            for (int j = 0; j < WV; ++j) {
+                const int i = t + j * kBlock;
+                const int row = i / CPR, part = i - (i / CPR) * CPR;
+                const int k = k0 + part * (16 / T::bytes);
+                const bool ok = row < m_valid && k < p.Ktot;
+                const uint32_t wo =
+                    ok ? (uint32_t)(((size_t)(oc0 + row) * p.Ktot + k) * T::bytes) : GS_OOB;
+                wpre[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)wo, 0, 0);
             }
+        }
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int k = k0 + (t >> 6) + (kBlock / DC_TN) * s;
+            const bool kin = k < p.Ktot;
+            const int kc = kin ? k : 0;
+            const int cl = kc / KK, tap = kc - (kc / KK) * KK;
+            const int c = G * p.Cg + cl;
+            const int g = c / p.Cog;
+            int off[4];
+            if constexpr (TABLE) {
+                const int e = ((g - g_first) * KK + tap) * DC_TN + pos;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) off[q] = tb_off[q * TE + e];
+            } else {
+                const Corners cr = sample_of(g, tap);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    off[q] = cr.off[q];
+                    cw[s][q] = cr.w[q];
+                }
+            }
+            const uint32_t pb = (uint32_t)c * p.x_plane_bytes;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                xpre[s][q] = T::load(xr, (kin && off[q] >= 0) ? pb + (uint32_t)off[q] * T::bytes
+                                                              : GS_OOB);
+        }
+    };
+
+    if constexpr (TABLE) __syncthreads();  // the table is complete before the first gathers
+    prefetch(0);
+    for (int k0 = 0; k0 < p.Ktot; k0 += DC_TK) {
+        __syncthreads();  // the previous chunk's LDS reads are done
+        // ---- W tile: TM x 32 into LDS
+        if (wvec) {
+#pragma unroll
+            for (int j = 0; j < WV; ++j) {
+                const int i = t + j * kBlock;
+                const int row = i / CPR, part = i - (i / CPR) * CPR;
+                *(u32x4 *)&As[row * LK + part * (16 / T::bytes)] = wpre[j];
+            }
+        } else {
+            for (int e = t; e < TM * DC_TK; e += kBlock) {
+                const int m = e / DC_TK, kk = e - m * DC_TK;
+                const int k = k0 + kk;
+                const bool ok = m < m_valid && k < p.Ktot;
+                const uint32_t wo =
+                    ok ? (uint32_t)(((size_t)(oc0 + m) * p.Ktot + k) * T::bytes) : GS_OOB;
+                As[m * LK + kk] = T::load_raw(wr, wo);
+            }
+        }
+        // ---- column tile: 32 x 64, this thread's position, NS of the K slots
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int kk = (t >> 6) + (kBlock / DC_TN) * s;
+            float w4[4];
+            if constexpr (TABLE) {
+                const int k = k0 + kk;
+                const int kc = k < p.Ktot ? k : 0;
+                const int cl = kc / KK, tap = kc - (kc / KK) * KK;
+                const int g = (G * p.Cg + cl) / p.Cog;
+                const int e = ((g - g_first) * KK + tap) * DC_TN + pos;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) w4[q] = tb_w[q * TE + e];
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) w4[q] = cw[s][q];
+            }
+            float v = w4[0] * xpre[s][0];
+#pragma unroll
+            for (int q = 1; q < 4; ++q) v = fmaf(w4[q], xpre[s][q], v);
             Bs[pos * LK + kk] = to_raw<T>(v);
         }
         __syncthreads();
-        // ---- MFMA: wave `wave` owns rows [wave * 32 * MB, +32 * MB), all 64 positions
-        if constexpr (T::bytes == 4) {
+        prefetch(k0 + DC_TK);
+        mfma_chunk<T, MB, LK>(As, Bs, acc, wave, lane);
+    }
+    store_tile<T, MB>(p, acc, n, oc0, m_valid, nt, wave, lane);
+}
+
+// ------------------------------------------- channels-last implicit GEMM
+//
+// When every conv group and offset group holds a multiple of 8 channels, the
+// sampled columns come from a channels-last copy of X, (N, H, W, C): the 8
+// consecutive channels a thread samples at one corner are one 16-byte load
+// (two for fp32), instead of 8 scalar gathers from 8 planes.  K is walked
+// kernel position first: chunk i covers kernel position i / (Cgp / 32) and
+// 32 channels of the conv group, Cgp = Cg rounded up to 32, so one set of
+// corners serves the whole chunk.  W is copied to match, (OC, kernel
+// positions, Cgp), zero beyond Cg.  Summing K in another order than the
+// oracle only changes fp32 rounding order.
+
+// X (N, C, S) -> Xt (N, S, C), S = H * W: 64 x 64 tiles through LDS.
+template <typename raw_t>
+__global__ __launch_bounds__(kBlock) void to_channels_last(const raw_t *__restrict__ X,
+                                                          raw_t *__restrict__ Xt, int C, int S,
+                                                          int c_tiles, int s_tiles) {
+    __shared__ raw_t tile[64][65];
+    const int b = blockIdx.x;
+    const int st = b % s_tiles;
+    const int ct = (b / s_tiles) % c_tiles;
+    const int n = b / (s_tiles * c_tiles);
+    const int t = threadIdx.x, col = t & 63, r4 = t >> 6;
+    const raw_t *src = X + (size_t)n * C * S;
 #pragma unroll
-            for (int ks = 0; ks < DC_TK / 2; ++ks) {
-                const int kk = 2 * ks + (lane >> 5);
-                float b[2];
+    for (int i = 0; i < 16; ++i) {
+        const int c = ct * 64 + r4 + 4 * i, sp = st * 64 + col;
+        tile[r4 + 4 * i][col] = (c < C && sp < S) ? src[(size_t)c * S + sp] : (raw_t)0;
+    }
+    __syncthreads();
+    raw_t *dst = Xt + (size_t)n * S * C;
 #pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-                    b[nb] = __builtin_bit_cast(float, (uint32_t)Bs[(32 * nb + (lane & 31)) * LK + kk]);
+    for (int i = 0; i < 16; ++i) {
+        const int sp = st * 64 + r4 + 4 * i, c = ct * 64 + col;
+        if (sp < S && c < C) dst[(size_t)sp * C + c] = tile[col][r4 + 4 * i];
+    }
+}
+
+// W (OC, Cg, KK) -> W2 (OC, KK, Cgp), zero for channels Cg .. Cgp-1.
+template <typename raw_t>
+__global__ __launch_bounds__(kBlock) void w_tap_major(const raw_t *__restrict__ W,
+                                                     raw_t *__restrict__ W2, int OC, int Cg, int KK,
+                                                     int Cgp) {
+    const size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x;
+    if (i >= (size_t)OC * KK * Cgp) return;
+    const int cl = (int)(i % Cgp);
+    const size_t rest = i / Cgp;
+    const int tap = (int)(rest % KK);
+    const size_t oc = rest / KK;
+    W2[i] = cl < Cg ? W[(oc * Cg + cl) * KK + tap] : (raw_t)0;
+}
+
+// Eight elements of type T from 8 * T::bytes consecutive bytes, widened.
+template <typename T>
+__device__ __forceinline__ void unpack8(const u32x4 *v, float (&x)[8]) {
+    if constexpr (T::bytes == 4) {
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb) {
-                    const int m = (wave * MB + mb) * 32 + (lane & 31);
-                    const float a = __builtin_bit_cast(float, (uint32_t)As[m * LK + kk]);
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int nb = 0; nb < 2; ++nb)
-                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b[nb], acc[mb][nb], 0, 0, 0);
-                }
+            for (int e = 0; e < 4; ++e) {
+                // through a scalar: a bit cast of the vector element itself
+                // reads element 0 with this compiler
+                const uint32_t u = v[h][e];
+                x[4 * h + e] = __builtin_bit_cast(float, u);
             }
-        } else {
+    } else {
 #pragma unroll
-            for (int ks = 0; ks < DC_TK / 16; ++ks) {
-                const int kk = 16 * ks + 8 * (lane >> 5);
-                u32x4 bv[2];
-#pragma unroll
-                for (int nb = 0; nb < 2; ++nb)
-                    bv[nb] = *(const u32x4 *)&Bs[(32 * nb + (lane & 31)) * LK + kk];
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb) {
-                    const int m = (wave * MB + mb) * 32 + (lane & 31);
-                    const u32x4 av = *(const u32x4 *)&As[m * LK + kk];
-#pragma unroll
-                    for (int nb = 0; nb < 2; ++nb) {
-                        if constexpr (__is_same(T, BF16))
-                            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                __builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bv[nb]),
-                                acc[mb][nb], 0, 0, 0);
-                        else
-                            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                                __builtin_bit_cast(halfx8, av), __builtin_bit_cast(halfx8, bv[nb]),
-                                acc[mb][nb], 0, 0, 0);
-                    }
-                }
-            }
+        for (int e = 0; e < 4; ++e) {
+            x[2 * e] = T::from_raw((uint16_t)(v[0][e] & 0xffffu));
+            x[2 * e + 1] = T::from_raw((uint16_t)(v[0][e] >> 16));
         }
     }
+}
 
-    // ---- epilogue: lane holds column (lane & 31) + 32 nb and rows
-    // 8 (r / 4) + 4 (lane / 32) + (r % 4) of each 32 x 32 block
-    const rsrc_t yr = make_rsrc((char *)p.Y + (size_t)n * p.OC * npos * T::bytes,
-                                (uint32_t)((size_t)p.OC * npos * T::bytes));
+template <typename T>
+__device__ __forceinline__ void pack8(const float (&x)[8], u32x4 *v) {
+    if constexpr (T::bytes == 4) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[h][e] = __builtin_bit_cast(uint32_t, x[4 * h + e]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            v[0][e] = (uint32_t)to_raw<T>(x[2 * e]) | ((uint32_t)to_raw<T>(x[2 * e + 1]) << 16);
+    }
+}
+
+template <typename T, int MB, bool TABLE>
+__global__ __launch_bounds__(kBlock) void deform_conv2d_cl(DeformParams p) {
+    using raw_t = typename T::raw_t;
+    constexpr int TM = 4 * 32 * MB;
+    constexpr int PAD = 16 / T::bytes;
+    constexpr int LK = DC_TK + PAD;
+    constexpr int TE = DC_TABLE * DC_TN;
+    constexpr int VPC = 8 * T::bytes / 16;          // 16-byte loads per corner
+    __shared__ __align__(16) raw_t As[TM * LK];
+    __shared__ __align__(16) raw_t Bs[DC_TN * LK];
+    __shared__ int tb_off[TABLE ? 4 * TE : 1];
+    __shared__ float tb_w[TABLE ? 4 * TE : 1];
+
+    const int lb = xcd_logical_block_runs(p.nblocks);
+    if (lb >= p.nblocks) return;
+    const int nt = lb % p.n_tiles;
+    int rest = lb / p.n_tiles;
+    const int mt = rest % p.m_tiles;
+    rest /= p.m_tiles;
+    const int G = rest % p.group;
+    const int n = rest / p.group;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int npos = p.OH * p.OW;
+    const int KK = p.KH * p.KW;
+    const int g_first = (G * p.Cg) / p.Cog;
+
+    const int pos = lane;                           // this thread's output position
+    const int o = nt * DC_TN + pos;
+    const bool o_ok = o < npos;
+    const int oh = o_ok ? o / p.OW : 0, ow = o_ok ? o - (o / p.OW) * p.OW : 0;
+
+    if constexpr (TABLE) {
+        const int entries = p.og_span * KK * DC_TN;
+        for (int e = t; e < entries; e += kBlock) {
+            const int gt = e / DC_TN;
+            const int gi = gt / KK, tap = gt - gi * KK;
+            const Corners c = sample_corners<T>(p, n, o, o_ok, oh, ow, g_first + gi, tap);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                tb_off[q * TE + e] = c.off[q];
+                tb_w[q * TE + e] = c.w[q];
+            }
+        }
+        __syncthreads();
+    }
+
+    // channels-last X of image n; pixel s, channel c at (s * C + c) * bytes
+    const rsrc_t xr = make_rsrc((const char *)p.Xt + (size_t)n * p.x_img_bytes, p.x_img_bytes);
+    const int oc0 = G * p.OCg + mt * TM;
+    const int m_valid = min(TM, p.OCg - mt * TM);
+    const rsrc_t wr = make_rsrc(p.W2, p.w2_bytes);
+
+    floatx16 acc[MB][2];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int m = (wave * MB + mb) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            const bool mok = m < m_valid;
-            const float bias = (mok && p.B) ? ld<T>(p.B, oc0 + m) : 0.0f;
+        for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-                const int oo = nt * DC_TN + 32 * nb + (lane & 31);
-                const bool ok = mok && oo < npos;
-                const uint32_t yo =
-                    ok ? (uint32_t)(((size_t)(oc0 + m) * npos + oo) * T::bytes) : GS_OOB;
-                T::store(acc[mb][nb][r] + bias, yr, yo);
+            for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
+
+    const int cpt = p.Cgp / DC_TK;                  // chunks per kernel position
+    const int nch = KK * cpt;
+    constexpr int CPR = DC_TK * T::bytes / 16;      // 16-byte parts per W row
+    constexpr int WV = TM * CPR / kBlock;
+    u32x4 wpre[WV];
+    u32x4 xpre[4][VPC];
+    float wq[4];
+    Corners cc;                                     // corners of (ctap, cg), non-table path
+    int ctap = -1, cg = -1;
+    // Issue chunk i's loads: the W tile rows, and the four corners of this
+    // thread's position for channels c0 + 8 * wave .. +7.
+    auto prefetch = [&](int i) {
+        const int tap = i / cpt;
+        const int c0 = (i - tap * cpt) * DC_TK;
+#pragma unroll
+        for (int j = 0; j < WV; ++j) {
+            const int e = t + j * kBlock;
+            const int row = e / CPR, part = e - (e / CPR) * CPR;
+            const uint32_t wo =
+                row < m_valid
+                    ? (uint32_t)(((size_t)(oc0 + row) * p.K2 + (size_t)i * DC_TK + part * (16 / T::bytes)) *
+                                 T::bytes)
+                    : GS_OOB;
+            wpre[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)wo, 0, 0);
+        }
+        const int cl = c0 + 8 * wave;
+        const bool cv = cl < p.Cg;                  // past Cg: padding, W2 is zero there
+        const int c = G * p.Cg + (cv ? cl : 0);
+        const int g = c / p.Cog;
+        int off[4];
+        if constexpr (TABLE) {
+            const int e = ((g - g_first) * KK + tap) * DC_TN + pos;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                off[q] = tb_off[q * TE + e];
+                wq[q] = tb_w[q * TE + e];
+            }
+        } else {
+            if (tap != ctap || g != cg) {           // uniform across the wave
+                cc = sample_corners<T>(p, n, o, o_ok, oh, ow, g, tap);
+                ctap = tap;
+                cg = g;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                off[q] = cc.off[q];
+                wq[q] = cc.w[q];
             }
         }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t xo =
+                (cv && off[q] >= 0) ? ((uint32_t)off[q] * (uint32_t)p.C + (uint32_t)c) * T::bytes : GS_OOB;
+#pragma unroll
+            for (int v = 0; v < VPC; ++v)
+                xpre[q][v] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(xo + 16 * v), 0, 0);
+        }
+    };
+
+    prefetch(0);
+    for (int i = 0; i < nch; ++i) {
+        __syncthreads();  // the previous chunk's LDS reads are done
+#pragma unroll
+        for (int j = 0; j < WV; ++j) {
+            const int e = t + j * kBlock;
+            const int row = e / CPR, part = e - (e / CPR) * CPR;
+            *(u32x4 *)&As[row * LK + part * (16 / T::bytes)] = wpre[j];
+        }
+        {
+            float v[8], x[8];
+            unpack8<T>(xpre[0], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = wq[0] * x[e];
+#pragma unroll
+            for (int q = 1; q < 4; ++q) {
+                unpack8<T>(xpre[q], x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = fmaf(wq[q], x[e], v[e]);
+            }
+            u32x4 packed[VPC];
+            pack8<T>(v, packed);
+#pragma unroll
+            for (int h = 0; h < VPC; ++h)
+                *(u32x4 *)&Bs[pos * LK + 8 * wave + h * (16 / T::bytes)] = packed[h];
+        }
+        __syncthreads();
+        if (i + 1 < nch) prefetch(i + 1);
+        mfma_chunk<T, MB, LK>(As, Bs, acc, wave, lane);
+    }
+    store_tile<T, MB>(p, acc, n, oc0, m_valid, nt, wave, lane);
 }
 
 // ----------------------------------------------------------- direct kernel
@@ -414,6 +737,28 @@ static int mfma_launch(const DeformParams &p, hipStream_t s) {
     return (int)hipGetLastError();
 }
 
+template <typename T>
+static int cl_launch(const DeformParams &p, hipStream_t s) {
+    using raw_t = typename T::raw_t;
+    const int S = p.H * p.W, KK = p.KH * p.KW;
+    const int c_tiles = (p.C + 63) / 64, s_tiles = (S + 63) / 64;
+    hipLaunchKernelGGL((to_channels_last<raw_t>), dim3((unsigned)((size_t)p.N * c_tiles * s_tiles)),
+                       dim3(kBlock), 0, s, (const raw_t *)p.X, (raw_t *)p.Xt, p.C, S, c_tiles, s_tiles);
+    const size_t w2 = (size_t)p.OC * KK * p.Cgp;
+    hipLaunchKernelGGL((w_tap_major<raw_t>), dim3((unsigned)((w2 + kBlock - 1) / kBlock)), dim3(kBlock), 0,
+                       s, (const raw_t *)p.Wt, (raw_t *)p.W2, p.OC, p.Cg, KK, p.Cgp);
+    const dim3 grid(8 * kRun * ((p.nblocks + 8 * kRun - 1) / (8 * kRun)));
+    const bool table = p.og_span * KK <= DC_TABLE;
+    if (p.OCg > 128) {
+        if (table) hipLaunchKernelGGL((deform_conv2d_cl<T, 2, true>), grid, dim3(kBlock), 0, s, p);
+        else hipLaunchKernelGGL((deform_conv2d_cl<T, 2, false>), grid, dim3(kBlock), 0, s, p);
+    } else {
+        if (table) hipLaunchKernelGGL((deform_conv2d_cl<T, 1, true>), grid, dim3(kBlock), 0, s, p);
+        else hipLaunchKernelGGL((deform_conv2d_cl<T, 1, false>), grid, dim3(kBlock), 0, s, p);
+    }
+    return (int)hipGetLastError();
+}
+
 template <int R, typename T>
 static int direct_launch(const DeformParams &p, hipStream_t s) {
     const size_t total = (size_t)p.N * p.OC * p.npos;
@@ -431,8 +776,15 @@ static int direct_by_rank(const DeformParams &p, int rank, hipStream_t s) {
     }
 }
 
-int launch_deform_conv(const DeformParams &p, int rank, int dtype, bool mfma, hipStream_t s) {
-    if (mfma) {
+int launch_deform_conv(const DeformParams &p, int rank, int dtype, int path, hipStream_t s) {
+    if (path == DC_PATH_CL) {
+        switch (dtype) {
+        case 0: return cl_launch<F32>(p, s);
+        case 1: return cl_launch<F16>(p, s);
+        default: return cl_launch<BF16>(p, s);
+        }
+    }
+    if (path == DC_PATH_GATHER) {
         switch (dtype) {
         case 0: return mfma_launch<F32>(p, s);
         case 1: return mfma_launch<F16>(p, s);

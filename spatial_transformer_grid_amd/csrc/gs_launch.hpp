@@ -176,7 +176,18 @@ struct DeformParams {
     uint32_t x_plane_bytes;                  // one input plane; C planes < 2^31 bytes
     uint32_t w_bytes;                        // all of W (< 2^31)
     uint32_t npos;                           // output positions per plane
+    int w_vec;                               // W rows allow 16-byte loads
+    // channels-last path: workspace copies of X (N, H, W, C) and of W
+    // (OC, KH*KW, Cgp), Cgp = Cg rounded up to 32, K2 = KH*KW*Cgp
+    void *Xt, *W2;
+    int Cgp, K2;
+    uint32_t x_img_bytes;                    // one image of Xt (< 2^31)
+    uint32_t w2_bytes;                       // all of W2 (< 2^31)
 };
+
+// DeformConv kernels: direct (one lane per output, double sums), implicit
+// GEMM gathering from X's planes, implicit GEMM on a channels-last copy.
+enum { DC_PATH_DIRECT = 0, DC_PATH_GATHER = 1, DC_PATH_CL = 2 };
 
 // Launchers (gs_kernels.hip, gs_resize.hip, gs_nd.hip, gs_deform.hip).  Return 0 on success or the hipError_t of the
 // launch.  `rank` is 2 or 3; `dtype` 0 f32, 1 f16, 2 bf16; `vec_in` selects
@@ -190,7 +201,7 @@ int launch_grid_sample_nd(const NdParams &p, int rank, int mode, bool double_gri
                           hipStream_t stream);
 // `mfma`: the 2-D matrix-core kernel (dtype 0 f32, 1 f16, 2 bf16); else the
 // direct kernel (rank 1..3, dtype 0..3 with 3 = f64).
-int launch_deform_conv(const DeformParams &p, int rank, int dtype, bool mfma, hipStream_t stream);
+int launch_deform_conv(const DeformParams &p, int rank, int dtype, int path, hipStream_t stream);
 // `d3`: the third axis from the end is resized; `mode` 0 nearest, 1 linear,
 // 2 cubic.
 int launch_resize(const ResizeParams &p, bool d3, int mode, int dtype, bool vec_in,

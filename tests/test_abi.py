@@ -35,7 +35,7 @@ def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "gs_abi_version", "gs_status_string", "gs_affine_grid", "gs_grid_sample_2d",
         "gs_grid_sample_3d", "gs_affine_grid_sample_fused", "gs_resize", "gs_resize_output_shape",
-        "gs_grid_sample", "gs_deform_conv"])
+        "gs_grid_sample", "gs_deform_conv", "gs_deform_conv_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol(gs):
@@ -272,7 +272,7 @@ def test_deform_conv_rejects(gs):
         a = lambda v: gs.int64_array(v) if v is not None else None
         return lib.gs_deform_conv(X, dt, gs.int64_array(xs), len(xs) if rank is None else rank, W,
                                   gs.int64_array(ws), off, None, None, a(st), a(pd), a(dl), grp,
-                                  og, Y, None)
+                                  og, Y, None, 0, None)
 
     assert f([1, 4, 8, 8], [6, 4, 3, 3], dt=5) == 3              # integer data
     assert f([1, 4, 8, 8], [6, 4, 3, 3], rank=6) == 2
@@ -287,3 +287,28 @@ def test_deform_conv_rejects(gs):
     assert f([1, 4, 8, 8], [6, 4, 3, 3], off=None) == 1
     assert f([0, 4, 8, 8], [6, 4, 3, 3], X=None, W=None, off=None, Y=None) == 0
     assert f([1, 4, 1 << 24, 2], [6, 4, 3, 1]) == 5
+    assert lib.gs_deform_conv(FAKE, 0, gs.int64_array([1, 4, 8, 8]), 4, FAKE,
+                              gs.int64_array([6, 4, 3, 3]), FAKE, None, None, None, None, None, 1,
+                              1, FAKE, None, -1, None) == 4         # negative workspace size
+
+
+def test_deform_conv_workspace_size(gs):
+    """Channels-last copies of X and of W (kernel-position major, channels
+    rounded up to 32), each rounded up to 256 bytes; none when the conv or
+    offset groups are not multiples of 8 channels, for double or for 1-D and
+    3-D data."""
+    ws = gs.deform_conv_workspace_size
+    up = lambda b: (b + 255) // 256 * 256
+    # 2 x 64 x 10 x 12 bf16, W 48 x 64 x 3 x 3: X 2*64*120*2 bytes, W 48*9*64*2
+    assert ws([2, 64, 10, 12], [48, 64, 3, 3], gs.GS_BF16, pads=[1, 1, 1, 1]) == \
+        up(2 * 64 * 120 * 2) + up(48 * 9 * 64 * 2)
+    # fp32, 40 channels per group, 2 groups: W's channels padded to 64
+    assert ws([1, 80, 7, 7], [16, 40, 3, 3], gs.GS_F32, group=2, offset_group=2) == \
+        up(80 * 49 * 4) + up(16 * 9 * 64 * 4)
+    assert ws([1, 12, 7, 7], [16, 12, 3, 3], gs.GS_F32) == 0                    # 12 channels
+    assert ws([1, 16, 7, 7], [16, 16, 3, 3], gs.GS_F32, offset_group=4) == 0    # 4 per offset group
+    assert ws([1, 16, 7, 7], [16, 16, 3, 3], gs.GS_F64) == 0
+    assert ws([1, 16, 7], [16, 16, 3], gs.GS_F32) == 0
+    assert ws([1, 16, 7, 7, 7], [16, 16, 3, 3, 3], gs.GS_F32) == 0
+    with pytest.raises(gs.GSError):
+        ws([1, 16, 2, 7], [16, 16, 3, 3], gs.GS_F32)                          # input too small

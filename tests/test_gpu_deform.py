@@ -11,6 +11,12 @@
   fp32 2e-5 * S; fp16 2e-3 * S and bf16 1e-2 * S (the sampled values are
   rounded to the data type before the product) plus one unit in the last
   place of the output type.
+* 2-D cases whose conv and offset groups hold multiples of 8 channels run on
+  the channels-last copy of X by default: channel counts that fill whole
+  32-channel chunks and ones padded up to the next chunk, offset groups that
+  change within a kernel position's chunks, kernels too large for the
+  sampling table; the same cases with an empty workspace take the gather
+  kernel instead.
 * double data and 1-D / 3-D data (the direct kernel, summing in double in the
   oracle's order): bit for bit after the output conversion.
 """
@@ -69,12 +75,14 @@ def rounded(ref, kind):
 
 
 def run(gsa, X, Wt, off, B, mask, kind, st=None, pd=None, dl=None, grp=1, og=1, exact=False,
-        what=""):
+        what="", no_workspace=False):
     torch = torch_mod()
-    note("deform %s %s X=%s W=%s st=%s pd=%s dl=%s group=%d og=%d mask=%s bias=%s" % (
-        what, kind, X.shape, Wt.shape, st, pd, dl, grp, og, mask is not None, B is not None))
+    note("deform %s %s X=%s W=%s st=%s pd=%s dl=%s group=%d og=%d mask=%s bias=%s ws=%s" % (
+        what, kind, X.shape, Wt.shape, st, pd, dl, grp, og, mask is not None, B is not None,
+        not no_workspace))
     (Xd, Xo), (Wd, Wo), (Od, Oo), (Bd, Bo), (Md, Mo) = (to_dev(a, kind) for a in (X, Wt, off, B, mask))
-    Y = gsa.deform_conv(Xd, Wd, Od, Bd, Md, st, pd, dl, grp, og)
+    ws = torch.empty(0, dtype=torch.uint8, device="cuda") if no_workspace else None
+    Y = gsa.deform_conv(Xd, Wd, Od, Bd, Md, st, pd, dl, grp, og, workspace=ws)
     torch.cuda.synchronize()
     got = Y.double().cpu().numpy()
     ref = oracle.deform_conv(Xo, Wo, Oo, Bo, Mo, st, pd, dl, grp, og)
@@ -170,3 +178,49 @@ def test_1d_3d_direct_exact(gsa, kind, rank):
     if kind != "f64":
         X, Wt, off, M, B = (a.astype(np.float32) for a in (X, Wt, off, M, B))
     run(gsa, X, Wt, off, B, M, kind, st, pd, dl, grp, og, exact=True, what="%d-D direct" % rank)
+
+
+CASES_CL = [
+    # n, c, h, w, oc, kh, kw, strides, pads, dilations, group, offset_group
+    (2, 64, 9, 70, 33, 3, 3, (1, 1), (0, 1, 0, 1), (1, 1), 1, 1),          # 2 chunks/tap, ragged tile
+    (1, 40, 14, 15, 70, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 1, 5),         # Cg padded, og varies
+    (2, 32, 10, 11, 300, 3, 3, (2, 2), (1, 1, 1, 1), (1, 1), 2, 2),        # groups, 256-row tiles
+    (1, 16, 18, 19, 24, 7, 7, (1, 1), (3, 3, 3, 3), (1, 1), 1, 1),         # 49 taps: no table
+    (1, 24, 8, 9, 9, 1, 1, (1, 1), (0, 0, 0, 0), (1, 1), 3, 3),            # 8 of 32 channels used
+    (1, 48, 12, 13, 130, 3, 2, (1, 2), (2, 0, 1, 1), (2, 1), 2, 6),        # og span 3 per group
+    (2, 32, 10, 10, 40, 2, 2, (1, 1), (1, 0, 0, 1), (1, 1), 1, 2),         # og changes inside a chunk
+]
+
+
+@pytest.mark.parametrize("kind,ci,ws", list(itertools.product(
+    ["f32", "f16", "bf16"], range(len(CASES_CL)), [True, False])))
+def test_2d_channels_last(gsa, kind, ci, ws):
+    n, c, h, w, oc, kh, kw, st, pd, dl, grp, og = CASES_CL[ci]
+    assert gsa.deform_conv_workspace_size(
+        (n, c, h, w), (oc, c // grp, kh, kw), {"f32": 0, "f16": 1, "bf16": 2}[kind], list(st),
+        list(pd), list(dl), grp, og) > 0
+    X, Wt, off, B, M = case(400 + ci, n, c, h, w, oc, kh, kw, st, pd, dl, grp, og, True, True)
+    run(gsa, X, Wt, off, B, M, kind, list(st), list(pd), list(dl), grp, og,
+        what="2-D channels-last case %d" % ci, no_workspace=not ws)
+
+
+def test_channels_last_non_finite_x(gsa):
+    """An infinite X value outside every sample's support leaves the outputs
+    finite (corners outside the image, or of zero weight from outside, read
+    no X); one inside the support of a sample makes it non-finite as in the
+    oracle."""
+    torch = torch_mod()
+    n, c, h, w, oc = 1, 8, 6, 7, 4
+    X = np.zeros((n, c, h, w), np.float32)
+    X[0, 3, 5, 6] = np.inf
+    Wt = np.ones((oc, c, 1, 1), np.float32)
+    off = np.zeros((n, 2, h, w), np.float32)
+    off[0, :, 0, 0] = 100.0                 # far outside: reads nothing
+    off[0, 0, 2, 2] = 0.5                   # between rows 2 and 3: finite
+    Y = gsa.deform_conv(torch.from_numpy(X).cuda(), torch.from_numpy(Wt).cuda(),
+                        torch.from_numpy(off).cuda())
+    got = Y.cpu().numpy()
+    ref = oracle.deform_conv(X, Wt, off)
+    assert np.array_equal(np.isfinite(got), np.isfinite(ref))
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
