@@ -446,8 +446,8 @@ int gs_resize(const void *X, int x_dtype, const int64_t *x_shape, int rank, cons
 namespace {
 
 // Bytes of the channels-last workspace (a copy of X as (N, H, W, C), then W
-// as (OC, KH*KW, Cgp)); 0 when that kernel does not apply: it needs 2-D
-// fp32 / fp16 / bf16 data and conv and offset groups of a multiple of 8
+// packed for the matrix cores); 0 when that kernel does not apply: it needs
+// 2-D fp32 / fp16 / bf16 data and conv and offset groups of a multiple of 8
 // channels.
 constexpr int64_t kWsAlign = 256;
 int64_t round_ws(int64_t b) { return (b + kWsAlign - 1) / kWsAlign * kWsAlign; }
@@ -456,7 +456,10 @@ bool cl_applies(int r, int dtype, int64_t Cg, int64_t Cog) {
     return r == 2 && dtype != GS_F64 && Cg % 8 == 0 && Cog % 8 == 0;
 }
 
-int64_t cl_w2_elems(int64_t OC, int64_t Cg, int64_t K) { return OC * K * ((Cg + 31) / 32 * 32); }
+// W packed per conv group: output channels rounded up to 32, channels to 32
+int64_t cl_w2_elems(int64_t group, int64_t OCg, int64_t Cg, int64_t K) {
+    return group * ((OCg + 31) / 32 * 32) * K * ((Cg + 31) / 32 * 32);
+}
 
 // Shared validation of gs_deform_conv and gs_deform_conv_workspace_size:
 // fills p (pointers aside), the rank, and the output count.
@@ -545,8 +548,10 @@ int deform_setup(int dtype, const int64_t *x_shape, int x_rank, const int64_t *w
     p.Cgp = (int)((Cg + 31) / 32 * 32);
     p.K2 = (int)(K * p.Cgp);
     p.x_img_bytes = (uint32_t)(C * plane * bytes);
-    const int64_t w2 = cl_w2_elems(OC, Cg, K) * bytes;
+    p.Rg = (int)((OCg + 31) / 32);
+    const int64_t w2 = cl_w2_elems(group, OCg, Cg, K) * bytes;
     p.w2_bytes = w2 <= kInt32Max ? (uint32_t)w2 : 0;
+    p.w2_group_bytes = (uint32_t)(w2 / group);
     r_out = r;
     N_out = N;
     return GS_OK;

@@ -360,11 +360,10 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_mfma(DeformParams p) {
 // When every conv group and offset group holds a multiple of 8 channels, the
 // sampled columns come from a channels-last copy of X, (N, H, W, C): the 8
 // consecutive channels a thread samples at one corner are one 16-byte load
-// (two for fp32), instead of 8 scalar gathers from 8 planes.  K is walked
-// kernel position first: chunk i covers kernel position i / (Cgp / 32) and
-// 32 channels of the conv group, Cgp = Cg rounded up to 32, so one set of
-// corners serves the whole chunk.  W is copied to match, (OC, kernel
-// positions, Cgp), zero beyond Cg.  Summing K in another order than the
+// (two for fp32), instead of 8 scalar gathers from 8 planes.  K is walked in
+// chunks of one kernel position and 32 channels of the conv group (Cgp = Cg
+// rounded up to 32), so one set of corners serves a whole chunk.  W is copied
+// to match the chunk order, zero beyond Cg.  Summing K in another order than the
 // oracle only changes fp32 rounding order.
 
 // X (N, C, S) -> Xt (N, S, C), S = H * W: 64 x 64 tiles through LDS.
@@ -393,18 +392,51 @@ __global__ __launch_bounds__(kBlock) void to_channels_last(const raw_t *__restri
     }
 }
 
-// W (OC, Cg, KK) -> W2 (OC, KK, Cgp), zero for channels Cg .. Cgp-1.
-template <typename raw_t>
-__global__ __launch_bounds__(kBlock) void w_tap_major(const raw_t *__restrict__ W,
-                                                     raw_t *__restrict__ W2, int OC, int Cg, int KK,
-                                                     int Cgp) {
-    const size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x;
-    if (i >= (size_t)OC * KK * Cgp) return;
-    const int cl = (int)(i % Cgp);
-    const size_t rest = i / Cgp;
-    const int tap = (int)(rest % KK);
-    const size_t oc = rest / KK;
-    W2[i] = cl < Cg ? W[(oc * Cg + cl) * KK + tap] : (raw_t)0;
+// Chunk i of the channels-last kernel covers one kernel position and 32
+// channels of the conv group (Cgp = Cg rounded up to 32).  The table path
+// walks the channel slices outermost (a slice's corners stay in L1 across
+// the kernel positions), the other path the kernel positions outermost (its
+// corners change once per position).
+__device__ __forceinline__ void chunk_coords(int i, int KK, int cpt, bool slice_major, int &tap,
+                                             int &c0) {
+    const int sl = slice_major ? i / KK : i - (i / cpt) * cpt;
+    tap = slice_major ? i - sl * KK : i / cpt;
+    c0 = sl * DC_TK;
+}
+
+// W (OC, Cg, KK) -> W2, packed in the order the matrix cores take the A
+// operand: for conv group G, 32-row block R of its OCg rows (rounded up to
+// 32), chunk i and load v, lane l's 16 bytes at
+// ((((G * Rg + R) * nch + i) * AV + v) * 64 + l) * 16.  Lane l holds row
+// R * 32 + l % 32 and, within the chunk, k = 16 v + 8 (l / 32) + 0..7 for
+// fp16 / bf16, k = 16 (l / 32) + 4 v + 0..3 for fp32.  Rows past OCg and
+// channels past Cg are zero.  One thread per element.
+template <typename raw_t, int AV>
+__global__ __launch_bounds__(kBlock) void w_pack_mfma(const raw_t *__restrict__ W,
+                                                     raw_t *__restrict__ W2, int group, int OCg, int Cg,
+                                                     int KK, int Cgp, int slice_major) {
+    constexpr int EPL = 16 / sizeof(raw_t);         // elements per lane and load
+    const int Rg = (OCg + 31) / 32;
+    const int cpt = Cgp / DC_TK, nch = KK * cpt;
+    const size_t total = (size_t)group * Rg * nch * AV * 64 * EPL;
+    const size_t j = (size_t)blockIdx.x * kBlock + threadIdx.x;
+    if (j >= total) return;
+    const int e = (int)(j % EPL);
+    size_t u = j / EPL;
+    const int l = (int)(u % 64);
+    u /= 64;
+    const int v = (int)(u % AV);
+    u /= AV;
+    const int i = (int)(u % nch);
+    u /= nch;
+    const int R = (int)(u % Rg);
+    const int G = (int)(u / Rg);
+    const int row = R * 32 + (l & 31);
+    const int kc = EPL == 4 ? 16 * (l >> 5) + 4 * v + e : 16 * v + 8 * (l >> 5) + e;
+    int tap, c0;
+    chunk_coords(i, KK, cpt, slice_major != 0, tap, c0);
+    const int cl = c0 + kc;
+    W2[j] = (row < OCg && cl < Cg) ? W[(((size_t)G * OCg + row) * Cg + cl) * KK + tap] : (raw_t)0;
 }
 
 // Eight elements of type T from 8 * T::bytes consecutive bytes, widened.
@@ -443,6 +475,59 @@ __device__ __forceinline__ void pack8(const float (&x)[8], u32x4 *v) {
     }
 }
 
+// MFMA over one chunk with the A operand (W rows) in registers, loaded in
+// the instruction's layout, and the column tile Bs ([position][k], pitch LK)
+// in LDS.  Inside a chunk the k of an fp32 step ks is 16 * (lane / 32) + ks
+// for both operands (any pairing of A and B columns sums the same terms);
+// fp16 / bf16 keep the native order, k = 16 ks + 8 (lane / 32) + 0..7.
+template <typename T, int MB, int LK, int AV>
+__device__ __forceinline__ void mfma_chunk_regs(const u32x4 (&a)[MB][AV], const typename T::raw_t *Bs,
+                                                floatx16 (&acc)[MB][2], int lane) {
+    if constexpr (T::bytes == 4) {
+#pragma unroll
+        for (int kq = 0; kq < 4; ++kq) {
+            u32x4 b[2];
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+                b[nb] = *(const u32x4 *)&Bs[(32 * nb + (lane & 31)) * LK + 16 * (lane >> 5) + 4 * kq];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb) {
+                    const uint32_t au = a[mb][kq][e];
+#pragma unroll
+                    for (int nb = 0; nb < 2; ++nb) {
+                        const uint32_t bu = b[nb][e];
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                            __builtin_bit_cast(float, au), __builtin_bit_cast(float, bu), acc[mb][nb],
+                            0, 0, 0);
+                    }
+                }
+        }
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            u32x4 bv[2];
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb)
+                bv[nb] = *(const u32x4 *)&Bs[(32 * nb + (lane & 31)) * LK + 16 * ks + 8 * (lane >> 5)];
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 2; ++nb) {
+                    if constexpr (__is_same(T, BF16))
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            __builtin_bit_cast(bf16x8, a[mb][ks]), __builtin_bit_cast(bf16x8, bv[nb]),
+                            acc[mb][nb], 0, 0, 0);
+                    else
+                        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            __builtin_bit_cast(halfx8, a[mb][ks]), __builtin_bit_cast(halfx8, bv[nb]),
+                            acc[mb][nb], 0, 0, 0);
+                }
+        }
+    }
+}
+
 template <typename T, int MB, bool TABLE>
 __global__ __launch_bounds__(kBlock) void deform_conv2d_cl(DeformParams p) {
     using raw_t = typename T::raw_t;
@@ -451,8 +536,8 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_cl(DeformParams p) {
     constexpr int LK = DC_TK + PAD;
     constexpr int TE = DC_TABLE * DC_TN;
     constexpr int VPC = 8 * T::bytes / 16;          // 16-byte loads per corner
-    __shared__ __align__(16) raw_t As[TM * LK];
-    __shared__ __align__(16) raw_t Bs[DC_TN * LK];
+    constexpr int AV = T::bytes == 4 ? 4 : 2;       // 16-byte A loads per 32-row block and chunk
+    __shared__ __align__(16) raw_t Bs[2][DC_TN * LK];  // column tiles, double-buffered
     __shared__ int tb_off[TABLE ? 4 * TE : 1];
     __shared__ float tb_w[TABLE ? 4 * TE : 1];
 
@@ -471,7 +556,11 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_cl(DeformParams p) {
     const int KK = p.KH * p.KW;
     const int g_first = (G * p.Cg) / p.Cog;
 
-    const int pos = lane;                           // this thread's output position
+    // This thread samples output position pos and channels c0 + 8 cgp ..
+    // +7 of each chunk: the four lanes of a position read one 64-byte run of
+    // a pixel, so a wave's load touches 16 pixels.
+    const int cgp = t & 3;
+    const int pos = (t >> 2) & (DC_TN - 1);
     const int o = nt * DC_TN + pos;
     const bool o_ok = o < npos;
     const int oh = o_ok ? o / p.OW : 0, ow = o_ok ? o - (o / p.OW) * p.OW : 0;
@@ -481,7 +570,10 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_cl(DeformParams p) {
         for (int e = t; e < entries; e += kBlock) {
             const int gt = e / DC_TN;
             const int gi = gt / KK, tap = gt - gi * KK;
-            const Corners c = sample_corners<T>(p, n, o, o_ok, oh, ow, g_first + gi, tap);
+            const int oe = nt * DC_TN + (e & (DC_TN - 1));
+            const bool oe_ok = oe < npos;
+            const int ohe = oe_ok ? oe / p.OW : 0, owe = oe_ok ? oe - (oe / p.OW) * p.OW : 0;
+            const Corners c = sample_corners<T>(p, n, oe, oe_ok, ohe, owe, g_first + gi, tap);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 tb_off[q * TE + e] = c.off[q];
@@ -495,7 +587,8 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_cl(DeformParams p) {
     const rsrc_t xr = make_rsrc((const char *)p.Xt + (size_t)n * p.x_img_bytes, p.x_img_bytes);
     const int oc0 = G * p.OCg + mt * TM;
     const int m_valid = min(TM, p.OCg - mt * TM);
-    const rsrc_t wr = make_rsrc(p.W2, p.w2_bytes);
+    // packed W of conv group G; 32-row blocks past the group's last read zeros
+    const rsrc_t wr = make_rsrc((const char *)p.W2 + (size_t)G * p.w2_group_bytes, p.w2_group_bytes);
 
     floatx16 acc[MB][2];
 #pragma unroll
@@ -507,30 +600,37 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_cl(DeformParams p) {
 
     const int cpt = p.Cgp / DC_TK;                  // chunks per kernel position
     const int nch = KK * cpt;
-    constexpr int CPR = DC_TK * T::bytes / 16;      // 16-byte parts per W row
-    constexpr int WV = TM * CPR / kBlock;
-    u32x4 wpre[WV];
-    u32x4 xpre[4][VPC];
-    float wq[4];
+    // Two register sets: chunk i's loads were issued two chunks earlier,
+    // into set i % 2.
+    u32x4 a0[MB][AV], a1[MB][AV];
+    u32x4 x0[4][VPC], x1[4][VPC];
+    float q0[4], q1[4];
     Corners cc;                                     // corners of (ctap, cg), non-table path
     int ctap = -1, cg = -1;
-    // Issue chunk i's loads: the W tile rows, and the four corners of this
-    // thread's position for channels c0 + 8 * wave .. +7.
-    auto prefetch = [&](int i) {
-        const int tap = i / cpt;
-        const int c0 = (i - tap * cpt) * DC_TK;
+    // Past the last chunk the loads fetch the last chunk again (unused):
+    // issuing the same loads every chunk keeps the waits counted, not full.
+    // This wave's packed A of chunk i: one coalesced 1 KB load per 32-row
+    // block and v.
+    auto load_a = [&](int i, u32x4 (&a)[MB][AV]) {
+        i = min(i, nch - 1);
 #pragma unroll
-        for (int j = 0; j < WV; ++j) {
-            const int e = t + j * kBlock;
-            const int row = e / CPR, part = e - (e / CPR) * CPR;
-            const uint32_t wo =
-                row < m_valid
-                    ? (uint32_t)(((size_t)(oc0 + row) * p.K2 + (size_t)i * DC_TK + part * (16 / T::bytes)) *
-                                 T::bytes)
-                    : GS_OOB;
-            wpre[j] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)wo, 0, 0);
+        for (int mb = 0; mb < MB; ++mb) {
+            const int R = mt * (TM / 32) + wave * MB + mb;
+#pragma unroll
+            for (int v = 0; v < AV; ++v) {
+                const uint32_t wo =
+                    R < p.Rg ? (uint32_t)((((size_t)R * nch + i) * AV + v) * 64 + lane) * 16 : GS_OOB;
+                a[mb][v] = __builtin_amdgcn_raw_buffer_load_b128(wr, (int)wo, 0, 0);
+            }
         }
-        const int cl = c0 + 8 * wave;
+    };
+    // The four corners of this thread's position for channels c0 + 8 cgp ..
+    // +7 of chunk i, and their weights.
+    auto load_x = [&](int i, u32x4 (&xpre)[4][VPC], float (&wq)[4]) {
+        i = min(i, nch - 1);
+        int tap, c0;
+        chunk_coords(i, KK, cpt, TABLE, tap, c0);
+        const int cl = c0 + 8 * cgp;
         const bool cv = cl < p.Cg;                  // past Cg: padding, W2 is zero there
         const int c = G * p.Cg + (cv ? cl : 0);
         const int g = c / p.Cog;
@@ -543,7 +643,7 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_cl(DeformParams p) {
                 wq[q] = tb_w[q * TE + e];
             }
         } else {
-            if (tap != ctap || g != cg) {           // uniform across the wave
+            if (tap != ctap || g != cg) {
                 cc = sample_corners<T>(p, n, o, o_ok, oh, ow, g, tap);
                 ctap = tap;
                 cg = g;
@@ -564,15 +664,21 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_cl(DeformParams p) {
         }
     };
 
-    prefetch(0);
-    for (int i = 0; i < nch; ++i) {
-        __syncthreads();  // the previous chunk's LDS reads are done
-#pragma unroll
-        for (int j = 0; j < WV; ++j) {
-            const int e = t + j * kBlock;
-            const int row = e / CPR, part = e - (e / CPR) * CPR;
-            *(u32x4 *)&As[row * LK + part * (16 / T::bytes)] = wpre[j];
-        }
+    // loads issued per chunk: chunk i's are complete once no more than one
+    // chunk's worth (chunk i + 1's) is outstanding
+    constexpr int kLoads = MB * AV + 4 * VPC;
+    static_assert(kLoads < 64, "vmcnt field");
+    // One chunk: sample its columns into this chunk's LDS buffer; issue the
+    // corner loads of the chunk two ahead into the registers just read;
+    // multiply; then issue that chunk's A loads into the A registers just
+    // used.
+    auto step = [&](int i, u32x4 (&a)[MB][AV], u32x4 (&xpre)[4][VPC], float (&wq)[4]) {
+        raw_t *bs = Bs[i & 1];
+        // keep the scheduler from pulling this chunk's work above the
+        // previous chunk's loads (it would then wait for those loads)
+        __builtin_amdgcn_sched_barrier(0);
+        // vmcnt(kLoads), expcnt and lgkmcnt left free
+        __builtin_amdgcn_s_waitcnt((kLoads & 15) | ((kLoads >> 4) << 14) | 0x0f70);
         {
             float v[8], x[8];
             unpack8<T>(xpre[0], x);
@@ -588,12 +694,27 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_cl(DeformParams p) {
             pack8<T>(v, packed);
 #pragma unroll
             for (int h = 0; h < VPC; ++h)
-                *(u32x4 *)&Bs[pos * LK + 8 * wave + h * (16 / T::bytes)] = packed[h];
+                *(u32x4 *)&bs[pos * LK + 8 * cgp + h * (16 / T::bytes)] = packed[h];
         }
+        // Every wave's column writes of chunk i are visible, and every wave
+        // has finished reading the other buffer (chunk i - 1).
         __syncthreads();
-        if (i + 1 < nch) prefetch(i + 1);
-        mfma_chunk<T, MB, LK>(As, Bs, acc, wave, lane);
+        load_x(i + 2, xpre, wq);
+        mfma_chunk_regs<T, MB, LK, AV>(a, bs, acc, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        load_a(i + 2, a);
+    };
+
+    load_x(0, x0, q0);
+    load_a(0, a0);
+    load_x(1, x1, q1);
+    load_a(1, a1);
+    int i = 0;
+    for (; i + 1 < nch; i += 2) {
+        step(i, a0, x0, q0);
+        step(i + 1, a1, x1, q1);
     }
+    if (i < nch) step(i, a0, x0, q0);
     store_tile<T, MB>(p, acc, n, oc0, m_valid, nt, wave, lane);
 }
 
@@ -744,11 +865,13 @@ static int cl_launch(const DeformParams &p, hipStream_t s) {
     const int c_tiles = (p.C + 63) / 64, s_tiles = (S + 63) / 64;
     hipLaunchKernelGGL((to_channels_last<raw_t>), dim3((unsigned)((size_t)p.N * c_tiles * s_tiles)),
                        dim3(kBlock), 0, s, (const raw_t *)p.X, (raw_t *)p.Xt, p.C, S, c_tiles, s_tiles);
-    const size_t w2 = (size_t)p.OC * KK * p.Cgp;
-    hipLaunchKernelGGL((w_tap_major<raw_t>), dim3((unsigned)((w2 + kBlock - 1) / kBlock)), dim3(kBlock), 0,
-                       s, (const raw_t *)p.Wt, (raw_t *)p.W2, p.OC, p.Cg, KK, p.Cgp);
-    const dim3 grid(8 * kRun * ((p.nblocks + 8 * kRun - 1) / (8 * kRun)));
     const bool table = p.og_span * KK <= DC_TABLE;
+    constexpr int AV = T::bytes == 4 ? 4 : 2;
+    const size_t w2 = (size_t)p.w2_bytes / T::bytes;
+    hipLaunchKernelGGL((w_pack_mfma<raw_t, AV>), dim3((unsigned)((w2 + kBlock - 1) / kBlock)), dim3(kBlock),
+                       0, s, (const raw_t *)p.Wt, (raw_t *)p.W2, p.group, p.OCg, p.Cg, KK, p.Cgp,
+                       (int)table);
+    const dim3 grid(8 * kRun * ((p.nblocks + 8 * kRun - 1) / (8 * kRun)));
     if (p.OCg > 128) {
         if (table) hipLaunchKernelGGL((deform_conv2d_cl<T, 2, true>), grid, dim3(kBlock), 0, s, p);
         else hipLaunchKernelGGL((deform_conv2d_cl<T, 2, false>), grid, dim3(kBlock), 0, s, p);

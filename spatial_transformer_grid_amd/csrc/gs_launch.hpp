@@ -177,11 +177,13 @@ struct DeformParams {
     uint32_t w_bytes;                        // all of W (< 2^31)
     uint32_t npos;                           // output positions per plane
     int w_vec;                               // W rows allow 16-byte loads
-    // channels-last path: workspace copies of X (N, H, W, C) and of W
-    // (OC, KH*KW, Cgp), Cgp = Cg rounded up to 32, K2 = KH*KW*Cgp
+    // channels-last path: workspace copies of X (N, H, W, C) and of W packed
+    // in the matrix cores' operand order: per conv group Rg = ceil(OCg / 32)
+    // blocks of 32 rows x K2 = KH*KW*Cgp, Cgp = Cg rounded up to 32
     void *Xt, *W2;
-    int Cgp, K2;
+    int Cgp, K2, Rg;
     uint32_t x_img_bytes;                    // one image of Xt (< 2^31)
+    uint32_t w2_group_bytes;                 // one conv group of W2
     uint32_t w2_bytes;                       // all of W2 (< 2^31)
 };
 

@@ -299,12 +299,14 @@ def test_deform_conv_workspace_size(gs):
     3-D data."""
     ws = gs.deform_conv_workspace_size
     up = lambda b: (b + 255) // 256 * 256
-    # 2 x 64 x 10 x 12 bf16, W 48 x 64 x 3 x 3: X 2*64*120*2 bytes, W 48*9*64*2
+    # 2 x 64 x 10 x 12 bf16, W 48 x 64 x 3 x 3: X 2*64*120*2 bytes, W with
+    # its 48 output channels padded to 64
     assert ws([2, 64, 10, 12], [48, 64, 3, 3], gs.GS_BF16, pads=[1, 1, 1, 1]) == \
-        up(2 * 64 * 120 * 2) + up(48 * 9 * 64 * 2)
-    # fp32, 40 channels per group, 2 groups: W's channels padded to 64
+        up(2 * 64 * 120 * 2) + up(64 * 9 * 64 * 2)
+    # fp32, 40 channels per group, 2 groups of 8 output channels: each group's
+    # rows padded to 32, its channels to 64
     assert ws([1, 80, 7, 7], [16, 40, 3, 3], gs.GS_F32, group=2, offset_group=2) == \
-        up(80 * 49 * 4) + up(16 * 9 * 64 * 4)
+        up(80 * 49 * 4) + up(2 * 32 * 9 * 64 * 4)
     assert ws([1, 12, 7, 7], [16, 12, 3, 3], gs.GS_F32) == 0                    # 12 channels
     assert ws([1, 16, 7, 7], [16, 16, 3, 3], gs.GS_F32, offset_group=4) == 0    # 4 per offset group
     assert ws([1, 16, 7, 7], [16, 16, 3, 3], gs.GS_F64) == 0
