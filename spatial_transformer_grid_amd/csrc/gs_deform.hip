@@ -368,11 +368,10 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_mfma(DeformParams p) {
 
 // X (N, C, S) -> Xt (N, S, C), S = H * W: 64 x 64 tiles through LDS.
 template <typename raw_t>
-__global__ __launch_bounds__(kBlock) void to_channels_last(const raw_t *__restrict__ X,
-                                                          raw_t *__restrict__ Xt, int C, int S,
-                                                          int c_tiles, int s_tiles) {
+__device__ __forceinline__ void to_channels_last_scalar(const raw_t *__restrict__ X,
+                                                        raw_t *__restrict__ Xt, int C, int S,
+                                                        int c_tiles, int s_tiles, int b) {
     __shared__ raw_t tile[64][65];
-    const int b = blockIdx.x;
     const int st = b % s_tiles;
     const int ct = (b / s_tiles) % c_tiles;
     const int n = b / (s_tiles * c_tiles);
@@ -389,6 +388,48 @@ __global__ __launch_bounds__(kBlock) void to_channels_last(const raw_t *__restri
     for (int i = 0; i < 16; ++i) {
         const int sp = st * 64 + r4 + 4 * i, c = ct * 64 + col;
         if (sp < S && c < C) dst[(size_t)sp * C + c] = tile[col][r4 + 4 * i];
+    }
+}
+
+// As to_channels_last_scalar with 16-byte accesses on both sides: VW = 16 /
+// sizeof(raw_t) spatial elements per load, VW channels per store.  Needs S
+// and C to be multiples of VW (and 16-byte aligned X, Xt).
+template <typename raw_t>
+__device__ __forceinline__ void to_channels_last_tile(const raw_t *__restrict__ X,
+                                                      raw_t *__restrict__ Xt, int C, int S,
+                                                      int c_tiles, int s_tiles, int b) {
+    constexpr int VW = 16 / sizeof(raw_t);
+    constexpr int P = 64 + 2;                       // LDS row pitch (elements)
+    __shared__ raw_t tile[64 * P];                  // [c][s]
+    const int st = b % s_tiles;
+    const int ct = (b / s_tiles) % c_tiles;
+    const int n = b / (s_tiles * c_tiles);
+    const int t = threadIdx.x;
+    const raw_t *src = X + (size_t)n * C * S;
+    constexpr int PER = 64 / VW;                    // vectors per tile row
+#pragma unroll
+    for (int i = 0; i < 64 * PER / kBlock; ++i) {
+        const int idx = t + i * kBlock;
+        const int cl = idx / PER, sv = idx - (idx / PER) * PER;
+        const int c = ct * 64 + cl, sp = st * 64 + sv * VW;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (c < C && sp < S) v = *(const u32x4 *)(src + (size_t)c * S + sp);
+        const raw_t *e = (const raw_t *)&v;
+#pragma unroll
+        for (int k = 0; k < VW; ++k) tile[cl * P + sv * VW + k] = e[k];
+    }
+    __syncthreads();
+    raw_t *dst = Xt + (size_t)n * S * C;
+#pragma unroll
+    for (int i = 0; i < 64 * PER / kBlock; ++i) {
+        const int idx = t + i * kBlock;
+        const int sl = idx / PER, cv = idx - (idx / PER) * PER;
+        const int sp = st * 64 + sl, c = ct * 64 + cv * VW;
+        u32x4 v;
+        raw_t *e = (raw_t *)&v;
+#pragma unroll
+        for (int k = 0; k < VW; ++k) e[k] = tile[(cv * VW + k) * P + sl];
+        if (sp < S && c < C) *(u32x4 *)(dst + (size_t)sp * C + c) = v;
     }
 }
 
@@ -410,33 +451,57 @@ __device__ __forceinline__ void chunk_coords(int i, int KK, int cpt, bool slice_
 // ((((G * Rg + R) * nch + i) * AV + v) * 64 + l) * 16.  Lane l holds row
 // R * 32 + l % 32 and, within the chunk, k = 16 v + 8 (l / 32) + 0..7 for
 // fp16 / bf16, k = 16 (l / 32) + 4 v + 0..3 for fp32.  Rows past OCg and
-// channels past Cg are zero.  One thread per element.
+// channels past Cg are zero.  One thread per 16-byte unit.
 template <typename raw_t, int AV>
-__global__ __launch_bounds__(kBlock) void w_pack_mfma(const raw_t *__restrict__ W,
-                                                     raw_t *__restrict__ W2, int group, int OCg, int Cg,
-                                                     int KK, int Cgp, int slice_major) {
+__device__ __forceinline__ void w_pack_unit(const raw_t *__restrict__ W, raw_t *__restrict__ W2,
+                                            int group, int OCg, int Cg, int KK, int Cgp,
+                                            int slice_major, uint32_t j) {
     constexpr int EPL = 16 / sizeof(raw_t);         // elements per lane and load
     const int Rg = (OCg + 31) / 32;
     const int cpt = Cgp / DC_TK, nch = KK * cpt;
-    const size_t total = (size_t)group * Rg * nch * AV * 64 * EPL;
-    const size_t j = (size_t)blockIdx.x * kBlock + threadIdx.x;
-    if (j >= total) return;
-    const int e = (int)(j % EPL);
-    size_t u = j / EPL;
-    const int l = (int)(u % 64);
-    u /= 64;
+    // W2 holds fewer than 2^31 bytes, so 32-bit indices suffice
+    const uint32_t units = (uint32_t)group * Rg * nch * AV * 64;
+    if (j >= units) return;
+    const int l = (int)(j % 64);
+    uint32_t u = j / 64;
     const int v = (int)(u % AV);
     u /= AV;
-    const int i = (int)(u % nch);
-    u /= nch;
-    const int R = (int)(u % Rg);
-    const int G = (int)(u / Rg);
+    const int i = (int)(u % (uint32_t)nch);
+    u /= (uint32_t)nch;
+    const int R = (int)(u % (uint32_t)Rg);
+    const int G = (int)(u / (uint32_t)Rg);
     const int row = R * 32 + (l & 31);
-    const int kc = EPL == 4 ? 16 * (l >> 5) + 4 * v + e : 16 * v + 8 * (l >> 5) + e;
     int tap, c0;
     chunk_coords(i, KK, cpt, slice_major != 0, tap, c0);
-    const int cl = c0 + kc;
-    W2[j] = (row < OCg && cl < Cg) ? W[(((size_t)G * OCg + row) * Cg + cl) * KK + tap] : (raw_t)0;
+    const int k0 = EPL == 4 ? 16 * (l >> 5) + 4 * v : 16 * v + 8 * (l >> 5);
+    const raw_t *wrow = W + (((size_t)G * OCg + row) * Cg) * KK + tap;
+    u32x4 out;
+    raw_t *e = (raw_t *)&out;
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) {
+        const int cl = c0 + k0 + k;
+        e[k] = (row < OCg && cl < Cg) ? wrow[(size_t)cl * KK] : (raw_t)0;
+    }
+    *(u32x4 *)(W2 + (size_t)j * EPL) = out;
+}
+
+// The channels-last kernel's preparation in one launch: blocks below
+// x_blocks transpose 64 x 64 tiles of X, the rest pack W (one 16-byte unit
+// per thread); the two halves touch disjoint memory.
+template <typename raw_t, int AV, bool VEC>
+__global__ __launch_bounds__(kBlock) void cl_prepare(const raw_t *__restrict__ X, raw_t *__restrict__ Xt,
+                                                    int C, int S, int c_tiles, int s_tiles, int x_blocks,
+                                                    const raw_t *__restrict__ W, raw_t *__restrict__ W2,
+                                                    int group, int OCg, int Cg, int KK, int Cgp,
+                                                    int slice_major) {
+    const int b = blockIdx.x;
+    if (b < x_blocks) {
+        if constexpr (VEC) to_channels_last_tile<raw_t>(X, Xt, C, S, c_tiles, s_tiles, b);
+        else to_channels_last_scalar<raw_t>(X, Xt, C, S, c_tiles, s_tiles, b);
+    } else {
+        w_pack_unit<raw_t, AV>(W, W2, group, OCg, Cg, KK, Cgp, slice_major,
+                               (uint32_t)(b - x_blocks) * kBlock + threadIdx.x);
+    }
 }
 
 // Eight elements of type T from 8 * T::bytes consecutive bytes, widened.
@@ -863,14 +928,21 @@ static int cl_launch(const DeformParams &p, hipStream_t s) {
     using raw_t = typename T::raw_t;
     const int S = p.H * p.W, KK = p.KH * p.KW;
     const int c_tiles = (p.C + 63) / 64, s_tiles = (S + 63) / 64;
-    hipLaunchKernelGGL((to_channels_last<raw_t>), dim3((unsigned)((size_t)p.N * c_tiles * s_tiles)),
-                       dim3(kBlock), 0, s, (const raw_t *)p.X, (raw_t *)p.Xt, p.C, S, c_tiles, s_tiles);
+    const int x_blocks = (int)((size_t)p.N * c_tiles * s_tiles);
     const bool table = p.og_span * KK <= DC_TABLE;
     constexpr int AV = T::bytes == 4 ? 4 : 2;
-    const size_t w2 = (size_t)p.w2_bytes / T::bytes;
-    hipLaunchKernelGGL((w_pack_mfma<raw_t, AV>), dim3((unsigned)((w2 + kBlock - 1) / kBlock)), dim3(kBlock),
-                       0, s, (const raw_t *)p.Wt, (raw_t *)p.W2, p.group, p.OCg, p.Cg, KK, p.Cgp,
-                       (int)table);
+    const int w_blocks = (int)(((size_t)p.w2_bytes / 16 + kBlock - 1) / kBlock);
+    constexpr int VW = 16 / sizeof(raw_t);
+    // C is a multiple of 8 on this path
+    const dim3 pgrid((unsigned)(x_blocks + w_blocks));
+    if (S % VW == 0 && (uintptr_t)p.X % 16 == 0)
+        hipLaunchKernelGGL((cl_prepare<raw_t, AV, true>), pgrid, dim3(kBlock), 0, s, (const raw_t *)p.X,
+                           (raw_t *)p.Xt, p.C, S, c_tiles, s_tiles, x_blocks, (const raw_t *)p.Wt,
+                           (raw_t *)p.W2, p.group, p.OCg, p.Cg, KK, p.Cgp, (int)table);
+    else
+        hipLaunchKernelGGL((cl_prepare<raw_t, AV, false>), pgrid, dim3(kBlock), 0, s, (const raw_t *)p.X,
+                           (raw_t *)p.Xt, p.C, S, c_tiles, s_tiles, x_blocks, (const raw_t *)p.Wt,
+                           (raw_t *)p.W2, p.group, p.OCg, p.Cg, KK, p.Cgp, (int)table);
     const dim3 grid(8 * kRun * ((p.nblocks + 8 * kRun - 1) / (8 * kRun)));
     if (p.OCg > 128) {
         if (table) hipLaunchKernelGGL((deform_conv2d_cl<T, 2, true>), grid, dim3(kBlock), 0, s, p);
