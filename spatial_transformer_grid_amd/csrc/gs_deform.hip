@@ -603,8 +603,11 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_cl(DeformParams p) {
     constexpr int VPC = 8 * T::bytes / 16;          // 16-byte loads per corner
     constexpr int AV = T::bytes == 4 ? 4 : 2;       // 16-byte A loads per 32-row block and chunk
     __shared__ __align__(16) raw_t Bs[2][DC_TN * LK];  // column tiles, double-buffered
-    __shared__ int tb_off[TABLE ? 4 * TE : 1];
+    // corner byte offsets of the pixel's channel run in Xt (out-of-range
+    // offset for corners outside the image) and mask-folded weights
+    __shared__ uint32_t tb_off[TABLE ? 4 * TE : 1];
     __shared__ float tb_w[TABLE ? 4 * TE : 1];
+    const uint32_t pix_bytes = (uint32_t)p.C * T::bytes;
 
     const int lb = xcd_logical_block_runs(p.nblocks);
     if (lb >= p.nblocks) return;
@@ -641,7 +644,7 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_cl(DeformParams p) {
             const Corners c = sample_corners<T>(p, n, oe, oe_ok, ohe, owe, g_first + gi, tap);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                tb_off[q * TE + e] = c.off[q];
+                tb_off[q * TE + e] = c.off[q] >= 0 ? (uint32_t)c.off[q] * pix_bytes : GS_OOB;
                 tb_w[q * TE + e] = c.w[q];
             }
         }
@@ -699,7 +702,7 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_cl(DeformParams p) {
         const bool cv = cl < p.Cg;                  // past Cg: padding, W2 is zero there
         const int c = G * p.Cg + (cv ? cl : 0);
         const int g = c / p.Cog;
-        int off[4];
+        uint32_t off[4];
         if constexpr (TABLE) {
             const int e = ((g - g_first) * KK + tap) * DC_TN + pos;
 #pragma unroll
@@ -715,14 +718,16 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_cl(DeformParams p) {
             }
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                off[q] = cc.off[q];
+                off[q] = cc.off[q] >= 0 ? (uint32_t)cc.off[q] * pix_bytes : GS_OOB;
                 wq[q] = cc.w[q];
             }
         }
+        // an out-of-range corner offset stays out of range (below 2^32) with
+        // the channel's bytes added
+        const uint32_t cbytes = (uint32_t)c * T::bytes;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const uint32_t xo =
-                (cv && off[q] >= 0) ? ((uint32_t)off[q] * (uint32_t)p.C + (uint32_t)c) * T::bytes : GS_OOB;
+            const uint32_t xo = cv ? off[q] + cbytes : GS_OOB;
 #pragma unroll
             for (int v = 0; v < VPC; ++v)
                 xpre[q][v] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)(xo + 16 * v), 0, 0);
