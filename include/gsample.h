@@ -145,6 +145,42 @@ int gs_grid_sample_2d(const void *X, int x_dtype, const int64_t *x_shape, const 
                       int align_corners, void *Y, void *stream);
 
 /*
+ * GridSample, 2 spatial dimensions, with a workspace for grids whose
+ * locations scatter over the input (GridSample page, as gs_grid_sample_2d).
+ * Same arguments, results and errors as gs_grid_sample_2d (GS_ERR_ATTR also
+ * for a negative workspace_bytes), plus:
+ *
+ *   workspace, workspace_bytes   device scratch owned by the caller (256-byte
+ *                aligned), at least gs_grid_sample_2d_workspace_size() bytes;
+ *                overwritten; not to be shared by calls that may run at the
+ *                same time.  NULL / too small: exactly gs_grid_sample_2d.
+ *
+ * With the workspace the call first probes 64 of the sampler's output tiles
+ * on the device; when most of them read from more of X than fits a tile's
+ * LDS slot (e.g. a random flow), X is copied to channels-last slices of 32
+ * bytes of channels, (N, C / CS, H_in, W_in, CS), in the workspace and
+ * sampled from there, several channels per load.  Otherwise the call runs as
+ * gs_grid_sample_2d.  Both compute the same taps, weights and fp32 sums in
+ * the same order (nearest copies the element bit for bit).  Only fp32 / fp16
+ * / bf16 X with an fp32 grid and C * sizeof(element) a multiple of 32 bytes
+ * use it; other types run as gs_grid_sample_2d.
+ */
+int gs_grid_sample_2d_ws(const void *X, int x_dtype, const int64_t *x_shape, const void *grid,
+                         int grid_dtype, const int64_t *grid_shape, int mode, int padding,
+                         int align_corners, void *Y, void *workspace, int64_t workspace_bytes,
+                         void *stream);
+
+/*
+ * Bytes of workspace gs_grid_sample_2d_ws can use for these shapes (host
+ * only; the grid's values are not read): 256 + N * C * H_in * W_in *
+ * sizeof(element), or 0 when the gather path does not apply.  Written to
+ * *bytes.  Errors: GS_ERR_NULL, GS_ERR_DTYPE, GS_ERR_SHAPE (negative extent,
+ * batch mismatch, last grid dim not 2).
+ */
+int gs_grid_sample_2d_workspace_size(int x_dtype, const int64_t *x_shape,
+                                     const int64_t *grid_shape, int64_t *bytes);
+
+/*
  * GridSample, 3 spatial dimensions.  As gs_grid_sample_2d with
  *   X (N, C, D_in, H_in, W_in), grid (N, D_out, H_out, W_out, 3) whose
  *   components are x (W), y (H), z (D), Y (N, C, D_out, H_out, W_out);

@@ -26,6 +26,7 @@ from ._binding import (  # noqa: F401
     deform_conv_workspace_size,
     dtype_code,
     grid_sample,
+    grid_sample_2d_workspace_size,
     lib,
     resize,
     resize_output_shape,
@@ -34,5 +35,5 @@ from ._binding import (  # noqa: F401
 
 __all__ = ["affine_grid", "grid_sample", "affine_grid_sample_fused", "resize",
            "resize_output_shape", "resize_to", "deform_conv", "deform_conv_output_shape",
-           "deform_conv_workspace_size", "dtype_code",
+           "deform_conv_workspace_size", "dtype_code", "grid_sample_2d_workspace_size",
            "GSError", "lib"]

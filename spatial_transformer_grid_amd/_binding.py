@@ -38,6 +38,9 @@ SIGNATURES = {
     "gs_grid_sample_3d": ([_P, _I, _PI64, _P, _I, _PI64, _I, _I, _I, _P, _P], _I),
     "gs_affine_grid_sample_fused": ([_P, _I, _P, _I, _PI64, _I, _PI64, _I, _I, _I, _P, _P], _I),
     "gs_grid_sample": ([_P, _I, _PI64, _I, _P, _I, _PI64, _I, _I, _I, _P, _P], _I),
+    "gs_grid_sample_2d_ws": ([_P, _I, _PI64, _P, _I, _PI64, _I, _I, _I, _P, _P, ctypes.c_int64, _P],
+                             _I),
+    "gs_grid_sample_2d_workspace_size": ([_I, _PI64, _PI64, _PI64], _I),
     "gs_deform_conv": ([_P, _I, _PI64, _I, _P, _PI64, _P, _P, _P, _PI64, _PI64, _PI64, _I, _I,
                         _P, _P, ctypes.c_int64, _P], _I),
     "gs_deform_conv_workspace_size": ([_I, _PI64, _I, _PI64, _PI64, _PI64, _PI64, _I, _I, _PI64],
@@ -146,10 +149,24 @@ def _out_tensor(out, shape, like):
     return out
 
 
+def grid_sample_2d_workspace_size(x_shape, grid_shape, dtype) -> int:
+    """Bytes of workspace gs_grid_sample_2d_ws can use (0: none helps)."""
+    need = ctypes.c_int64(0)
+    _check(lib().gs_grid_sample_2d_workspace_size(dtype, int64_array(x_shape),
+                                                  int64_array(grid_shape), ctypes.byref(need)),
+           "gs_grid_sample_2d_workspace_size")
+    return need.value
+
+
 def grid_sample(X, grid, mode: str = "linear", padding_mode: str = "zeros",
-                align_corners: int = 0, out=None, stream=None):
+                align_corners: int = 0, out=None, stream=None, workspace=None):
     """GridSample(X, grid) -> Y on the GPU: gs_grid_sample_2d / _3d for 2 and
-    3 spatial dimensions, gs_grid_sample for 1 to 6."""
+    3 spatial dimensions, gs_grid_sample for 1 to 6.
+
+    `workspace` (2-D only): a device tensor of scratch bytes, or "auto" for
+    one of the size the library asks for from torch's allocator; with it the
+    call is gs_grid_sample_2d_ws, which gathers from a channels-last copy of X
+    when the grid scatters its locations (a random flow)."""
     X = _device_tensor(X, "X")
     grid = _device_tensor(grid, "grid")
     r = X.dim() - 2
@@ -161,6 +178,18 @@ def grid_sample(X, grid, mode: str = "linear", padding_mode: str = "zeros",
     rest = (ctypes.c_void_p(grid.data_ptr()), dtype_code(grid), int64_array(grid.shape),
             MODES[mode], PADDINGS[padding_mode], int(align_corners),
             ctypes.c_void_p(Y.data_ptr()), _stream(stream, X.device))
+    if r == 2 and workspace is not None:
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise ValueError('workspace must be a tensor or "auto"')
+            need = grid_sample_2d_workspace_size(tuple(X.shape), tuple(grid.shape),
+                                                 dtype_code(X))
+            workspace = _torch().empty(need, dtype=_torch().uint8, device=X.device)
+        ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace.numel() else None
+        st = lib().gs_grid_sample_2d_ws(*args, *rest[:-1], ws_ptr,
+                                        workspace.numel() * workspace.element_size(), rest[-1])
+        _check(st, "gs_grid_sample_2d_ws")
+        return Y
     if r in (2, 3):
         name = "gs_grid_sample_%dd" % r
         st = getattr(lib(), name)(*args, *rest)

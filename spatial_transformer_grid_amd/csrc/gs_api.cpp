@@ -65,10 +65,32 @@ Extents spatial3(const int64_t *sp, int r) {
 
 int hip_status(int rc) { return rc == 0 ? GS_OK : GS_ERR_HIP; }
 
-// Shared validation and launch of the sampler (fused or not).
+// Workspace of the 2D gather path: kProbes verdict words (padded to 256
+// bytes), then X in channels-last slices of 32 bytes of channels.  0 when the
+// path does not apply: it needs fp32 / fp16 / bf16 X whose channels fill
+// whole 32-byte slices, an image of X and the channel planes of an image of Y
+// each below 2^31 bytes.
+constexpr int64_t kVerdictBytes = 256;
+
+int64_t gather_workspace_bytes(int x_dtype, const int64_t *x_shape, const int64_t *out_sp) {
+    if (!valid_x_dtype(x_dtype)) return 0;
+    const int bytes = elem_bytes(x_dtype);
+    const int64_t N = x_shape[0], C = x_shape[1];
+    if (N < 1 || C < 1 || (C * bytes) % 32 != 0) return 0;
+    int64_t img = 0, outp = 0;
+    if (!product_within(x_shape + 1, 3, kInt32Max / bytes, &img) || img == 0) return 0;
+    const int64_t co[3] = {C, out_sp[0], out_sp[1]};
+    if (!product_within(co, 3, kInt32Max / bytes, &outp)) return 0;
+    if (N > (int64_t(1) << 40) / (img * bytes)) return 0;
+    return kVerdictBytes + N * img * bytes;
+}
+
+// Shared validation and launch of the sampler (fused or not).  With a large
+// enough workspace (2D, unfused) the gather path is enqueued too, and the
+// device picks one of the two.
 int sample(int r, const void *theta, const void *X, int x_dtype, const int64_t *x_shape,
            const void *grid, const int64_t *out_sp, int mode, int padding, int align_corners,
-           void *Y, void *stream) {
+           void *Y, void *stream, void *workspace = nullptr, int64_t workspace_bytes = 0) {
     for (int i = 0; i < r + 2; ++i)
         if (x_shape[i] < 0) return GS_ERR_SHAPE;
     for (int i = 0; i < r; ++i)
@@ -130,6 +152,28 @@ int sample(int r, const void *theta, const void *X, int x_dtype, const int64_t *
     p.nblocks = (int)(N * groups * tiles);
     p.vec_out = q > 1 && out.w % q == 0 && (uintptr_t)Y % (uintptr_t)(q * bytes) == 0;
     p.vec_grid = r == 2 && q == 4 && grid != nullptr && out.w % 4 == 0 && (uintptr_t)grid % 16 == 0;
+    p.gather_verdicts = nullptr;
+    if (r == 2 && !theta && workspace && (uintptr_t)workspace % 256 == 0) {
+        const int64_t need = gather_workspace_bytes(x_dtype, x_shape, out_sp);
+        if (need > 0 && workspace_bytes >= need) {
+            gs::GatherParams g;
+            g.verdicts = (int *)workspace;
+            g.Xt = (char *)workspace + kVerdictBytes;
+            const int64_t pairs = N * (C * bytes / 32);
+            const int64_t tpp = out.h * ((out.w + 127) / 128);
+            const int64_t blocks = (pairs >= 8 ? (pairs + 7) / 8 * 8 : pairs) * tpp;
+            if (blocks > kMaxBlocks * 8) return GS_ERR_TOO_LARGE;
+            g.pairs = (int)pairs;
+            g.tiles_per_pair = (int)tpp;
+            g.xcd_pairs = pairs >= 8;
+            g.gather_blocks = (int)blocks;
+            p.gather_verdicts = g.verdicts;
+            const int rc = gs::launch_grid_gather(p, g, mode, padding, x_dtype,
+                                                  in.w % (16 / bytes) == 0 && (uintptr_t)X % 16 == 0,
+                                                  (hipStream_t)stream);
+            if (rc) return hip_status(rc);
+        }
+    }
     return hip_status(gs::launch_grid_sample(p, r, theta != nullptr, mode, padding, x_dtype,
                                              vec_in, (hipStream_t)stream));
 }
@@ -268,6 +312,36 @@ int gs_grid_sample_2d(const void *X, int x_dtype, const int64_t *x_shape, const 
                       int align_corners, void *Y, void *stream) {
     return grid_sample_rank(2, X, x_dtype, x_shape, grid, grid_dtype, grid_shape, mode, padding,
                             align_corners, Y, stream);
+}
+
+int gs_grid_sample_2d_workspace_size(int x_dtype, const int64_t *x_shape,
+                                     const int64_t *grid_shape, int64_t *bytes) {
+    if (!x_shape || !grid_shape || !bytes) return GS_ERR_NULL;
+    if (!valid_any_dtype(x_dtype)) return GS_ERR_DTYPE;
+    for (int i = 0; i < 4; ++i)
+        if (x_shape[i] < 0 || grid_shape[i] < 0) return GS_ERR_SHAPE;
+    if (grid_shape[0] != x_shape[0] || grid_shape[3] != 2) return GS_ERR_SHAPE;
+    *bytes = gather_workspace_bytes(x_dtype, x_shape, grid_shape + 1);
+    return GS_OK;
+}
+
+int gs_grid_sample_2d_ws(const void *X, int x_dtype, const int64_t *x_shape, const void *grid,
+                         int grid_dtype, const int64_t *grid_shape, int mode, int padding,
+                         int align_corners, void *Y, void *workspace, int64_t workspace_bytes,
+                         void *stream) {
+    if (!x_shape || !grid_shape) return GS_ERR_NULL;
+    if (workspace_bytes < 0) return GS_ERR_ATTR;
+    if (!valid_x_dtype(x_dtype) || grid_dtype != GS_F32)
+        return grid_sample_rank(2, X, x_dtype, x_shape, grid, grid_dtype, grid_shape, mode,
+                                padding, align_corners, Y, stream);
+    if (!valid_grid_dtype(grid_dtype)) return GS_ERR_DTYPE;
+    int rc = check_attrs(mode, padding, align_corners);
+    if (rc) return rc;
+    for (int i = 0; i < 4; ++i)
+        if (grid_shape[i] < 0) return GS_ERR_SHAPE;
+    if (grid_shape[0] != x_shape[0] || grid_shape[3] != 2) return GS_ERR_SHAPE;
+    return sample(2, nullptr, X, x_dtype, x_shape, grid, grid_shape + 1, mode, padding,
+                  align_corners, Y, stream, workspace, workspace_bytes);
 }
 
 int gs_grid_sample_3d(const void *X, int x_dtype, const int64_t *x_shape, const void *grid,

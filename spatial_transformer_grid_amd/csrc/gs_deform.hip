@@ -20,6 +20,7 @@
 // per output, summed in double.
 #include "gs_device.hpp"
 #include "gs_launch.hpp"
+#include "gs_layout.hpp"
 
 #include <stdint.h>
 
@@ -366,73 +367,6 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_mfma(DeformParams p) {
 // to match the chunk order, zero beyond Cg.  Summing K in another order than the
 // oracle only changes fp32 rounding order.
 
-// X (N, C, S) -> Xt (N, S, C), S = H * W: 64 x 64 tiles through LDS.
-template <typename raw_t>
-__device__ __forceinline__ void to_channels_last_scalar(const raw_t *__restrict__ X,
-                                                        raw_t *__restrict__ Xt, int C, int S,
-                                                        int c_tiles, int s_tiles, int b) {
-    __shared__ raw_t tile[64][65];
-    const int st = b % s_tiles;
-    const int ct = (b / s_tiles) % c_tiles;
-    const int n = b / (s_tiles * c_tiles);
-    const int t = threadIdx.x, col = t & 63, r4 = t >> 6;
-    const raw_t *src = X + (size_t)n * C * S;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int c = ct * 64 + r4 + 4 * i, sp = st * 64 + col;
-        tile[r4 + 4 * i][col] = (c < C && sp < S) ? src[(size_t)c * S + sp] : (raw_t)0;
-    }
-    __syncthreads();
-    raw_t *dst = Xt + (size_t)n * S * C;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int sp = st * 64 + r4 + 4 * i, c = ct * 64 + col;
-        if (sp < S && c < C) dst[(size_t)sp * C + c] = tile[col][r4 + 4 * i];
-    }
-}
-
-// As to_channels_last_scalar with 16-byte accesses on both sides: VW = 16 /
-// sizeof(raw_t) spatial elements per load, VW channels per store.  Needs S
-// and C to be multiples of VW (and 16-byte aligned X, Xt).
-template <typename raw_t>
-__device__ __forceinline__ void to_channels_last_tile(const raw_t *__restrict__ X,
-                                                      raw_t *__restrict__ Xt, int C, int S,
-                                                      int c_tiles, int s_tiles, int b) {
-    constexpr int VW = 16 / sizeof(raw_t);
-    constexpr int P = 64 + 2;                       // LDS row pitch (elements)
-    __shared__ raw_t tile[64 * P];                  // [c][s]
-    const int st = b % s_tiles;
-    const int ct = (b / s_tiles) % c_tiles;
-    const int n = b / (s_tiles * c_tiles);
-    const int t = threadIdx.x;
-    const raw_t *src = X + (size_t)n * C * S;
-    constexpr int PER = 64 / VW;                    // vectors per tile row
-#pragma unroll
-    for (int i = 0; i < 64 * PER / kBlock; ++i) {
-        const int idx = t + i * kBlock;
-        const int cl = idx / PER, sv = idx - (idx / PER) * PER;
-        const int c = ct * 64 + cl, sp = st * 64 + sv * VW;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (c < C && sp < S) v = *(const u32x4 *)(src + (size_t)c * S + sp);
-        const raw_t *e = (const raw_t *)&v;
-#pragma unroll
-        for (int k = 0; k < VW; ++k) tile[cl * P + sv * VW + k] = e[k];
-    }
-    __syncthreads();
-    raw_t *dst = Xt + (size_t)n * S * C;
-#pragma unroll
-    for (int i = 0; i < 64 * PER / kBlock; ++i) {
-        const int idx = t + i * kBlock;
-        const int sl = idx / PER, cv = idx - (idx / PER) * PER;
-        const int sp = st * 64 + sl, c = ct * 64 + cv * VW;
-        u32x4 v;
-        raw_t *e = (raw_t *)&v;
-#pragma unroll
-        for (int k = 0; k < VW; ++k) e[k] = tile[(cv * VW + k) * P + sl];
-        if (sp < S && c < C) *(u32x4 *)(dst + (size_t)sp * C + c) = v;
-    }
-}
-
 // Chunk i of the channels-last kernel covers one kernel position and 32
 // channels of the conv group (Cgp = Cg rounded up to 32).  The table path
 // walks the channel slices outermost (a slice's corners stay in L1 across
@@ -496,8 +430,8 @@ __global__ __launch_bounds__(kBlock) void cl_prepare(const raw_t *__restrict__ X
                                                     int slice_major) {
     const int b = blockIdx.x;
     if (b < x_blocks) {
-        if constexpr (VEC) to_channels_last_tile<raw_t>(X, Xt, C, S, c_tiles, s_tiles, b);
-        else to_channels_last_scalar<raw_t>(X, Xt, C, S, c_tiles, s_tiles, b);
+        if constexpr (VEC) to_channels_last_tile<raw_t>(X, Xt, C, S, c_tiles, s_tiles, b, C);
+        else to_channels_last_scalar<raw_t>(X, Xt, C, S, c_tiles, s_tiles, b, C);
     } else {
         w_pack_unit<raw_t, AV>(W, W2, group, OCg, Cg, KK, Cgp, slice_major,
                                (uint32_t)(b - x_blocks) * kBlock + threadIdx.x);

@@ -61,6 +61,16 @@ struct F32 {
     }
 };
 
+// The fp32 value as computed: an empty asm statement the compiler cannot look
+// through.  Without it the FMA that produced a value can be fused with its
+// conversion to fp16 / bf16 (v_fma_mix*), which rounds the exact result once
+// to the half type instead of rounding the fp32 result, and the last bit of
+// a half output then depends on how a kernel was scheduled.
+__device__ __forceinline__ float settle(float v) {
+    __asm__ volatile("" : "+v"(v));
+    return v;
+}
+
 struct Half16Base {
     static constexpr int bytes = 2;
     typedef uint16_t raw_t;
@@ -81,7 +91,7 @@ struct F16 : Half16Base {
     }
     // round to nearest even (v_cvt_f16_f32)
     __device__ __forceinline__ static void store(float v, rsrc_t r, uint32_t off) {
-        store_raw(__builtin_bit_cast(uint16_t, (_Float16)v), r, off);
+        store_raw(__builtin_bit_cast(uint16_t, (_Float16)settle(v)), r, off);
     }
 };
 
@@ -94,7 +104,7 @@ struct BF16 : Half16Base {
     }
     // round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
     __device__ __forceinline__ static void store(float v, rsrc_t r, uint32_t off) {
-        store_raw(__builtin_bit_cast(uint16_t, (__bf16)v), r, off);
+        store_raw(__builtin_bit_cast(uint16_t, (__bf16)settle(v)), r, off);
     }
 };
 
@@ -315,11 +325,79 @@ template <>
 __device__ __forceinline__ uint32_t to_raw<F32>(float v) { return __builtin_bit_cast(uint32_t, v); }
 template <>
 __device__ __forceinline__ uint16_t to_raw<F16>(float v) {
-    return __builtin_bit_cast(uint16_t, (_Float16)v);
+    return __builtin_bit_cast(uint16_t, (_Float16)settle(v));
 }
 template <>
 __device__ __forceinline__ uint16_t to_raw<BF16>(float v) {
-    return __builtin_bit_cast(uint16_t, (__bf16)v);
+    return __builtin_bit_cast(uint16_t, (__bf16)settle(v));
+}
+
+// ------------------------------------------------------------------ taps
+
+template <int MODE>
+struct AxisK {
+    static constexpr int K = MODE == MODE_NEAREST ? 1 : (MODE == MODE_LINEAR ? 2 : 4);
+};
+
+template <int K>
+struct AxisTaps {
+    int idx[K];
+    bool ok[K];
+    float w[K];
+};
+
+// Taps of one axis of n pixels for pixel coordinate pc (finite, |pc| <= 2^24).
+template <int MODE, int PAD>
+__device__ __forceinline__ void axis_taps(float pc, int n, int ac, AxisTaps<AxisK<MODE>::K> &a) {
+    if constexpr (MODE == MODE_NEAREST) {
+        float q = pad_coordinate<PAD>(pc, n, ac);
+        int i = (int)rintf(q);
+        a.idx[0] = i;
+        a.ok[0] = (uint32_t)i < (uint32_t)n;
+        a.w[0] = 1.0f;
+    } else if constexpr (MODE == MODE_LINEAR) {
+        float q = pad_coordinate<PAD>(pc, n, ac);
+        float fl = floorf(q);
+        int i0 = (int)fl;
+        float t = q - fl;
+        a.idx[0] = i0;
+        a.idx[1] = i0 + 1;
+        a.ok[0] = (uint32_t)i0 < (uint32_t)n;
+        a.ok[1] = (uint32_t)(i0 + 1) < (uint32_t)n;
+        a.w[0] = 1.0f - t;
+        a.w[1] = t;
+    } else {
+        // cubic: the location is not padded; each tap is
+        float fl = floorf(pc);
+        int i0 = (int)fl;
+        cubic_weights(pc - fl, a.w);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            int i = i0 - 1 + j;
+            if constexpr (PAD == PAD_ZEROS) {
+                a.idx[j] = i;
+                a.ok[j] = (uint32_t)i < (uint32_t)n;
+            } else {
+                a.idx[j] = pad_tap<PAD>(i, n, ac);
+                a.ok[j] = true;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------- gather path choice
+
+// Tiles the 2D gather path probes; its verdicts (1 = the tile's locations are
+// scattered beyond what LDS staging holds) are kProbes words in device memory.
+constexpr int kProbes = 64;
+
+// True when at least half of the probed tiles are scattered.  Uniform across
+// the block (the 64 words load through the scalar cache).
+__device__ __forceinline__ bool gather_chosen(const int *verdicts) {
+    int count = 0;
+#pragma unroll
+    for (int i = 0; i < kProbes; ++i) count += verdicts[i];
+    return count * 2 >= kProbes;
 }
 
 }  // namespace gs

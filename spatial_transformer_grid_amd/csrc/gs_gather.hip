@@ -1,0 +1,271 @@
+// gs_gather.hip -- 2D GridSample for grids that are not locally smooth, on a
+// channels-last copy of X, for gfx950.
+//
+// The tuned sampler stages each tile's input box in LDS; when the grid
+// scatters a tile's locations over the whole image (a random flow) the box
+// does not fit, and gathering every tap of every channel from the planes of
+// X costs one scattered load per (tap, channel).  With a caller-provided
+// workspace the library instead:
+//
+//  1. probes 64 of the sampler's tiles spread over the batch: a tile counts
+//     as scattered when the bounding box of its locations (plus the tap
+//     window) cannot be staged -- more than 256 input rows or more than the
+//     16 KB slot;
+//  2. if most probed tiles are scattered, copies X to channels-last slices
+//     (N, C / CS, H, W, CS) of CS = 32 / sizeof(T) channels in the workspace
+//     and samples from it: two lanes share an output location and each loads
+//     VW = 16 / sizeof(T) channels of a tap in one 16-byte load.  One slice
+//     plane of an image (H * W * 32 bytes, 2 MB for 256 x 256) fits an XCD's
+//     L2, and the blocks are ordered so that each XCD walks its own
+//     (image, slice) planes one after another: the random taps hit L2;
+//  3. otherwise the tuned sampler runs as usual.
+//
+// All three launches are enqueued every time; the ones the probe does not
+// choose return at once.  The per-output arithmetic is the tuned sampler's:
+// the same taps and weights (GridSample page: Summary; Attributes
+// align_corners, mode, padding_mode), the same fp32 sum in the same tap
+// order, one rounding to T at the store.
+#include "gs_device.hpp"
+#include "gs_launch.hpp"
+#include "gs_layout.hpp"
+
+#include <limits.h>
+#include <stdint.h>
+
+namespace gs {
+
+constexpr int kGatherLocs = 128;     // output locations per block (one row segment)
+constexpr int kSliceBytes = 32;      // bytes of one pixel's channel slice
+
+// Block b probes tile (b * tiles) / 64 of the sampler's tiling (geometry in
+// p) and writes verdicts[b]: 1 when the tile's locations are scattered.
+template <int MODE>
+__global__ __launch_bounds__(kBlock) void gather_probe(SampleParams p, int elem_bytes, int *verdicts) {
+    __shared__ int red[kBlock / 64][4];
+    const int64_t total = (int64_t)p.N * p.tiles_per_n;
+    const int64_t tb = ((int64_t)blockIdx.x * total) / kProbes;
+    const int n = (int)(tb / p.tiles_per_n);
+    const int tile = (int)(tb - (int64_t)n * p.tiles_per_n);
+    const int tx = tile % p.tiles_w, ty = tile / p.tiles_w;
+    const int count = p.tile_w * p.tile_h;
+    int mm[4] = {INT_MAX, INT_MAX, INT_MAX, INT_MAX};  // min x, -max x, min y, -max y
+    for (int i = threadIdx.x; i < count; i += kBlock) {
+        const int ox = tx * p.tile_w + i % p.tile_w, oy = ty * p.tile_h + i / p.tile_w;
+        if (ox >= p.out_w || oy >= p.out_h) continue;
+        const float *g = p.grid + ((size_t)n * p.out_count + (uint32_t)oy * (uint32_t)p.out_w + ox) * 2;
+        const float u = unnormalize(g[0], p.in_w, p.align_corners);
+        const float v = unnormalize(g[1], p.in_h, p.align_corners);
+        if (!__builtin_isfinite(u) || !__builtin_isfinite(v)) continue;
+        const int xi = (int)floorf(fminf(fmaxf(u, -1.0e6f), 1.0e6f));
+        const int yi = (int)floorf(fminf(fmaxf(v, -1.0e6f), 1.0e6f));
+        mm[0] = min(mm[0], xi);
+        mm[1] = min(mm[1], -xi);
+        mm[2] = min(mm[2], yi);
+        mm[3] = min(mm[3], -yi);
+    }
+    block_min<4>(mm, red);
+    if (threadIdx.x == 0) {
+        int verdict = 0;
+        if (mm[0] != INT_MAX) {
+            constexpr int K = AxisK<MODE>::K;
+            const int64_t sx = (int64_t)(-mm[1]) - mm[0] + K, sy = (int64_t)(-mm[3]) - mm[2] + K;
+            verdict = (sy > 256 || sx * sy * elem_bytes > 16384) ? 1 : 0;
+        }
+        verdicts[blockIdx.x] = verdict;
+    }
+}
+
+// The sliced channels-last copy, when the probe chose gathering.
+template <typename raw_t, bool VEC>
+__global__ __launch_bounds__(kBlock) void gather_prepare(const raw_t *__restrict__ X,
+                                                        raw_t *__restrict__ Xt, int C, int S,
+                                                        int c_tiles, int s_tiles,
+                                                        const int *verdicts) {
+    if (!gather_chosen(verdicts)) return;
+    constexpr int CS = kSliceBytes / sizeof(raw_t);
+    if constexpr (VEC) to_channels_last_tile<raw_t>(X, Xt, C, S, c_tiles, s_tiles, blockIdx.x, CS);
+    else to_channels_last_scalar<raw_t>(X, Xt, C, S, c_tiles, s_tiles, blockIdx.x, CS);
+}
+
+// VW elements of type T from one 16-byte load, widened.
+template <typename T>
+__device__ __forceinline__ void widen16(const u32x4 &v, float *x) {
+    if constexpr (T::bytes == 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t u = v[e];
+            x[e] = __builtin_bit_cast(float, u);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[2 * e] = T::from_raw((uint16_t)(v[e] & 0xffffu));
+            x[2 * e + 1] = T::from_raw((uint16_t)(v[e] >> 16));
+        }
+    }
+}
+
+// Raw element e of a 16-byte vector of T.
+template <typename T>
+__device__ __forceinline__ typename T::raw_t raw_at(const u32x4 &v, int e) {
+    if constexpr (T::bytes == 4) return v[e];
+    else return (uint16_t)(e & 1 ? v[e >> 1] >> 16 : v[e >> 1] & 0xffffu);
+}
+
+// Block order: with `xcd_pairs`, hardware block b runs on XCD b % 8 as that
+// XCD's (b / 8)-th block, which walks (image, slice) pairs x, x + 8, x + 16,
+// ... one after another, all row segments of a pair before the next;
+// otherwise blocks walk the pairs in order.  A block owns 128 consecutive
+// output locations of one row; lane t serves location t / 2 and channels
+// VW * (t % 2) .. + VW - 1 of the slice.
+template <int MODE, int PAD, typename T>
+__global__ __launch_bounds__(kBlock) void grid_sample_gather(SampleParams p, const void *Xt,
+                                                            const int *verdicts, int pairs,
+                                                            int tiles_per_pair, int xcd_pairs) {
+    if (!gather_chosen(verdicts)) return;
+    using raw_t = typename T::raw_t;
+    constexpr int K = AxisK<MODE>::K;
+    constexpr int TAPS = K * K;
+    constexpr int VW = 16 / T::bytes;
+    constexpr int CS = kSliceBytes / T::bytes;
+    const int b = blockIdx.x;
+    int pair, tile;
+    if (xcd_pairs) {
+        const int k = b >> 3;
+        const int pl = k / tiles_per_pair;
+        tile = k - pl * tiles_per_pair;
+        pair = pl * 8 + (b & 7);
+    } else {
+        pair = b / tiles_per_pair;
+        tile = b - pair * tiles_per_pair;
+    }
+    if (pair >= pairs) return;
+    const int nsl = p.C / CS;
+    const int n = pair / nsl, sl = pair - (pair / nsl) * nsl;
+    const int segs = (p.out_w + kGatherLocs - 1) / kGatherLocs;
+    const int oy = tile / segs, seg = tile - (tile / segs) * segs;
+    const int t = threadIdx.x;
+    const int slot = t & 1;
+    const int ox = seg * kGatherLocs + (t >> 1);
+    const bool live = ox < p.out_w;
+    const int cx = live ? ox : p.out_w - 1;
+
+    // taps and weights of the location (the tuned sampler's steps)
+    const float *gp = p.grid + ((size_t)n * p.out_count + (uint32_t)oy * (uint32_t)p.out_w + cx) * 2;
+    const float g[2] = {gp[0], gp[1]};
+    const int ext[2] = {p.in_w, p.in_h};
+    AxisTaps<K> ax[2];
+    bool any = true;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const float u = unnormalize(g[k], ext[k], p.align_corners);
+        const bool fin = __builtin_isfinite(u);
+        const float pc = fin ? clampf(u, -kCoordLimit, kCoordLimit) : 0.0f;
+        axis_taps<MODE, PAD>(pc, ext[k], p.align_corners, ax[k]);
+        bool axis_any = false;
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            ax[k].ok[j] = ax[k].ok[j] && fin;
+            axis_any = axis_any || ax[k].ok[j];
+        }
+        any = any && axis_any;
+    }
+    const uint32_t lane_bytes = (uint32_t)slot * 16;
+    uint32_t off[TAPS];
+    float w[TAPS];
+#pragma unroll
+    for (int tap = 0; tap < TAPS; ++tap) {
+        const int jx = tap % K, jy = tap / K;
+        const bool ok = any && ax[0].ok[jx] && ax[1].ok[jy];
+        off[tap] = ok ? (uint32_t)(ax[1].idx[jy] * p.in_w + ax[0].idx[jx]) * kSliceBytes + lane_bytes
+                      : GS_OOB;
+        w[tap] = (1.0f * ax[0].w[jx]) * ax[1].w[jy];
+    }
+
+    // the slice plane of (n, sl): H * W pixels of 32 bytes
+    const uint32_t plane_bytes = (uint32_t)p.in_h * (uint32_t)p.in_w * kSliceBytes;
+    const rsrc_t xr = make_rsrc((const char *)Xt + (size_t)pair * plane_bytes, plane_bytes);
+    // one resource over the image's C output planes (< 2^31 bytes); a lane's
+    // channels are per-lane offsets into it
+    const rsrc_t yr = make_rsrc((char *)p.Y + (size_t)n * p.C * p.out_plane_bytes,
+                                (uint32_t)p.C * p.out_plane_bytes);
+    const uint32_t yoff = ((uint32_t)oy * (uint32_t)p.out_w + ox) * T::bytes;
+    const int c = sl * CS + VW * slot;
+    // every tap's load is issued before any is used
+    u32x4 v[TAPS];
+#pragma unroll
+    for (int tap = 0; tap < TAPS; ++tap) v[tap] = __builtin_amdgcn_raw_buffer_load_b128(xr, (int)off[tap], 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (MODE == MODE_NEAREST) {
+#pragma unroll
+        for (int e = 0; e < VW; ++e)
+            T::store_raw(raw_at<T>(v[0], e), yr, live ? (uint32_t)(c + e) * p.out_plane_bytes + yoff : GS_OOB);
+    } else {
+        float acc[VW], x[VW];
+        widen16<T>(v[0], x);
+#pragma unroll
+        for (int e = 0; e < VW; ++e) acc[e] = w[0] * x[e];
+#pragma unroll
+        for (int tap = 1; tap < TAPS; ++tap) {
+            widen16<T>(v[tap], x);
+#pragma unroll
+            for (int e = 0; e < VW; ++e) acc[e] = fmaf(w[tap], x[e], acc[e]);
+        }
+#pragma unroll
+        for (int e = 0; e < VW; ++e)
+            T::store(acc[e], yr, live ? (uint32_t)(c + e) * p.out_plane_bytes + yoff : GS_OOB);
+    }
+}
+
+// --------------------------------------------------------------- dispatch
+
+template <int MODE, int PAD, typename T>
+static int gather_launch(const SampleParams &p, const GatherParams &g, bool vec_in, hipStream_t s) {
+    using raw_t = typename T::raw_t;
+    hipLaunchKernelGGL((gather_probe<MODE>), dim3(kProbes), dim3(kBlock), 0, s, p, (int)T::bytes,
+                       g.verdicts);
+    const int S = p.in_h * p.in_w;
+    const int c_tiles = (p.C + 63) / 64, s_tiles = (S + 63) / 64;
+    const dim3 xg((unsigned)((size_t)p.N * c_tiles * s_tiles));
+    if (vec_in)
+        hipLaunchKernelGGL((gather_prepare<raw_t, true>), xg, dim3(kBlock), 0, s, (const raw_t *)p.X,
+                           (raw_t *)g.Xt, p.C, S, c_tiles, s_tiles, (const int *)g.verdicts);
+    else
+        hipLaunchKernelGGL((gather_prepare<raw_t, false>), xg, dim3(kBlock), 0, s, (const raw_t *)p.X,
+                           (raw_t *)g.Xt, p.C, S, c_tiles, s_tiles, (const int *)g.verdicts);
+    hipLaunchKernelGGL((grid_sample_gather<MODE, PAD, T>), dim3((unsigned)g.gather_blocks), dim3(kBlock), 0,
+                       s, p, (const void *)g.Xt, (const int *)g.verdicts, g.pairs, g.tiles_per_pair,
+                       g.xcd_pairs);
+    return (int)hipGetLastError();
+}
+
+template <int MODE, int PAD>
+static int gather_by_dtype(const SampleParams &p, const GatherParams &g, int dtype, bool vec_in,
+                           hipStream_t s) {
+    switch (dtype) {
+    case 0: return gather_launch<MODE, PAD, F32>(p, g, vec_in, s);
+    case 1: return gather_launch<MODE, PAD, F16>(p, g, vec_in, s);
+    default: return gather_launch<MODE, PAD, BF16>(p, g, vec_in, s);
+    }
+}
+
+template <int MODE>
+static int gather_by_padding(const SampleParams &p, const GatherParams &g, int padding, int dtype,
+                             bool vec_in, hipStream_t s) {
+    switch (padding) {
+    case PAD_ZEROS: return gather_by_dtype<MODE, PAD_ZEROS>(p, g, dtype, vec_in, s);
+    case PAD_BORDER: return gather_by_dtype<MODE, PAD_BORDER>(p, g, dtype, vec_in, s);
+    default: return gather_by_dtype<MODE, PAD_REFLECTION>(p, g, dtype, vec_in, s);
+    }
+}
+
+int launch_grid_gather(const SampleParams &p, const GatherParams &g, int mode, int padding,
+                       int dtype, bool vec_in, hipStream_t s) {
+    switch (mode) {
+    case MODE_LINEAR: return gather_by_padding<MODE_LINEAR>(p, g, padding, dtype, vec_in, s);
+    case MODE_NEAREST: return gather_by_padding<MODE_NEAREST>(p, g, padding, dtype, vec_in, s);
+    default: return gather_by_padding<MODE_CUBIC>(p, g, padding, dtype, vec_in, s);
+    }
+}
+
+}  // namespace gs

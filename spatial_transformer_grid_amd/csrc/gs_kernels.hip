@@ -114,57 +114,6 @@ __global__ __launch_bounds__(kBlock) void affine_grid_kernel(AffineParams p) {
 
 // ------------------------------------------------------------------ taps
 
-template <int MODE>
-struct AxisK {
-    static constexpr int K = MODE == MODE_NEAREST ? 1 : (MODE == MODE_LINEAR ? 2 : 4);
-};
-
-template <int K>
-struct AxisTaps {
-    int idx[K];
-    bool ok[K];
-    float w[K];
-};
-
-// Taps of one axis of n pixels for pixel coordinate pc (finite, |pc| <= 2^24).
-template <int MODE, int PAD>
-__device__ __forceinline__ void axis_taps(float pc, int n, int ac, AxisTaps<AxisK<MODE>::K> &a) {
-    if constexpr (MODE == MODE_NEAREST) {
-        float q = pad_coordinate<PAD>(pc, n, ac);
-        int i = (int)rintf(q);
-        a.idx[0] = i;
-        a.ok[0] = (uint32_t)i < (uint32_t)n;
-        a.w[0] = 1.0f;
-    } else if constexpr (MODE == MODE_LINEAR) {
-        float q = pad_coordinate<PAD>(pc, n, ac);
-        float fl = floorf(q);
-        int i0 = (int)fl;
-        float t = q - fl;
-        a.idx[0] = i0;
-        a.idx[1] = i0 + 1;
-        a.ok[0] = (uint32_t)i0 < (uint32_t)n;
-        a.ok[1] = (uint32_t)(i0 + 1) < (uint32_t)n;
-        a.w[0] = 1.0f - t;
-        a.w[1] = t;
-    } else {
-        // cubic: the location is not padded; each tap is
-        float fl = floorf(pc);
-        int i0 = (int)fl;
-        cubic_weights(pc - fl, a.w);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            int i = i0 - 1 + j;
-            if constexpr (PAD == PAD_ZEROS) {
-                a.idx[j] = i;
-                a.ok[j] = (uint32_t)i < (uint32_t)n;
-            } else {
-                a.idx[j] = pad_tap<PAD>(i, n, ac);
-                a.ok[j] = true;
-            }
-        }
-    }
-}
-
 // Per-tap offsets of the tap product, from per-axis parts: a part of an
 // invalid tap is `bad`, and the sum saturates, so any invalid tap yields an
 // offset >= bad.
@@ -232,6 +181,7 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
     __shared__ int red[kBlock / 64][2 * R];
     __shared__ int row_lo[MAXR], row_hi[MAXR], row_xs[MAXR], row_base[MAXR + 1];
 
+    if (p.gather_verdicts && gather_chosen(p.gather_verdicts)) return;  // the gather path runs
     const int lb = xcd_logical_block_runs(p.nblocks);
     if (lb >= p.nblocks) return;
     const int tile = lb % p.tiles_per_n;

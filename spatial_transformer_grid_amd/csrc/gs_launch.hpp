@@ -41,6 +41,18 @@ struct SampleParams {
     int nblocks;               // N * cgroups * tiles_per_n
     int vec_out;               // Y rows allow one vector store per lane
     int vec_grid;              // 2D grid rows allow 16-byte loads of 4 vectors
+    const int *gather_verdicts;  // non-NULL: skip when the gather path was chosen
+};
+
+// The 2D gather path on a channels-last copy of X (workspace: kProbes verdict
+// words, then Xt in slices of 32 bytes of channels, (N, C / CS, H, W, CS)).
+struct GatherParams {
+    void *Xt;
+    int *verdicts;
+    int pairs;                 // N * C / CS (image, slice) planes
+    int tiles_per_pair;        // out_h * ceil(out_w / 128)
+    int xcd_pairs;             // blocks ordered per XCD (pairs >= 8)
+    int gather_blocks;         // launch size
 };
 
 // Outputs per lane Q (consecutive along W) and the LDS bytes for staging.
@@ -195,6 +207,8 @@ enum { DC_PATH_DIRECT = 0, DC_PATH_GATHER = 1, DC_PATH_CL = 2 };
 // launch.  `rank` is 2 or 3; `dtype` 0 f32, 1 f16, 2 bf16; `vec_in` selects
 // 16-byte staging loads (input rows a whole number of 16-byte chunks).
 int launch_grid_sample(const SampleParams &p, int rank, bool fused, int mode, int padding,
+                       int dtype, bool vec_in, hipStream_t stream);
+int launch_grid_gather(const SampleParams &p, const GatherParams &g, int mode, int padding,
                        int dtype, bool vec_in, hipStream_t stream);
 int launch_affine_grid(const AffineParams &p, int rank, hipStream_t stream);
 // `rank` 1..6 spatial axes; `double_grid`: the grid is double (coordinates in

@@ -35,7 +35,8 @@ def test_header_declares_the_expected_entry_points():
     assert declared_functions() == sorted([
         "gs_abi_version", "gs_status_string", "gs_affine_grid", "gs_grid_sample_2d",
         "gs_grid_sample_3d", "gs_affine_grid_sample_fused", "gs_resize", "gs_resize_output_shape",
-        "gs_grid_sample", "gs_deform_conv", "gs_deform_conv_workspace_size"])
+        "gs_grid_sample", "gs_deform_conv", "gs_deform_conv_workspace_size",
+        "gs_grid_sample_2d_ws", "gs_grid_sample_2d_workspace_size"])
 
 
 def test_library_exports_every_declared_symbol(gs):
@@ -314,3 +315,19 @@ def test_deform_conv_workspace_size(gs):
     assert ws([1, 16, 7, 7, 7], [16, 16, 3, 3, 3], gs.GS_F32) == 0
     with pytest.raises(gs.GSError):
         ws([1, 16, 2, 7], [16, 16, 3, 3], gs.GS_F32)                          # input too small
+
+
+def test_grid_sample_2d_workspace_size(gs):
+    """256 bytes of probe verdicts plus X in channels-last slices; none when
+    the channels do not fill 32-byte slices, for types the gather path does
+    not take, or when an image or its output planes exceed 2^31 bytes."""
+    ws = gs.grid_sample_2d_workspace_size
+    assert ws((16, 128, 256, 256), (16, 256, 256, 2), gs.GS_F32) == 256 + 16 * 128 * 256 * 256 * 4
+    assert ws((2, 16, 5, 7), (2, 3, 4, 2), gs.GS_BF16) == 256 + 2 * 16 * 35 * 2
+    assert ws((2, 8, 5, 7), (2, 3, 4, 2), gs.GS_F32) == 256 + 2 * 8 * 35 * 4
+    assert ws((2, 12, 5, 7), (2, 3, 4, 2), gs.GS_F32) == 0     # 48-byte pixel runs
+    assert ws((2, 8, 5, 7), (2, 3, 4, 2), gs.GS_F16) == 0      # 16-byte pixel runs
+    assert ws((2, 8, 5, 7), (2, 3, 4, 2), gs.GS_F64) == 0
+    assert ws((1, 64, 8192, 8192), (1, 4, 4, 2), gs.GS_F32) == 0  # 16 GiB image
+    with pytest.raises(gs.GSError):
+        ws((2, 8, 5, 7), (3, 3, 4, 2), gs.GS_F32)              # batch mismatch

@@ -1,0 +1,170 @@
+"""The 2-D gather path (gs_grid_sample_2d_ws) against the oracle and against
+the plain sampler.
+
+* Random-flow grids (locations i.i.d. over [-1.2, 1.2]): the device probe
+  must choose the gather path (its 64 verdict words, the workspace's first
+  256 bytes, sum to 32 or more), and the result must equal gs_grid_sample_2d
+  bit for bit -- the same taps, weights and fp32 sums in the same order -- and
+  the oracle within the tolerances of tests/parity.py.  Every mode, padding,
+  align_corners and element type; one, three and many 32-byte channel slices,
+  fewer (image, slice) planes than XCDs and more; output rows that end in a
+  ragged 128-location segment; non-finite locations.
+* Near-identity affine grids: the probe keeps the staged sampler (verdicts
+  sum below 32), and the result equals gs_grid_sample_2d bit for bit.  So do
+  random flows over images small enough for a tile's LDS slot.
+* Without a workspace, or one too small, the call is gs_grid_sample_2d.
+"""
+
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from parity import check, from_gpu, note, torch_mod, x_to_gpu
+
+pytestmark = pytest.mark.gpu
+
+MODES = ["nearest", "linear", "cubic"]
+PADS = ["zeros", "border", "reflection"]
+
+
+@pytest.fixture(scope="module")
+def gsa():
+    torch = torch_mod()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import spatial_transformer_grid_amd as gsa
+
+    gsa.lib()
+    return gsa
+
+
+def verdict_sum(ws):
+    return int(ws[:256].cpu().numpy().view(np.int32)[:64].sum())
+
+
+def run_case(gsa, X32, G, kind, mode, pad, ac, expect_gather, what):
+    torch = torch_mod()
+    note("gather %s %s %s %s ac=%d X=%s G=%s" % (what, kind, mode, pad, ac, X32.shape, G.shape))
+    Xd, Xo = x_to_gpu(X32, kind)
+    Gd = torch.from_numpy(np.ascontiguousarray(G, np.float32)).cuda()
+    need = gsa.grid_sample_2d_workspace_size(tuple(X32.shape), tuple(G.shape), gsa.dtype_code(Xd))
+    assert need > 0
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    Yw = gsa.grid_sample(Xd, Gd, mode, pad, ac, workspace=ws)
+    Yp = gsa.grid_sample(Xd, Gd, mode, pad, ac)
+    torch.cuda.synchronize()
+    vs = verdict_sum(ws)
+    assert (vs >= 32) == expect_gather, "verdicts %d" % vs
+    a = Yw.view(torch.int16 if kind != "f32" else torch.int32).cpu().numpy()
+    b = Yp.view(torch.int16 if kind != "f32" else torch.int32).cpu().numpy()
+    ref = oracle.grid_sample(Xo, G, mode, pad, ac)
+    if not np.array_equal(a, b):
+        bad = np.argwhere(a != b)
+        i = tuple(bad[0])
+        raise AssertionError("%s: %d elements differ from the plain sampler, first %s: %r vs %r, "
+                             "oracle %r, location %r" % (what, len(bad), i, float(Yw[i]),
+                                                         float(Yp[i]), ref[i], G[i[0], i[2], i[3]]))
+    check(from_gpu(Yw), ref, mode, kind, float(np.abs(Xo).max()), what)
+
+
+def random_grid(rng, n, ho, wo):
+    return rng.uniform(-1.2, 1.2, (n, ho, wo, 2)).astype(np.float32)
+
+
+# Input planes larger than a tile's 16 KB LDS slot (fp32 and half), so that
+# scattered locations cannot be staged.
+CASES = [
+    # n, c (f32), c (half), h, w, ho, wo
+    (2, 16, 32, 96, 104, 9, 140),    # two row segments, the second ragged; 4 planes
+    (1, 24, 48, 100, 110, 17, 64),   # three slices, one plane row segment
+    (3, 64, 128, 91, 101, 5, 13),    # 24 planes (XCD order), narrow rows
+]
+
+
+@pytest.mark.parametrize("kind,ci,mode,pad,ac", list(itertools.product(
+    ["f32", "f16", "bf16"], range(len(CASES)), MODES, PADS, [0, 1])))
+def test_random_flow_takes_the_gather_path(gsa, kind, ci, mode, pad, ac):
+    n, c32, c16, h, w, ho, wo = CASES[ci]
+    c = c32 if kind == "f32" else c16
+    rng = np.random.default_rng(1000 + ci)
+    X = rng.uniform(-1, 1, (n, c, h, w)).astype(np.float32)
+    G = random_grid(rng, n, ho, wo)
+    run_case(gsa, X, G, kind, mode, pad, ac, True, "case %d" % ci)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_non_finite_locations(gsa, mode):
+    rng = np.random.default_rng(7)
+    X = rng.uniform(-1, 1, (1, 8, 100, 100)).astype(np.float32)
+    G = random_grid(rng, 1, 6, 20)
+    G[0, 0, :4, 0] = np.nan
+    G[0, 1, 2:5, 1] = np.inf
+    G[0, 2, 7, :] = -np.inf
+    run_case(gsa, X, G, "f32", mode, "reflection", 1, True, "non-finite")
+
+
+def test_many_slices(gsa):
+    """Few output rows, 32 channel slices walked in XCD order."""
+    rng = np.random.default_rng(8)
+    X = rng.uniform(-1, 1, (1, 256, 90, 91)).astype(np.float32)
+    G = random_grid(rng, 1, 2, 40)
+    run_case(gsa, X, G, "f32", "cubic", "border", 0, True, "many slices")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_affine_grid_keeps_the_staged_sampler(gsa, mode):
+    rng = np.random.default_rng(9)
+    X = rng.uniform(-1, 1, (2, 16, 40, 48)).astype(np.float32)
+    theta = np.tile(np.array([[0.9, 0.05, 0.02], [-0.04, 1.1, -0.03]], np.float32), (2, 1, 1))
+    G = oracle.affine_grid(theta, (2, 16, 36, 44), 0).astype(np.float32)
+    run_case(gsa, X, G, "f32", mode, "zeros", 0, False, "affine")
+
+
+def test_small_image_keeps_the_staged_sampler(gsa):
+    """A whole 23 x 37 plane fits a tile's LDS slot: scattered locations are
+    still staged."""
+    rng = np.random.default_rng(12)
+    X = rng.uniform(-1, 1, (2, 16, 23, 37)).astype(np.float32)
+    G = random_grid(rng, 2, 9, 70)
+    run_case(gsa, X, G, "f32", "linear", "border", 1, False, "small image")
+
+
+def test_without_workspace_is_the_plain_sampler(gsa):
+    torch = torch_mod()
+    rng = np.random.default_rng(10)
+    X = torch.from_numpy(rng.uniform(-1, 1, (1, 16, 100, 100)).astype(np.float32)).cuda()
+    G = torch.from_numpy(random_grid(rng, 1, 8, 8)).cuda()
+    a = gsa.grid_sample(X, G, "cubic", "zeros", 0, workspace=torch.empty(0, dtype=torch.uint8,
+                                                                          device="cuda"))
+    small = torch.zeros(64, dtype=torch.uint8, device="cuda")
+    b = gsa.grid_sample(X, G, "cubic", "zeros", 0, workspace=small)
+    c = gsa.grid_sample(X, G, "cubic", "zeros", 0)
+    torch.cuda.synchronize()
+    assert torch.equal(a, c) and torch.equal(b, c)
+    assert int(small.sum()) == 0            # too small: untouched
+
+
+def test_full_size_random_flow_sampled(gsa):
+    """The flow2d_bicubic workload at its full size through the gather path:
+    the verdicts, bit-equality with the plain sampler, and 4,096 sampled
+    outputs against the oracle computed one by one."""
+    torch = torch_mod()
+    wl = W.WORKLOADS["flow2d_bicubic"]
+    inp = W.make_inputs(wl)
+    note("gather full-size flow2d_bicubic")
+    X = torch.from_numpy(inp["X"]).cuda()
+    G = torch.from_numpy(inp["grid"]).cuda()
+    Yw = gsa.grid_sample(X, G, wl.mode, wl.padding, wl.align_corners, workspace="auto")
+    Yp = gsa.grid_sample(X, G, wl.mode, wl.padding, wl.align_corners)
+    torch.cuda.synchronize()
+    assert torch.equal(Yw, Yp)
+    rng = np.random.default_rng(11)
+    flat = rng.integers(0, Yw.numel(), 4096)
+    ref = oracle.grid_sample_points(inp["X"], inp["grid"], flat, wl.mode, wl.padding,
+                                    wl.align_corners)
+    got = Yw.reshape(-1)[torch.from_numpy(flat).cuda()].double().cpu().numpy()
+    assert np.abs(got - ref).max() <= 1e-4 * float(np.abs(inp["X"]).max())
+    del X, G, Yw, Yp
