@@ -209,6 +209,16 @@ def run_paths(torch, gsa, flush_buf):
         us, _ = time_kernel(torch, lambda: gsa.grid_sample(X, grid, mode, pad, 0, out=Y), 30)
         record("stn2d_batch/%s-%s" % (mode, pad), w.name, "gs_grid_sample_2d", us, outputs,
                X.numel() * 4, fp, gbytes + outputs * 4)
+    # the same call with a workspace: the probe keeps the staged sampler (the
+    # difference is the probe and two launches that return at once)
+    ws = torch.empty(gsa.grid_sample_2d_workspace_size(tuple(X.shape), tuple(grid.shape), 0),
+                     dtype=torch.uint8, device="cuda")
+    fp = footprint_elements(g_host, (h, wd), "linear", "zeros", 0) * c * 4
+    us, _ = time_kernel(torch, lambda: gsa.grid_sample(X, grid, "linear", "zeros", 0, out=Y,
+                                                       workspace=ws), 30)
+    record("stn2d_batch/linear-zeros-workspace", w.name, "gs_grid_sample_2d_ws (staged chosen)", us,
+           outputs, X.numel() * 4, fp, gbytes + outputs * 4)
+    del ws
     fp = footprint_elements(g_host, (h, wd), "linear", "zeros", 0) * c * 4
     us, _ = time_kernel(torch, lambda: gsa.affine_grid_sample_fused(th, X, w.out_spatial, "linear",
                                                                       "zeros", 0, out=Y), 30)
@@ -227,7 +237,16 @@ def run_paths(torch, gsa, flush_buf):
     us, _ = time_kernel(torch, lambda: gsa.grid_sample(X, G, "cubic", "reflection", 1, out=Y), 20)
     record("flow2d_bicubic/cubic-reflection", w.name, "gs_grid_sample_2d", us, w.outputs,
            X.numel() * 4, fp, G.numel() * 4 + w.outputs * 4)
-    del X, Y, G, inp
+    # with a workspace: probe, sliced channels-last copy of X, gather (the
+    # whole call is timed, the copy included)
+    ws = torch.empty(gsa.grid_sample_2d_workspace_size(tuple(X.shape), tuple(G.shape), 0),
+                     dtype=torch.uint8, device="cuda")
+    us, _ = time_kernel(torch, lambda: gsa.grid_sample(X, G, "cubic", "reflection", 1, out=Y,
+                                                       workspace=ws), 20)
+    record("flow2d_bicubic/cubic-reflection-workspace", w.name,
+           "gs_grid_sample_2d_ws (gather path)", us, w.outputs, X.numel() * 4, fp,
+           G.numel() * 4 + w.outputs * 4)
+    del X, Y, G, inp, ws
 
     # 3D volumetric, fused trilinear + border (working set fits the MALL:
     # report the flushed time as the figure and the warm one beside it)

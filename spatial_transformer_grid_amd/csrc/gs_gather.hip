@@ -32,6 +32,7 @@
 #include <limits.h>
 #include <stdint.h>
 
+
 namespace gs {
 
 constexpr int kGatherLocs = 128;     // output locations per block (one row segment)
@@ -75,16 +76,24 @@ __global__ __launch_bounds__(kBlock) void gather_probe(SampleParams p, int elem_
     }
 }
 
-// The sliced channels-last copy, when the probe chose gathering.
+// The copy of X, which the probe may not choose, uses one block per resident
+// slot of the device (one round of blocks covers it) and strides over its
+// tiles, so that skipping it costs little.
+
+// The sliced channels-last copy, when the probe chose gathering: tiles
+// blockIdx.x, + gridDim.x, ...
 template <typename raw_t, bool VEC>
 __global__ __launch_bounds__(kBlock) void gather_prepare(const raw_t *__restrict__ X,
                                                         raw_t *__restrict__ Xt, int C, int S,
-                                                        int c_tiles, int s_tiles,
+                                                        int c_tiles, int s_tiles, int tiles,
                                                         const int *verdicts) {
     if (!gather_chosen(verdicts)) return;
     constexpr int CS = kSliceBytes / sizeof(raw_t);
-    if constexpr (VEC) to_channels_last_tile<raw_t>(X, Xt, C, S, c_tiles, s_tiles, blockIdx.x, CS);
-    else to_channels_last_scalar<raw_t>(X, Xt, C, S, c_tiles, s_tiles, blockIdx.x, CS);
+    for (int b = blockIdx.x; b < tiles; b += gridDim.x) {
+        if constexpr (VEC) to_channels_last_tile<raw_t>(X, Xt, C, S, c_tiles, s_tiles, b, CS);
+        else to_channels_last_scalar<raw_t>(X, Xt, C, S, c_tiles, s_tiles, b, CS);
+        __syncthreads();  // the tile's LDS reads are done before the next tile's writes
+    }
 }
 
 // VW elements of type T from one 16-byte load, widened.
@@ -119,16 +128,36 @@ __device__ __forceinline__ typename T::raw_t raw_at(const u32x4 &v, int e) {
 // output locations of one row; lane t serves location t / 2 and channels
 // VW * (t % 2) .. + VW - 1 of the slice.
 template <int MODE, int PAD, typename T>
+__device__ __forceinline__ void gather_block(const SampleParams &p, const void *Xt, int pairs,
+                                             int tiles_per_pair, int xcd_pairs, int b);
+
+// Hardware block b covers kGatherTPB consecutive logical blocks (of its
+// XCD's sequence when xcd_pairs): half as many blocks to dispatch, or to
+// skip, and measured no slower than one (four or more per block were).
+constexpr int kGatherTPB = 2;
+
+template <int MODE, int PAD, typename T>
 __global__ __launch_bounds__(kBlock) void grid_sample_gather(SampleParams p, const void *Xt,
                                                             const int *verdicts, int pairs,
-                                                            int tiles_per_pair, int xcd_pairs) {
+                                                            int tiles_per_pair, int xcd_pairs,
+                                                            int blocks) {
     if (!gather_chosen(verdicts)) return;
+    const int b = blockIdx.x;
+    for (int j = 0; j < kGatherTPB; ++j) {
+        // keep the XCD (b % 8) and take the next logical blocks of its sequence
+        const int lb = xcd_pairs ? ((b >> 3) * kGatherTPB + j) * 8 + (b & 7) : b * kGatherTPB + j;
+        if (lb < blocks) gather_block<MODE, PAD, T>(p, Xt, pairs, tiles_per_pair, xcd_pairs, lb);
+    }
+}
+
+template <int MODE, int PAD, typename T>
+__device__ __forceinline__ void gather_block(const SampleParams &p, const void *Xt, int pairs,
+                                             int tiles_per_pair, int xcd_pairs, int b) {
     using raw_t = typename T::raw_t;
     constexpr int K = AxisK<MODE>::K;
     constexpr int TAPS = K * K;
     constexpr int VW = 16 / T::bytes;
     constexpr int CS = kSliceBytes / T::bytes;
-    const int b = blockIdx.x;
     int pair, tile;
     if (xcd_pairs) {
         const int k = b >> 3;
@@ -219,6 +248,17 @@ __global__ __launch_bounds__(kBlock) void grid_sample_gather(SampleParams p, con
 
 // --------------------------------------------------------------- dispatch
 
+// Blocks of `kernel` the device holds at once, a multiple of 8 (whole XCD
+// rounds), at least 8.
+static int resident_blocks(const void *kernel) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kBlock, 0) != hipSuccess)
+        return 2048;
+    return max(8, (per_cu * cus) / 8 * 8);
+}
+
 template <int MODE, int PAD, typename T>
 static int gather_launch(const SampleParams &p, const GatherParams &g, bool vec_in, hipStream_t s) {
     using raw_t = typename T::raw_t;
@@ -226,16 +266,22 @@ static int gather_launch(const SampleParams &p, const GatherParams &g, bool vec_
                        g.verdicts);
     const int S = p.in_h * p.in_w;
     const int c_tiles = (p.C + 63) / 64, s_tiles = (S + 63) / 64;
-    const dim3 xg((unsigned)((size_t)p.N * c_tiles * s_tiles));
+    const int tiles = p.N * c_tiles * s_tiles;
+    const void *prep = vec_in ? (const void *)gather_prepare<raw_t, true> : (const void *)gather_prepare<raw_t, false>;
+    const dim3 xg((unsigned)min(tiles, resident_blocks(prep)));
     if (vec_in)
         hipLaunchKernelGGL((gather_prepare<raw_t, true>), xg, dim3(kBlock), 0, s, (const raw_t *)p.X,
-                           (raw_t *)g.Xt, p.C, S, c_tiles, s_tiles, (const int *)g.verdicts);
+                           (raw_t *)g.Xt, p.C, S, c_tiles, s_tiles, tiles, (const int *)g.verdicts);
     else
         hipLaunchKernelGGL((gather_prepare<raw_t, false>), xg, dim3(kBlock), 0, s, (const raw_t *)p.X,
-                           (raw_t *)g.Xt, p.C, S, c_tiles, s_tiles, (const int *)g.verdicts);
-    hipLaunchKernelGGL((grid_sample_gather<MODE, PAD, T>), dim3((unsigned)g.gather_blocks), dim3(kBlock), 0,
-                       s, p, (const void *)g.Xt, (const int *)g.verdicts, g.pairs, g.tiles_per_pair,
-                       g.xcd_pairs);
+                           (raw_t *)g.Xt, p.C, S, c_tiles, s_tiles, tiles, (const int *)g.verdicts);
+    // one block per logical block: the dispatcher hands each XCD its blocks
+    // in order, which keeps the XCD on one slice plane at a time (a
+    // grid-stride loop lets blocks drift apart and was 1.5x slower)
+    const dim3 gg((unsigned)((g.gather_blocks + 8 * kGatherTPB - 1) / (8 * kGatherTPB) * 8));
+    hipLaunchKernelGGL((grid_sample_gather<MODE, PAD, T>), gg, dim3(kBlock), 0, s, p, (const void *)g.Xt,
+                       (const int *)g.verdicts, g.pairs, g.tiles_per_pair, g.xcd_pairs,
+                       g.gather_blocks);
     return (int)hipGetLastError();
 }
 
