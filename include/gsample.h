@@ -406,8 +406,9 @@ int gs_deform_conv(const void *X, int dtype, const int64_t *x_shape, int x_rank,
  * Bytes of workspace gs_deform_conv uses for these shapes and attributes (the
  * same arguments, same validation and errors), 0 when no workspace helps:
  * N*C*D1*..*Dr elements for X, plus group * (oC/group rounded up to 32) *
- * k1*..*kr * (C/group rounded up to 32) for W, each part rounded up to 256
- * bytes.  Written to *bytes (host).
+ * k1*..*kr * (C/group rounded up to the chunk, 64 for fp16 / bf16 with more
+ * than 128 output channels per group, else 32) for W, each part rounded up
+ * to 256 bytes.  Written to *bytes (host).
  */
 int gs_deform_conv_workspace_size(int dtype, const int64_t *x_shape, int x_rank,
                                   const int64_t *w_shape, const int64_t *strides,

@@ -534,9 +534,16 @@ bool cl_applies(int r, int dtype, int64_t Cg, int64_t Cog) {
     return r == 2 && dtype != GS_F64 && Cg % 8 == 0 && Cog % 8 == 0;
 }
 
-// W packed per conv group: output channels rounded up to 32, channels to 32
-int64_t cl_w2_elems(int64_t group, int64_t OCg, int64_t Cg, int64_t K) {
-    return group * ((OCg + 31) / 32 * 32) * K * ((Cg + 31) / 32 * 32);
+// Channels per chunk of the channels-last kernel: 64 for fp16 / bf16 with
+// more than 128 output channels per group (its 8-wave blocks), else 32.
+int64_t cl_chunk(int dtype, int64_t OCg) {
+    return (dtype == GS_F16 || dtype == GS_BF16) && OCg > 128 ? 64 : 32;
+}
+
+// W packed per conv group: output channels rounded up to 32, channels to the
+// chunk size
+int64_t cl_w2_elems(int64_t group, int64_t OCg, int64_t Cg, int64_t K, int64_t tk) {
+    return group * ((OCg + 31) / 32 * 32) * K * ((Cg + tk - 1) / tk * tk);
 }
 
 // Shared validation of gs_deform_conv and gs_deform_conv_workspace_size:
@@ -623,11 +630,12 @@ int deform_setup(int dtype, const int64_t *x_shape, int x_rank, const int64_t *w
     p.x_plane_bytes = (uint32_t)(plane * bytes);
     p.w_bytes = (uint32_t)(OC * Cg * K * bytes);
     p.npos = (uint32_t)npos;
-    p.Cgp = (int)((Cg + 31) / 32 * 32);
+    const int64_t tk = cl_chunk(dtype, OCg);
+    p.Cgp = (int)((Cg + tk - 1) / tk * tk);
     p.K2 = (int)(K * p.Cgp);
     p.x_img_bytes = (uint32_t)(C * plane * bytes);
     p.Rg = (int)((OCg + 31) / 32);
-    const int64_t w2 = cl_w2_elems(group, OCg, Cg, K) * bytes;
+    const int64_t w2 = cl_w2_elems(group, OCg, Cg, K, tk) * bytes;
     p.w2_bytes = w2 <= kInt32Max ? (uint32_t)w2 : 0;
     p.w2_group_bytes = (uint32_t)(w2 / group);
     r_out = r;

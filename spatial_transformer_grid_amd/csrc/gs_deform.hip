@@ -24,6 +24,8 @@
 
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace gs {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
@@ -367,16 +369,16 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_mfma(DeformParams p) {
 // to match the chunk order, zero beyond Cg.  Summing K in another order than the
 // oracle only changes fp32 rounding order.
 
-// Chunk i of the channels-last kernel covers one kernel position and 32
-// channels of the conv group (Cgp = Cg rounded up to 32).  The table path
-// walks the channel slices outermost (a slice's corners stay in L1 across
-// the kernel positions), the other path the kernel positions outermost (its
-// corners change once per position).
-__device__ __forceinline__ void chunk_coords(int i, int KK, int cpt, bool slice_major, int &tap,
-                                             int &c0) {
+// Chunk i of the channels-last kernel covers one kernel position and tk (32
+// or 64) channels of the conv group (Cgp = Cg rounded up to tk).  The table
+// path walks the channel slices outermost (a slice's corners stay in L1
+// across the kernel positions), the other path the kernel positions
+// outermost (its corners change once per position).
+__device__ __forceinline__ void chunk_coords(int i, int KK, int cpt, bool slice_major, int tk,
+                                             int &tap, int &c0) {
     const int sl = slice_major ? i / KK : i - (i / cpt) * cpt;
     tap = slice_major ? i - sl * KK : i / cpt;
-    c0 = sl * DC_TK;
+    c0 = sl * tk;
 }
 
 // W (OC, Cg, KK) -> W2, packed in the order the matrix cores take the A
@@ -384,15 +386,17 @@ __device__ __forceinline__ void chunk_coords(int i, int KK, int cpt, bool slice_
 // 32), chunk i and load v, lane l's 16 bytes at
 // ((((G * Rg + R) * nch + i) * AV + v) * 64 + l) * 16.  Lane l holds row
 // R * 32 + l % 32 and, within the chunk, k = 16 v + 8 (l / 32) + 0..7 for
-// fp16 / bf16, k = 16 (l / 32) + 4 v + 0..3 for fp32.  Rows past OCg and
-// channels past Cg are zero.  One thread per 16-byte unit.
+// fp16 / bf16 (AV = tk / 16), k = 16 (l / 32) + 4 v + 0..3 for fp32 (tk =
+// 32, AV = 4).  Rows past OCg and channels past Cg are zero.  One thread per
+// 16-byte unit.
 template <typename raw_t, int AV>
 __device__ __forceinline__ void w_pack_unit(const raw_t *__restrict__ W, raw_t *__restrict__ W2,
                                             int group, int OCg, int Cg, int KK, int Cgp,
                                             int slice_major, uint32_t j) {
     constexpr int EPL = 16 / sizeof(raw_t);         // elements per lane and load
+    constexpr int TKC = EPL == 4 ? 32 : 16 * AV;    // chunk size
     const int Rg = (OCg + 31) / 32;
-    const int cpt = Cgp / DC_TK, nch = KK * cpt;
+    const int cpt = Cgp / TKC, nch = KK * cpt;
     // W2 holds fewer than 2^31 bytes, so 32-bit indices suffice
     const uint32_t units = (uint32_t)group * Rg * nch * AV * 64;
     if (j >= units) return;
@@ -406,7 +410,7 @@ __device__ __forceinline__ void w_pack_unit(const raw_t *__restrict__ W, raw_t *
     const int G = (int)(u / (uint32_t)Rg);
     const int row = R * 32 + (l & 31);
     int tap, c0;
-    chunk_coords(i, KK, cpt, slice_major != 0, tap, c0);
+    chunk_coords(i, KK, cpt, slice_major != 0, TKC, tap, c0);
     const int k0 = EPL == 4 ? 16 * (l >> 5) + 4 * v : 16 * v + 8 * (l >> 5);
     const raw_t *wrow = W + (((size_t)G * OCg + row) * Cg) * KK + tap;
     u32x4 out;
@@ -505,7 +509,7 @@ __device__ __forceinline__ void mfma_chunk_regs(const u32x4 (&a)[MB][AV], const 
         }
     } else {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int ks = 0; ks < AV; ++ks) {
             u32x4 bv[2];
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb)
@@ -527,15 +531,22 @@ __device__ __forceinline__ void mfma_chunk_regs(const u32x4 (&a)[MB][AV], const 
     }
 }
 
-template <typename T, int MB, bool TABLE>
-__global__ __launch_bounds__(kBlock) void deform_conv2d_cl(DeformParams p) {
+// NW waves per block (4, or 8 for fp16 / bf16 with 256 output channels per
+// block), chunks of TK = 8 * NW channels, loads DEPTH chunks ahead (8 waves:
+// one chunk ahead, so that four waves fit a SIMD).
+template <typename T, int MB, bool TABLE, int NW>
+__global__ __launch_bounds__(64 * NW) void deform_conv2d_cl(DeformParams p) {
     using raw_t = typename T::raw_t;
-    constexpr int TM = 4 * 32 * MB;
+    constexpr int NT = 64 * NW;                     // threads
+    constexpr int TK = 8 * NW;                      // channels per chunk
+    constexpr int DEPTH = NW == 8 ? 1 : 2;
+    constexpr int TM = NW * 32 * MB;
     constexpr int PAD = 16 / T::bytes;
-    constexpr int LK = DC_TK + PAD;
+    constexpr int LK = TK + PAD;
     constexpr int TE = DC_TABLE * DC_TN;
     constexpr int VPC = 8 * T::bytes / 16;          // 16-byte loads per corner
-    constexpr int AV = T::bytes == 4 ? 4 : 2;       // 16-byte A loads per 32-row block and chunk
+    constexpr int AV = T::bytes == 4 ? 4 : TK / 16; // 16-byte A loads per 32-row block and chunk
+    static_assert(T::bytes == 2 || NW == 4, "fp32 runs four waves");
     __shared__ __align__(16) raw_t Bs[2][DC_TN * LK];  // column tiles, double-buffered
     // corner byte offsets of the pixel's channel run in Xt (out-of-range
     // offset for corners outside the image) and mask-folded weights
@@ -561,7 +572,7 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_cl(DeformParams p) {
     // This thread samples output position pos and channels c0 + 8 cgp ..
     // +7 of each chunk: the four lanes of a position read one 64-byte run of
     // a pixel, so a wave's load touches 16 pixels.
-    const int cgp = t & 3;
+    const int cgp = (t & 3) + 4 * (t >> 8);
     const int pos = (t >> 2) & (DC_TN - 1);
     const int o = nt * DC_TN + pos;
     const bool o_ok = o < npos;
@@ -569,7 +580,7 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_cl(DeformParams p) {
 
     if constexpr (TABLE) {
         const int entries = p.og_span * KK * DC_TN;
-        for (int e = t; e < entries; e += kBlock) {
+        for (int e = t; e < entries; e += NT) {
             const int gt = e / DC_TN;
             const int gi = gt / KK, tap = gt - gi * KK;
             const int oe = nt * DC_TN + (e & (DC_TN - 1));
@@ -600,12 +611,12 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_cl(DeformParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[mb][nb][r] = 0.0f;
 
-    const int cpt = p.Cgp / DC_TK;                  // chunks per kernel position
+    const int cpt = p.Cgp / TK;                     // chunks per kernel position
     const int nch = KK * cpt;
-    // Two register sets: chunk i's loads were issued two chunks earlier,
-    // into set i % 2.
-    u32x4 a0[MB][AV], a1[MB][AV];
-    u32x4 x0[4][VPC], x1[4][VPC];
+    // DEPTH register sets: chunk i's loads were issued DEPTH chunks earlier,
+    // into set i % DEPTH.
+    u32x4 a0[MB][AV], a1[DEPTH == 2 ? MB : 1][AV];
+    u32x4 x0[4][VPC], x1[DEPTH == 2 ? 4 : 1][VPC];
     float q0[4], q1[4];
     Corners cc;                                     // corners of (ctap, cg), non-table path
     int ctap = -1, cg = -1;
@@ -631,7 +642,7 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_cl(DeformParams p) {
     auto load_x = [&](int i, u32x4 (&xpre)[4][VPC], float (&wq)[4]) {
         i = min(i, nch - 1);
         int tap, c0;
-        chunk_coords(i, KK, cpt, TABLE, tap, c0);
+        chunk_coords(i, KK, cpt, TABLE, TK, tap, c0);
         const int cl = c0 + 8 * cgp;
         const bool cv = cl < p.Cg;                  // past Cg: padding, W2 is zero there
         const int c = G * p.Cg + (cv ? cl : 0);
@@ -668,9 +679,9 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_cl(DeformParams p) {
         }
     };
 
-    // loads issued per chunk: chunk i's are complete once no more than one
-    // chunk's worth (chunk i + 1's) is outstanding
-    constexpr int kLoads = MB * AV + 4 * VPC;
+    // loads issued per chunk: chunk i's are complete once no more than
+    // DEPTH - 1 chunks' worth is outstanding
+    constexpr int kLoads = (DEPTH - 1) * (MB * AV + 4 * VPC);
     static_assert(kLoads < 64, "vmcnt field");
     // One chunk: sample its columns into this chunk's LDS buffer; issue the
     // corner loads of the chunk two ahead into the registers just read;
@@ -703,22 +714,26 @@ __global__ __launch_bounds__(kBlock) void deform_conv2d_cl(DeformParams p) {
         // Every wave's column writes of chunk i are visible, and every wave
         // has finished reading the other buffer (chunk i - 1).
         __syncthreads();
-        load_x(i + 2, xpre, wq);
+        load_x(i + DEPTH, xpre, wq);
         mfma_chunk_regs<T, MB, LK, AV>(a, bs, acc, lane);
         __builtin_amdgcn_sched_barrier(0);
-        load_a(i + 2, a);
+        load_a(i + DEPTH, a);
     };
 
     load_x(0, x0, q0);
     load_a(0, a0);
-    load_x(1, x1, q1);
-    load_a(1, a1);
-    int i = 0;
-    for (; i + 1 < nch; i += 2) {
-        step(i, a0, x0, q0);
-        step(i + 1, a1, x1, q1);
+    if constexpr (DEPTH == 2) {
+        load_x(1, x1, q1);
+        load_a(1, a1);
+        int i = 0;
+        for (; i + 1 < nch; i += 2) {
+            step(i, a0, x0, q0);
+            step(i + 1, a1, x1, q1);
+        }
+        if (i < nch) step(i, a0, x0, q0);
+    } else {
+        for (int i = 0; i < nch; ++i) step(i, a0, x0, q0);
     }
-    if (i < nch) step(i, a0, x0, q0);
     store_tile<T, MB>(p, acc, n, oc0, m_valid, nt, wave, lane);
 }
 
@@ -869,26 +884,41 @@ static int cl_launch(const DeformParams &p, hipStream_t s) {
     const int c_tiles = (p.C + 63) / 64, s_tiles = (S + 63) / 64;
     const int x_blocks = (int)((size_t)p.N * c_tiles * s_tiles);
     const bool table = p.og_span * KK <= DC_TABLE;
-    constexpr int AV = T::bytes == 4 ? 4 : 2;
+    const bool wide = p.OCg > 128;
+    const bool eight = T::bytes == 2 && wide;       // 8 waves, chunks of 64 channels
     const int w_blocks = (int)(((size_t)p.w2_bytes / 16 + kBlock - 1) / kBlock);
     constexpr int VW = 16 / sizeof(raw_t);
     // C is a multiple of 8 on this path
     const dim3 pgrid((unsigned)(x_blocks + w_blocks));
-    if (S % VW == 0 && (uintptr_t)p.X % 16 == 0)
-        hipLaunchKernelGGL((cl_prepare<raw_t, AV, true>), pgrid, dim3(kBlock), 0, s, (const raw_t *)p.X,
-                           (raw_t *)p.Xt, p.C, S, c_tiles, s_tiles, x_blocks, (const raw_t *)p.Wt,
-                           (raw_t *)p.W2, p.group, p.OCg, p.Cg, KK, p.Cgp, (int)table);
-    else
-        hipLaunchKernelGGL((cl_prepare<raw_t, AV, false>), pgrid, dim3(kBlock), 0, s, (const raw_t *)p.X,
-                           (raw_t *)p.Xt, p.C, S, c_tiles, s_tiles, x_blocks, (const raw_t *)p.Wt,
-                           (raw_t *)p.W2, p.group, p.OCg, p.Cg, KK, p.Cgp, (int)table);
+    const bool vec = S % VW == 0 && (uintptr_t)p.X % 16 == 0;
+    constexpr int AV4 = T::bytes == 4 ? 4 : 2;      // chunks of 32 channels
+    auto prepare = [&](auto av) {
+        constexpr int AV = decltype(av)::value;
+        if (vec)
+            hipLaunchKernelGGL((cl_prepare<raw_t, AV, true>), pgrid, dim3(kBlock), 0, s, (const raw_t *)p.X,
+                               (raw_t *)p.Xt, p.C, S, c_tiles, s_tiles, x_blocks, (const raw_t *)p.Wt,
+                               (raw_t *)p.W2, p.group, p.OCg, p.Cg, KK, p.Cgp, (int)table);
+        else
+            hipLaunchKernelGGL((cl_prepare<raw_t, AV, false>), pgrid, dim3(kBlock), 0, s, (const raw_t *)p.X,
+                               (raw_t *)p.Xt, p.C, S, c_tiles, s_tiles, x_blocks, (const raw_t *)p.Wt,
+                               (raw_t *)p.W2, p.group, p.OCg, p.Cg, KK, p.Cgp, (int)table);
+    };
     const dim3 grid(8 * kRun * ((p.nblocks + 8 * kRun - 1) / (8 * kRun)));
-    if (p.OCg > 128) {
-        if (table) hipLaunchKernelGGL((deform_conv2d_cl<T, 2, true>), grid, dim3(kBlock), 0, s, p);
-        else hipLaunchKernelGGL((deform_conv2d_cl<T, 2, false>), grid, dim3(kBlock), 0, s, p);
+    if constexpr (T::bytes == 2) {
+        if (eight) {
+            prepare(std::integral_constant<int, 4>());
+            if (table) hipLaunchKernelGGL((deform_conv2d_cl<T, 1, true, 8>), grid, dim3(512), 0, s, p);
+            else hipLaunchKernelGGL((deform_conv2d_cl<T, 1, false, 8>), grid, dim3(512), 0, s, p);
+            return (int)hipGetLastError();
+        }
+    }
+    prepare(std::integral_constant<int, AV4>());
+    if (wide) {
+        if (table) hipLaunchKernelGGL((deform_conv2d_cl<T, 2, true, 4>), grid, dim3(kBlock), 0, s, p);
+        else hipLaunchKernelGGL((deform_conv2d_cl<T, 2, false, 4>), grid, dim3(kBlock), 0, s, p);
     } else {
-        if (table) hipLaunchKernelGGL((deform_conv2d_cl<T, 1, true>), grid, dim3(kBlock), 0, s, p);
-        else hipLaunchKernelGGL((deform_conv2d_cl<T, 1, false>), grid, dim3(kBlock), 0, s, p);
+        if (table) hipLaunchKernelGGL((deform_conv2d_cl<T, 1, true, 4>), grid, dim3(kBlock), 0, s, p);
+        else hipLaunchKernelGGL((deform_conv2d_cl<T, 1, false, 4>), grid, dim3(kBlock), 0, s, p);
     }
     return (int)hipGetLastError();
 }

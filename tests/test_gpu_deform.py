@@ -13,10 +13,11 @@
   place of the output type.
 * 2-D cases whose conv and offset groups hold multiples of 8 channels run on
   the channels-last copy of X by default: channel counts that fill whole
-  32-channel chunks and ones padded up to the next chunk, offset groups that
-  change within a kernel position's chunks, kernels too large for the
-  sampling table; the same cases with an empty workspace take the gather
-  kernel instead.
+  chunks and ones padded up to the next chunk, offset groups that change
+  within a kernel position's chunks, kernels too large for the sampling
+  table, and (fp16 / bf16 with more than 128 output channels per group) the
+  8-wave blocks with 64-channel chunks; the same cases with an empty
+  workspace take the gather kernel instead.
 * double data and 1-D / 3-D data (the direct kernel, summing in double in the
   oracle's order): bit for bit after the output conversion.
 """
@@ -189,6 +190,8 @@ CASES_CL = [
     (1, 24, 8, 9, 9, 1, 1, (1, 1), (0, 0, 0, 0), (1, 1), 3, 3),            # 8 of 32 channels used
     (1, 48, 12, 13, 130, 3, 2, (1, 2), (2, 0, 1, 1), (2, 1), 2, 6),        # og span 3 per group
     (2, 32, 10, 10, 40, 2, 2, (1, 1), (1, 0, 0, 1), (1, 1), 1, 2),         # og changes inside a chunk
+    (1, 32, 14, 15, 144, 5, 5, (1, 1), (2, 2, 2, 2), (1, 1), 1, 1),        # wide: 8 waves, no table
+    (1, 96, 9, 11, 200, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 1, 3),         # wide, og changes in a chunk
 ]
 
 
