@@ -157,9 +157,10 @@ int gs_grid_sample_2d(const void *X, int x_dtype, const int64_t *x_shape, const 
  *
  * With the workspace the call first probes 64 of the sampler's output tiles
  * on the device; when most of them read from more of X than fits a tile's
- * LDS slot (e.g. a random flow), X is copied to channels-last slices of 32
- * bytes of channels, (N, C / CS, H_in, W_in, CS), in the workspace and
- * sampled from there, several channels per load.  Otherwise the call runs as
+ * LDS slot (e.g. a random flow), X is copied to channels-last slices of 64
+ * bytes of channels (32 when C * sizeof(element) is not a multiple of 64),
+ * (N, C / CS, H_in, W_in, CS), in the workspace and sampled from there,
+ * several channels per load.  Otherwise the call runs as
  * gs_grid_sample_2d.  Both compute the same taps, weights and fp32 sums in
  * the same order (nearest copies the element bit for bit).  Only fp32 / fp16
  * / bf16 X with an fp32 grid and C * sizeof(element) a multiple of 32 bytes

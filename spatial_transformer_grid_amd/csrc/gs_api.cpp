@@ -66,10 +66,10 @@ Extents spatial3(const int64_t *sp, int r) {
 int hip_status(int rc) { return rc == 0 ? GS_OK : GS_ERR_HIP; }
 
 // Workspace of the 2D gather path: kProbes verdict words (padded to 256
-// bytes), then X in channels-last slices of 32 bytes of channels.  0 when the
-// path does not apply: it needs fp32 / fp16 / bf16 X whose channels fill
-// whole 32-byte slices, an image of X and the channel planes of an image of Y
-// each below 2^31 bytes.
+// bytes), then X in channels-last slices of 64 (or 32) bytes of channels.  0
+// when the path does not apply: it needs fp32 / fp16 / bf16 X whose channels
+// fill whole 32-byte slices, an image of X and the channel planes of an image
+// of Y each below 2^31 bytes.
 constexpr int64_t kVerdictBytes = 256;
 
 int64_t gather_workspace_bytes(int x_dtype, const int64_t *x_shape, const int64_t *out_sp) {
@@ -163,8 +163,13 @@ int sample(int r, const void *theta, const void *X, int x_dtype, const int64_t *
             gs::GatherParams g;
             g.verdicts = (int *)workspace;
             g.Xt = (char *)workspace + kVerdictBytes;
-            const int64_t pairs = N * (C * bytes / 32);
-            const int64_t tpp = out.h * ((out.w + 127) / 128);
+            // 64-byte slices when the channels fill them (fewer, longer
+            // loads per tap), else 32
+            const int sb = (C * bytes) % 64 == 0 ? 64 : 32;
+            const int64_t locs = 256 * 16 / sb;
+            const int64_t pairs = N * (C * bytes / sb);
+            const int64_t tpp = out.h * ((out.w + locs - 1) / locs);
+            g.slice_bytes = sb;
             const int64_t blocks = (pairs >= 8 ? (pairs + 7) / 8 * 8 : pairs) * tpp;
             if (blocks > kMaxBlocks * 8) return GS_ERR_TOO_LARGE;
             g.pairs = (int)pairs;

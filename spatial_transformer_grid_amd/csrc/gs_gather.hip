@@ -12,12 +12,13 @@
 //     window) cannot be staged -- more than 256 input rows or more than the
 //     16 KB slot;
 //  2. if most probed tiles are scattered, copies X to channels-last slices
-//     (N, C / CS, H, W, CS) of CS = 32 / sizeof(T) channels in the workspace
-//     and samples from it: two lanes share an output location and each loads
-//     VW = 16 / sizeof(T) channels of a tap in one 16-byte load.  One slice
-//     plane of an image (H * W * 32 bytes, 2 MB for 256 x 256) fits an XCD's
-//     L2, and the blocks are ordered so that each XCD walks its own
-//     (image, slice) planes one after another: the random taps hit L2;
+//     (N, C / CS, H, W, CS) of SB = 64 bytes of channels (32 when C does not
+//     fill 64-byte slices) in the workspace and samples from it: SB / 16
+//     lanes share an output location and each loads VW = 16 / sizeof(T)
+//     channels of a tap in one 16-byte load.  One slice plane of an image
+//     (H * W * SB bytes, 4 MB for 256 x 256) is about an XCD's L2, and the
+//     blocks are ordered so that each XCD walks its own (image, slice)
+//     planes one after another: the random taps mostly hit L2;
 //  3. otherwise the tuned sampler runs as usual.
 //
 // All three launches are enqueued every time; the ones the probe does not
@@ -35,8 +36,9 @@
 
 namespace gs {
 
-constexpr int kGatherLocs = 128;     // output locations per block (one row segment)
-constexpr int kSliceBytes = 32;      // bytes of one pixel's channel slice
+// SB bytes of channels per pixel slice (64, or 32 when the channels do not
+// fill 64); SB / 16 lanes per output location, kBlock * 16 / SB locations
+// per block (one row segment).
 
 // Block b probes tile (b * tiles) / 64 of the sampler's tiling (geometry in
 // p) and writes verdicts[b]: 1 when the tile's locations are scattered.
@@ -82,13 +84,13 @@ __global__ __launch_bounds__(kBlock) void gather_probe(SampleParams p, int elem_
 
 // The sliced channels-last copy, when the probe chose gathering: tiles
 // blockIdx.x, + gridDim.x, ...
-template <typename raw_t, bool VEC>
+template <typename raw_t, bool VEC, int SB>
 __global__ __launch_bounds__(kBlock) void gather_prepare(const raw_t *__restrict__ X,
                                                         raw_t *__restrict__ Xt, int C, int S,
                                                         int c_tiles, int s_tiles, int tiles,
                                                         const int *verdicts) {
     if (!gather_chosen(verdicts)) return;
-    constexpr int CS = kSliceBytes / sizeof(raw_t);
+    constexpr int CS = SB / sizeof(raw_t);
     for (int b = blockIdx.x; b < tiles; b += gridDim.x) {
         if constexpr (VEC) to_channels_last_tile<raw_t>(X, Xt, C, S, c_tiles, s_tiles, b, CS);
         else to_channels_last_scalar<raw_t>(X, Xt, C, S, c_tiles, s_tiles, b, CS);
@@ -127,7 +129,7 @@ __device__ __forceinline__ typename T::raw_t raw_at(const u32x4 &v, int e) {
 // otherwise blocks walk the pairs in order.  A block owns 128 consecutive
 // output locations of one row; lane t serves location t / 2 and channels
 // VW * (t % 2) .. + VW - 1 of the slice.
-template <int MODE, int PAD, typename T>
+template <int MODE, int PAD, typename T, int SB>
 __device__ __forceinline__ void gather_block(const SampleParams &p, const void *Xt, int pairs,
                                              int tiles_per_pair, int xcd_pairs, int b);
 
@@ -136,7 +138,7 @@ __device__ __forceinline__ void gather_block(const SampleParams &p, const void *
 // skip, and measured no slower than one (four or more per block were).
 constexpr int kGatherTPB = 2;
 
-template <int MODE, int PAD, typename T>
+template <int MODE, int PAD, typename T, int SB>
 __global__ __launch_bounds__(kBlock) void grid_sample_gather(SampleParams p, const void *Xt,
                                                             const int *verdicts, int pairs,
                                                             int tiles_per_pair, int xcd_pairs,
@@ -146,18 +148,20 @@ __global__ __launch_bounds__(kBlock) void grid_sample_gather(SampleParams p, con
     for (int j = 0; j < kGatherTPB; ++j) {
         // keep the XCD (b % 8) and take the next logical blocks of its sequence
         const int lb = xcd_pairs ? ((b >> 3) * kGatherTPB + j) * 8 + (b & 7) : b * kGatherTPB + j;
-        if (lb < blocks) gather_block<MODE, PAD, T>(p, Xt, pairs, tiles_per_pair, xcd_pairs, lb);
+        if (lb < blocks) gather_block<MODE, PAD, T, SB>(p, Xt, pairs, tiles_per_pair, xcd_pairs, lb);
     }
 }
 
-template <int MODE, int PAD, typename T>
+template <int MODE, int PAD, typename T, int SB>
 __device__ __forceinline__ void gather_block(const SampleParams &p, const void *Xt, int pairs,
                                              int tiles_per_pair, int xcd_pairs, int b) {
     using raw_t = typename T::raw_t;
     constexpr int K = AxisK<MODE>::K;
     constexpr int TAPS = K * K;
     constexpr int VW = 16 / T::bytes;
-    constexpr int CS = kSliceBytes / T::bytes;
+    constexpr int CS = SB / T::bytes;
+    constexpr int kLanesPerLoc = SB / 16;
+    constexpr int kGatherLocs = kBlock / kLanesPerLoc;
     int pair, tile;
     if (xcd_pairs) {
         const int k = b >> 3;
@@ -174,8 +178,8 @@ __device__ __forceinline__ void gather_block(const SampleParams &p, const void *
     const int segs = (p.out_w + kGatherLocs - 1) / kGatherLocs;
     const int oy = tile / segs, seg = tile - (tile / segs) * segs;
     const int t = threadIdx.x;
-    const int slot = t & 1;
-    const int ox = seg * kGatherLocs + (t >> 1);
+    const int slot = t & (kLanesPerLoc - 1);
+    const int ox = seg * kGatherLocs + t / kLanesPerLoc;
     const bool live = ox < p.out_w;
     const int cx = live ? ox : p.out_w - 1;
 
@@ -206,13 +210,13 @@ __device__ __forceinline__ void gather_block(const SampleParams &p, const void *
     for (int tap = 0; tap < TAPS; ++tap) {
         const int jx = tap % K, jy = tap / K;
         const bool ok = any && ax[0].ok[jx] && ax[1].ok[jy];
-        off[tap] = ok ? (uint32_t)(ax[1].idx[jy] * p.in_w + ax[0].idx[jx]) * kSliceBytes + lane_bytes
+        off[tap] = ok ? (uint32_t)(ax[1].idx[jy] * p.in_w + ax[0].idx[jx]) * SB + lane_bytes
                       : GS_OOB;
         w[tap] = (1.0f * ax[0].w[jx]) * ax[1].w[jy];
     }
 
-    // the slice plane of (n, sl): H * W pixels of 32 bytes
-    const uint32_t plane_bytes = (uint32_t)p.in_h * (uint32_t)p.in_w * kSliceBytes;
+    // the slice plane of (n, sl): H * W pixels of SB bytes
+    const uint32_t plane_bytes = (uint32_t)p.in_h * (uint32_t)p.in_w * SB;
     const rsrc_t xr = make_rsrc((const char *)Xt + (size_t)pair * plane_bytes, plane_bytes);
     // one resource over the image's C output planes (< 2^31 bytes); a lane's
     // channels are per-lane offsets into it
@@ -259,7 +263,7 @@ static int resident_blocks(const void *kernel) {
     return max(8, (per_cu * cus) / 8 * 8);
 }
 
-template <int MODE, int PAD, typename T>
+template <int MODE, int PAD, typename T, int SB>
 static int gather_launch(const SampleParams &p, const GatherParams &g, bool vec_in, hipStream_t s) {
     using raw_t = typename T::raw_t;
     hipLaunchKernelGGL((gather_probe<MODE>), dim3(kProbes), dim3(kBlock), 0, s, p, (int)T::bytes,
@@ -267,31 +271,36 @@ static int gather_launch(const SampleParams &p, const GatherParams &g, bool vec_
     const int S = p.in_h * p.in_w;
     const int c_tiles = (p.C + 63) / 64, s_tiles = (S + 63) / 64;
     const int tiles = p.N * c_tiles * s_tiles;
-    const void *prep = vec_in ? (const void *)gather_prepare<raw_t, true> : (const void *)gather_prepare<raw_t, false>;
+    const void *prep = vec_in ? (const void *)gather_prepare<raw_t, true, SB>
+                              : (const void *)gather_prepare<raw_t, false, SB>;
     const dim3 xg((unsigned)min(tiles, resident_blocks(prep)));
     if (vec_in)
-        hipLaunchKernelGGL((gather_prepare<raw_t, true>), xg, dim3(kBlock), 0, s, (const raw_t *)p.X,
+        hipLaunchKernelGGL((gather_prepare<raw_t, true, SB>), xg, dim3(kBlock), 0, s, (const raw_t *)p.X,
                            (raw_t *)g.Xt, p.C, S, c_tiles, s_tiles, tiles, (const int *)g.verdicts);
     else
-        hipLaunchKernelGGL((gather_prepare<raw_t, false>), xg, dim3(kBlock), 0, s, (const raw_t *)p.X,
+        hipLaunchKernelGGL((gather_prepare<raw_t, false, SB>), xg, dim3(kBlock), 0, s, (const raw_t *)p.X,
                            (raw_t *)g.Xt, p.C, S, c_tiles, s_tiles, tiles, (const int *)g.verdicts);
     // one block per logical block: the dispatcher hands each XCD its blocks
     // in order, which keeps the XCD on one slice plane at a time (a
     // grid-stride loop lets blocks drift apart and was 1.5x slower)
     const dim3 gg((unsigned)((g.gather_blocks + 8 * kGatherTPB - 1) / (8 * kGatherTPB) * 8));
-    hipLaunchKernelGGL((grid_sample_gather<MODE, PAD, T>), gg, dim3(kBlock), 0, s, p, (const void *)g.Xt,
-                       (const int *)g.verdicts, g.pairs, g.tiles_per_pair, g.xcd_pairs,
-                       g.gather_blocks);
+    hipLaunchKernelGGL((grid_sample_gather<MODE, PAD, T, SB>), gg, dim3(kBlock), 0, s, p,
+                       (const void *)g.Xt, (const int *)g.verdicts, g.pairs, g.tiles_per_pair,
+                       g.xcd_pairs, g.gather_blocks);
     return (int)hipGetLastError();
 }
 
 template <int MODE, int PAD>
 static int gather_by_dtype(const SampleParams &p, const GatherParams &g, int dtype, bool vec_in,
                            hipStream_t s) {
+    const bool wide = g.slice_bytes == 64;
     switch (dtype) {
-    case 0: return gather_launch<MODE, PAD, F32>(p, g, vec_in, s);
-    case 1: return gather_launch<MODE, PAD, F16>(p, g, vec_in, s);
-    default: return gather_launch<MODE, PAD, BF16>(p, g, vec_in, s);
+    case 0: return wide ? gather_launch<MODE, PAD, F32, 64>(p, g, vec_in, s)
+                        : gather_launch<MODE, PAD, F32, 32>(p, g, vec_in, s);
+    case 1: return wide ? gather_launch<MODE, PAD, F16, 64>(p, g, vec_in, s)
+                        : gather_launch<MODE, PAD, F16, 32>(p, g, vec_in, s);
+    default: return wide ? gather_launch<MODE, PAD, BF16, 64>(p, g, vec_in, s)
+                         : gather_launch<MODE, PAD, BF16, 32>(p, g, vec_in, s);
     }
 }
 

@@ -45,12 +45,14 @@ struct SampleParams {
 };
 
 // The 2D gather path on a channels-last copy of X (workspace: kProbes verdict
-// words, then Xt in slices of 32 bytes of channels, (N, C / CS, H, W, CS)).
+// words, then Xt in slices of 64 or 32 bytes of channels, (N, C / CS, H, W,
+// CS)).
 struct GatherParams {
     void *Xt;
     int *verdicts;
+    int slice_bytes;           // bytes of channels per pixel slice: 64 or 32
     int pairs;                 // N * C / CS (image, slice) planes
-    int tiles_per_pair;        // out_h * ceil(out_w / 128)
+    int tiles_per_pair;        // out_h * ceil(out_w / (256 * 16 / slice_bytes))
     int xcd_pairs;             // blocks ordered per XCD (pairs >= 8)
     int gather_blocks;         // launch size
 };

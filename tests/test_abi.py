@@ -325,6 +325,7 @@ def test_grid_sample_2d_workspace_size(gs):
     assert ws((16, 128, 256, 256), (16, 256, 256, 2), gs.GS_F32) == 256 + 16 * 128 * 256 * 256 * 4
     assert ws((2, 16, 5, 7), (2, 3, 4, 2), gs.GS_BF16) == 256 + 2 * 16 * 35 * 2
     assert ws((2, 8, 5, 7), (2, 3, 4, 2), gs.GS_F32) == 256 + 2 * 8 * 35 * 4
+    assert ws((2, 24, 5, 7), (2, 3, 4, 2), gs.GS_F32) == 256 + 2 * 24 * 35 * 4  # 32-byte slices
     assert ws((2, 12, 5, 7), (2, 3, 4, 2), gs.GS_F32) == 0     # 48-byte pixel runs
     assert ws((2, 8, 5, 7), (2, 3, 4, 2), gs.GS_F16) == 0      # 16-byte pixel runs
     assert ws((2, 8, 5, 7), (2, 3, 4, 2), gs.GS_F64) == 0

@@ -6,9 +6,10 @@ the plain sampler.
   256 bytes, sum to 32 or more), and the result must equal gs_grid_sample_2d
   bit for bit -- the same taps, weights and fp32 sums in the same order -- and
   the oracle within the tolerances of tests/parity.py.  Every mode, padding,
-  align_corners and element type; one, three and many 32-byte channel slices,
-  fewer (image, slice) planes than XCDs and more; output rows that end in a
-  ragged 128-location segment; non-finite locations.
+  align_corners and element type; 64-byte channel slices (one, four, many)
+  and 32-byte ones (three, one), fewer (image, slice) planes than XCDs and
+  more; output rows that end in a ragged 64- or 128-location segment;
+  non-finite locations.
 * Near-identity affine grids: the probe keeps the staged sampler (verdicts
   sum below 32), and the result equals gs_grid_sample_2d bit for bit.  So do
   random flows over images small enough for a tile's LDS slot.
@@ -78,9 +79,10 @@ def random_grid(rng, n, ho, wo):
 # scattered locations cannot be staged.
 CASES = [
     # n, c (f32), c (half), h, w, ho, wo
-    (2, 16, 32, 96, 104, 9, 140),    # two row segments, the second ragged; 4 planes
-    (1, 24, 48, 100, 110, 17, 64),   # three slices, one plane row segment
-    (3, 64, 128, 91, 101, 5, 13),    # 24 planes (XCD order), narrow rows
+    (2, 16, 32, 96, 104, 9, 140),    # one 64-byte slice, three row segments, the last ragged
+    (1, 24, 48, 100, 110, 17, 64),   # three 32-byte slices, one ragged row segment
+    (3, 64, 128, 91, 101, 5, 13),    # 12 planes of 64-byte slices (XCD order), narrow rows
+    (2, 8, 16, 97, 99, 4, 300),      # one 32-byte slice, three row segments
 ]
 
 
