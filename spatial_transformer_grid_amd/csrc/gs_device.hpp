@@ -254,12 +254,45 @@ __device__ __forceinline__ int xcd_logical_block_runs(int nblocks) {
 
 // ------------------------------------------------------- block reduction
 
+// DPP lane moves within a row of 16 lanes (no LDS round trip, unlike a
+// shuffle): quad permutations, half-row and row mirrors, shift right by n
+// (lanes with no source keep `old`).
+template <int CTRL>
+__device__ __forceinline__ int dpp_move(int old, int v) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, 0xf, 0xf, false);
+}
+constexpr int kDppQuad1032 = 0xb1, kDppQuad2301 = 0x4e, kDppHalfMirror = 0x141,
+              kDppMirror = 0x140, kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114,
+              kDppShr8 = 0x118;
+
+// Minimum over the wave, uniform (every lane and an SGPR hold it).
+__device__ __forceinline__ int wave_min(int v) {
+    v = min(v, dpp_move<kDppQuad1032>(v, v));
+    v = min(v, dpp_move<kDppQuad2301>(v, v));
+    v = min(v, dpp_move<kDppHalfMirror>(v, v));
+    v = min(v, dpp_move<kDppMirror>(v, v));
+    const int a = min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16));
+    const int b = min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48));
+    return min(a, b);
+}
+
+// Inclusive prefix sum over the wave's 64 lanes.
+__device__ __forceinline__ int wave_inclusive_sum(int v) {
+    v += dpp_move<kDppShr1>(0, v);
+    v += dpp_move<kDppShr2>(0, v);
+    v += dpp_move<kDppShr4>(0, v);
+    v += dpp_move<kDppShr8>(0, v);
+    // add the totals of the rows before this lane's row
+    const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+              r2 = __builtin_amdgcn_readlane(v, 47);
+    const int row = (threadIdx.x & 63) >> 4;
+    return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
 template <int NV>
 __device__ __forceinline__ void block_min(int (&v)[NV], int (*red)[NV]) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) v[i] = min(v[i], __shfl_xor(v[i], off, 64));
+    for (int i = 0; i < NV; ++i) v[i] = wave_min(v[i]);
     const int wave = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0)
 #pragma unroll

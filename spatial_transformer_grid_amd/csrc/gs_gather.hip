@@ -155,7 +155,6 @@ __global__ __launch_bounds__(kBlock) void grid_sample_gather(SampleParams p, con
 template <int MODE, int PAD, typename T, int SB>
 __device__ __forceinline__ void gather_block(const SampleParams &p, const void *Xt, int pairs,
                                              int tiles_per_pair, int xcd_pairs, int b) {
-    using raw_t = typename T::raw_t;
     constexpr int K = AxisK<MODE>::K;
     constexpr int TAPS = K * K;
     constexpr int VW = 16 / T::bytes;

@@ -1,8 +1,9 @@
 // gs_kernels.hip -- grid generator and sampler kernels for gfx950.
 //
 // Sampler layout: a 256-thread block (4 wave64) owns one output tile of one
-// image, 16 x 16 locations in 2D or 8 x 8 x 4 in 3D, one location per lane.
-// Each lane computes its sampling location, per-axis taps and weights once.
+// image (tile_shape: 1,024 locations in 2D nearest / linear, 4 consecutive
+// per lane; 512 in 3D, 2 per lane; 256 for cubic, 1 per lane).  Each lane
+// computes its sampling locations, per-axis taps and weights once.
 // The block then reduces the bounding box of all its taps and picks one of two
 // channel loops, uniformly for the whole block:
 //
@@ -180,6 +181,9 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
     __shared__ __align__(16) raw_t lds[BUDGET];
     __shared__ int red[kBlock / 64][2 * R];
     __shared__ int row_lo[MAXR], row_hi[MAXR], row_xs[MAXR], row_base[MAXR + 1];
+    // row of every chunk of the plan (16-byte chunks only; MAXR = 256 fits a byte)
+    constexpr int NCHUNK = VEC ? BUDGET / CH : 1;
+    __shared__ uint8_t chunk_row[NCHUNK];
 
     if (p.gather_verdicts && gather_chosen(p.gather_verdicts)) return;  // the gather path runs
     const int lb = xcd_logical_block_runs(p.nblocks);
@@ -297,6 +301,13 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
     // ---- staging plan: every input row (z, y) of the box gets the interval
     // of 16-byte chunks that covers the x taps the block reads in that row;
     // rows are packed one after another in the LDS slot.
+    // The y (and z) taps of an output are consecutive rows for nearest,
+    // linear and zero-padded cubic; then an output records its x interval
+    // once, at its first row inside the box, and a row's interval is the
+    // union of what the K rows (per axis) ending at it recorded.  Otherwise
+    // (border / reflection cubic) every tap row records it.
+    constexpr bool CONSEC = MODE != MODE_CUBIC || PAD == PAD_ZEROS;
+    constexpr int KY = CONSEC ? K : 1, KZ = CONSEC && R == 3 ? K : 1;
     const int64_t nrows = (int64_t)span[1] * span[2];
     int total_chunks = INT_MAX;
     if (tile_any && nrows <= MAXR) {
@@ -314,18 +325,35 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
                     xl = min(xl, ax[q][0].idx[j]);
                     xh = max(xh, ax[q][0].idx[j]);
                 }
+            if constexpr (CONSEC) {
+                bool oky = false, okz = R == 2;
 #pragma unroll
-            for (int jz = 0; jz < (R == 3 ? K : 1); ++jz)
-#pragma unroll
-                for (int jy = 0; jy < K; ++jy) {
-                    const bool ok = xl <= xh && ax[q][1].ok[jy] && (R == 2 || ax[q][R - 1].ok[jz]);
-                    if (ok) {
-                        const int r = (R == 3 ? (ax[q][R - 1].idx[jz] - lo[2]) * span[1] : 0) +
-                                      ax[q][1].idx[jy] - lo[1];
-                        atomicMin(&row_lo[r], xl);
-                        atomicMax(&row_hi[r], xh);
-                    }
+                for (int j = 0; j < K; ++j) {
+                    oky = oky || ax[q][1].ok[j];
+                    if (R == 3) okz = okz || ax[q][R - 1].ok[j];
                 }
+                if (xl <= xh && oky && okz) {
+                    const int by = max(ax[q][1].idx[0], lo[1]) - lo[1];
+                    const int bz = R == 3 ? max(ax[q][R - 1].idx[0], lo[2]) - lo[2] : 0;
+                    const int r = bz * span[1] + by;
+                    atomicMin(&row_lo[r], xl);
+                    atomicMax(&row_hi[r], xh);
+                }
+            } else {
+#pragma unroll
+                for (int jz = 0; jz < (R == 3 ? K : 1); ++jz)
+#pragma unroll
+                    for (int jy = 0; jy < K; ++jy) {
+                        const bool ok =
+                            xl <= xh && ax[q][1].ok[jy] && (R == 2 || ax[q][R - 1].ok[jz]);
+                        if (ok) {
+                            const int r = (R == 3 ? (ax[q][R - 1].idx[jz] - lo[2]) * span[1] : 0) +
+                                          ax[q][1].idx[jy] - lo[1];
+                            atomicMin(&row_lo[r], xl);
+                            atomicMax(&row_hi[r], xh);
+                        }
+                    }
+            }
         }
         __syncthreads();
         if (t < 64) {
@@ -333,20 +361,30 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
             // wave-wide prefix sum
             constexpr int RPL = MAXR / 64;
             int cnt[RPL], xs[RPL], sum = 0;
+            const int r0 = RPL * t;
+            int ry = r0 % span[1], rz = r0 / span[1];
 #pragma unroll
             for (int i = 0; i < RPL; ++i) {
-                const int r = RPL * t + i;
-                const bool e = r < nrows && row_hi[r] >= row_lo[r];
-                xs[i] = e ? (row_lo[r] & ~(CH - 1)) : 0;
-                cnt[i] = e ? (row_hi[r] - xs[i] + CH) / CH : 0;
-                sum += cnt[i];
-            }
-            int incl = sum;
+                const int r = r0 + i;
+                int rl = INT_MAX, rh = INT_MIN;
+                if (r < nrows) {
 #pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const int v = __shfl_up(incl, d, 64);
-                if (t >= d) incl += v;
+                    for (int dz = 0; dz < KZ; ++dz)
+#pragma unroll
+                        for (int dy = 0; dy < KY; ++dy)
+                            if (dz <= rz && dy <= ry) {
+                                const int sr = r - dz * span[1] - dy;
+                                rl = min(rl, row_lo[sr]);
+                                rh = max(rh, row_hi[sr]);
+                            }
+                }
+                const bool e = rh >= rl;
+                xs[i] = e ? (rl & ~(CH - 1)) : 0;
+                cnt[i] = e ? (rh - xs[i] + CH) / CH : 0;
+                sum += cnt[i];
+                if (++ry == span[1]) ry = 0, ++rz;
             }
+            const int incl = wave_inclusive_sum(sum);
             int run = incl - sum;
 #pragma unroll
             for (int i = 0; i < RPL; ++i) {
@@ -358,6 +396,14 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
         }
         __syncthreads();
         total_chunks = __builtin_amdgcn_readfirstlane(row_base[MAXR]);
+        if constexpr (VEC) {
+            // the row of every chunk, for the copy loop below
+            if (total_chunks < NCHUNK) {
+                if (t < nrows)
+                    for (int c = row_base[t]; c < row_base[t + 1]; ++c) chunk_row[c] = (uint8_t)t;
+                __syncthreads();
+            }
+        }
     }
     // slot stride: the plan plus one zero chunk; as many channels per LDS fill
     // as the budget holds (the next fill is in flight while one is read)
@@ -476,9 +522,13 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
             const int u = div_small(i, total_chunks, inv_tc);
             const int c = i - u * total_chunks;
             int r = 0;
+            if constexpr (VEC) {
+                r = chunk_row[c];
+            } else {
 #pragma unroll
-            for (int step = MAXR / 2; step > 0; step >>= 1)
-                if (row_base[r + step] <= c) r += step;
+                for (int step = MAXR / 2; step > 0; step >>= 1)
+                    if (row_base[r + step] <= c) r += step;
+            }
             const int cx = c - row_base[r];
             int z = 0, y = r;
             if (R == 3) {

@@ -68,7 +68,8 @@ struct Geo {
 // Output tile of a 256-thread block: 2D nearest / linear 128 x 8 when an
 // output row fits in 128 locations (no tile boundary crosses the rows the
 // block reads), else 64 x 16, and 32 x 32 for rows of at most 32; 2D cubic
-// 16 x 16; 3D nearest / linear 16 x 8 x 4; 3D cubic 8 x 8 x 4.  Chosen by
+// 16 x 16; 3D nearest / linear 32 x 4 x 4 (each output row segment of a
+// block is a whole 128-byte line of fp32 Y); 3D cubic 8 x 8 x 4.  Chosen by
 // measurement on the workloads the library is tuned for.
 inline void tile_shape(int r, int mode, int out_w, int *w, int *h, int *d) {
     if (r == 2 && mode != 2) {
@@ -78,7 +79,7 @@ inline void tile_shape(int r, int mode, int out_w, int *w, int *h, int *d) {
     } else if (r == 2) {
         *w = 16, *h = 16, *d = 1;
     } else if (mode != 2) {
-        *w = 16, *h = 8, *d = 4;
+        *w = 32, *h = 4, *d = 4;
     } else {
         *w = 8, *h = 8, *d = 4;
     }
