@@ -184,6 +184,7 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
     // row of every chunk of the plan (16-byte chunks only; MAXR = 256 fits a byte)
     constexpr int NCHUNK = VEC ? BUDGET / CH : 1;
     __shared__ uint8_t chunk_row[NCHUNK];
+    __shared__ int wave_sum[kBlock / 64];
 
     if (p.gather_verdicts && gather_chosen(p.gather_verdicts)) return;  // the gather path runs
     const int lb = xcd_logical_block_runs(p.nblocks);
@@ -288,6 +289,11 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
         mm[2 * k] = lo;
         mm[2 * k + 1] = nhi;
     }
+    // the row records of the plan below start empty (block_min's barrier
+    // orders this before their first update)
+    static_assert(MAXR == kBlock, "one plan row per thread");
+    row_lo[t] = INT_MAX;
+    row_hi[t] = INT_MIN;
     block_min<2 * R>(mm, red);
     int lo[3] = {0, 0, 0}, span[3] = {1, 1, 1};
     const bool tile_any = mm[0] != INT_MAX;
@@ -311,11 +317,6 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
     const int64_t nrows = (int64_t)span[1] * span[2];
     int total_chunks = INT_MAX;
     if (tile_any && nrows <= MAXR) {
-        for (int r = t; r < MAXR; r += kBlock) {
-            row_lo[r] = INT_MAX;
-            row_hi[r] = INT_MIN;
-        }
-        __syncthreads();
 #pragma unroll
         for (int q = 0; q < Q; ++q) {
             int xl = INT_MAX, xh = INT_MIN;
@@ -356,54 +357,49 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
             }
         }
         __syncthreads();
-        if (t < 64) {
-            // chunks per row, MAXR / 64 consecutive rows per lane, and a
-            // wave-wide prefix sum
-            constexpr int RPL = MAXR / 64;
-            int cnt[RPL], xs[RPL], sum = 0;
-            const int r0 = RPL * t;
-            int ry = r0 % span[1], rz = r0 / span[1];
+        // row t of the box: its chunk interval (the union over the rows that
+        // end at it), a block-wide prefix sum of the chunk counts (per wave,
+        // then the totals of the waves before), and its chunks' entries in
+        // the chunk -> row table
+        int rl = INT_MAX, rh = INT_MIN;
+        if (t < nrows) {
+            const int ry = t % span[1], rz = t / span[1];
 #pragma unroll
-            for (int i = 0; i < RPL; ++i) {
-                const int r = r0 + i;
-                int rl = INT_MAX, rh = INT_MIN;
-                if (r < nrows) {
+            for (int dz = 0; dz < KZ; ++dz)
 #pragma unroll
-                    for (int dz = 0; dz < KZ; ++dz)
+                for (int dy = 0; dy < KY; ++dy)
+                    if (dz <= rz && dy <= ry) {
+                        const int sr = t - dz * span[1] - dy;
+                        rl = min(rl, row_lo[sr]);
+                        rh = max(rh, row_hi[sr]);
+                    }
+        }
+        const bool e = rh >= rl;
+        const int xs = e ? (rl & ~(CH - 1)) : 0;
+        // (capped: a plan beyond the budget is not staged, and the sum of
+        // the counts must not overflow)
+        const int cnt = e ? min((rh - xs + CH) / CH, BUDGET) : 0;
+        const int incl = wave_inclusive_sum(cnt);
+        if ((t & 63) == 63) wave_sum[t >> 6] = incl;
+        __syncthreads();
+        int before = 0;
+        total_chunks = 0;
 #pragma unroll
-                        for (int dy = 0; dy < KY; ++dy)
-                            if (dz <= rz && dy <= ry) {
-                                const int sr = r - dz * span[1] - dy;
-                                rl = min(rl, row_lo[sr]);
-                                rh = max(rh, row_hi[sr]);
-                            }
-                }
-                const bool e = rh >= rl;
-                xs[i] = e ? (rl & ~(CH - 1)) : 0;
-                cnt[i] = e ? (rh - xs[i] + CH) / CH : 0;
-                sum += cnt[i];
-                if (++ry == span[1]) ry = 0, ++rz;
-            }
-            const int incl = wave_inclusive_sum(sum);
-            int run = incl - sum;
-#pragma unroll
-            for (int i = 0; i < RPL; ++i) {
-                row_base[RPL * t + i] = run;
-                row_xs[RPL * t + i] = xs[i];
-                run += cnt[i];
-            }
-            if (t == 63) row_base[MAXR] = incl;
+        for (int wv = 0; wv < kBlock / 64; ++wv) {
+            const int ws = wave_sum[wv];
+            before += wv < (t >> 6) ? ws : 0;
+            total_chunks += ws;
+        }
+        total_chunks = __builtin_amdgcn_readfirstlane(total_chunks);
+        const int base = before + incl - cnt;
+        row_base[t] = base;
+        row_xs[t] = xs;
+        if (t == kBlock - 1) row_base[MAXR] = base + cnt;
+        if constexpr (VEC) {
+            if (total_chunks < NCHUNK)
+                for (int c = base; c < base + cnt; ++c) chunk_row[c] = (uint8_t)t;
         }
         __syncthreads();
-        total_chunks = __builtin_amdgcn_readfirstlane(row_base[MAXR]);
-        if constexpr (VEC) {
-            // the row of every chunk, for the copy loop below
-            if (total_chunks < NCHUNK) {
-                if (t < nrows)
-                    for (int c = row_base[t]; c < row_base[t + 1]; ++c) chunk_row[c] = (uint8_t)t;
-                __syncthreads();
-            }
-        }
     }
     // slot stride: the plan plus one zero chunk; as many channels per LDS fill
     // as the budget holds (the next fill is in flight while one is read)
@@ -418,6 +414,7 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
     // ---- tap weights
     float w[Q][NT];
     float wz[Q][4], wy[Q][4], wx[Q][4];
+    auto tap_weights = [&]() {
 #pragma unroll
     for (int q = 0; q < Q; ++q) {
         if constexpr (SEPARABLE) {
@@ -444,6 +441,7 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
             }
         }
     }
+    };
 
     // Tap offsets = row part (z, y) + column part (x).  row_part(q, jz, jy)
     // returns the row part of a valid row; an invalid tap gets `cap`.  For 3D
@@ -499,16 +497,26 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
     if (staged) {
         // ------------------------------------------------ staged in LDS
         // LDS element offset of pixel x of row r within a slot:
-        // row_base[r] * CH - row_xs[r] + x; invalid taps read the zero chunk
-        build_offsets(
-            [&](int iz, int iy) {
-                const int r = (R == 3 ? (iz - lo[2]) * span[1] : 0) + iy - lo[1];
-                return row_base[r] * CH - row_xs[r];
-            },
-            1, (uint32_t)(SS - 1));
+        // row_base[r] * CH - row_xs[r] + x; invalid taps read the zero chunk.
+        // 3D computes them (and the weights) while the first fill loads; 2D
+        // before, which keeps fewer registers live across the copy setup.
+        constexpr bool LATE = R == 3;
+        auto staged_offsets = [&]() {
+            build_offsets(
+                [&](int iz, int iy) {
+                    const int r = (R == 3 ? (iz - lo[2]) * span[1] : 0) + iy - lo[1];
+                    return row_base[r] * CH - row_xs[r];
+                },
+                1, (uint32_t)(SS - 1));
+        };
+        if constexpr (!LATE) {
+            tap_weights();
+            staged_offsets();
+        }
         // this thread's copy items: item i = t + e * 256 is chunk c of channel
-        // slot u, i = u * total_chunks + c; c is found in the row table by a
-        // branch-free binary search.  Items past the plan load through the
+        // slot u, i = u * total_chunks + c; c's row comes from the chunk ->
+        // row table (16-byte chunks) or a branch-free binary search over the
+        // row bases.  Items past the plan load through the
         // out-of-range offset (zeros) into slot 0's zero chunk, so the copy
         // loop has no branches: a branch would make the compiler wait for
         // every load in flight before the next one.
@@ -565,6 +573,10 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
             for (int e = 0; e < EMAX; ++e) pre[e] = load_chunk(r, goff[e]);
         };
         prefetch(cbeg);
+        if constexpr (LATE) {
+            tap_weights();
+            staged_offsets();
+        }
         for (int c0 = cbeg; c0 < cend; c0 += U) {
             __syncthreads();  // the previous fill's LDS reads are done
 #pragma unroll
@@ -608,6 +620,7 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
         }
     } else {
         // ------------------------------------------------- direct gather
+        tap_weights();
         build_offsets(
             [&](int iz, int iy) { return ((R == 3 ? iz * p.in_h : 0) + iy) * p.in_w * T::bytes; },
             T::bytes, GS_OOB);
