@@ -65,12 +65,14 @@ Extents spatial3(const int64_t *sp, int r) {
 
 int hip_status(int rc) { return rc == 0 ? GS_OK : GS_ERR_HIP; }
 
-// Workspace of the 2D gather path: kProbes verdict words (padded to 256
-// bytes), then X in channels-last slices of 64 (or 32) bytes of channels.  0
+// Workspace of the 2D gather path: an 8,448-byte header (kProbes verdict
+// words, then the gather kernel's 64 tile counters on separate 128-byte
+// lines), then X in channels-last slices
+// of 64 (or 32) bytes of channels.  0
 // when the path does not apply: it needs fp32 / fp16 / bf16 X whose channels
 // fill whole 32-byte slices, an image of X and the channel planes of an image
 // of Y each below 2^31 bytes.
-constexpr int64_t kVerdictBytes = 256;
+constexpr int64_t kGatherHeaderBytes = 8448;  // 64 verdict words, then 64 counters 128 bytes apart
 
 int64_t gather_workspace_bytes(int x_dtype, const int64_t *x_shape, const int64_t *out_sp) {
     if (!valid_x_dtype(x_dtype)) return 0;
@@ -82,7 +84,7 @@ int64_t gather_workspace_bytes(int x_dtype, const int64_t *x_shape, const int64_
     const int64_t co[3] = {C, out_sp[0], out_sp[1]};
     if (!product_within(co, 3, kInt32Max / bytes, &outp)) return 0;
     if (N > (int64_t(1) << 40) / (img * bytes)) return 0;
-    return kVerdictBytes + N * img * bytes;
+    return kGatherHeaderBytes + N * img * bytes;
 }
 
 // Shared validation and launch of the sampler (fused or not).  With a large
@@ -162,7 +164,8 @@ int sample(int r, const void *theta, const void *X, int x_dtype, const int64_t *
         if (need > 0 && workspace_bytes >= need) {
             gs::GatherParams g;
             g.verdicts = (int *)workspace;
-            g.Xt = (char *)workspace + kVerdictBytes;
+            g.counters = (int *)((char *)workspace + 256);
+            g.Xt = (char *)workspace + kGatherHeaderBytes;
             // 64-byte slices when the channels fill them (fewer, longer
             // loads per tap), else 32
             const int sb = (C * bytes) % 64 == 0 ? 64 : 32;

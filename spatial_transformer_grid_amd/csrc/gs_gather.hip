@@ -40,11 +40,19 @@ namespace gs {
 // fill 64); SB / 16 lanes per output location, kBlock * 16 / SB locations
 // per block (one row segment).
 
+// Tile counters of the gather kernel (below): 64 on separate 128-byte lines.
+constexpr int kGatherGrab = 2;
+constexpr int kCounterStride = 32;  // ints: 128 bytes
+constexpr int kCounters = 64;       // 8 sequences x 8 counters
+
 // Block b probes tile (b * tiles) / 64 of the sampler's tiling (geometry in
 // p) and writes verdicts[b]: 1 when the tile's locations are scattered.
 template <int MODE>
-__global__ __launch_bounds__(kBlock) void gather_probe(SampleParams p, int elem_bytes, int *verdicts) {
+__global__ __launch_bounds__(kBlock) void gather_probe(SampleParams p, int elem_bytes, int *verdicts,
+                                                      int *counters) {
     __shared__ int red[kBlock / 64][4];
+    // the gather kernel's tile counters (it runs after this launch)
+    if (blockIdx.x == 0 && threadIdx.x < kCounters) counters[threadIdx.x * kCounterStride] = 0;
     const int64_t total = (int64_t)p.N * p.tiles_per_n;
     const int64_t tb = ((int64_t)blockIdx.x * total) / kProbes;
     const int n = (int)(tb / p.tiles_per_n);
@@ -133,22 +141,46 @@ template <int MODE, int PAD, typename T, int SB>
 __device__ __forceinline__ void gather_block(const SampleParams &p, const void *Xt, int pairs,
                                              int tiles_per_pair, int xcd_pairs, int b);
 
-// Hardware block b covers kGatherTPB consecutive logical blocks (of its
-// XCD's sequence when xcd_pairs): half as many blocks to dispatch, or to
-// skip, and measured no slower than one (four or more per block were).
-constexpr int kGatherTPB = 2;
-
+// One block per resident slot of the device.  The logical blocks form one
+// sequence per XCD (8 with xcd_pairs: blocks b % 8 == x serve XCD x's), or
+// one; a sequence is dealt in grabs of kGatherGrab consecutive logical
+// blocks by S = min(8, its blocks) counters that take turns (counter j hands
+// out grabs j, j + S, j + 2S, ...), so the sequence advances in order, as a
+// full grid would be dispatched, and no counter sees more than a few
+// blocks' atomics.  Counters sit on separate 128-byte lines; the probe zeroes
+// them.  A block asks for its next grab while it works on the current one.
+// When the probe keeps the staged sampler, only one round of blocks starts
+// and exits.
 template <int MODE, int PAD, typename T, int SB>
 __global__ __launch_bounds__(kBlock) void grid_sample_gather(SampleParams p, const void *Xt,
-                                                            const int *verdicts, int pairs,
-                                                            int tiles_per_pair, int xcd_pairs,
-                                                            int blocks) {
+                                                            const int *verdicts, int *counters,
+                                                            int pairs, int tiles_per_pair,
+                                                            int xcd_pairs, int blocks) {
+    __shared__ int next[2];
     if (!gather_chosen(verdicts)) return;
-    const int b = blockIdx.x;
-    for (int j = 0; j < kGatherTPB; ++j) {
-        // keep the XCD (b % 8) and take the next logical blocks of its sequence
-        const int lb = xcd_pairs ? ((b >> 3) * kGatherTPB + j) * 8 + (b & 7) : b * kGatherTPB + j;
-        if (lb < blocks) gather_block<MODE, PAD, T, SB>(p, Xt, pairs, tiles_per_pair, xcd_pairs, lb);
+    const int nseq = xcd_pairs ? 8 : 1;
+    const int x = (int)blockIdx.x % nseq;                 // sequence
+    const int rank = (int)blockIdx.x / nseq;              // block's rank among its sequence's
+    const int S = min(8, (int)gridDim.x / nseq);          // gridDim.x is a multiple of 8
+    const int jc = rank % S;
+    const int steps = blocks / nseq;                      // logical blocks per sequence
+    int *ctr = counters + (x * 8 + jc) * kCounterStride;
+    if (threadIdx.x == 0) next[0] = atomicAdd(ctr, 1);
+    __syncthreads();
+    int m = __builtin_amdgcn_readfirstlane(next[0]);
+    for (int it = 0;; ++it) {
+        const int k0 = (m * S + jc) * kGatherGrab;
+        if (k0 >= steps) break;
+        if (threadIdx.x == 0) next[(it + 1) & 1] = atomicAdd(ctr, 1);
+#pragma unroll
+        for (int i = 0; i < kGatherGrab; ++i) {
+            const int k = k0 + i;
+            if (k < steps)
+                gather_block<MODE, PAD, T, SB>(p, Xt, pairs, tiles_per_pair, xcd_pairs,
+                                               xcd_pairs ? k * 8 + x : k);
+        }
+        __syncthreads();  // the next grab is visible
+        m = __builtin_amdgcn_readfirstlane(next[(it + 1) & 1]);
     }
 }
 
@@ -266,7 +298,7 @@ template <int MODE, int PAD, typename T, int SB>
 static int gather_launch(const SampleParams &p, const GatherParams &g, bool vec_in, hipStream_t s) {
     using raw_t = typename T::raw_t;
     hipLaunchKernelGGL((gather_probe<MODE>), dim3(kProbes), dim3(kBlock), 0, s, p, (int)T::bytes,
-                       g.verdicts);
+                       g.verdicts, g.counters);
     const int S = p.in_h * p.in_w;
     const int c_tiles = (p.C + 63) / 64, s_tiles = (S + 63) / 64;
     const int tiles = p.N * c_tiles * s_tiles;
@@ -279,13 +311,13 @@ static int gather_launch(const SampleParams &p, const GatherParams &g, bool vec_
     else
         hipLaunchKernelGGL((gather_prepare<raw_t, false, SB>), xg, dim3(kBlock), 0, s, (const raw_t *)p.X,
                            (raw_t *)g.Xt, p.C, S, c_tiles, s_tiles, tiles, (const int *)g.verdicts);
-    // one block per logical block: the dispatcher hands each XCD its blocks
-    // in order, which keeps the XCD on one slice plane at a time (a
-    // grid-stride loop lets blocks drift apart and was 1.5x slower)
-    const dim3 gg((unsigned)((g.gather_blocks + 8 * kGatherTPB - 1) / (8 * kGatherTPB) * 8));
+    // one round of resident blocks, a multiple of 8 (one counter per XCD)
+    const void *gk = (const void *)grid_sample_gather<MODE, PAD, T, SB>;
+    const int want = (g.gather_blocks + 7) / 8 * 8;
+    const dim3 gg((unsigned)min(want, resident_blocks(gk)));
     hipLaunchKernelGGL((grid_sample_gather<MODE, PAD, T, SB>), gg, dim3(kBlock), 0, s, p,
-                       (const void *)g.Xt, (const int *)g.verdicts, g.pairs, g.tiles_per_pair,
-                       g.xcd_pairs, g.gather_blocks);
+                       (const void *)g.Xt, (const int *)g.verdicts, g.counters, g.pairs,
+                       g.tiles_per_pair, g.xcd_pairs, g.gather_blocks);
     return (int)hipGetLastError();
 }
 

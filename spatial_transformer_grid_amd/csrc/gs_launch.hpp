@@ -50,6 +50,7 @@ struct SampleParams {
 struct GatherParams {
     void *Xt;
     int *verdicts;
+    int *counters;             // 64 tile counters of the gather kernel, 128 bytes apart
     int slice_bytes;           // bytes of channels per pixel slice: 64 or 32
     int pairs;                 // N * C / CS (image, slice) planes
     int tiles_per_pair;        // out_h * ceil(out_w / (256 * 16 / slice_bytes))

@@ -318,14 +318,15 @@ def test_deform_conv_workspace_size(gs):
 
 
 def test_grid_sample_2d_workspace_size(gs):
-    """256 bytes of probe verdicts plus X in channels-last slices; none when
-    the channels do not fill 32-byte slices, for types the gather path does
-    not take, or when an image or its output planes exceed 2^31 bytes."""
+    """An 8,448-byte header (probe verdicts, tile counters) plus X in
+    channels-last slices; none when the channels do not fill 32-byte slices,
+    for types the gather path does not take, or when an image or its output
+    planes exceed 2^31 bytes."""
     ws = gs.grid_sample_2d_workspace_size
-    assert ws((16, 128, 256, 256), (16, 256, 256, 2), gs.GS_F32) == 256 + 16 * 128 * 256 * 256 * 4
-    assert ws((2, 16, 5, 7), (2, 3, 4, 2), gs.GS_BF16) == 256 + 2 * 16 * 35 * 2
-    assert ws((2, 8, 5, 7), (2, 3, 4, 2), gs.GS_F32) == 256 + 2 * 8 * 35 * 4
-    assert ws((2, 24, 5, 7), (2, 3, 4, 2), gs.GS_F32) == 256 + 2 * 24 * 35 * 4  # 32-byte slices
+    assert ws((16, 128, 256, 256), (16, 256, 256, 2), gs.GS_F32) == 8448 + 16 * 128 * 256 * 256 * 4
+    assert ws((2, 16, 5, 7), (2, 3, 4, 2), gs.GS_BF16) == 8448 + 2 * 16 * 35 * 2
+    assert ws((2, 8, 5, 7), (2, 3, 4, 2), gs.GS_F32) == 8448 + 2 * 8 * 35 * 4
+    assert ws((2, 24, 5, 7), (2, 3, 4, 2), gs.GS_F32) == 8448 + 2 * 24 * 35 * 4  # 32-byte slices
     assert ws((2, 12, 5, 7), (2, 3, 4, 2), gs.GS_F32) == 0     # 48-byte pixel runs
     assert ws((2, 8, 5, 7), (2, 3, 4, 2), gs.GS_F16) == 0      # 16-byte pixel runs
     assert ws((2, 8, 5, 7), (2, 3, 4, 2), gs.GS_F64) == 0
