@@ -533,7 +533,7 @@ __device__ __forceinline__ void mfma_chunk_regs(const u32x4 (&a)[MB][AV], const 
 
 // NW waves per block (4, or 8 for fp16 / bf16 with 256 output channels per
 // block), chunks of TK = 8 * NW channels, loads DEPTH chunks ahead (8 waves:
-// one chunk ahead, so that four waves fit a SIMD).
+// corner gathers two chunks ahead and A one, so that four waves fit a SIMD).
 template <typename T, int MB, bool TABLE, int NW>
 __global__ __launch_bounds__(64 * NW) void deform_conv2d_cl(DeformParams p) {
     using raw_t = typename T::raw_t;
@@ -618,6 +618,8 @@ __global__ __launch_bounds__(64 * NW) void deform_conv2d_cl(DeformParams p) {
     u32x4 a0[MB][AV], a1[DEPTH == 2 ? MB : 1][AV];
     u32x4 x0[4][VPC], x1[DEPTH == 2 ? 4 : 1][VPC];
     float q0[4], q1[4];
+    u32x4 x8[NW == 8 ? 4 : 1][VPC];                 // eight waves: the second corner set
+    float q8[4];
     Corners cc;                                     // corners of (ctap, cg), non-table path
     int ctap = -1, cg = -1;
     // Past the last chunk the loads fetch the last chunk again (unused):
@@ -720,6 +722,57 @@ __global__ __launch_bounds__(64 * NW) void deform_conv2d_cl(DeformParams p) {
         load_a(i + DEPTH, a);
     };
 
+    // Eight waves: the corner gathers (scattered, the long wait) run two
+    // chunks ahead and A one.  Issue order per step: A of the next chunk,
+    // then the corners of the one after, so a step finds (oldest first) its
+    // corners, its A, the next chunk's corners outstanding.  It waits for its
+    // corners, samples, and waits for its A only before the MFMAs.
+    constexpr int kCornerLoads = 4 * VPC;
+    constexpr int kCornersDone = kCornerLoads + MB * AV;  // A and next corners may be out
+    static_assert(kCornersDone < 64, "vmcnt field");
+    auto step8 = [&](int i, u32x4 (&xpre)[4][VPC], float (&wq)[4]) {
+        raw_t *bs = Bs[i & 1];
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt((kCornersDone & 15) | ((kCornersDone >> 4) << 14) | 0x0f70);
+        {
+            float v[8], x[8];
+            unpack8<T>(xpre[0], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = wq[0] * x[e];
+#pragma unroll
+            for (int q = 1; q < 4; ++q) {
+                unpack8<T>(xpre[q], x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) v[e] = fmaf(wq[q], x[e], v[e]);
+            }
+            u32x4 packed[VPC];
+            pack8<T>(v, packed);
+#pragma unroll
+            for (int h = 0; h < VPC; ++h)
+                *(u32x4 *)&bs[pos * LK + 8 * cgp + h * (16 / T::bytes)] = packed[h];
+        }
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt((kCornerLoads & 15) | ((kCornerLoads >> 4) << 14) | 0x0f70);
+        mfma_chunk_regs<T, MB, LK, AV>(a0, bs, acc, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        load_a(i + 1, a0);
+        load_x(i + 2, xpre, wq);
+    };
+
+    if constexpr (NW == 8) {
+        load_x(0, x0, q0);
+        load_a(0, a0);
+        load_x(1, x8, q8);
+        int i = 0;
+        for (; i + 1 < nch; i += 2) {
+            step8(i, x0, q0);
+            step8(i + 1, x8, q8);
+        }
+        if (i < nch) step8(i, x0, q0);
+        store_tile<T, MB>(p, acc, n, oc0, m_valid, nt, wave, lane);
+        return;
+    }
     load_x(0, x0, q0);
     load_a(0, a0);
     if constexpr (DEPTH == 2) {
