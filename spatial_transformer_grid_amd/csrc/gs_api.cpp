@@ -299,7 +299,7 @@ int gs_affine_grid(const void *theta, int theta_dtype, const int64_t *size, int 
     if (!product_within(size + 2, r, kInt32Max, &count)) return GS_ERR_TOO_LARGE;
     if (N == 0 || count == 0) return GS_OK;
     if (!theta || !grid) return GS_ERR_NULL;
-    const int64_t tiles = (count + kBlockThreads - 1) / kBlockThreads;
+    const int64_t tiles = (count + gs::kAffineLocs - 1) / gs::kAffineLocs;
     if (tiles > kMaxBlocks || N * tiles > kMaxBlocks) return GS_ERR_TOO_LARGE;
     const Extents out = spatial3(size + 2, r);
     gs::AffineParams p;

@@ -90,6 +90,9 @@ struct GridElem<double> {
     __device__ static double narrow(double v) { return v; }
 };
 
+// A block writes kAffineLocs consecutive locations of one sample: lane t the
+// locations t, t + 256, ... (each store instruction of a wave stays
+// contiguous), theta read once.
 template <int R, typename TT>
 __global__ __launch_bounds__(kBlock) void affine_grid_kernel(AffineParams p) {
     using E = GridElem<TT>;
@@ -98,19 +101,24 @@ __global__ __launch_bounds__(kBlock) void affine_grid_kernel(AffineParams p) {
     if (lb >= p.nblocks) return;
     const int n = lb / p.tiles_per_n;
     const int tile = lb - n * p.tiles_per_n;
-    const uint32_t l = (uint32_t)tile * kBlock + threadIdx.x;
-    if (l >= p.out_count) return;
-    int d, h, w;
-    decompose<R>(l, p.out_w, p.out_h, p.div_w_m, p.div_w_s, p.div_h_m, p.div_h_s, d, h, w);
     const TT *tp = (const TT *)p.theta + (size_t)n * R * (R + 1);
     F th[R * (R + 1)];
 #pragma unroll
     for (int i = 0; i < R * (R + 1); ++i) th[i] = E::widen(tp[i]);
-    F g[R];
-    affine_vector<R, F>(th, d, h, w, p.out_d, p.out_h, p.out_w, p.align_corners, g);
-    TT *out = (TT *)p.grid + ((size_t)n * p.out_count + l) * R;
+    TT *gn = (TT *)p.grid + (size_t)n * p.out_count * R;
 #pragma unroll
-    for (int k = 0; k < R; ++k) out[k] = E::narrow(g[k]);
+    for (int j = 0; j < kAffineLocs / kBlock; ++j) {
+        const uint32_t l = (uint32_t)tile * kAffineLocs + (uint32_t)(j * kBlock) + threadIdx.x;
+        if (l < p.out_count) {
+            int d, h, w;
+            decompose<R>(l, p.out_w, p.out_h, p.div_w_m, p.div_w_s, p.div_h_m, p.div_h_s, d, h, w);
+            F g[R];
+            affine_vector<R, F>(th, d, h, w, p.out_d, p.out_h, p.out_w, p.align_corners, g);
+            TT *out = gn + (size_t)l * R;
+#pragma unroll
+            for (int k = 0; k < R; ++k) out[k] = E::narrow(g[k]);
+        }
+    }
 }
 
 // ------------------------------------------------------------------ taps

@@ -89,6 +89,9 @@ inline void tile_shape(int r, int mode, int out_w, int *w, int *h, int *d) {
 // Elements per 16-byte chunk of the LDS staging copy.
 inline int stage_chunk_elems(int elem_bytes) { return 16 / elem_bytes; }
 
+// Locations per block of the grid generator.
+constexpr int kAffineLocs = 1024;
+
 struct AffineParams {
     const void *theta;   // (N, R, R+1), element type theta_dtype
     void *grid;          // (N, out..., R), element type theta_dtype
