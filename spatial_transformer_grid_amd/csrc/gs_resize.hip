@@ -142,6 +142,11 @@ __global__ __launch_bounds__(kBlock) void resize_kernel(ResizeParams p) {
     // the chunk after the budget receives the copy items past the plan
     __shared__ __align__(16) raw_t lds[BUDGET + CH];
     __shared__ int red[kBlock / 64][4];
+    // 2D cubic filters in two passes: the staged rows along x for the tile's
+    // columns (fp32, HROWS values), then each output along y
+    constexpr bool SEP = MODE == RZ_CUBIC && !D3;
+    constexpr int HROWS = 3072;
+    __shared__ float hbuf[SEP ? HROWS : 1];
 
     const int lb = xcd_logical_block_runs(p.nblocks);
     if (lb >= p.nblocks) return;
@@ -228,6 +233,25 @@ __global__ __launch_bounds__(kBlock) void resize_kernel(ResizeParams p) {
         const int rowlen = nch * CH;
         int U = min(UMAX, BUDGET / SS);
         U = (int)min<int64_t>(U, (int64_t)0x7fffffff / ip);
+        // two passes when a plane's filtered rows fit (tile_w is a power of
+        // two; at most 256 so that thread t keeps column t % tile_w)
+        const int tw = p.tile_w;
+        const bool sep = SEP && tw <= kBlock && nr * tw <= HROWS;
+        if (sep) U = min(U, HROWS / (nr * tw));
+        // pass 1: thread t filters column t % tw of rows t / tw, + 256 / tw, ...
+        const int hx = t & (tw - 1), hg = t / tw, hstep = kBlock / tw;
+        int hcol[K];
+        float hw[K];
+        if (sep) {
+            RzTaps<K> hc;
+            resize_taps<MODE>(resize_location(min(tx * tw + hx, aw.m - 1), aw, p.ct), aw.n,
+                              p.nearest_mode, p.cubic_a, p.exclude_outside, hc);
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                hcol[j] = hc.idx[j] - xs;
+                hw[j] = hc.w[j];
+            }
+        }
         // LDS element offsets of the taps within a slot
         int colpart[Q][K], rowpart[KD][K];
 #pragma unroll
@@ -283,6 +307,36 @@ __global__ __launch_bounds__(kBlock) void resize_kernel(ResizeParams p) {
             __syncthreads();  // this fill is in LDS
             if (c0 + U < pend) prefetch(c0 + U);
             const int nv = min(U, pend - c0);
+            if constexpr (SEP) {
+                if (sep) {
+                    // the same fp32 operations in the same order as resize_sum:
+                    // x first (pass 1), then y (pass 2)
+                    for (int u = 0; u < nv; ++u)
+                        for (int r = hg; r < nr; r += hstep) {
+                            const raw_t *row = lds + u * SS + r * rowlen;
+                            float sy = hw[0] * T::from_raw(row[hcol[0]]);
+#pragma unroll
+                            for (int j = 1; j < K; ++j) sy = fmaf(hw[j], T::from_raw(row[hcol[j]]), sy);
+                            hbuf[(u * nr + r) * tw + hx] = sy;
+                        }
+                    __syncthreads();  // every filtered row is in LDS
+                    const int lx = ox0 - tx * tw;
+                    for (int u = 0; u < nv; ++u) {
+                        const float *hu = hbuf + u * nr * tw;
+                        raw_t v[Q];
+#pragma unroll
+                        for (int q = 0; q < Q; ++q) {
+                            float sz = wy[0] * hu[(ry.idx[0] - r_lo) * tw + lx + q];
+#pragma unroll
+                            for (int j = 1; j < K; ++j)
+                                sz = fmaf(wy[j], hu[(ry.idx[j] - r_lo) * tw + lx + q], sz);
+                            v[q] = to_raw<T>(wz[0] * sz);
+                        }
+                        store_outputs<T, Q>(v, make_rsrc(yb + (size_t)(c0 + u) * op, op), yoff, vec_out);
+                    }
+                    continue;
+                }
+            }
             for (int u = 0; u < nv; ++u) {
                 const raw_t *sl = lds + u * SS;
                 raw_t tv[Q][KD][K][K];
