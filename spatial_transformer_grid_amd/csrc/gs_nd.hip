@@ -242,7 +242,50 @@ __device__ __forceinline__ void nd_channels(const NdParams &p, int n, int cbeg, 
     const uint32_t ip = p.in_plane_bytes, op = p.out_plane_bytes;
     const char *xn = (const char *)p.X + ((size_t)n * p.C) * ip;
     char *yn = (char *)p.Y + ((size_t)n * p.C) * op;
-    for (int c = cbeg; c < cend; ++c) {
+    int c = cbeg;
+    // With few taps, UC channels at a time: every load of the UC channels is
+    // issued before the first sum, so a lane keeps 8 loads in flight (one
+    // channel of 2 taps left it waiting on 2).  Each channel's sum is the
+    // same as below, term by term.
+    constexpr int UC = TAPS >= 8 ? 1 : 8 / TAPS;
+    if constexpr (UC > 1) {
+        double tw[TAPS];
+        bool tv[TAPS];
+        uint32_t to[TAPS];
+#pragma unroll
+        for (int t = 0; t < TAPS; ++t) {
+            double ww = 1.0;
+            bool valid = true;
+            uint32_t off = 0;
+#pragma unroll
+            for (int a = 0; a < R; ++a) {
+                const int s = (t >> (LK * (R - 1 - a))) & (K - 1);
+                ww = ww * pick(w[a], s);
+                valid = valid && pick(ok[a], s);
+                off = off * (uint32_t)p.in_ext[a] + (uint32_t)pick(idx[a], s);
+            }
+            tw[t] = ww;
+            tv[t] = valid;
+            to[t] = valid ? off * (uint32_t)T::bytes : GS_OOB;
+        }
+        for (; c + UC <= cend; c += UC) {
+            double xv[UC][TAPS];
+#pragma unroll
+            for (int u = 0; u < UC; ++u) {
+                const rsrc_t r = make_rsrc(xn + (size_t)(c + u) * ip, ip);
+#pragma unroll
+                for (int t = 0; t < TAPS; ++t) xv[u][t] = T::load(r, to[t]);
+            }
+#pragma unroll
+            for (int u = 0; u < UC; ++u) {
+                double acc = 0.0;
+#pragma unroll
+                for (int t = 0; t < TAPS; ++t) acc = tv[t] ? acc + tw[t] * xv[u][t] : acc;
+                T::store(acc, make_rsrc(yn + (size_t)(c + u) * op, op), o * (uint32_t)T::bytes);
+            }
+        }
+    }
+    for (; c < cend; ++c) {
         const rsrc_t r = make_rsrc(xn + (size_t)c * ip, ip);
         double acc = 0.0;
         auto tap = [&](int t) {
