@@ -244,10 +244,11 @@ __device__ __forceinline__ void nd_channels(const NdParams &p, int n, int cbeg, 
     char *yn = (char *)p.Y + ((size_t)n * p.C) * op;
     int c = cbeg;
     // With few taps, UC channels at a time: every load of the UC channels is
-    // issued before the first sum, so a lane keeps 8 loads in flight (one
-    // channel of 2 taps left it waiting on 2).  Each channel's sum is the
-    // same as below, term by term.
-    constexpr int UC = TAPS >= 8 ? 1 : 8 / TAPS;
+    // issued before the first sum, so a lane keeps 8 loads in flight (16 for
+    // 8 taps; one channel of 2 taps left it waiting on 2).  Measured on the
+    // 1-D, 2-D and 3-D linear workloads: 4 channels of 4 taps were slower
+    // than 2.  Each channel's sum is the same as below, term by term.
+    constexpr int UC = TAPS > 8 ? 1 : (TAPS == 8 ? 2 : 8 / TAPS);
     if constexpr (UC > 1) {
         double tw[TAPS];
         bool tv[TAPS];
