@@ -632,7 +632,11 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
         build_offsets(
             [&](int iz, int iy) { return ((R == 3 ? iz * p.in_h : 0) + iy) * p.in_w * T::bytes; },
             T::bytes, GS_OOB);
-        constexpr int UD = SEPARABLE ? 1 : (MODE == MODE_NEAREST ? 8 : (TAPS * Q >= 16 ? 1 : 2));
+        // channels whose loads are all issued before any is used (measured on
+        // a random flow: cubic 2 channels 25% faster than 1, 4 slower; 2D
+        // linear 4 channels 5% faster than 1)
+        constexpr int UD = SEPARABLE ? 1
+                           : (MODE == MODE_NEAREST ? 8 : (MODE == MODE_LINEAR && R == 2 ? 4 : 2));
         int c = cbeg;
         for (; c + UD <= cend; c += UD) {
             if constexpr (SEPARABLE) {
