@@ -633,10 +633,12 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
             [&](int iz, int iy) { return ((R == 3 ? iz * p.in_h : 0) + iy) * p.in_w * T::bytes; },
             T::bytes, GS_OOB);
         // channels whose loads are all issued before any is used (measured on
-        // a random flow: cubic 2 channels 25% faster than 1, 4 slower; 2D
-        // linear 4 channels 5% faster than 1)
+        // a random flow: 2D cubic 2 channels 25% faster than 1, 4 slower).
+        // Linear stays at 1: more would raise the registers of the whole
+        // kernel (the staged path's too: 81 -> 118 VGPRs in 2D, one block
+        // less per CU, 1.5% slower on stn2d_batch)
         constexpr int UD = SEPARABLE ? 1
-                           : (MODE == MODE_NEAREST ? 8 : (MODE == MODE_LINEAR && R == 2 ? 4 : 2));
+                           : (MODE == MODE_NEAREST ? 8 : (MODE == MODE_CUBIC ? 2 : 1));
         int c = cbeg;
         for (; c + UD <= cend; c += UD) {
             if constexpr (SEPARABLE) {
