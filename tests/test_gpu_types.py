@@ -13,7 +13,8 @@ X with double and fp32 grids in 1-D, 2D and 3D; fp16 and bf16 grids (widened
 exactly to fp32); every integer type with values spanning its range;
 non-finite locations; sizes that span several 256-location tiles with a
 ragged tail and channel counts that leave a remainder after the channel
-groups.
+groups; launches large enough that blocks take whole channel loops in
+batches, against one-channel launches and the oracle.
 """
 
 import itertools
@@ -228,3 +229,49 @@ def test_affine_grid_types(gsa, kind, rank, ac):
     got = g.view(torch.int16).cpu().numpy().view(np.uint16)
     ref32 = oracle.affine_grid(W.half_bits_to_f32(bits, kind), size, ac)
     assert np.array_equal(got, W.to_half_bits(ref32, kind))
+
+
+# Enough locations that a launch reaches its block target with one channel
+# group (each block takes every channel of its image), and channel counts
+# that leave a remainder after the kernel's channel batches (8 / taps
+# channels per batch; 2 for 8 taps).
+BATCH_CASES = [
+    # rank, mode, kind, X shape, grid shape
+    (1, "linear", "f32", (1, 7, 5000), (1, 600000, 1)),
+    (1, "nearest", "uint8", (1, 11, 5000), (1, 600000, 1)),
+    (1, "cubic", "f32", (1, 5, 5000), (1, 600000, 1)),
+    (2, "linear", "uint8", (1, 5, 64, 64), (1, 800, 800, 2)),
+    (2, "linear", "f64", (1, 3, 64, 64), (1, 800, 800, 2)),
+    (3, "linear", "f64", (1, 3, 16, 16, 16), (1, 86, 86, 86, 3)),
+    (3, "linear", "uint8", (1, 5, 16, 16, 16), (1, 86, 86, 86, 3)),
+]
+
+
+@pytest.mark.parametrize("ci", range(len(BATCH_CASES)))
+def test_channel_batches(gsa, ci):
+    """The any-rank kernel with whole channel loops per block: bit-identical
+    to one-channel launches (one channel per block, no batch) everywhere, and
+    to the oracle on the first locations."""
+    torch = torch_mod()
+    rank, mode, kind, xs, gsh = BATCH_CASES[ci]
+    rng = np.random.default_rng(70 + ci)
+    note("channel batches rank %d %s %s X=%s grid=%s" % (rank, mode, kind, xs, gsh))
+    if kind == "uint8":
+        X = rng.integers(0, 256, xs, dtype=np.uint8)
+    elif kind == "f64":
+        X = rng.normal(0, 1, xs)
+    else:
+        X = rng.uniform(-1, 1, xs).astype(np.float32)
+    G = rng.uniform(-1.1, 1.1, gsh).astype(np.float32)
+    Xd, Gd = tgpu(X), tgpu(G)
+    Y = gsa.grid_sample(Xd, Gd, mode, "zeros", 0)
+    for c in range(xs[1]):
+        Yc = gsa.grid_sample(Xd[:, c:c + 1].contiguous(), Gd, mode, "zeros", 0)
+        assert torch.equal(Y[:, c:c + 1], Yc), "channel %d differs from its own launch" % c
+    # the oracle on the first 2,000 locations (a grid of one row of them)
+    flat = G.reshape(1, -1, rank)[:, :2000]
+    sub = flat.reshape((1, 2000) + (1,) * (rank - 1) + (rank,))
+    got = gpu_values(Y, kind).reshape(1, xs[1], -1)[:, :, :2000]
+    ref = expected(oracle.grid_sample(X, sub, mode, "zeros", 0), kind).reshape(1, xs[1], -1)
+    assert np.array_equal(got, ref), "%d of %d outputs differ from the oracle" % (
+        (got != ref).sum(), got.size)
