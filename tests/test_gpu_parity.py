@@ -126,6 +126,31 @@ def test_grid_sample_direct_gather_path(gsa, rank, mode, pad, ac, kind):
           "direct %dD %s/%s/%d/%s" % (rank, mode, pad, ac, kind))
 
 
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", MODES)
+def test_direct_gather_channel_batches(gsa, mode, kind):
+    """Random locations over a plane too large to stage (the direct-gather
+    loop).  Cubic has 4,096 tiles here, so each block takes all 5 channels:
+    two 2-channel batches and a remainder; nearest and linear split the
+    channels over groups of 2.  Every mode equals one-channel launches bit
+    for bit, and the oracle at 4,096 sampled outputs."""
+    torch = torch_mod()
+    note("direct-gather channel batches %s %s" % (mode, kind))
+    rng = np.random.default_rng(77 + MODES.index(mode))
+    X = rng.uniform(-1, 1, (1, 5, 200, 200)).astype(np.float32)
+    G = rng.uniform(-1.2, 1.2, (1, 1024, 1024, 2)).astype(np.float32)
+    Xd, Xin = x_to_gpu(X, kind)
+    Gd = to_gpu_f32(G)
+    Y = gsa.grid_sample(Xd, Gd, mode, "reflection", 1)
+    for c in range(5):
+        Yc = gsa.grid_sample(Xd[:, c:c + 1].contiguous(), Gd, mode, "reflection", 1)
+        assert torch.equal(Y[:, c:c + 1], Yc), "channel %d differs from its own launch" % c
+    flat = np.random.default_rng(78).integers(0, Y.numel(), 4096)
+    ref = oracle.grid_sample_points(Xin, G, flat, mode, "reflection", 1)
+    got = from_gpu(Y).reshape(-1)[flat]
+    check(got, ref, mode, kind, np.abs(Xin).max(), "direct batches %s %s" % (mode, kind))
+
+
 @pytest.mark.parametrize("mode,pad", list(itertools.product(MODES, PADS)))
 def test_grid_sample_many_tiles(gsa, mode, pad):
     """Several tiles per image, ragged tail, channel count with a remainder."""
