@@ -83,6 +83,8 @@ CASES = [
     (1, 24, 48, 100, 110, 17, 64),   # three 32-byte slices, one ragged row segment
     (3, 64, 128, 91, 101, 5, 13),    # 12 planes of 64-byte slices (XCD order), narrow rows
     (2, 8, 16, 97, 99, 4, 300),      # one 32-byte slice, three row segments
+    (1, 128, 256, 96, 104, 1, 50),   # 8 slices, one row: one block per XCD (one counter)
+    (1, 128, 256, 96, 104, 2, 50),   # 8 slices, two rows: two counters per XCD
 ]
 
 
