@@ -21,11 +21,11 @@
 //     planes one after another: the random taps mostly hit L2;
 //  3. otherwise the tuned sampler runs as usual.
 //
-// All three launches are enqueued every time; the ones the probe does not
-// choose return at once.  The per-output arithmetic is the tuned sampler's:
-// the same taps and weights (GridSample page: Summary; Attributes
-// align_corners, mode, padding_mode), the same fp32 sum in the same tap
-// order, one rounding to T at the store.
+// All four launches (probe, copy, gather, tuned sampler) are enqueued every
+// time; the ones the probe does not choose return at once.  The per-output
+// arithmetic is the tuned sampler's: the same taps and weights (GridSample
+// page: Summary; Attributes align_corners, mode, padding_mode), the same fp32
+// sum in the same tap order, one rounding to T at the store.
 #include "gs_device.hpp"
 #include "gs_launch.hpp"
 #include "gs_layout.hpp"
@@ -131,12 +131,13 @@ __device__ __forceinline__ typename T::raw_t raw_at(const u32x4 &v, int e) {
     else return (uint16_t)(e & 1 ? v[e >> 1] >> 16 : v[e >> 1] & 0xffffu);
 }
 
-// Block order: with `xcd_pairs`, hardware block b runs on XCD b % 8 as that
-// XCD's (b / 8)-th block, which walks (image, slice) pairs x, x + 8, x + 16,
-// ... one after another, all row segments of a pair before the next;
-// otherwise blocks walk the pairs in order.  A block owns 128 consecutive
-// output locations of one row; lane t serves location t / 2 and channels
-// VW * (t % 2) .. + VW - 1 of the slice.
+// One logical block b: with `xcd_pairs`, b % 8 is the XCD whose sequence it
+// belongs to, and that XCD's sequence walks (image, slice) pairs x, x + 8,
+// x + 16, and so on, all row segments of a pair before the next; otherwise
+// the logical blocks walk the pairs in order.  A logical block owns
+// kBlock * 16 / SB consecutive output locations of one row; lane t serves
+// location t / (SB / 16) and channels VW * (t % (SB / 16)) .. + VW - 1 of
+// the slice.
 template <int MODE, int PAD, typename T, int SB>
 __device__ __forceinline__ void gather_block(const SampleParams &p, const void *Xt, int pairs,
                                              int tiles_per_pair, int xcd_pairs, int b);
