@@ -175,9 +175,9 @@ int gs_grid_sample_2d_ws(const void *X, int x_dtype, const int64_t *x_shape, con
  * Bytes of workspace gs_grid_sample_2d_ws can use for these shapes (host
  * only; the grid's values are not read): 8448 + N * C * H_in * W_in *
  * sizeof(element) (an 8,448-byte header of probe verdicts and tile
- * counters, then the copy of X), or 0 when the gather path does not apply.  Written to
- * *bytes.  Errors: GS_ERR_NULL, GS_ERR_DTYPE, GS_ERR_SHAPE (negative extent,
- * batch mismatch, last grid dim not 2).
+ * counters, then the copy of X), or 0 when the gather path does not apply.
+ * Written to *bytes.  Errors: GS_ERR_NULL, GS_ERR_DTYPE, GS_ERR_SHAPE
+ * (negative extent, batch mismatch, last grid dim not 2).
  */
 int gs_grid_sample_2d_workspace_size(int x_dtype, const int64_t *x_shape,
                                      const int64_t *grid_shape, int64_t *bytes);
