@@ -170,6 +170,9 @@ __global__ __launch_bounds__(kBlock) void grid_sample_gather(SampleParams p, con
     __syncthreads();
     int m = __builtin_amdgcn_readfirstlane(next[0]);
     for (int it = 0;; ++it) {
+        // (m outside [0, steps) only from a counter the probe did not reset;
+        // below steps <= 2^27 the product does not overflow)
+        if (m < 0 || m >= steps) break;
         const int k0 = (m * S + jc) * kGatherGrab;
         if (k0 >= steps) break;
         if (threadIdx.x == 0) next[(it + 1) & 1] = atomicAdd(ctr, 1);
