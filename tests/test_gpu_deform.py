@@ -192,6 +192,7 @@ CASES_CL = [
     (2, 32, 10, 10, 40, 2, 2, (1, 1), (1, 0, 0, 1), (1, 1), 1, 2),         # og changes inside a chunk
     (1, 32, 14, 15, 144, 5, 5, (1, 1), (2, 2, 2, 2), (1, 1), 1, 1),        # wide: 8 waves, no table
     (1, 96, 9, 11, 200, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 1, 3),         # wide, og changes in a chunk
+    (1, 32, 8, 9, 160, 1, 1, (1, 1), (0, 0, 0, 0), (1, 1), 1, 1),          # wide, a single chunk
 ]
 
 
