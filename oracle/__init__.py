@@ -28,6 +28,9 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _RESIZE_SRC = os.path.join(_HERE, "resize.c")
 _DEFORM_SRC = os.path.join(_HERE, "deform_conv.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# the same sources built with -fopenmp: the output loops run on every host
+# core (for timing the oracle and for large parity checks); values identical
+_OMP_LIB = os.path.join(_HERE, "liboracle_omp.so")
 
 MODES = {"linear": 0, "nearest": 1, "cubic": 2}
 PADDINGS = {"zeros": 0, "border": 1, "reflection": 2}
@@ -38,20 +41,34 @@ ASPECT_POLICIES = {"stretch": 0, "not_larger": 1, "not_smaller": 2}
 
 _lock = threading.Lock()
 _default = None
+_parallel = None
 
 # A handle from load_library() can be passed as `lib=` to run the same calls
 # against another build of the oracle source (used by the mutation tests).
 
 
+# ORACLE_LIB names another build of the oracle to load instead of
+# liboracle.so, and ORACLE_EXTRA_CFLAGS adds compiler flags to every build
+# made by build(): the sanitizer test uses both to run the pin batteries on an
+# AddressSanitizer / UndefinedBehaviorSanitizer build.
+_ENV_LIB = os.environ.get("ORACLE_LIB")
+
+
 def build(force: bool = True, src: str = _SRC, out: str = _LIB,
-          resize_src: str = _RESIZE_SRC, deform_src: str = _DEFORM_SRC) -> str:
+          resize_src: str = _RESIZE_SRC, deform_src: str = _DEFORM_SRC,
+          openmp: bool = False, extra_flags=()) -> str:
     """Compile oracle.c, resize.c and deform_conv.c (or other copies of them)
-    into one shared library."""
+    into one shared library.  With the default arguments both the serial
+    library and its OpenMP build are made."""
+    if out == _LIB and not openmp and src == _SRC:
+        build(force, src, _OMP_LIB, resize_src, deform_src, openmp=True)
     if not force and os.path.exists(out):
         return out
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
-           "-Wall", "-Wextra", "-o", tmp, src, resize_src, deform_src, "-lm"]
+    env_flags = os.environ.get("ORACLE_EXTRA_CFLAGS", "").split()
+    cmd = (["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+            "-Wall", "-Wextra"] + (["-fopenmp"] if openmp else []) + list(extra_flags) + env_flags
+           + ["-o", tmp, src, resize_src, deform_src, "-lm"])
     subprocess.run(cmd, check=True)
     os.replace(tmp, out)
     return out
@@ -74,6 +91,7 @@ def _bind(path: str):
                                               c_int, c_int, c_int, p_i64, i64, p_f64]
     lib.oracle_grid_sample_points.restype = c_int
     lib.oracle_abi_version.restype = c_int
+    lib.oracle_threads.restype = c_int
     lib.oracle_grid_sample_ex.argtypes = [p_f32, p_f64, c_int, i64, i64, p_i64, p_f32, p_f64,
                                           p_i64, c_int, c_int, c_int, p_f64]
     lib.oracle_grid_sample_ex.restype = c_int
@@ -104,10 +122,30 @@ def _load():
     global _default
     with _lock:
         if _default is None:
-            if not os.path.exists(_LIB):
-                build()
-            _default = _bind(_LIB)
+            if _ENV_LIB:
+                _default = _bind(_ENV_LIB)
+            else:
+                if not os.path.exists(_LIB):
+                    build()
+                _default = _bind(_LIB)
         return _default
+
+
+def parallel():
+    """Handle of the OpenMP build (same sources, same values, output loops on
+    every core OpenMP is given); pass it as `lib=`."""
+    global _parallel
+    with _lock:
+        if _parallel is None:
+            if not os.path.exists(_OMP_LIB):
+                build(force=True, out=_OMP_LIB, openmp=True)
+            _parallel = _bind(_OMP_LIB)
+        return _parallel
+
+
+def threads(lib=None) -> int:
+    """Threads the output loops of a build use (1 for the serial build)."""
+    return int((lib or _load()).oracle_threads())
 
 
 def load_library(path: str):
@@ -328,8 +366,9 @@ def resize_points(X: np.ndarray, out_shape, flat_index: np.ndarray, scales=None,
 
 
 def to_integer(values: np.ndarray, dtype) -> np.ndarray:
-    """The final cast of integer inputs (GridSample page, Outputs: computed as
-    floating point and cast to integer at the end).  Reading: truncation
+    """The final cast of integer inputs (GridSample page, Outputs: integer
+    inputs are interpolated in floating point and the result converted to
+    the integer type).  Reading: truncation
     toward zero, as a C conversion does, saturated to the range of the type
     (cubic weights can overshoot it); a NaN becomes 0."""
     dtype = np.dtype(dtype)

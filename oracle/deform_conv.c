@@ -43,6 +43,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* Every output is computed on its own; a build with -fopenmp splits the
+ * output loops over threads without changing any value. */
+#ifdef _OPENMP
+#define OR_PARALLEL_FOR _Pragma("omp parallel for schedule(dynamic, 256)")
+#else
+#define OR_PARALLEL_FOR
+#endif
+
 #define DC_MAX_RANK 3
 
 /* Linear interpolation of one plane of X (float64, spatial extents in_sp) at
@@ -205,10 +213,13 @@ int oracle_deform_conv(const double *X, int r, int64_t N, int64_t C, const int64
     if (dc_setup(&P, X, r, N, C, in_sp, Wt, OC, ksz, offset, B, mask, out_sp, strides, pads,
                  dilations, group, offset_group, coord_f32))
         return -1;
-    for (int64_t n = 0; n < N; ++n)
-        for (int64_t oc = 0; oc < OC; ++oc)
-            for (int64_t o = 0; o < P.out_count; ++o)
-                Y[(n * OC + oc) * P.out_count + o] = dc_value(&P, n, oc, o);
+    OR_PARALLEL_FOR
+    for (int64_t f = 0; f < N * OC * P.out_count; ++f) {
+        const int64_t o = f % P.out_count;
+        const int64_t oc = (f / P.out_count) % OC;
+        const int64_t n = f / (P.out_count * OC);
+        Y[f] = dc_value(&P, n, oc, o);
+    }
     return 0;
 }
 
@@ -227,10 +238,12 @@ int oracle_deform_conv_points(const double *X, int r, int64_t N, int64_t C,
     if (dc_setup(&P, X, r, N, C, in_sp, Wt, OC, ksz, offset, B, mask, out_sp, strides, pads,
                  dilations, group, offset_group, coord_f32))
         return -1;
+    for (int64_t i = 0; i < count; ++i)
+        if (flat[i] < 0 || flat[i] >= N * OC * P.out_count)
+            return -1;
+    OR_PARALLEL_FOR
     for (int64_t i = 0; i < count; ++i) {
         const int64_t f = flat[i];
-        if (f < 0 || f >= N * OC * P.out_count)
-            return -1;
         const int64_t o = f % P.out_count;
         const int64_t oc = (f / P.out_count) % OC;
         const int64_t n = f / (P.out_count * OC);

@@ -48,6 +48,18 @@
 #include <stdint.h>
 #include <stdlib.h>
 
+/* Every output is computed on its own.  A build with -fopenmp (used to time
+ * the oracle on all host cores, and for large parity checks) splits the
+ * output loops over threads; each output still runs the same code, so the
+ * values do not depend on the thread count.  Without -fopenmp the loops are
+ * serial. */
+#ifdef _OPENMP
+#include <omp.h>
+#define OR_PARALLEL_FOR _Pragma("omp parallel for schedule(dynamic, 256)")
+#else
+#define OR_PARALLEL_FOR
+#endif
+
 #define OR_MODE_LINEAR 0
 #define OR_MODE_NEAREST 1
 #define OR_MODE_CUBIC 2
@@ -65,6 +77,16 @@
 #define OR_COORD_LIMIT 16777216.0f
 
 int oracle_abi_version(void) { return 1; }
+
+/* Threads the output loops use: 1 unless built with -fopenmp. */
+int oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 int oracle_grid_sample_ex(const float *X, const double *Xd, int r, int64_t N, int64_t C,
                           const int64_t *in_spatial, const float *grid, const double *gridd,
@@ -116,9 +138,11 @@ int oracle_affine_grid(const float *theta, int r, int64_t N, const int64_t *out_
             return -1;
         count *= out_spatial[a];
     }
-    for (int64_t n = 0; n < N; ++n) {
+    OR_PARALLEL_FOR
+    for (int64_t nf = 0; nf < N * count; ++nf) {
+        const int64_t n = nf / count, flat = nf % count;
         const float *th = theta + n * r * (r + 1);
-        for (int64_t flat = 0; flat < count; ++flat) {
+        {
             /* split the flat location into per-axis indices (outermost first) */
             int64_t idx[OR_MAX_RANK];
             int64_t rem = flat;
@@ -170,9 +194,11 @@ int oracle_affine_grid_d(const double *theta, int r, int64_t N, const int64_t *o
             return -1;
         count *= out_spatial[a];
     }
-    for (int64_t n = 0; n < N; ++n) {
+    OR_PARALLEL_FOR
+    for (int64_t nf = 0; nf < N * count; ++nf) {
+        const int64_t n = nf / count, flat = nf % count;
         const double *th = theta + n * r * (r + 1);
-        for (int64_t flat = 0; flat < count; ++flat) {
+        {
             int64_t idx[OR_MAX_RANK];
             int64_t rem = flat;
             for (int a = r - 1; a >= 0; --a) {
@@ -597,14 +623,14 @@ int oracle_grid_sample_ex(const float *X, const double *Xd, int r, int64_t N, in
     if (setup_problem(&P, X, Xd, r, N, C, in_spatial, grid, gridd, out_spatial, mode, padding,
                       align_corners))
         return -1;
-    axis_taps taps[OR_MAX_RANK];
-    for (int64_t n = 0; n < N; ++n) {
-        for (int64_t o = 0; o < P.out_count; ++o) {
-            int live = location_taps(&P, n, o, taps);
-            for (int64_t c = 0; c < C; ++c) {
-                double v = live ? sample_value(&P, taps, n, c) : 0.0;
-                Y[(n * C + c) * P.out_count + o] = v;
-            }
+    OR_PARALLEL_FOR
+    for (int64_t no = 0; no < N * P.out_count; ++no) {
+        const int64_t n = no / P.out_count, o = no % P.out_count;
+        axis_taps taps[OR_MAX_RANK];
+        int live = location_taps(&P, n, o, taps);
+        for (int64_t c = 0; c < C; ++c) {
+            double v = live ? sample_value(&P, taps, n, c) : 0.0;
+            Y[(n * C + c) * P.out_count + o] = v;
         }
     }
     return 0;
@@ -635,11 +661,13 @@ int oracle_grid_sample_points_ex(const float *X, const double *Xd, int r, int64_
     if (setup_problem(&P, X, Xd, r, N, C, in_spatial, grid, gridd, out_spatial, mode, padding,
                       align_corners))
         return -1;
-    axis_taps taps[OR_MAX_RANK];
-    for (int64_t i = 0; i < count; ++i) {
-        int64_t f = flat[i];
-        if (f < 0 || f >= N * C * P.out_count)
+    for (int64_t i = 0; i < count; ++i)
+        if (flat[i] < 0 || flat[i] >= N * C * P.out_count)
             return -1;
+    OR_PARALLEL_FOR
+    for (int64_t i = 0; i < count; ++i) {
+        axis_taps taps[OR_MAX_RANK];
+        int64_t f = flat[i];
         int64_t o = f % P.out_count;
         int64_t nc = f / P.out_count;
         int64_t c = nc % C;

@@ -40,6 +40,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* Every output is computed on its own; a build with -fopenmp splits the
+ * output loops over threads without changing any value. */
+#ifdef _OPENMP
+#define OR_PARALLEL_FOR _Pragma("omp parallel for schedule(dynamic, 256)")
+#else
+#define OR_PARALLEL_FOR
+#endif
+
 #define RZ_MODE_NEAREST 0
 #define RZ_MODE_LINEAR 1
 #define RZ_MODE_CUBIC 2
@@ -323,6 +331,7 @@ int oracle_resize(const float *X, int rank, const int64_t *in_shape, const int64
     if (rz_setup(&P, X, rank, in_shape, out_shape, scales, mode, ct, nearest_mode, cubic_a,
                  exclude_outside))
         return -1;
+    OR_PARALLEL_FOR
     for (int64_t o = 0; o < P.out_count; ++o)
         Y[o] = rz_value(&P, o);
     return 0;
@@ -340,10 +349,11 @@ int oracle_resize_points(const float *X, int rank, const int64_t *in_shape,
     if (rz_setup(&P, X, rank, in_shape, out_shape, scales, mode, ct, nearest_mode, cubic_a,
                  exclude_outside))
         return -1;
-    for (int64_t i = 0; i < count; ++i) {
+    for (int64_t i = 0; i < count; ++i)
         if (flat[i] < 0 || flat[i] >= P.out_count)
             return -1;
+    OR_PARALLEL_FOR
+    for (int64_t i = 0; i < count; ++i)
         Y[i] = rz_value(&P, flat[i]);
-    }
     return 0;
 }

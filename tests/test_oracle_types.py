@@ -4,8 +4,8 @@
   the printed GridSample examples still hold to their printed precision;
 * fp16 grid: widened exactly to fp32, so it equals the fp32 oracle on the
   same values;
-* integer X (GridSample page, Outputs: intermediate values in floating point,
-  cast to integer at the end): hand-worked values of the cast -- truncation
+* integer X (GridSample page, Outputs: interpolation in floating point, the
+  result converted to the integer type): hand-worked values of the cast -- truncation
   toward zero, saturation at the type's range -- including a cubic overshoot
   worked out from Keys' weights by hand, and nearest copying integers exactly.
 """
