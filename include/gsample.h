@@ -45,21 +45,30 @@
 extern "C" {
 #endif
 
-#define GS_ABI_VERSION 1
+#define GS_ABI_VERSION 2
 
+/* Status codes.  Every entry point returns an int holding one of them (an
+ * enum passed as int keeps the ABI independent of the compiler's enum
+ * size).  GS_ERR_LAYOUT is reserved for strided tensors and is never
+ * returned: every tensor is dense and row-major. */
 typedef enum {
     GS_OK = 0,
     GS_ERR_NULL = 1,      /* a required pointer is NULL while its tensor is non-empty */
     GS_ERR_SHAPE = 2,     /* shapes inconsistent with each other or negative */
     GS_ERR_DTYPE = 3,     /* unsupported element type or type combination */
     GS_ERR_ATTR = 4,      /* mode / padding / align_corners out of range */
-    GS_ERR_TOO_LARGE = 5, /* an extent exceeds what the kernels index */
-    GS_ERR_HIP = 6        /* the HIP runtime reported an error at launch */
+    GS_ERR_LAYOUT = 5,    /* reserved: a tensor layout other than dense row-major */
+    GS_ERR_TOO_LARGE = 6, /* an extent exceeds what the kernels index */
+    GS_ERR_HIP = 7        /* the HIP runtime reported an error at launch */
 } gs_status;
 
 /* Element types (GridSample page, Type Constraints; bfloat16 from version 22):
  * X / Y of GridSample may be any of them; grids are GS_F32, GS_F16, GS_BF16
- * or GS_F64; Resize takes GS_F32, GS_F16 and GS_BF16; theta is GS_F32. */
+ * or GS_F64; Resize takes GS_F32, GS_F16 and GS_BF16; theta of
+ * gs_affine_grid is GS_F32, GS_F16, GS_BF16 or GS_F64 (the grid takes its
+ * type), theta of gs_affine_grid_sample_fused is GS_F32.  Types and the
+ * enums below are passed as int; the stream is a hipStream_t passed as
+ * void *, so the header needs no HIP include. */
 typedef enum {
     GS_F32 = 0,
     GS_F16 = 1,
@@ -175,7 +184,10 @@ int gs_grid_sample_2d_ws(const void *X, int x_dtype, const int64_t *x_shape, con
  * Bytes of workspace gs_grid_sample_2d_ws can use for these shapes (host
  * only; the grid's values are not read): 8448 + N * C * H_in * W_in *
  * sizeof(element) (an 8,448-byte header of probe verdicts and tile
- * counters, then the copy of X), or 0 when the gather path does not apply.
+ * counters, then the copy of X), or 0 when the gather path does not apply
+ * (element type, channel bytes, an image or its output planes of 2^31 bytes
+ * or more, or more than 2^27 (image, slice, row segment) tiles: then
+ * gs_grid_sample_2d_ws runs the plain sampler alone).
  * Written to *bytes.  Errors: GS_ERR_NULL, GS_ERR_DTYPE, GS_ERR_SHAPE
  * (negative extent, batch mismatch, last grid dim not 2).
  */

@@ -15,7 +15,8 @@ import threading
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgsample.so")
 
-GS_OK, GS_ERR_NULL, GS_ERR_SHAPE, GS_ERR_DTYPE, GS_ERR_ATTR, GS_ERR_TOO_LARGE, GS_ERR_HIP = range(7)
+(GS_OK, GS_ERR_NULL, GS_ERR_SHAPE, GS_ERR_DTYPE, GS_ERR_ATTR, GS_ERR_LAYOUT, GS_ERR_TOO_LARGE,
+ GS_ERR_HIP) = range(8)
 (GS_F32, GS_F16, GS_BF16, GS_F64, GS_I8, GS_U8, GS_I16, GS_U16, GS_I32, GS_U32, GS_I64,
  GS_U64) = range(12)
 MODES = {"linear": 0, "bilinear": 0, "nearest": 1, "cubic": 2, "bicubic": 2}

@@ -76,17 +76,42 @@ int hip_status(int rc) { return rc == 0 ? GS_OK : GS_ERR_HIP; }
 // of Y each below 2^31 bytes.
 constexpr int64_t kGatherHeaderBytes = 8448;  // 64 verdict words, then 64 counters 128 bytes apart
 
-int64_t gather_workspace_bytes(int x_dtype, const int64_t *x_shape, const int64_t *out_sp) {
-    if (!valid_x_dtype(x_dtype)) return 0;
+// Launch layout of the gather path: bytes of channels per slice (64 when the
+// channels fill them: fewer, longer loads per tap; else 32), (image, slice)
+// planes, tiles per plane (output rows x 256-lane row segments) and the tile
+// count the gather kernel hands out (planes rounded up to a multiple of the 8
+// XCDs when there are at least 8).
+struct GatherLayout {
+    int slice_bytes;
+    int64_t pairs, tiles_per_pair, blocks;
+};
+
+// True when the gather path applies to these shapes, with its layout.
+bool gather_layout(int x_dtype, const int64_t *x_shape, const int64_t *out_sp, GatherLayout *L) {
+    if (!valid_x_dtype(x_dtype)) return false;
     const int bytes = elem_bytes(x_dtype);
     const int64_t N = x_shape[0], C = x_shape[1];
-    if (N < 1 || C < 1 || (C * bytes) % 32 != 0) return 0;
+    if (N < 1 || C < 1 || (C * bytes) % 32 != 0) return false;
     int64_t img = 0, outp = 0;
-    if (!product_within(x_shape + 1, 3, kInt32Max / bytes, &img) || img == 0) return 0;
+    if (!product_within(x_shape + 1, 3, kInt32Max / bytes, &img) || img == 0) return false;
     const int64_t co[3] = {C, out_sp[0], out_sp[1]};
-    if (!product_within(co, 3, kInt32Max / bytes, &outp)) return 0;
-    if (N > (int64_t(1) << 40) / (img * bytes)) return 0;
-    return kGatherHeaderBytes + N * img * bytes;
+    if (!product_within(co, 3, kInt32Max / bytes, &outp)) return false;
+    if (N > (int64_t(1) << 40) / (img * bytes)) return false;
+    L->slice_bytes = (C * bytes) % 64 == 0 ? 64 : 32;
+    const int64_t locs = 256 * 16 / L->slice_bytes;
+    L->pairs = N * (C * bytes / L->slice_bytes);
+    L->tiles_per_pair = out_sp[0] * ((out_sp[1] + locs - 1) / locs);
+    L->blocks = (L->pairs >= 8 ? (L->pairs + 7) / 8 * 8 : L->pairs) * L->tiles_per_pair;
+    // the tile counters and indices are 32-bit; beyond this the plain
+    // sampler runs alone
+    return L->blocks <= kMaxBlocks * 8;
+}
+
+int64_t gather_workspace_bytes(int x_dtype, const int64_t *x_shape, const int64_t *out_sp) {
+    GatherLayout L;
+    if (!gather_layout(x_dtype, x_shape, out_sp, &L)) return 0;
+    return kGatherHeaderBytes + x_shape[0] * x_shape[1] * x_shape[2] * x_shape[3] *
+                                    elem_bytes(x_dtype);
 }
 
 // Shared validation and launch of the sampler (fused or not).  With a large
@@ -164,24 +189,17 @@ int sample(int r, const void *theta, const void *X, int x_dtype, const int64_t *
     p.gather_verdicts = nullptr;
     if (r == 2 && !theta && workspace && (uintptr_t)workspace % 256 == 0) {
         const int64_t need = gather_workspace_bytes(x_dtype, x_shape, out_sp);
-        if (need > 0 && workspace_bytes >= need) {
+        GatherLayout L;
+        if (need > 0 && workspace_bytes >= need && gather_layout(x_dtype, x_shape, out_sp, &L)) {
             gs::GatherParams g;
             g.verdicts = (int *)workspace;
             g.counters = (int *)((char *)workspace + 256);
             g.Xt = (char *)workspace + kGatherHeaderBytes;
-            // 64-byte slices when the channels fill them (fewer, longer
-            // loads per tap), else 32
-            const int sb = (C * bytes) % 64 == 0 ? 64 : 32;
-            const int64_t locs = 256 * 16 / sb;
-            const int64_t pairs = N * (C * bytes / sb);
-            const int64_t tpp = out.h * ((out.w + locs - 1) / locs);
-            g.slice_bytes = sb;
-            const int64_t blocks = (pairs >= 8 ? (pairs + 7) / 8 * 8 : pairs) * tpp;
-            if (blocks > kMaxBlocks * 8) return GS_ERR_TOO_LARGE;
-            g.pairs = (int)pairs;
-            g.tiles_per_pair = (int)tpp;
-            g.xcd_pairs = pairs >= 8;
-            g.gather_blocks = (int)blocks;
+            g.slice_bytes = L.slice_bytes;
+            g.pairs = (int)L.pairs;
+            g.tiles_per_pair = (int)L.tiles_per_pair;
+            g.xcd_pairs = L.pairs >= 8;
+            g.gather_blocks = (int)L.blocks;
             p.gather_verdicts = g.verdicts;
             const int rc = gs::launch_grid_gather(p, g, mode, padding, x_dtype,
                                                   in.w % (16 / bytes) == 0 && (uintptr_t)X % 16 == 0,
@@ -278,6 +296,7 @@ const char *gs_status_string(int status) {
     case GS_ERR_SHAPE: return "inconsistent or negative shape";
     case GS_ERR_DTYPE: return "unsupported element type";
     case GS_ERR_ATTR: return "mode, padding or align_corners out of range";
+    case GS_ERR_LAYOUT: return "tensor layout other than dense row-major (reserved)";
     case GS_ERR_TOO_LARGE: return "tensor too large for the kernels' indexing";
     case GS_ERR_HIP: return "HIP launch error";
     default: return "unknown status";

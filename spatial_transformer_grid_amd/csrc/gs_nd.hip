@@ -2,8 +2,9 @@
 // element type, for gfx950.
 //
 // The GridSample page defines the operator for X of rank r+2 in general
-// (Summary), for X of every numeric type -- integer inputs computed in
-// floating point and cast to integer at the end (Outputs) -- and for fp16,
+// (Summary), for X of every numeric type -- an integer input is interpolated
+// in floating point and only the result is converted back to the integer
+// type (Outputs) -- and for fp16,
 // fp32 and double grids (Type Constraints; bfloat16 from version 22).  The
 // tuned 2D/3D kernels cover fp32 / fp16 / bf16 X with fp32 grids; this kernel
 // covers the rest.

@@ -48,8 +48,8 @@ def test_library_exports_every_declared_symbol(gs):
 
 def test_abi_version_and_status_strings(gs):
     lib = gs.lib()
-    assert lib.gs_abi_version() == 1
-    for code in range(7):
+    assert lib.gs_abi_version() == 2
+    for code in range(8):
         s = lib.gs_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.gs_status_string(99).decode() == "unknown status"
@@ -84,8 +84,8 @@ def sample2d(gs, **kw):
     (dict(X=None), 1),
     (dict(Y=None), 1),
     (dict(grid=None), 1),
-    (dict(x_shape=[2, 3, 1 << 15, 1 << 14]), 5),  # input plane above 2^28
-    (dict(grid_shape=[2, 1 << 15, 1 << 14, 2]), 5),
+    (dict(x_shape=[2, 3, 1 << 15, 1 << 14]), 6),  # input plane above 2^28: GS_ERR_TOO_LARGE
+    (dict(grid_shape=[2, 1 << 15, 1 << 14, 2]), 6),
 ])
 def test_grid_sample_2d_rejects(gs, kw, status):
     assert sample2d(gs, **kw) == status
@@ -123,7 +123,7 @@ def test_affine_grid_rejects(gs):
     assert f([2, 3, 4, 5], theta=None) == 1
     assert f([2, 3, 4, 5], grid=None) == 1
     assert f([0, 3, 4, 5], theta=None, grid=None) == 0
-    assert f([2, 3, 1 << 16, 1 << 16]) == 5
+    assert f([2, 3, 1 << 16, 1 << 16]) == gs.GS_ERR_TOO_LARGE
     assert lib.gs_affine_grid(FAKE, 0, None, 4, 0, FAKE, None) == 1
 
 
@@ -187,7 +187,7 @@ def test_resize_shape_rules(gs):
     assert resize_call(gs, [2, 3, 0, 5], [2, 3, 8, 10]) == 2        # empty input, output not
     assert resize_call(gs, [2, 3, 4, 5], [2, 3, 0, 10], X=None, Y=None) == 0
     assert resize_call(gs, [0, 3, 4, 5], [0, 3, 8, 10], X=None, Y=None) == 0
-    assert resize_call(gs, [1, 1, 1 << 15, 1 << 14], [1, 1, 2, 2]) == 5
+    assert resize_call(gs, [1, 1, 1 << 15, 1 << 14], [1, 1, 2, 2]) == gs.GS_ERR_TOO_LARGE
 
 
 def test_resize_output_shape_matches_oracle(gs, oracle_mod):
@@ -253,7 +253,7 @@ def test_grid_sample_any_rank_rejects(gs):
     assert f([1, 2, 3], [1, 4, 1], gdt=4) == 3                # integer grids are not allowed
     assert f([1, 2, 3], [1, 4, 1], grid=None) == 1
     assert f([1, 2, 3], [1, 0, 1], X=None, Y=None, grid=None) == 0
-    assert f([1, 2, 1 << 28], [1, 4, 1], xdt=3) == 5          # 2^28 doubles: above 2^30 bytes
+    assert f([1, 2, 1 << 28], [1, 4, 1], xdt=3) == gs.GS_ERR_TOO_LARGE  # 2^28 doubles: above 2^30 bytes
 
 
 def test_binding_dtype_codes(gs):
@@ -287,7 +287,7 @@ def test_deform_conv_rejects(gs):
     assert f([1, 4, 8, 8], [6, 4, 3, 3], X=None) == 1
     assert f([1, 4, 8, 8], [6, 4, 3, 3], off=None) == 1
     assert f([0, 4, 8, 8], [6, 4, 3, 3], X=None, W=None, off=None, Y=None) == 0
-    assert f([1, 4, 1 << 24, 2], [6, 4, 3, 1]) == 5
+    assert f([1, 4, 1 << 24, 2], [6, 4, 3, 1]) == gs.GS_ERR_TOO_LARGE
     assert lib.gs_deform_conv(FAKE, 0, gs.int64_array([1, 4, 8, 8]), 4, FAKE,
                               gs.int64_array([6, 4, 3, 3]), FAKE, None, None, None, None, None, 1,
                               1, FAKE, None, -1, None) == 4         # negative workspace size
@@ -331,5 +331,12 @@ def test_grid_sample_2d_workspace_size(gs):
     assert ws((2, 8, 5, 7), (2, 3, 4, 2), gs.GS_F16) == 0      # 16-byte pixel runs
     assert ws((2, 8, 5, 7), (2, 3, 4, 2), gs.GS_F64) == 0
     assert ws((1, 64, 8192, 8192), (1, 4, 4, 2), gs.GS_F32) == 0  # 16 GiB image
+    # tall, narrow outputs over many slices (each image's Y just below
+    # 2^31 bytes): 8 images x 128 slices x (2^18 - 1) rows is more tiles than
+    # the gather kernel hands out (2^27), so only the plain sampler runs (no
+    # workspace); 4 images fit
+    tall = (1 << 18) - 1
+    assert ws((8, 4096, 4, 4), (8, tall, 1, 2), gs.GS_F16) == 0
+    assert ws((4, 4096, 4, 4), (4, tall, 1, 2), gs.GS_F16) == 8448 + 4 * 4096 * 16 * 2
     with pytest.raises(gs.GSError):
         ws((2, 8, 5, 7), (3, 3, 4, 2), gs.GS_F32)              # batch mismatch
