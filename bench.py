@@ -5,24 +5,38 @@ One step = the whole hot path over one batch of the 2D STN workload:
 theta (64,2,3) -> gs_affine_grid -> grid (64,128,128,2) -> gs_grid_sample_2d
 (bilinear, zeros, align_corners=0) on X (64,64,128,128) fp32 -> Y.
 
-Prints ONE JSON line.  `value` is output elements per second of the whole step
-(inputs resident in HBM, K back-to-back steps between two synchronisations).
-`roofline` describes the dominant kernel (the sampler): algorithmic bytes per
-launch (distinct X elements the launch reads with non-zero weight, the grid,
-and Y) divided by its mean duration, measured with events on the launch stream
-inside the timed region.  `traffic` is the HBM byte count from rocprofv3
-counters (profiles/sampler_traffic.json) when those were taken on the current
-kernel source, else null.  `cpu_baseline` times the plain CPU oracle on the
-same workload.  `paths` reports the other workload shapes, Resize included
-(kernel time only).
+Prints ONE JSON line.
+
+* `value`: output elements per second of the whole step (inputs resident in
+  HBM, K back-to-back steps between two synchronisations).
+* `roofline`: the dominant kernel (the sampler).  Algorithmic bytes per launch
+  (distinct X elements the launch reads with a non-zero weight, the grid, and
+  Y) divided by its median duration over launches that each follow a pass
+  over 512 MiB, which evicts the 256 MB Infinity Cache (events on the launch
+  stream); the mean duration of the launches inside the timed steps is kept
+  beside it (`achieved_in_loop`, `frac_in_loop`).  `traffic` is the HBM byte
+  count from rocprofv3 counters (profiles/counters_bench_paths.json) when they
+  were taken on the current kernel sources, else null.
+* `cpu_baseline`: the oracle (its OpenMP build, every host core) timed on the
+  same step; the same leg compares every bench path's output with the oracle
+  (`paths[i].max_err`).
+* `paths`: the other workload shapes, Resize, the other element types and the
+  DeformConv layer (kernel time only, cold and warm), each with the L2 hit
+  rate and HBM traffic of its kernel from the stored counters.
+
+`python bench.py --summarize-counters DIR...` turns rocprofv3 output (CSV)
+into profiles/counters_bench_paths.json and its Markdown summaries.
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
+import platform
 import statistics
 import sys
 import time
@@ -36,8 +50,41 @@ import workloads as W  # noqa: E402
 
 HBM_PEAK_GBPS = 8000.0
 METRIC = "GridSample output elem/s + achieved HBM GB/s (% of MI355X peak), 1 GPU"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sampler_traffic.json")
-KERNEL_SOURCES = ["gs_kernels.hip", "gs_device.hpp", "gs_launch.hpp", "gs_api.cpp"]
+PROFILES = os.path.join(ROOT, "profiles")
+COUNTER_FILE = os.path.join(PROFILES, "counters_bench_paths.json")
+CSRC = os.path.join(ROOT, "spatial_transformer_grid_amd", "csrc")
+KERNEL_SOURCES = ["gs_kernels.hip", "gs_gather.hip", "gs_resize.hip", "gs_nd.hip", "gs_deform.hip",
+                  "gs_device.hpp", "gs_launch.hpp", "gs_layout.hpp", "gs_api.cpp"]
+FLUSH_MIB = 512
+
+# The kernel (as the profiler names it) that dominates each path, and its
+# launch size in threads where one kernel runs at two sizes.
+HEADLINE_KERNEL = ("gs::grid_sample_kernel<2, 0, 0, gs::F32, false, true>", None)
+PATH_KERNELS = {
+    "stn2d_batch/linear-zeros": HEADLINE_KERNEL,
+    "stn2d_batch/nearest-border": ("gs::grid_sample_kernel<2, 1, 1, gs::F32, false, true>", None),
+    "stn2d_batch/linear-zeros-workspace": HEADLINE_KERNEL,
+    "stn2d_batch/fused-linear-zeros": ("gs::grid_sample_kernel<2, 0, 0, gs::F32, true, true>", None),
+    "flow2d_bicubic/cubic-reflection": ("gs::grid_sample_kernel<2, 2, 2, gs::F32, false, true>",
+                                        None),
+    "flow2d_bicubic/cubic-reflection-workspace": ("gs::grid_sample_gather<2, 2, gs::F32, 64>",
+                                                  None),
+    "vol3d/fused-linear-border": ("gs::grid_sample_kernel<3, 0, 1, gs::F32, true, true>", None),
+    "vol3d/unfused-linear-border": ("gs::grid_sample_kernel<3, 0, 1, gs::F32, false, true>", None),
+    "flow2d_half/bf16-linear-zeros": ("gs::grid_sample_kernel<2, 0, 0, gs::BF16, false, true>",
+                                      None),
+    "flow2d_half/f16-linear-zeros": ("gs::grid_sample_kernel<2, 0, 0, gs::F16, false, true>", None),
+    "stn2d_u8/linear-zeros": ("gs::grid_sample_nd_kernel<2, 0, float>", None),
+    "signal1d_f32/linear-zeros": ("gs::grid_sample_nd_kernel<1, 0, float>", None),
+    "vol3d_f64/linear-border": ("gs::grid_sample_nd_kernel<3, 0, double>", None),
+    "dcn2d_resnet/bf16": ("gs::deform_conv2d_cl<gs::BF16, 1, true, 8>", None),
+    "dcn2d_resnet/f32": ("gs::deform_conv2d_cl<gs::F32, 2, true, 4>", None),
+    "resize2d_up2_linear": ("gs::resize_kernel<1, gs::F32, true, false>", 1048576),
+    "resize2d_up2_nearest": ("gs::resize_kernel<0, gs::F32, true, false>", None),
+    "resize2d_up2_cubic": ("gs::resize_kernel<2, gs::F32, true, false>", None),
+    "resize2d_down2_linear": ("gs::resize_kernel<1, gs::F32, true, false>", 524288),
+    "resize3d_up2_linear": ("gs::resize_kernel<1, gs::F32, true, true>", None),
+}
 
 
 def log(msg):
@@ -48,7 +95,7 @@ def log(msg):
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "spatial_transformer_grid_amd", "csrc", name), "rb") as f:
+        with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -132,11 +179,32 @@ def footprint_elements(grid: np.ndarray, in_sp, mode, pad, ac) -> int:
     return int(total)
 
 
+# ------------------------------------------------------------------ counters
+
+def load_counters():
+    """Stored per-kernel counters when they were taken on the current kernel
+    sources, else None."""
+    if not os.path.exists(COUNTER_FILE):
+        return None
+    with open(COUNTER_FILE) as f:
+        data = json.load(f)
+    if data.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    return data
+
+
+def counter_row(counters, kernel, grid=None):
+    """The stored row of `kernel` (at launch size `grid` when given)."""
+    if counters is None:
+        return None
+    rows = [r for r in counters["kernels"] if r["kernel"] == kernel
+            and (grid is None or r["grid"] == grid)]
+    if len(rows) != 1:
+        return None
+    return rows[0]
+
+
 # ------------------------------------------------------------------- timing
-
-def elapsed_ms(pairs):
-    return [a.elapsed_time(b) for a, b in pairs]
-
 
 def time_kernel(torch, fn, reps, flush=None):
     """Median and mean duration (us) of fn(), events on the current stream."""
@@ -151,8 +219,20 @@ def time_kernel(torch, fn, reps, flush=None):
         b.record()
         ev.append((a, b))
     torch.cuda.synchronize()
-    ms = elapsed_ms(ev)
+    ms = [a.elapsed_time(b) for a, b in ev]
     return statistics.median(ms) * 1e3, statistics.mean(ms) * 1e3
+
+
+def make_flush(torch):
+    """A read-only pass over 512 MiB: evicts the Infinity Cache without
+    leaving dirty lines whose write-back would land in the next timed launch."""
+    buf = torch.ones(FLUSH_MIB * 1024 * 1024 // 4, device="cuda")
+    sink = torch.empty((), device="cuda")
+
+    def flush():
+        torch.sum(buf, dim=0, out=sink)
+
+    return flush, buf
 
 
 def copy_bandwidth(torch, mib=512, reps=10):
@@ -168,18 +248,31 @@ def copy_bandwidth(torch, mib=512, reps=10):
 
 # ------------------------------------------------------------------ paths
 
-def run_paths(torch, gsa, flush_buf):
-    """Kernel-only measurements of every workload shape (median of events)."""
-    out = []
+class ErrJob:
+    """A bench path's output kept on the host for the oracle comparison of the
+    CPU-baseline leg.  `ref(lib, b)` gives the oracle's float64 values of
+    image (or leading slice) b; `images` are the slices compared."""
 
-    # a read-only pass over 512 MiB evicts the Infinity Cache without leaving
-    # dirty lines whose write-back would land in the next timed launch
-    sink = torch.empty((), device="cuda")
+    def __init__(self, path, got, ref, images, mode, kind, xmax, exact=False):
+        self.path, self.got, self.ref, self.images = path, got, ref, images
+        self.mode, self.kind, self.xmax, self.exact = mode, kind, xmax, exact
 
-    def flush():
-        torch.sum(flush_buf, dim=0, out=sink)
 
-    def record(name, workload, kernel, us, outputs, x_bytes_full, x_bytes_fp, other_bytes, warm_us=None):
+def host_values(torch, Y):
+    """Y on the host as float64-convertible values (half types widened)."""
+    torch.cuda.synchronize()
+    if Y.dtype in (torch.float16, torch.bfloat16):
+        return Y.float().cpu().numpy()
+    return Y.cpu().numpy()
+
+
+def run_paths(torch, gsa, flush, counters):
+    """Kernel-only measurements of every workload shape (median of events),
+    and the outputs for the oracle comparison."""
+    out, jobs = [], []
+
+    def record(name, workload, kernel, us, outputs, x_bytes_full, x_bytes_fp, other_bytes,
+               warm_us=None):
         comp = x_bytes_fp + other_bytes
         rec = {"path": name, "workload": workload, "kernel": kernel, "kernel_us": round(us, 2),
                "out_elems_per_s": outputs / (us * 1e-6),
@@ -189,10 +282,12 @@ def run_paths(torch, gsa, flush_buf):
         if warm_us is not None:
             rec["warm_kernel_us"] = round(warm_us, 2)
             rec["warm_GBps"] = comp / (warm_us * 1e-6) / 1e9
+        attach_counters(rec, counters)
         out.append(rec)
-        log("%-28s %8.1f us  %7.0f GB/s  %.3f of peak" % (name, us, rec["GBps"], rec["frac_hbm_peak"]))
+        log("%-36s %8.1f us  %7.0f GB/s  %.3f of peak" % (name, us, rec["GBps"],
+                                                          rec["frac_hbm_peak"]))
 
-    # 2D STN batch: nearest + border and fused bilinear
+    # 2D STN batch: bilinear + zeros, nearest + border, fused bilinear
     w = W.WORKLOADS["stn2d_batch"]
     inp = W.make_inputs(w)
     n, c, h, wd = w.x_shape
@@ -204,96 +299,166 @@ def run_paths(torch, gsa, flush_buf):
     g_host = grid.cpu().numpy()
     outputs = w.outputs
     gbytes = grid.numel() * 4
+    xmax = float(np.abs(inp["X"]).max())
+    stn_ref = {}
+
+    def stn_ref_fn(mode, pad, inp=inp, size=size):
+        def ref(lib, b):
+            import oracle
+            key = ("grid", id(lib))
+            if key not in stn_ref:
+                stn_ref[key] = oracle.affine_grid(inp["theta"], size, 0, lib=lib)
+            return oracle.grid_sample(inp["X"][b:b + 1], stn_ref[key][b:b + 1], mode, pad, 0,
+                                      lib=lib)
+        return ref
+
     for mode, pad in (("linear", "zeros"), ("nearest", "border")):
         fp = footprint_elements(g_host, (h, wd), mode, pad, 0) * c * 4
-        us, _ = time_kernel(torch, lambda: gsa.grid_sample(X, grid, mode, pad, 0, out=Y), 30)
-        record("stn2d_batch/%s-%s" % (mode, pad), w.name, "gs_grid_sample_2d", us, outputs,
-               X.numel() * 4, fp, gbytes + outputs * 4)
+        fn = lambda: gsa.grid_sample(X, grid, mode, pad, 0, out=Y)
+        us, _ = time_kernel(torch, fn, 30, flush)
+        warm, _ = time_kernel(torch, fn, 30)
+        name = "stn2d_batch/%s-%s" % (mode, pad)
+        record(name, w.name, "gs_grid_sample_2d", us, outputs, X.numel() * 4, fp,
+               gbytes + outputs * 4, warm)
+        fn()
+        jobs.append(ErrJob(name, host_values(torch, Y), stn_ref_fn(mode, pad), range(n), mode,
+                           "f32", xmax))
     # the same call with a workspace: the probe keeps the staged sampler (the
     # difference is the probe and two launches that return at once)
     ws = torch.empty(gsa.grid_sample_2d_workspace_size(tuple(X.shape), tuple(grid.shape), 0),
                      dtype=torch.uint8, device="cuda")
     fp = footprint_elements(g_host, (h, wd), "linear", "zeros", 0) * c * 4
-    us, _ = time_kernel(torch, lambda: gsa.grid_sample(X, grid, "linear", "zeros", 0, out=Y,
-                                                       workspace=ws), 30)
-    record("stn2d_batch/linear-zeros-workspace", w.name, "gs_grid_sample_2d_ws (staged chosen)", us,
-           outputs, X.numel() * 4, fp, gbytes + outputs * 4)
+    fn = lambda: gsa.grid_sample(X, grid, "linear", "zeros", 0, out=Y, workspace=ws)
+    us, _ = time_kernel(torch, fn, 30, flush)
+    warm, _ = time_kernel(torch, fn, 30)
+    record("stn2d_batch/linear-zeros-workspace", w.name, "gs_grid_sample_2d_ws (staged chosen)",
+           us, outputs, X.numel() * 4, fp, gbytes + outputs * 4, warm)
+    fn()
+    jobs.append(ErrJob("stn2d_batch/linear-zeros-workspace", host_values(torch, Y),
+                       stn_ref_fn("linear", "zeros"), range(n), "linear", "f32", xmax))
     del ws
-    fp = footprint_elements(g_host, (h, wd), "linear", "zeros", 0) * c * 4
-    us, _ = time_kernel(torch, lambda: gsa.affine_grid_sample_fused(th, X, w.out_spatial, "linear",
-                                                                      "zeros", 0, out=Y), 30)
+    fn = lambda: gsa.affine_grid_sample_fused(th, X, w.out_spatial, "linear", "zeros", 0, out=Y)
+    us, _ = time_kernel(torch, fn, 30, flush)
+    warm, _ = time_kernel(torch, fn, 30)
     record("stn2d_batch/fused-linear-zeros", w.name, "gs_affine_grid_sample_fused", us, outputs,
-           X.numel() * 4, fp, th.numel() * 4 + outputs * 4)
+           X.numel() * 4, fp, th.numel() * 4 + outputs * 4, warm)
+    fn()
+    jobs.append(ErrJob("stn2d_batch/fused-linear-zeros", host_values(torch, Y),
+                       stn_ref_fn("linear", "zeros"), range(n), "linear", "f32", xmax))
     del X, Y, grid
 
     # 2D random flow, bicubic + reflection
     w = W.WORKLOADS["flow2d_bicubic"]
-    inp = W.make_inputs(w)
+    inp3 = W.make_inputs(w)
     n, c, h, wd = w.x_shape
-    X = torch.from_numpy(inp["X"]).cuda()
-    G = torch.from_numpy(inp["grid"]).cuda()
+    X = torch.from_numpy(inp3["X"]).cuda()
+    G = torch.from_numpy(inp3["grid"]).cuda()
     Y = torch.empty((n, c) + w.out_spatial, device="cuda")
-    fp = footprint_elements(inp["grid"], (h, wd), "cubic", "reflection", 1) * c * 4
-    us, _ = time_kernel(torch, lambda: gsa.grid_sample(X, G, "cubic", "reflection", 1, out=Y), 20)
+    fp = footprint_elements(inp3["grid"], (h, wd), "cubic", "reflection", 1) * c * 4
+    fn = lambda: gsa.grid_sample(X, G, "cubic", "reflection", 1, out=Y)
+    us, _ = time_kernel(torch, fn, 10, flush)
     record("flow2d_bicubic/cubic-reflection", w.name, "gs_grid_sample_2d", us, w.outputs,
            X.numel() * 4, fp, G.numel() * 4 + w.outputs * 4)
+
+    def flow_ref(lib, b):
+        import oracle
+        return oracle.grid_sample(inp3["X"][b:b + 1], inp3["grid"][b:b + 1], "cubic",
+                                  "reflection", 1, lib=lib)
+
+    fn()
+    Yplain = Y.clone()
+    jobs.append(ErrJob("flow2d_bicubic/cubic-reflection", host_values(torch, Y), flow_ref,
+                       range(n), "cubic", "f32", float(np.abs(inp3["X"]).max())))
     # with a workspace: probe, sliced channels-last copy of X, gather (the
-    # whole call is timed, the copy included)
+    # whole call is timed, the copy included); same outputs bit for bit
     ws = torch.empty(gsa.grid_sample_2d_workspace_size(tuple(X.shape), tuple(G.shape), 0),
                      dtype=torch.uint8, device="cuda")
-    us, _ = time_kernel(torch, lambda: gsa.grid_sample(X, G, "cubic", "reflection", 1, out=Y,
-                                                       workspace=ws), 20)
+    fn = lambda: gsa.grid_sample(X, G, "cubic", "reflection", 1, out=Y, workspace=ws)
+    us, _ = time_kernel(torch, fn, 20, flush)
     record("flow2d_bicubic/cubic-reflection-workspace", w.name,
            "gs_grid_sample_2d_ws (gather path)", us, w.outputs, X.numel() * 4, fp,
            G.numel() * 4 + w.outputs * 4)
-    del X, Y, G, inp, ws
+    fn()
+    torch.cuda.synchronize()
+    out[-1]["identical_to_plain_sampler"] = bool(torch.equal(Y, Yplain))
+    jobs.append(ErrJob("flow2d_bicubic/cubic-reflection-workspace", host_values(torch, Y),
+                       flow_ref, range(n), "cubic", "f32", float(np.abs(inp3["X"]).max())))
+    del X, Y, G, ws, Yplain
 
     # 3D volumetric, fused trilinear + border (working set fits the MALL:
     # report the flushed time as the figure and the warm one beside it)
     w = W.WORKLOADS["vol3d"]
-    inp = W.make_inputs(w)
+    inp4 = W.make_inputs(w)
     n, c = w.x_shape[:2]
-    X = torch.from_numpy(inp["X"]).cuda()
-    th = torch.from_numpy(inp["theta"]).cuda()
+    X = torch.from_numpy(inp4["X"]).cuda()
+    th = torch.from_numpy(inp4["theta"]).cuda()
     Y = torch.empty((n, c) + w.out_spatial, device="cuda")
     grid = gsa.affine_grid(th, (n, c) + w.out_spatial, 0)
     fp = footprint_elements(grid.cpu().numpy(), w.x_shape[2:], "linear", "border", 0) * c * 4
+    vol_size = (n, c) + w.out_spatial
+
+    def vol_ref(lib, b, c=c, out_spatial=w.out_spatial):
+        import oracle
+        G4 = oracle.affine_grid(inp4["theta"][b:b + 1], (1, c) + out_spatial, 0, lib=lib)
+        return oracle.grid_sample(inp4["X"][b:b + 1], G4, "linear", "border", 0, lib=lib)
+
+    xmax = float(np.abs(inp4["X"]).max())
     fn = lambda: gsa.affine_grid_sample_fused(th, X, w.out_spatial, "linear", "border", 0, out=Y)
     us, _ = time_kernel(torch, fn, 20, flush)
     warm, _ = time_kernel(torch, fn, 20)
     record("vol3d/fused-linear-border", w.name, "gs_affine_grid_sample_fused", us, w.outputs,
            X.numel() * 4, fp, th.numel() * 4 + w.outputs * 4, warm)
+    fn()
+    jobs.append(ErrJob("vol3d/fused-linear-border", host_values(torch, Y), vol_ref, range(n),
+                       "linear", "f32", xmax))
     fn = lambda: gsa.grid_sample(X, grid, "linear", "border", 0, out=Y)
     us, _ = time_kernel(torch, fn, 20, flush)
     warm, _ = time_kernel(torch, fn, 20)
     record("vol3d/unfused-linear-border", w.name, "gs_grid_sample_3d", us, w.outputs,
            X.numel() * 4, fp, grid.numel() * 4 + w.outputs * 4, warm)
-    del X, Y, grid
+    fn()
+    jobs.append(ErrJob("vol3d/unfused-linear-border", host_values(torch, Y), vol_ref, range(n),
+                       "linear", "f32", xmax))
+    del X, Y, grid, vol_size
 
     # 2D large half precision, smooth flow
     w = W.WORKLOADS["flow2d_half"]
-    inp = W.make_inputs(w)
+    inp5 = W.make_inputs(w)
     n, c, h, wd = w.x_shape
-    G = torch.from_numpy(inp["grid"]).cuda()
-    fp = footprint_elements(inp["grid"], (h, wd), "linear", "zeros", 0) * c * 2
+    G = torch.from_numpy(inp5["grid"]).cuda()
+    fp = footprint_elements(inp5["grid"], (h, wd), "linear", "zeros", 0) * c * 2
     for kind, tdt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
-        X = torch.from_numpy(inp["X_bits"][kind].view(np.int16)).cuda().view(tdt)
+        X = torch.from_numpy(inp5["X_bits"][kind].view(np.int16)).cuda().view(tdt)
         Y = torch.empty((n, c) + w.out_spatial, device="cuda", dtype=tdt)
-        us, _ = time_kernel(torch, lambda: gsa.grid_sample(X, G, "linear", "zeros", 0, out=Y), 20)
-        record("flow2d_half/%s-linear-zeros" % kind, w.name, "gs_grid_sample_2d", us, w.outputs,
-               X.numel() * 2, fp, G.numel() * 4 + w.outputs * 2)
-        del X, Y
+        fn = lambda: gsa.grid_sample(X, G, "linear", "zeros", 0, out=Y)
+        us, _ = time_kernel(torch, fn, 20, flush)
+        warm, _ = time_kernel(torch, fn, 20)
+        name = "flow2d_half/%s-linear-zeros" % kind
+        record(name, w.name, "gs_grid_sample_2d", us, w.outputs, X.numel() * 2, fp,
+               G.numel() * 4 + w.outputs * 2, warm)
+        fn()
+        xh = inp5["X_half_as_f32"][kind]
 
-    # other ranks and element types (the any-rank kernel)
+        def half_ref(lib, b, xh=xh):
+            import oracle
+            return oracle.grid_sample(xh[b:b + 1], inp5["grid"][b:b + 1], "linear", "zeros", 0,
+                                      lib=lib)
+
+        jobs.append(ErrJob(name, host_values(torch, Y), half_ref, range(n), "linear", kind,
+                           float(np.abs(xh).max())))
+        del X, Y
+    del G
+
+    # other ranks and element types (the any-rank kernel; bit-exact)
     for name, tw in W.TYPE_WORKLOADS.items():
-        inp = W.make_type_inputs(tw)
+        inpt = W.make_type_inputs(tw)
         n, c = tw.x_shape[:2]
-        X = torch.from_numpy(inp["X"]).cuda()
-        if inp["theta"] is not None:
-            th = torch.from_numpy(inp["theta"]).cuda()
+        X = torch.from_numpy(inpt["X"]).cuda()
+        if inpt["theta"] is not None:
+            th = torch.from_numpy(inpt["theta"]).cuda()
             G = gsa.affine_grid(th, (n, c) + tw.out_spatial, tw.align_corners)
         else:
-            G = torch.from_numpy(inp["grid"]).cuda()
+            G = torch.from_numpy(inpt["grid"]).cuda()
         Y = torch.empty((n, c) + tw.out_spatial, dtype=X.dtype, device="cuda")
         es = X.element_size()
         fp = footprint_elements(G.cpu().numpy(), tw.x_shape[2:], tw.mode, tw.padding,
@@ -302,17 +467,37 @@ def run_paths(torch, gsa, flush_buf):
         fn()
         us, _ = time_kernel(torch, fn, 20, flush)
         warm, _ = time_kernel(torch, fn, 20)
-        record("%s/%s-%s" % (name, tw.mode, tw.padding), name, "gs_grid_sample (any-rank kernel)",
-               us, tw.outputs, X.numel() * es, fp, G.numel() * G.element_size() + tw.outputs * es,
-               warm)
-        del X, Y, G, inp
+        pname = "%s/%s-%s" % (name, tw.mode, tw.padding)
+        record(pname, name, "gs_grid_sample (any-rank kernel)", us, tw.outputs, X.numel() * es,
+               fp, G.numel() * G.element_size() + tw.outputs * es, warm)
+        fn()
+
+        def type_ref(lib, b, tw=tw, inpt=inpt):
+            import oracle
+            n_, c_ = inpt["x_shape"][:2]
+            if inpt["theta"] is not None:
+                Gr = oracle.affine_grid(inpt["theta"][b:b + 1], (1, c_) + tuple(tw.out_spatial),
+                                        tw.align_corners, lib=lib)
+            else:
+                Gr = inpt["grid"][b:b + 1]
+            v = oracle.grid_sample(inpt["X"][b:b + 1], Gr, tw.mode, tw.padding, tw.align_corners,
+                                   lib=lib)
+            if inpt["X"].dtype == np.uint8:
+                return oracle.to_integer(v, np.uint8).astype(np.float64)
+            if inpt["X"].dtype == np.float32:
+                return v.astype(np.float32).astype(np.float64)
+            return v
+
+        jobs.append(ErrJob(pname, host_values(torch, Y), type_ref, range(n), tw.mode, "exact",
+                           float(np.abs(inpt["X"].astype(np.float64)).max()), exact=True))
+        del X, Y, G, inpt
 
     # DeformConv layers: matrix-core throughput (flops of the convolution)
     for name, dw in W.DEFORM_WORKLOADS.items():
-        inp = W.make_deform_inputs(dw)
+        inpd = W.make_deform_inputs(dw)
         for kind in dw.dtypes:
             tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[kind]
-            d = {k: torch.from_numpy(v).cuda().to(tdt) for k, v in inp.items()}
+            d = {k: torch.from_numpy(v).cuda().to(tdt) for k, v in inpd.items()}
             Y = torch.empty(dw.out_shape(), dtype=tdt, device="cuda")
             ws = torch.empty(gsa.deform_conv_workspace_size(
                 dw.x_shape, dw.w_shape, gsa.dtype_code(d["X"]), None, list(dw.pads), None,
@@ -325,21 +510,29 @@ def run_paths(torch, gsa, flush_buf):
             peak = 157.3 if kind == "f32" else 2500.0
             tflops = dw.flops / (us * 1e-6) / 1e12
             es = 4 if kind == "f32" else 2
-            io = (inp["X"].size + inp["W"].size + inp["offset"].size + inp["mask"].size
-                  + inp["B"].size + Y.numel()) * es
-            out.append({"path": "%s/%s" % (name, kind), "workload": name,
-                        "kernel": "gs_deform_conv (implicit GEMM, MFMA)", "kernel_us": round(us, 2),
-                        "bound": "mfma", "TFLOPs": tflops, "peak_TFLOPs": peak,
-                        "frac_mfma_peak": tflops / peak, "flops": dw.flops, "io_bytes": io,
-                        "GBps_io": io / (us * 1e-6) / 1e9})
-            log("%-28s %8.1f us  %7.1f TFLOP/s  %.3f of the %s MFMA peak" % (
-                "%s/%s" % (name, kind), us, tflops, tflops / peak, kind))
-            del d, Y
+            io = (inpd["X"].size + inpd["W"].size + inpd["offset"].size + inpd["mask"].size
+                  + inpd["B"].size + Y.numel()) * es
+            pname = "%s/%s" % (name, kind)
+            rec = {"path": pname, "workload": name,
+                   "kernel": "gs_deform_conv (implicit GEMM, MFMA)", "kernel_us": round(us, 2),
+                   "bound": "mfma", "TFLOPs": tflops, "peak_TFLOPs": peak,
+                   "frac_mfma_peak": tflops / peak, "flops": dw.flops, "io_bytes": io,
+                   "GBps_io": io / (us * 1e-6) / 1e9}
+            attach_counters(rec, counters)
+            out.append(rec)
+            log("%-36s %8.1f us  %7.1f TFLOP/s  %.3f of the %s MFMA peak" % (
+                pname, us, tflops, tflops / peak, kind))
+            fn()
+            exact = {k: (v.float().cpu().numpy() if kind != "f32" else inpd[k])
+                     for k, v in d.items()}
+            jobs.append(deform_job(pname, host_values(torch, Y), exact, dw, kind))
+            del d, Y, ws
 
     # Resize workloads (fp32): at their scales every input element has a
     # non-zero weight, so all of X is compulsory
     for name, rw in W.RESIZE_WORKLOADS.items():
-        X = torch.from_numpy(W.make_resize_input(rw)).cuda()
+        Xh = W.make_resize_input(rw)
+        X = torch.from_numpy(Xh).cuda()
         rank = X.dim()
         axes = list(range(rank - len(rw.scales), rank))
         shape = gsa.resize_output_shape(X.shape, list(rw.scales), None, axes)
@@ -352,8 +545,248 @@ def run_paths(torch, gsa, flush_buf):
         warm, _ = time_kernel(torch, fn, 20)
         record(name, name, "gs_resize", us, Y.numel(), X.numel() * 4, X.numel() * 4,
                Y.numel() * 4, warm)
+        fn()
+
+        def resize_ref(lib, b, Xh=Xh, shape=tuple(shape), rw=rw, scales=scales):
+            import oracle
+            return oracle.resize(Xh[b:b + 1], (1,) + shape[1:], scales, rw.mode,
+                                 rw.coordinate_transformation_mode, lib=lib)
+
+        jobs.append(ErrJob(name, host_values(torch, Y), resize_ref, range(shape[0]), rw.mode,
+                           "f32", float(np.abs(Xh).max())))
         del X, Y
+    return out, jobs
+
+
+def deform_job(pname, got, exact, dw, kind):
+    """Oracle comparison of a DeformConv path on 32,768 random outputs."""
+    n, oc, oh, ow = dw.out_shape()
+    idx = np.unique(np.random.default_rng(dw.seed).integers(0, n * oc * oh * ow, 32768))
+    flat = got.reshape(-1)[idx][None]
+
+    def ref(lib, b):
+        import oracle
+        return oracle.deform_conv(exact["X"], exact["W"], exact["offset"], exact["B"],
+                                  exact["mask"], pads=list(dw.pads), group=dw.group,
+                                  offset_group=dw.offset_group, flat_index=idx, lib=lib)[None]
+
+    job = ErrJob(pname, flat, ref, [0], "linear", "deform-" + kind, 1.0)
+    job.sample = "32,768 random outputs"
+    return job
+
+
+def attach_counters(rec, counters):
+    """L2 hit rate and HBM traffic of the path's kernel from the stored
+    counters (null when they were taken on other kernel sources)."""
+    key = PATH_KERNELS.get(rec["path"])
+    row = counter_row(counters, *key) if key else None
+    rec["profiled_kernel"] = key[0] if key else None
+    rec["l2_hit_rate"] = row.get("l2_hit_rate") if row else None
+    rec["hbm_read_bytes"] = row.get("hbm_read_bytes") if row else None
+    rec["hbm_write_bytes"] = row.get("hbm_write_bytes") if row else None
+
+
+# ----------------------------------------------------- CPU-baseline leg
+# The one place the benchmark runs the oracle: it times the oracle on the
+# step's workload and compares every path's output with it.
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def tolerance_ok(err, ref, job):
+    if job.exact:
+        return bool(np.all(err == 0))
+    if job.kind.startswith("deform"):
+        return None  # reported only; the tests hold it to the derived bound
+    if job.mode == "nearest":
+        return bool(np.all(err == 0))
+    if job.kind == "f32":
+        return bool(err.max(initial=0.0) <= (1e-5 if job.mode == "linear" else 1e-4) * job.xmax)
+    return bool(np.all(err <= 2e-2 * np.maximum(np.abs(ref), 1e-3 * job.xmax)))
+
+
+def cpu_baseline_leg(inp, size, jobs, paths):
+    import oracle
+
+    oracle.build(force=False)
+    par = oracle.parallel()
+    threads = oracle.threads(par)
+    times = []
+    for rep in range(3):
+        a = time.perf_counter()
+        G = oracle.affine_grid(inp["theta"], size, 0, lib=par)
+        oracle.grid_sample(inp["X"], G, "linear", "zeros", 0, lib=par)
+        times.append(time.perf_counter() - a)
+        log("cpu oracle (%d threads) rep %d: %.2f s" % (threads, rep, times[-1]))
+    outputs = int(np.prod(size))
+    # one thread, on the first 8 images (a bounded sample of the same step)
+    a = time.perf_counter()
+    G8 = oracle.affine_grid(inp["theta"][:8], (8,) + tuple(size[1:]), 0)
+    oracle.grid_sample(inp["X"][:8], G8, "linear", "zeros", 0)
+    single = 8 * int(np.prod(size[1:])) / (time.perf_counter() - a)
+    cpu = {"value": outputs / statistics.median(times), "unit": "output elem/s",
+           "cores": threads, "kind": "oracle",
+           "sample": "the full stn2d_batch step (AffineGrid + bilinear/zeros GridSample, "
+                     "67,108,864 outputs) on the oracle's OpenMP build, median of 3 runs",
+           "threads": threads, "host_cpus": len(os.sched_getaffinity(0)),
+           "cpu_model": cpu_model(), "single_thread_value": single,
+           "single_thread_sample": "the first 8 images of the same step, serial build"}
+
+    by_path = {p["path"]: p for p in paths}
+    for job in jobs:
+        t0 = time.perf_counter()
+        worst, worst_rel, ok = 0.0, 0.0, True
+        for b in job.images:
+            ref = job.ref(par, b)
+            got = np.asarray(job.got[b:b + 1], dtype=np.float64).reshape(ref.shape)
+            err = np.abs(got - ref)
+            worst = max(worst, float(err.max(initial=0.0)))
+            if job.kind in ("f16", "bf16"):
+                rel = err / np.maximum(np.abs(ref), 1e-3 * job.xmax)
+                worst_rel = max(worst_rel, float(rel.max(initial=0.0)))
+            r = tolerance_ok(err, ref, job)
+            ok = ok and (r is None or r)
+        rec = by_path.get(job.path)
+        if rec is not None:
+            rec["max_err"] = {"max_abs_err": worst, "max_abs_err_over_max_abs_x":
+                              worst / max(job.xmax, 1e-30),
+                              "within_tolerance": None if job.kind.startswith("deform") else ok,
+                              "compared": getattr(job, "sample", "every output")}
+            if job.kind in ("f16", "bf16"):
+                rec["max_err"]["max_rel_err"] = worst_rel
+        log("oracle check %-36s max err %.3g (%.1f s)" % (job.path, worst,
+                                                         time.perf_counter() - t0))
+        job.got = None
+    return cpu
+
+
+# ----------------------------------------------------- counter summaries
+
+def _read_csvs(dirs, suffix):
+    rows = []
+    for d in dirs:
+        for path in sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)):
+            with open(path, newline="") as f:
+                rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _short_name(name: str) -> str:
+    """Kernel name without 'void ' and its argument list."""
+    name = name.strip()
+    if name.startswith("void "):
+        name = name[5:]
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
+def _dispatch_counters(rows):
+    """{dispatch id: (kernel, grid, {counter: value})} from rocprofv3's
+    counter-collection rows."""
+    out = {}
+    for r in rows:
+        key = (r.get("Process_Id", ""), r["Dispatch_Id"])
+        if key not in out:
+            out[key] = (_short_name(r["Kernel_Name"]), int(r["Grid_Size"]), {})
+        name = r["Counter_Name"]
+        out[key][2][name] = out[key][2].get(name, 0.0) + float(r["Counter_Value"])
     return out
+
+
+def summarize_counters(run_dirs, copy_dirs, command, copy_command):
+    """Write profiles/counters_bench_paths.json (and .md): per kernel and
+    launch size, the median per dispatch of FETCH_SIZE, WRITE_SIZE (KiB),
+    TCC_HIT and TCC_MISS; FETCH/WRITE scaled by the factors that make the same
+    counters read 512 MiB for a plain 512 MiB device copy."""
+    copy = _dispatch_counters(_read_csvs(copy_dirs, "counter_collection.csv"))
+    cf = [v[2]["FETCH_SIZE"] for v in copy.values() if "copy" in v[0] and "FETCH_SIZE" in v[2]]
+    cw = [v[2]["WRITE_SIZE"] for v in copy.values() if "copy" in v[0] and "WRITE_SIZE" in v[2]]
+    copy_kib = 512 * 1024
+    fetch_scale = copy_kib / statistics.median(cf) if cf else None
+    write_scale = copy_kib / statistics.median(cw) if cw else None
+    disp = _dispatch_counters(_read_csvs(run_dirs, "counter_collection.csv"))
+    groups = {}
+    for kernel, grid, vals in disp.values():
+        if not kernel.startswith("gs::"):
+            continue
+        groups.setdefault((kernel, grid), []).append(vals)
+    kernels = []
+    for (kernel, grid), lst in sorted(groups.items()):
+        row = {"kernel": kernel, "grid": grid}
+        for cname in ("FETCH_SIZE", "WRITE_SIZE", "TCC_HIT_sum", "TCC_MISS_sum"):
+            v = [d[cname] for d in lst if cname in d]
+            if v:
+                row[cname] = statistics.median(v)
+                row["dispatches_" + cname] = len(v)
+        if "FETCH_SIZE" in row and fetch_scale:
+            row["hbm_read_bytes"] = row["FETCH_SIZE"] * 1024 * fetch_scale
+        if "WRITE_SIZE" in row and write_scale:
+            row["hbm_write_bytes"] = row["WRITE_SIZE"] * 1024 * write_scale
+        if "TCC_HIT_sum" in row and "TCC_MISS_sum" in row:
+            tot = row["TCC_HIT_sum"] + row["TCC_MISS_sum"]
+            row["l2_hit_rate"] = row["TCC_HIT_sum"] / tot if tot else None
+        kernels.append(row)
+    data = {"kernel_source_digest": kernel_source_digest(), "command": command,
+            "copy_command": copy_command, "copy_kib": copy_kib,
+            "copy_fetch_size_kib": statistics.median(cf) if cf else None,
+            "copy_write_size_kib": statistics.median(cw) if cw else None,
+            "fetch_scale": fetch_scale, "write_scale": write_scale, "kernels": kernels}
+    with open(COUNTER_FILE, "w") as f:
+        json.dump(data, f, indent=1)
+    lines = ["# HBM traffic and L2 hit rate per dispatch of every bench kernel", "",
+             "Commands (repository root, MI355X), one counter set per run:", ""]
+    for c in command:
+        lines.append("    " + c)
+    for c in copy_command:
+        lines.append("    " + c)
+    lines += ["",
+              "Median per dispatch of each (kernel, launch size in threads).  FETCH_SIZE is "
+              "scaled by %.3f and WRITE_SIZE by %.3f, the factors that make each read 512 MiB "
+              "for a plain 512 MiB device copy.  L2 hit rate = TCC_HIT / (TCC_HIT + TCC_MISS).  "
+              "Kernel source digest %s." % (fetch_scale or float("nan"), write_scale or
+                                           float("nan"), data["kernel_source_digest"]), "",
+              "| kernel | grid (threads) | dispatches | HBM read MB | HBM write MB | L2 hit rate |",
+              "|---|---|---|---|---|---|"]
+    for r in sorted(kernels, key=lambda r: -(r.get("hbm_read_bytes") or 0)):
+        lines.append("| `%s` | %d | %d | %s | %s | %s |" % (
+            r["kernel"], r["grid"], max(v for k, v in r.items() if k.startswith("dispatches_")),
+            "%.1f" % (r["hbm_read_bytes"] / 1e6) if "hbm_read_bytes" in r else "-",
+            "%.1f" % (r["hbm_write_bytes"] / 1e6) if "hbm_write_bytes" in r else "-",
+            "%.3f" % r["l2_hit_rate"] if r.get("l2_hit_rate") is not None else "-"))
+    with open(os.path.join(PROFILES, "counters_bench_paths.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log("wrote %s (%d kernels)" % (COUNTER_FILE, len(kernels)))
+
+
+def summarize_stats(stats_dirs, command, out_name):
+    """Markdown table of rocprofv3 --kernel-trace --stats output."""
+    rows = _read_csvs(stats_dirs, "kernel_stats.csv")
+    lines = ["# rocprofv3 kernel statistics", "", "Command (repository root, MI355X):", "",
+             "    " + command, "", "Kernel source digest %s." % kernel_source_digest(), "",
+             "| kernel | calls | average (us) | min (us) | max (us) |", "|---|---|---|---|---|"]
+    rows = sorted(rows, key=lambda r: -float(r["TotalDurationNs"]))
+    for r in rows:
+        lines.append("| `%s` | %s | %.1f | %.1f | %.1f |" % (
+            _short_name(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+    with open(os.path.join(PROFILES, out_name), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log("wrote profiles/%s (%d kernels)" % (out_name, len(rows)))
 
 
 # --------------------------------------------------------------------- main
@@ -363,11 +796,29 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle timing")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-paths", action="store_true", help="skip the other workload shapes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 512 MiB device copy (counter calibration)")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
+                    help="rocprofv3 --pmc output directories of bench runs: write "
+                         "profiles/counters_bench_paths.json (no GPU needed)")
+    ap.add_argument("--copy-dirs", nargs="+", default=[], metavar="DIR",
+                    help="with --summarize-counters: the copy-calibration runs")
+    ap.add_argument("--commands", nargs="+", default=[], help="commands to cite in summaries")
+    ap.add_argument("--summarize-stats", nargs="+", metavar="DIR",
+                    help="rocprofv3 --kernel-trace --stats output directories")
+    ap.add_argument("--stats-name", default="kernel_stats_bench.md")
     args = ap.parse_args()
+
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.copy_dirs,
+                           [c for c in args.commands if "copy-calibration" not in c],
+                           [c for c in args.commands if "copy-calibration" in c])
+        return
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats, " ".join(args.commands), args.stats_name)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -422,53 +873,45 @@ def main():
     elapsed = t1 - t0
     sampler_ms = [e[1].elapsed_time(e[2]) for e in events]
     affine_ms = [e[0].elapsed_time(e[1]) for e in events]
-    sampler_us = statistics.mean(sampler_ms) * 1e3
+    in_loop_us = statistics.mean(sampler_ms) * 1e3
     outputs = w.outputs
     value = args.steps * outputs / elapsed
+
+    # the sampler alone, each launch after a pass that evicts the Infinity
+    # Cache: the median is the roofline figure
+    flush, flush_buf = make_flush(torch)
+    sample = lambda: gsa.grid_sample(X, grid, "linear", "zeros", 0, out=Y)
+    time_kernel(torch, sample, 3, flush)
+    flushed_us, _ = time_kernel(torch, sample, 30, flush)
 
     g_host = grid.cpu().numpy()
     fp_elems = footprint_elements(g_host, (h, wd), "linear", "zeros", 0)
     x_fp_bytes = fp_elems * c * 4
     algo_bytes = x_fp_bytes + grid.numel() * 4 + outputs * 4
-    achieved = algo_bytes / (sampler_us * 1e-6) / 1e9
+    achieved = algo_bytes / (flushed_us * 1e-6) / 1e9
+    achieved_in_loop = algo_bytes / (in_loop_us * 1e-6) / 1e9
+    counters = load_counters()
+    row = counter_row(counters, *HEADLINE_KERNEL)
     traffic = None
-    digest = kernel_source_digest()
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            tr = json.load(f)
-        if tr.get("kernel_source_digest") == digest:
-            traffic = tr.get("hbm_bytes_per_launch")
-    log("step %.1f us (affine %.1f us, sampler %.1f us); sampler %.0f GB/s on %.1f MB" % (
-        elapsed / args.steps * 1e6, statistics.mean(affine_ms) * 1e3, sampler_us, achieved,
-        algo_bytes / 1e6))
+    if row and "hbm_read_bytes" in row and "hbm_write_bytes" in row:
+        traffic = row["hbm_read_bytes"] + row["hbm_write_bytes"]
+    log("step %.1f us (affine %.1f us, sampler %.1f us in the loop, %.1f us flushed median); "
+        "%.0f GB/s on %.1f MB" % (elapsed / args.steps * 1e6, statistics.mean(affine_ms) * 1e3,
+                                  in_loop_us, flushed_us, achieved, algo_bytes / 1e6))
 
     copy_gbps = copy_bandwidth(torch)
     log("device copy: %.0f GB/s" % copy_gbps)
 
-    paths = None
+    paths, jobs = None, []
     if not args.no_paths:
-        flush_buf = torch.ones(512 * 1024 * 1024 // 4, device="cuda")
-        paths = run_paths(torch, gsa, flush_buf)
-        del flush_buf
+        paths, jobs = run_paths(torch, gsa, flush, counters)
+    del flush_buf
 
     cpu = None
     if not args.no_cpu_baseline:
-        import oracle  # the CPU-baseline leg is the one place the benchmark runs the oracle
+        cpu = cpu_baseline_leg(inp, size, jobs, paths or [])
 
-        oracle.build(force=False)
-        th_np = inp["theta"]
-        times = []
-        for rep in range(3):
-            a = time.perf_counter()
-            G = oracle.affine_grid(th_np, size, 0)
-            oracle.grid_sample(inp["X"], G, "linear", "zeros", 0)
-            times.append(time.perf_counter() - a)
-            log("cpu oracle rep %d: %.2f s" % (rep, times[-1]))
-        cpu = {"value": outputs / statistics.median(times), "unit": "output elem/s", "cores": 1,
-               "kind": "oracle",
-               "sample": "the full stn2d_batch step (AffineGrid + bilinear/zeros GridSample, "
-                         "67,108,864 outputs), median of 3 runs, one thread"}
-
+    digest = kernel_source_digest()
     result = {
         "metric": METRIC,
         "value": value,
@@ -489,9 +932,15 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "gs_grid_sample_2d (bilinear, zeros, fp32)",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "timing": "median of 30 launches, each after a read pass over 512 MiB "
+                               "(Infinity Cache evicted); events on the launch stream",
+                     "kernel_us": flushed_us,
+                     "achieved_in_loop": achieved_in_loop,
+                     "frac_in_loop": achieved_in_loop / HBM_PEAK_GBPS,
+                     "kernel_us_in_loop": in_loop_us,
                      "algorithmic_bytes_per_launch": algo_bytes,
                      "x_footprint_fraction": fp_elems / (n * h * wd),
-                     "kernel_us": sampler_us,
+                     "l2_hit_rate": row.get("l2_hit_rate") if row else None,
                      "affine_grid_us": statistics.mean(affine_ms) * 1e3,
                      "copy_GBps": copy_gbps, "kernel_source_digest": digest},
         "cpu_baseline": cpu,

@@ -7,10 +7,13 @@
   dilations, conv groups, offset groups spanning one or two groups per conv
   group, kernels whose sampling table fits LDS and ones that sample on the
   fly (7x7), with and without mask and bias.  Tolerance per output, from the
-  sum of the absolute values of its terms S (the oracle on |X|, |W|, |mask|):
-  fp32 2e-5 * S; fp16 2e-3 * S and bf16 1e-2 * S (the sampled values are
-  rounded to the data type before the product) plus one unit in the last
-  place of the output type.
+  sum of the absolute values of its terms S (the oracle on |X|, |W|, |mask|,
+  plus |B|): fp32 2e-5 * S; fp16 and bf16 (u + (K + 8) * 2^-24) * S, where
+  u = 2^-11 (fp16) or 2^-8 (bf16) bounds the one rounding of each sampled
+  value to the data type before its product (exact in fp32), K products per
+  output are accumulated in fp32 (at most K roundings of 2^-24 relative to
+  S), and 8 more cover the fp32 interpolation and mask products; plus one
+  unit in the last place of the output type.
 * 2-D cases whose conv and offset groups hold multiples of 8 channels run on
   the channels-last copy of X by default: channel counts that fill whole
   chunks and ones padded up to the next chunk, offset groups that change
@@ -75,6 +78,14 @@ def rounded(ref, kind):
     return W.half_bits_to_f32(W.to_half_bits(ref.astype(np.float32), "bf16"), "bf16").astype(np.float64)
 
 
+def deform_rel_tol(kind, K):
+    """Bound on |gpu - oracle| / S for K products per output (see above)."""
+    if kind == "f32":
+        return 2e-5
+    u = 2.0 ** -11 if kind == "f16" else 2.0 ** -8
+    return u + (K + 8) * 2.0 ** -24
+
+
 def run(gsa, X, Wt, off, B, mask, kind, st=None, pd=None, dl=None, grp=1, og=1, exact=False,
         what="", no_workspace=False):
     torch = torch_mod()
@@ -95,7 +106,8 @@ def run(gsa, X, Wt, off, B, mask, kind, st=None, pd=None, dl=None, grp=1, og=1, 
                            None if Mo is None else np.abs(Mo), st, pd, dl, grp, og)
     if Bo is not None:
         S = S + np.abs(Bo).reshape((1, -1) + (1,) * (S.ndim - 2))
-    rel = {"f32": 2e-5, "f16": 2e-3, "bf16": 1e-2}[kind]
+    K = int(np.prod(Wt.shape[1:]))  # products summed per output
+    rel = deform_rel_tol(kind, K)
     ulp = {"f32": 0.0, "f16": 2.0 ** -10, "bf16": 2.0 ** -7}[kind]
     tol = rel * S + ulp * np.abs(ref) + 1e-30
     err = np.abs(got - ref)

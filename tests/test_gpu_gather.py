@@ -151,24 +151,29 @@ def test_without_workspace_is_the_plain_sampler(gsa):
     assert int(small.sum()) == 0            # too small: untouched
 
 
-def test_full_size_random_flow_sampled(gsa):
+def test_full_size_random_flow_all_elements(gsa):
     """The flow2d_bicubic workload at its full size through the gather path:
-    the verdicts, bit-equality with the plain sampler, and 4,096 sampled
-    outputs against the oracle computed one by one."""
+    the verdicts, bit-equality with the plain sampler, and every output
+    against the oracle (its OpenMP build), image by image."""
     torch = torch_mod()
     wl = W.WORKLOADS["flow2d_bicubic"]
     inp = W.make_inputs(wl)
     note("gather full-size flow2d_bicubic")
     X = torch.from_numpy(inp["X"]).cuda()
     G = torch.from_numpy(inp["grid"]).cuda()
-    Yw = gsa.grid_sample(X, G, wl.mode, wl.padding, wl.align_corners, workspace="auto")
+    need = gsa.grid_sample_2d_workspace_size(tuple(X.shape), tuple(G.shape), gsa.dtype_code(X))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    Yw = gsa.grid_sample(X, G, wl.mode, wl.padding, wl.align_corners, workspace=ws)
     Yp = gsa.grid_sample(X, G, wl.mode, wl.padding, wl.align_corners)
     torch.cuda.synchronize()
+    assert verdict_sum(ws) >= 32
     assert torch.equal(Yw, Yp)
-    rng = np.random.default_rng(11)
-    flat = rng.integers(0, Yw.numel(), 4096)
-    ref = oracle.grid_sample_points(inp["X"], inp["grid"], flat, wl.mode, wl.padding,
-                                    wl.align_corners)
-    got = Yw.reshape(-1)[torch.from_numpy(flat).cuda()].double().cpu().numpy()
-    assert np.abs(got - ref).max() <= 1e-4 * float(np.abs(inp["X"]).max())
-    del X, G, Yw, Yp
+    del ws, Yp, X, G
+    got = from_gpu(Yw)
+    del Yw
+    par = oracle.parallel()
+    xmax = float(np.abs(inp["X"]).max())
+    for b in range(got.shape[0]):
+        ref = oracle.grid_sample(inp["X"][b:b + 1], inp["grid"][b:b + 1], wl.mode, wl.padding,
+                                 wl.align_corners, lib=par)
+        check(got[b:b + 1], ref, wl.mode, "f32", xmax, "gather full-size image %d" % b)
