@@ -429,6 +429,30 @@ int gs_deform_conv_workspace_size(int dtype, const int64_t *x_shape, int x_rank,
                                   const int64_t *pads, const int64_t *dilations, int group,
                                   int offset_group, int64_t *bytes);
 
+/*
+ * gs_deform_conv without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments (workspace and
+ * workspace_bytes left out), results and errors as gs_deform_conv called with
+ * a workspace of gs_deform_conv_workspace_size() bytes.
+ *
+ * The channels-last kernel's scratch space (the copy of X and the packed W)
+ * lives in a 64 MiB device array inside the library: each GPU the library
+ * runs on holds its own copy from the first call on that device until the
+ * process ends.  Shapes that need more than 64 MiB return GS_ERR_TOO_LARGE
+ * (no work is enqueued); shapes that need none (other ranks, types or
+ * channel counts) run as gs_deform_conv without a workspace.  The call
+ * allocates nothing.  Every call on a GPU shares that GPU's array, which
+ * keeps the last call's contents (every call rewrites what it reads): calls
+ * that may run at the same time on one GPU (on different streams, or from
+ * different threads) race and must be serialised by the caller.
+ */
+int gs_deform_conv_noalloc(const void *X, int dtype, const int64_t *x_shape, int x_rank,
+                           const void *W, const int64_t *w_shape, const void *offset,
+                           const void *B, const void *mask, const int64_t *strides,
+                           const int64_t *pads, const int64_t *dilations, int group,
+                           int offset_group, void *Y, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

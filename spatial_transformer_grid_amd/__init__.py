@@ -22,6 +22,7 @@ from ._binding import (  # noqa: F401
     affine_grid,
     affine_grid_sample_fused,
     deform_conv,
+    deform_conv_noalloc,
     deform_conv_output_shape,
     deform_conv_workspace_size,
     dtype_code,
@@ -34,6 +35,7 @@ from ._binding import (  # noqa: F401
 )
 
 __all__ = ["affine_grid", "grid_sample", "affine_grid_sample_fused", "resize",
-           "resize_output_shape", "resize_to", "deform_conv", "deform_conv_output_shape",
+           "resize_output_shape", "resize_to", "deform_conv", "deform_conv_noalloc",
+           "deform_conv_output_shape",
            "deform_conv_workspace_size", "dtype_code", "grid_sample_2d_workspace_size",
            "GSError", "lib"]

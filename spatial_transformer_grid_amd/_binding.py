@@ -46,6 +46,8 @@ SIGNATURES = {
                         _P, _P, ctypes.c_int64, _P], _I),
     "gs_deform_conv_workspace_size": ([_I, _PI64, _I, _PI64, _PI64, _PI64, _PI64, _I, _I, _PI64],
                                       _I),
+    "gs_deform_conv_noalloc": ([_P, _I, _PI64, _I, _P, _PI64, _P, _P, _P, _PI64, _PI64, _PI64, _I,
+                                _I, _P, _P], _I),
     "gs_resize_output_shape": ([_PI64, _I, _PI64, _I, _PF32, _PI64, _I, _PI64], _I),
     "gs_resize": ([_P, _I, _PI64, _I, _PI64, _PF32, _I, _I, _I, ctypes.c_float, _I, _P, _P], _I),
 }
@@ -300,14 +302,8 @@ def deform_conv_output_shape(x_shape, w_shape, strides=None, pads=None, dilation
     return (x_shape[0], w_shape[0], *out)
 
 
-def deform_conv(X, W, offset, B=None, mask=None, strides=None, pads=None, dilations=None,
-                group: int = 1, offset_group: int = 1, out=None, stream=None, workspace=None):
-    """DeformConv(X, W, offset, B, mask) -> Y on the GPU (gs_deform_conv).
-
-    Attribute names follow the convolution operators (strides, pads as begins
-    then ends, dilations, group, offset_group).  `workspace`: a device tensor
-    of scratch bytes; None takes one of the size the library asks for from
-    torch's allocator, and an empty tensor runs without one."""
+def _deform_tensors(X, W, offset, B, mask, strides, pads, dilations, offset_group, out):
+    """Checked device tensors of a DeformConv call and its output."""
     X = _device_tensor(X, "X")
     W = _device_tensor(W, "W")
     offset = _device_tensor(offset, "offset")
@@ -332,9 +328,28 @@ def deform_conv(X, W, offset, B=None, mask=None, strides=None, pads=None, dilati
                                                        *shape[2:]),))
     if B is not None and tuple(B.shape) != (W.shape[0],):
         raise ValueError("B must have shape (%d,)" % W.shape[0])
-    Y = _out_tensor(out, shape, X)
-    ptr = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
-    arr = lambda v: int64_array(v) if v is not None else None
+    return X, W, offset, B, mask, _out_tensor(out, shape, X)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _arr(v):
+    return int64_array(v) if v is not None else None
+
+
+def deform_conv(X, W, offset, B=None, mask=None, strides=None, pads=None, dilations=None,
+                group: int = 1, offset_group: int = 1, out=None, stream=None, workspace=None):
+    """DeformConv(X, W, offset, B, mask) -> Y on the GPU (gs_deform_conv).
+
+    Attribute names follow the convolution operators (strides, pads as begins
+    then ends, dilations, group, offset_group).  `workspace`: a device tensor
+    of scratch bytes; None takes one of the size the library asks for from
+    torch's allocator, and an empty tensor runs without one."""
+    X, W, offset, B, mask, Y = _deform_tensors(X, W, offset, B, mask, strides, pads, dilations,
+                                               offset_group, out)
+    ptr, arr = _ptr, _arr
     need = ctypes.c_int64(0)
     _check(lib().gs_deform_conv_workspace_size(
         dtype_code(X), int64_array(X.shape), X.dim(), int64_array(W.shape), arr(strides),
@@ -349,6 +364,24 @@ def deform_conv(X, W, offset, B=None, mask=None, strides=None, pads=None, dilati
                               arr(pads), arr(dilations), int(group), int(offset_group), ptr(Y),
                               ws_ptr, ws_bytes, _stream(stream, X.device))
     _check(st, "gs_deform_conv")
+    return Y
+
+
+def deform_conv_noalloc(X, W, offset, B=None, mask=None, strides=None, pads=None,
+                        dilations=None, group: int = 1, offset_group: int = 1, out=None,
+                        stream=None):
+    """DeformConv through gs_deform_conv_noalloc: the library's own 64 MiB
+    scratch array per GPU instead of a workspace (for callers that cannot
+    allocate; pass `out` to allocate nothing here either).  Calls that may
+    overlap on one GPU race on that array."""
+    X, W, offset, B, mask, Y = _deform_tensors(X, W, offset, B, mask, strides, pads, dilations,
+                                               offset_group, out)
+    st = lib().gs_deform_conv_noalloc(_ptr(X), dtype_code(X), int64_array(X.shape), X.dim(),
+                                      _ptr(W), int64_array(W.shape), _ptr(offset), _ptr(B),
+                                      _ptr(mask), _arr(strides), _arr(pads), _arr(dilations),
+                                      int(group), int(offset_group), _ptr(Y),
+                                      _stream(stream, X.device))
+    _check(st, "gs_deform_conv_noalloc")
     return Y
 
 

@@ -25,7 +25,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgsample.so")
 BUILD_DIR = os.path.join(PKG, "_build")
 
-SOURCES = ["gs_kernels.hip", "gs_gather.hip", "gs_resize.hip", "gs_nd.hip", "gs_deform.hip", "gs_api.cpp"]
+SOURCES = ["gs_kernels.hip", "gs_gather.hip", "gs_resize.hip", "gs_nd.hip", "gs_deform.hip",
+           "gs_noalloc.hip", "gs_api.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950",

@@ -36,7 +36,7 @@ def test_header_declares_the_expected_entry_points():
         "gs_abi_version", "gs_status_string", "gs_affine_grid", "gs_grid_sample_2d",
         "gs_grid_sample_3d", "gs_affine_grid_sample_fused", "gs_resize", "gs_resize_output_shape",
         "gs_grid_sample", "gs_deform_conv", "gs_deform_conv_workspace_size",
-        "gs_grid_sample_2d_ws", "gs_grid_sample_2d_workspace_size"])
+        "gs_grid_sample_2d_ws", "gs_grid_sample_2d_workspace_size", "gs_deform_conv_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(gs):
@@ -340,3 +340,16 @@ def test_grid_sample_2d_workspace_size(gs):
     assert ws((4, 4096, 4, 4), (4, tall, 1, 2), gs.GS_F16) == 8448 + 4 * 4096 * 16 * 2
     with pytest.raises(gs.GSError):
         ws((2, 8, 5, 7), (3, 3, 4, 2), gs.GS_F32)              # batch mismatch
+
+
+def test_deform_conv_noalloc_rejects_beyond_its_array(gs):
+    """A layer whose channels-last scratch exceeds the library's 64 MiB
+    array is rejected before anything is enqueued (host-side check)."""
+    f = gs.lib().gs_deform_conv_noalloc
+    a = gs.int64_array
+    st = f(FAKE, gs.GS_F32, a([8, 512, 64, 64]), 4, FAKE, a([16, 512, 3, 3]), FAKE, None, None,
+           None, None, None, 1, 1, FAKE, None)
+    assert st == gs.GS_ERR_TOO_LARGE
+    st = f(FAKE, 99, a([8, 512, 64, 64]), 4, FAKE, a([16, 512, 3, 3]), FAKE, None, None, None,
+           None, None, 1, 1, FAKE, None)
+    assert st == gs.GS_ERR_DTYPE
