@@ -714,17 +714,37 @@ def summarize_counters(run_dirs, copy_dirs, command, copy_command):
     TCC_HIT and TCC_MISS; FETCH/WRITE scaled by the factors that make the same
     counters read 512 MiB for a plain 512 MiB device copy."""
     copy = _dispatch_counters(_read_csvs(copy_dirs, "counter_collection.csv"))
-    cf = [v[2]["FETCH_SIZE"] for v in copy.values() if "copy" in v[0] and "FETCH_SIZE" in v[2]]
-    cw = [v[2]["WRITE_SIZE"] for v in copy.values() if "copy" in v[0] and "WRITE_SIZE" in v[2]]
+    # the 512 MiB copies are the largest copy dispatches of those runs
+    big = max((v[1] for v in copy.values() if "copy" in v[0].lower()), default=0)
+    sel = [v[2] for v in copy.values() if "copy" in v[0].lower() and v[1] == big]
+    cf = [d["FETCH_SIZE"] for d in sel if "FETCH_SIZE" in d]
+    cw = [d["WRITE_SIZE"] for d in sel if "WRITE_SIZE" in d]
     copy_kib = 512 * 1024
     fetch_scale = copy_kib / statistics.median(cf) if cf else None
     write_scale = copy_kib / statistics.median(cw) if cw else None
-    disp = _dispatch_counters(_read_csvs(run_dirs, "counter_collection.csv"))
+    # the bench launches the same kernels in the same order in every run, so
+    # a dispatch id names the same launch in each counter run: join them
+    merged = {}
+    for d in run_dirs:
+        for (_, did), (kernel, grid, vals) in _dispatch_counters(
+                _read_csvs([d], "counter_collection.csv")).items():
+            k0, g0, v0 = merged.setdefault(did, (kernel, grid, {}))
+            if (k0, g0) != (kernel, grid):
+                raise ValueError("dispatch %s is %s in one run and %s in another: the runs "
+                                 "did not launch the same sequence" % (did, k0, kernel))
+            v0.update(vals)
     groups = {}
-    for kernel, grid, vals in disp.values():
+    for kernel, grid, vals in merged.values():
         if not kernel.startswith("gs::"):
             continue
         groups.setdefault((kernel, grid), []).append(vals)
+    # launches that return at once because the device chose the other 2-D
+    # path (staged sampler or gather) move almost nothing: left out
+    for key, lst in groups.items():
+        moved = [d.get("FETCH_SIZE", 0.0) + d.get("WRITE_SIZE", 0.0) for d in lst]
+        top = max(moved) if moved else 0.0
+        active = [d for d, m in zip(lst, moved) if m >= 0.01 * top]
+        groups[key] = active if active else lst
     kernels = []
     for (kernel, grid), lst in sorted(groups.items()):
         row = {"kernel": kernel, "grid": grid}

@@ -65,3 +65,50 @@ def test_resize_workloads_read_every_input_element(oracle_mod, name):
     Y = oracle_mod.resize(X, shape, [1.0] + list(w.scales), w.mode,
                           w.coordinate_transformation_mode)
     assert (np.abs(Y).reshape(count, -1).max(1) > 0).all()
+
+
+HEADER = ('"Correlation_Id","Dispatch_Id","Agent_Id","Queue_Id","Process_Id","Thread_Id",'
+          '"Grid_Size","Kernel_Id","Kernel_Name","Workgroup_Size","LDS_Block_Size","Scratch_Size",'
+          '"VGPR_Count","Accum_VGPR_Count","SGPR_Count","Counter_Name","Counter_Value",'
+          '"Start_Timestamp","End_Timestamp"')
+
+
+def _write_run(path, pid, rows):
+    path.mkdir()
+    lines = [HEADER]
+    for did, kernel, grid, counter, value in rows:
+        lines.append('%d,%d,"Agent 1",1,%d,%d,%d,1,"%s",256,0,0,8,0,32,"%s",%f,1,2' % (
+            did, did, pid, pid, grid, kernel, counter, value))
+    (path / "run_counter_collection.csv").write_text("\n".join(lines) + "\n")
+
+
+def test_counter_summary_joins_runs_and_drops_skipped_launches(tmp_path, monkeypatch):
+    """The summary joins the counter runs by dispatch id, scales FETCH_SIZE /
+    WRITE_SIZE by the copy calibration, and leaves out launches that moved
+    almost nothing (the device chose the other 2-D path)."""
+    k = "void gs::grid_sample_kernel<2, 0, 0, gs::F32, false, true>(gs::SampleParams)"
+    copy = "__amd_rocclr_copyBuffer"
+    _write_run(tmp_path / "f", 1, [(1, k, 1024, "FETCH_SIZE", 100.0), (2, k, 1024, "FETCH_SIZE", 0.01),
+                                   (3, k, 1024, "FETCH_SIZE", 120.0)])
+    _write_run(tmp_path / "w", 2, [(1, k, 1024, "WRITE_SIZE", 50.0), (2, k, 1024, "WRITE_SIZE", 0.0),
+                                   (3, k, 1024, "WRITE_SIZE", 50.0)])
+    _write_run(tmp_path / "t", 3, [(d, k, 1024, c, v) for d, c, v in
+                                   [(1, "TCC_HIT_sum", 30), (1, "TCC_MISS_sum", 70),
+                                    (2, "TCC_HIT_sum", 1), (2, "TCC_MISS_sum", 1),
+                                    (3, "TCC_HIT_sum", 50), (3, "TCC_MISS_sum", 50)]])
+    _write_run(tmp_path / "cf", 4, [(1, copy, 512, "FETCH_SIZE", 3.0),
+                                    (2, copy, 1 << 20, "FETCH_SIZE", 262144.0)])
+    _write_run(tmp_path / "cw", 5, [(1, copy, 1 << 20, "WRITE_SIZE", 524288.0)])
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    monkeypatch.setattr(bench, "COUNTER_FILE", str(tmp_path / "c.json"))
+    bench.summarize_counters([str(tmp_path / d) for d in "fwt"],
+                             [str(tmp_path / "cf"), str(tmp_path / "cw")], ["cmd"], ["copy cmd"])
+    data = json.load(open(tmp_path / "c.json"))
+    assert data["fetch_scale"] == 2.0 and data["write_scale"] == 1.0
+    (row,) = data["kernels"]
+    assert row["kernel"] == "gs::grid_sample_kernel<2, 0, 0, gs::F32, false, true>"
+    assert row["dispatches_FETCH_SIZE"] == 2                 # dispatch 2 was skipped
+    assert row["hbm_read_bytes"] == 110.0 * 1024 * 2
+    assert row["hbm_write_bytes"] == 50.0 * 1024
+    assert row["l2_hit_rate"] == 40.0 / 100.0               # medians 40 hits, 60 misses
+    assert bench.counter_row(data, row["kernel"]) == row
