@@ -195,6 +195,76 @@ def test_fused_equals_unfused_and_oracle(gsa, rank, mode, pad, kind):
               "fused %dD %s/%s/%d" % (rank, mode, pad, ac))
 
 
+def rotation3(rng, angle):
+    """A rotation by `angle` about a random axis (Rodrigues)."""
+    a = rng.normal(size=3)
+    a /= np.linalg.norm(a)
+    K = np.array([[0, -a[2], a[1]], [a[2], 0, -a[0]], [-a[1], a[0], 0]])
+    return np.eye(3) + np.sin(angle) * K + (1 - np.cos(angle)) * K @ K
+
+
+def theta3_family(rng, n):
+    """3D affine matrices of every kind: near identity, large rotations with
+    translation, zoom in and out (out: more input rows than a tile's staging
+    plan holds, so those tiles gather directly), shear, a degenerate map
+    (every output at one point), non-finite and huge entries."""
+    out = []
+    for b in range(n):
+        kind = b % 9
+        M = np.eye(3)
+        t = rng.normal(0, 0.2, 3)
+        if kind == 0:
+            M = M + rng.normal(0, 0.1, (3, 3))
+        elif kind == 1:
+            M = rotation3(rng, rng.uniform(0.5, 1.2))
+        elif kind == 2:
+            M = 0.3 * rotation3(rng, 0.3)
+        elif kind == 3:
+            M = 3.0 * rotation3(rng, 0.4)
+        elif kind == 4:
+            M = M + np.triu(rng.normal(0, 0.8, (3, 3)), 1)
+        elif kind == 5:
+            M = np.zeros((3, 3))
+        th = np.concatenate([M, t[:, None]], 1)
+        if kind == 6:
+            th[1, 2] = np.nan
+        elif kind == 7:
+            th[0, 0] = 1e30
+        elif kind == 8:
+            th = th + rng.normal(0, 0.5, th.shape)
+        out.append(th)
+    return np.stack(out).astype(np.float32)
+
+
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+@pytest.mark.parametrize("ac", [0, 1])
+@pytest.mark.parametrize("pad", ["zeros", "border"])
+@pytest.mark.parametrize("mode", ["linear", "nearest"])
+def test_fused_3d_equals_unfused_over_theta_kinds(gsa, mode, pad, ac, kind):
+    """The 3D fused sampler equals AffineGrid + GridSample bit for bit over
+    several tiles with ragged edges, extents of 1 and 2, and theta of every
+    kind (staged and directly gathered tiles), and matches the oracle."""
+    rng = np.random.default_rng(310 + 2 * ac + (pad == "border"))
+    for xs, out in [((9, 3, 19, 21, 23), (17, 13, 70)), ((9, 2, 1, 5, 2), (1, 3, 40)),
+                    ((9, 2, 2, 1, 37), (5, 2, 33))]:
+        note("fused 3D theta kinds %s/%s ac=%d %s X=%s out=%s" % (mode, pad, ac, kind, xs, out))
+        X = rng.uniform(-1, 1, xs).astype(np.float32)
+        n, c = xs[:2]
+        theta = theta3_family(rng, n)
+        Xd, Xin = x_to_gpu(X, kind)
+        td = to_gpu_f32(theta)
+        fused = gsa.affine_grid_sample_fused(td, Xd, out, mode, pad, ac)
+        grid = gsa.affine_grid(td, (n, c) + out, ac)
+        unfused = gsa.grid_sample(Xd, grid, mode, pad, ac)
+        F, U = from_gpu(fused), from_gpu(unfused)
+        bad = ~((F == U) | (np.isnan(F) & np.isnan(U)))
+        assert not bad.any(), "fused differs from unfused at %s" % (np.argwhere(bad)[0],)
+        G = oracle.affine_grid(theta, (n, c) + out, ac)
+        ok = np.isfinite(theta).all(axis=(1, 2)) & (np.abs(theta).max(axis=(1, 2)) < 1e6)
+        check(F[ok], oracle.grid_sample(Xin[ok], G[ok], mode, pad, ac), mode, kind,
+              np.abs(Xin).max(), "fused 3D theta kinds %s/%s/%d" % (mode, pad, ac))
+
+
 # ------------------------------------------------------------- edge cases
 
 @pytest.mark.parametrize("mode", MODES)
