@@ -206,8 +206,14 @@ def counter_row(counters, kernel, grid=None):
 
 # ------------------------------------------------------------------- timing
 
-def time_kernel(torch, fn, reps, flush=None):
-    """Median and mean duration (us) of fn(), events on the current stream."""
+def time_kernel(torch, fn, reps, flush=None, warmup=5):
+    """Median and mean duration (us) of fn(), events on the current stream,
+    after `warmup` untimed calls (the first calls after host-side work run
+    while the GPU's clocks are still ramping up)."""
+    for _ in range(warmup):
+        if flush is not None:
+            flush()
+        fn()
     ev = []
     for _ in range(reps):
         if flush is not None:
@@ -241,7 +247,7 @@ def copy_bandwidth(torch, mib=512, reps=10):
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
-    med, _ = time_kernel(torch, lambda: dst.copy_(src), reps)
+    med, _ = time_kernel(torch, lambda: dst.copy_(src), reps, warmup=0)
     del src, dst
     return 2 * mib * 1024 * 1024 / (med * 1e-6) / 1e9
 
@@ -901,7 +907,6 @@ def main():
     # Cache: the median is the roofline figure
     flush, flush_buf = make_flush(torch)
     sample = lambda: gsa.grid_sample(X, grid, "linear", "zeros", 0, out=Y)
-    time_kernel(torch, sample, 3, flush)
     flushed_us, _ = time_kernel(torch, sample, 30, flush)
 
     g_host = grid.cpu().numpy()
@@ -952,8 +957,9 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "gs_grid_sample_2d (bilinear, zeros, fp32)",
                      "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-                     "timing": "median of 30 launches, each after a read pass over 512 MiB "
-                               "(Infinity Cache evicted); events on the launch stream",
+                     "timing": "median of 30 launches after 5 warm-up launches, each after a "
+                               "read pass over 512 MiB (Infinity Cache evicted); events on the "
+                               "launch stream",
                      "kernel_us": flushed_us,
                      "achieved_in_loop": achieved_in_loop,
                      "frac_in_loop": achieved_in_loop / HBM_PEAK_GBPS,

@@ -187,6 +187,11 @@ int sample(int r, const void *theta, const void *X, int x_dtype, const int64_t *
     p.vec_out = q > 1 && out.w % q == 0 && (uintptr_t)Y % (uintptr_t)(q * bytes) == 0;
     p.vec_grid = r == 2 && q == 4 && grid != nullptr && out.w % 4 == 0 && (uintptr_t)grid % 16 == 0;
     p.gather_verdicts = nullptr;
+    // runs of 16 tiles dealt to the XCDs in turn (one 128 x 128 image of a
+    // channel group per run); 32 for images of more tiles, whose footprints
+    // then share more of one XCD's L2 (2% faster on 256 x 256 half-precision
+    // flows, the same on volumes)
+    p.run = tiles > 16 ? 32 : 16;
     if (r == 2 && !theta && workspace && (uintptr_t)workspace % 256 == 0) {
         const int64_t need = gather_workspace_bytes(x_dtype, x_shape, out_sp);
         GatherLayout L;

@@ -251,6 +251,14 @@ __device__ __forceinline__ int xcd_logical_block_runs(int nblocks) {
     return grp * (8 * kRun) + (r & 7) * kRun + (r >> 3);
 }
 
+// As xcd_logical_block_runs with runs of `run` logical blocks (the launch
+// holds a multiple of 8 * run blocks).
+__device__ __forceinline__ int xcd_logical_block_run_of(int run) {
+    const int b = blockIdx.x;
+    const int grp = b / (8 * run), r = b - grp * (8 * run);
+    return grp * (8 * run) + (r & 7) * run + (r >> 3);
+}
+
 
 // ------------------------------------------------------- block reduction
 

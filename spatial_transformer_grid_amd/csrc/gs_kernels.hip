@@ -195,7 +195,7 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
     __shared__ int wave_sum[kBlock / 64];
 
     if (p.gather_verdicts && gather_chosen(p.gather_verdicts)) return;  // the gather path runs
-    const int lb = xcd_logical_block_runs(p.nblocks);
+    const int lb = xcd_logical_block_run_of(p.run);
     if (lb >= p.nblocks) return;
     const int tile = lb % p.tiles_per_n;
     const int ncg = lb / p.tiles_per_n;
@@ -700,18 +700,18 @@ __global__ __launch_bounds__(kBlock) void grid_sample_kernel(SampleParams p) {
 // --------------------------------------------------------------- dispatch
 
 static dim3 launch_grid(int nblocks) { return dim3(8 * ((nblocks + 7) / 8)); }
-static dim3 launch_grid_runs(int nblocks) {
-    return dim3(8 * kRun * ((nblocks + 8 * kRun - 1) / (8 * kRun)));
+static dim3 launch_grid_runs(int nblocks, int run) {
+    return dim3(8 * run * ((nblocks + 8 * run - 1) / (8 * run)));
 }
 
 template <int R, bool FUSED, int MODE, int PAD, typename T>
 static int launch_one(const SampleParams &p, bool vec, hipStream_t s) {
     if (vec)
         hipLaunchKernelGGL((grid_sample_kernel<R, MODE, PAD, T, FUSED, true>),
-                           launch_grid_runs(p.nblocks), dim3(kBlock), 0, s, p);
+                           launch_grid_runs(p.nblocks, p.run), dim3(kBlock), 0, s, p);
     else
         hipLaunchKernelGGL((grid_sample_kernel<R, MODE, PAD, T, FUSED, false>),
-                           launch_grid_runs(p.nblocks), dim3(kBlock), 0, s, p);
+                           launch_grid_runs(p.nblocks, p.run), dim3(kBlock), 0, s, p);
     return (int)hipGetLastError();
 }
 

@@ -42,6 +42,7 @@ struct SampleParams {
     int vec_out;               // Y rows allow one vector store per lane
     int vec_grid;              // 2D grid rows allow 16-byte loads of 4 vectors
     const int *gather_verdicts;  // non-NULL: skip when the gather path was chosen
+    int run;                   // logical blocks per XCD run (16 or 32)
 };
 
 // The 2D gather path on a channels-last copy of X (workspace: kProbes verdict
