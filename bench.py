@@ -254,6 +254,10 @@ def copy_bandwidth(torch, mib=512, reps=10):
 
 # ------------------------------------------------------------------ paths
 
+# Groups of bench paths, one per workload family (bench.py --paths).
+PATH_GROUPS = ("stn2d_batch", "flow2d_bicubic", "vol3d", "flow2d_half", "types", "deform",
+               "resize")
+
 class ErrJob:
     """A bench path's output kept on the host for the oracle comparison of the
     CPU-baseline leg.  `ref(lib, b)` gives the oracle's float64 values of
@@ -272,10 +276,14 @@ def host_values(torch, Y):
     return Y.cpu().numpy()
 
 
-def run_paths(torch, gsa, flush, counters):
+def run_paths(torch, gsa, flush, counters, only=None):
     """Kernel-only measurements of every workload shape (median of events),
-    and the outputs for the oracle comparison."""
+    and the outputs for the oracle comparison.  `only`: the path groups to
+    run (PATH_GROUPS), all when None."""
     out, jobs = [], []
+
+    def want(group):
+        return only is None or group in only
 
     def record(name, workload, kernel, us, outputs, x_bytes_full, x_bytes_fp, other_bytes,
                warm_us=None):
@@ -293,274 +301,282 @@ def run_paths(torch, gsa, flush, counters):
         log("%-36s %8.1f us  %7.0f GB/s  %.3f of peak" % (name, us, rec["GBps"],
                                                           rec["frac_hbm_peak"]))
 
-    # 2D STN batch: bilinear + zeros, nearest + border, fused bilinear
-    w = W.WORKLOADS["stn2d_batch"]
-    inp = W.make_inputs(w)
-    n, c, h, wd = w.x_shape
-    X = torch.from_numpy(inp["X"]).cuda()
-    th = torch.from_numpy(inp["theta"]).cuda()
-    size = (n, c) + w.out_spatial
-    grid = gsa.affine_grid(th, size, 0)
-    Y = torch.empty((n, c) + w.out_spatial, device="cuda")
-    g_host = grid.cpu().numpy()
-    outputs = w.outputs
-    gbytes = grid.numel() * 4
-    xmax = float(np.abs(inp["X"]).max())
-    stn_ref = {}
+    if want("stn2d_batch"):
+        # 2D STN batch: bilinear + zeros, nearest + border, fused bilinear
+        w = W.WORKLOADS["stn2d_batch"]
+        inp = W.make_inputs(w)
+        n, c, h, wd = w.x_shape
+        X = torch.from_numpy(inp["X"]).cuda()
+        th = torch.from_numpy(inp["theta"]).cuda()
+        size = (n, c) + w.out_spatial
+        grid = gsa.affine_grid(th, size, 0)
+        Y = torch.empty((n, c) + w.out_spatial, device="cuda")
+        g_host = grid.cpu().numpy()
+        outputs = w.outputs
+        gbytes = grid.numel() * 4
+        xmax = float(np.abs(inp["X"]).max())
+        stn_ref = {}
 
-    def stn_ref_fn(mode, pad, inp=inp, size=size):
-        def ref(lib, b):
-            import oracle
-            key = ("grid", id(lib))
-            if key not in stn_ref:
-                stn_ref[key] = oracle.affine_grid(inp["theta"], size, 0, lib=lib)
-            return oracle.grid_sample(inp["X"][b:b + 1], stn_ref[key][b:b + 1], mode, pad, 0,
-                                      lib=lib)
-        return ref
+        def stn_ref_fn(mode, pad, inp=inp, size=size):
+            def ref(lib, b):
+                import oracle
+                key = ("grid", id(lib))
+                if key not in stn_ref:
+                    stn_ref[key] = oracle.affine_grid(inp["theta"], size, 0, lib=lib)
+                return oracle.grid_sample(inp["X"][b:b + 1], stn_ref[key][b:b + 1], mode, pad, 0,
+                                          lib=lib)
+            return ref
 
-    for mode, pad in (("linear", "zeros"), ("nearest", "border")):
-        fp = footprint_elements(g_host, (h, wd), mode, pad, 0) * c * 4
-        fn = lambda: gsa.grid_sample(X, grid, mode, pad, 0, out=Y)
+        for mode, pad in (("linear", "zeros"), ("nearest", "border")):
+            fp = footprint_elements(g_host, (h, wd), mode, pad, 0) * c * 4
+            fn = lambda: gsa.grid_sample(X, grid, mode, pad, 0, out=Y)
+            us, _ = time_kernel(torch, fn, 30, flush)
+            warm, _ = time_kernel(torch, fn, 30)
+            name = "stn2d_batch/%s-%s" % (mode, pad)
+            record(name, w.name, "gs_grid_sample_2d", us, outputs, X.numel() * 4, fp,
+                   gbytes + outputs * 4, warm)
+            fn()
+            jobs.append(ErrJob(name, host_values(torch, Y), stn_ref_fn(mode, pad), range(n), mode,
+                               "f32", xmax))
+        # the same call with a workspace: the probe keeps the staged sampler (the
+        # difference is the probe and two launches that return at once)
+        ws = torch.empty(gsa.grid_sample_2d_workspace_size(tuple(X.shape), tuple(grid.shape), 0),
+                         dtype=torch.uint8, device="cuda")
+        fp = footprint_elements(g_host, (h, wd), "linear", "zeros", 0) * c * 4
+        fn = lambda: gsa.grid_sample(X, grid, "linear", "zeros", 0, out=Y, workspace=ws)
         us, _ = time_kernel(torch, fn, 30, flush)
         warm, _ = time_kernel(torch, fn, 30)
-        name = "stn2d_batch/%s-%s" % (mode, pad)
-        record(name, w.name, "gs_grid_sample_2d", us, outputs, X.numel() * 4, fp,
-               gbytes + outputs * 4, warm)
+        record("stn2d_batch/linear-zeros-workspace", w.name, "gs_grid_sample_2d_ws (staged chosen)",
+               us, outputs, X.numel() * 4, fp, gbytes + outputs * 4, warm)
         fn()
-        jobs.append(ErrJob(name, host_values(torch, Y), stn_ref_fn(mode, pad), range(n), mode,
-                           "f32", xmax))
-    # the same call with a workspace: the probe keeps the staged sampler (the
-    # difference is the probe and two launches that return at once)
-    ws = torch.empty(gsa.grid_sample_2d_workspace_size(tuple(X.shape), tuple(grid.shape), 0),
-                     dtype=torch.uint8, device="cuda")
-    fp = footprint_elements(g_host, (h, wd), "linear", "zeros", 0) * c * 4
-    fn = lambda: gsa.grid_sample(X, grid, "linear", "zeros", 0, out=Y, workspace=ws)
-    us, _ = time_kernel(torch, fn, 30, flush)
-    warm, _ = time_kernel(torch, fn, 30)
-    record("stn2d_batch/linear-zeros-workspace", w.name, "gs_grid_sample_2d_ws (staged chosen)",
-           us, outputs, X.numel() * 4, fp, gbytes + outputs * 4, warm)
-    fn()
-    jobs.append(ErrJob("stn2d_batch/linear-zeros-workspace", host_values(torch, Y),
-                       stn_ref_fn("linear", "zeros"), range(n), "linear", "f32", xmax))
-    del ws
-    fn = lambda: gsa.affine_grid_sample_fused(th, X, w.out_spatial, "linear", "zeros", 0, out=Y)
-    us, _ = time_kernel(torch, fn, 30, flush)
-    warm, _ = time_kernel(torch, fn, 30)
-    record("stn2d_batch/fused-linear-zeros", w.name, "gs_affine_grid_sample_fused", us, outputs,
-           X.numel() * 4, fp, th.numel() * 4 + outputs * 4, warm)
-    fn()
-    jobs.append(ErrJob("stn2d_batch/fused-linear-zeros", host_values(torch, Y),
-                       stn_ref_fn("linear", "zeros"), range(n), "linear", "f32", xmax))
-    del X, Y, grid
+        jobs.append(ErrJob("stn2d_batch/linear-zeros-workspace", host_values(torch, Y),
+                           stn_ref_fn("linear", "zeros"), range(n), "linear", "f32", xmax))
+        del ws
+        fn = lambda: gsa.affine_grid_sample_fused(th, X, w.out_spatial, "linear", "zeros", 0, out=Y)
+        us, _ = time_kernel(torch, fn, 30, flush)
+        warm, _ = time_kernel(torch, fn, 30)
+        record("stn2d_batch/fused-linear-zeros", w.name, "gs_affine_grid_sample_fused", us, outputs,
+               X.numel() * 4, fp, th.numel() * 4 + outputs * 4, warm)
+        fn()
+        jobs.append(ErrJob("stn2d_batch/fused-linear-zeros", host_values(torch, Y),
+                           stn_ref_fn("linear", "zeros"), range(n), "linear", "f32", xmax))
+        del X, Y, grid
 
-    # 2D random flow, bicubic + reflection
-    w = W.WORKLOADS["flow2d_bicubic"]
-    inp3 = W.make_inputs(w)
-    n, c, h, wd = w.x_shape
-    X = torch.from_numpy(inp3["X"]).cuda()
-    G = torch.from_numpy(inp3["grid"]).cuda()
-    Y = torch.empty((n, c) + w.out_spatial, device="cuda")
-    fp = footprint_elements(inp3["grid"], (h, wd), "cubic", "reflection", 1) * c * 4
-    fn = lambda: gsa.grid_sample(X, G, "cubic", "reflection", 1, out=Y)
-    us, _ = time_kernel(torch, fn, 10, flush)
-    record("flow2d_bicubic/cubic-reflection", w.name, "gs_grid_sample_2d", us, w.outputs,
-           X.numel() * 4, fp, G.numel() * 4 + w.outputs * 4)
+    if want("flow2d_bicubic"):
+        # 2D random flow, bicubic + reflection
+        w = W.WORKLOADS["flow2d_bicubic"]
+        inp3 = W.make_inputs(w)
+        n, c, h, wd = w.x_shape
+        X = torch.from_numpy(inp3["X"]).cuda()
+        G = torch.from_numpy(inp3["grid"]).cuda()
+        Y = torch.empty((n, c) + w.out_spatial, device="cuda")
+        fp = footprint_elements(inp3["grid"], (h, wd), "cubic", "reflection", 1) * c * 4
+        fn = lambda: gsa.grid_sample(X, G, "cubic", "reflection", 1, out=Y)
+        us, _ = time_kernel(torch, fn, 10, flush)
+        record("flow2d_bicubic/cubic-reflection", w.name, "gs_grid_sample_2d", us, w.outputs,
+               X.numel() * 4, fp, G.numel() * 4 + w.outputs * 4)
 
-    def flow_ref(lib, b):
-        import oracle
-        return oracle.grid_sample(inp3["X"][b:b + 1], inp3["grid"][b:b + 1], "cubic",
-                                  "reflection", 1, lib=lib)
+        def flow_ref(lib, b):
+            import oracle
+            return oracle.grid_sample(inp3["X"][b:b + 1], inp3["grid"][b:b + 1], "cubic",
+                                      "reflection", 1, lib=lib)
 
-    fn()
-    Yplain = Y.clone()
-    jobs.append(ErrJob("flow2d_bicubic/cubic-reflection", host_values(torch, Y), flow_ref,
-                       range(n), "cubic", "f32", float(np.abs(inp3["X"]).max())))
-    # with a workspace: probe, sliced channels-last copy of X, gather (the
-    # whole call is timed, the copy included); same outputs bit for bit
-    ws = torch.empty(gsa.grid_sample_2d_workspace_size(tuple(X.shape), tuple(G.shape), 0),
-                     dtype=torch.uint8, device="cuda")
-    fn = lambda: gsa.grid_sample(X, G, "cubic", "reflection", 1, out=Y, workspace=ws)
-    us, _ = time_kernel(torch, fn, 20, flush)
-    record("flow2d_bicubic/cubic-reflection-workspace", w.name,
-           "gs_grid_sample_2d_ws (gather path)", us, w.outputs, X.numel() * 4, fp,
-           G.numel() * 4 + w.outputs * 4)
-    fn()
-    torch.cuda.synchronize()
-    out[-1]["identical_to_plain_sampler"] = bool(torch.equal(Y, Yplain))
-    jobs.append(ErrJob("flow2d_bicubic/cubic-reflection-workspace", host_values(torch, Y),
-                       flow_ref, range(n), "cubic", "f32", float(np.abs(inp3["X"]).max())))
-    del X, Y, G, ws, Yplain
+        fn()
+        Yplain = Y.clone()
+        jobs.append(ErrJob("flow2d_bicubic/cubic-reflection", host_values(torch, Y), flow_ref,
+                           range(n), "cubic", "f32", float(np.abs(inp3["X"]).max())))
+        # with a workspace: probe, sliced channels-last copy of X, gather (the
+        # whole call is timed, the copy included); same outputs bit for bit
+        ws = torch.empty(gsa.grid_sample_2d_workspace_size(tuple(X.shape), tuple(G.shape), 0),
+                         dtype=torch.uint8, device="cuda")
+        fn = lambda: gsa.grid_sample(X, G, "cubic", "reflection", 1, out=Y, workspace=ws)
+        us, _ = time_kernel(torch, fn, 20, flush)
+        record("flow2d_bicubic/cubic-reflection-workspace", w.name,
+               "gs_grid_sample_2d_ws (gather path)", us, w.outputs, X.numel() * 4, fp,
+               G.numel() * 4 + w.outputs * 4)
+        fn()
+        torch.cuda.synchronize()
+        out[-1]["identical_to_plain_sampler"] = bool(torch.equal(Y, Yplain))
+        jobs.append(ErrJob("flow2d_bicubic/cubic-reflection-workspace", host_values(torch, Y),
+                           flow_ref, range(n), "cubic", "f32", float(np.abs(inp3["X"]).max())))
+        del X, Y, G, ws, Yplain
 
-    # 3D volumetric, fused trilinear + border (working set fits the MALL:
-    # report the flushed time as the figure and the warm one beside it)
-    w = W.WORKLOADS["vol3d"]
-    inp4 = W.make_inputs(w)
-    n, c = w.x_shape[:2]
-    X = torch.from_numpy(inp4["X"]).cuda()
-    th = torch.from_numpy(inp4["theta"]).cuda()
-    Y = torch.empty((n, c) + w.out_spatial, device="cuda")
-    grid = gsa.affine_grid(th, (n, c) + w.out_spatial, 0)
-    fp = footprint_elements(grid.cpu().numpy(), w.x_shape[2:], "linear", "border", 0) * c * 4
-    vol_size = (n, c) + w.out_spatial
+    if want("vol3d"):
+        # 3D volumetric, fused trilinear + border (working set fits the MALL:
+        # report the flushed time as the figure and the warm one beside it)
+        w = W.WORKLOADS["vol3d"]
+        inp4 = W.make_inputs(w)
+        n, c = w.x_shape[:2]
+        X = torch.from_numpy(inp4["X"]).cuda()
+        th = torch.from_numpy(inp4["theta"]).cuda()
+        Y = torch.empty((n, c) + w.out_spatial, device="cuda")
+        grid = gsa.affine_grid(th, (n, c) + w.out_spatial, 0)
+        fp = footprint_elements(grid.cpu().numpy(), w.x_shape[2:], "linear", "border", 0) * c * 4
+        vol_size = (n, c) + w.out_spatial
 
-    def vol_ref(lib, b, c=c, out_spatial=w.out_spatial):
-        import oracle
-        G4 = oracle.affine_grid(inp4["theta"][b:b + 1], (1, c) + out_spatial, 0, lib=lib)
-        return oracle.grid_sample(inp4["X"][b:b + 1], G4, "linear", "border", 0, lib=lib)
+        def vol_ref(lib, b, c=c, out_spatial=w.out_spatial):
+            import oracle
+            G4 = oracle.affine_grid(inp4["theta"][b:b + 1], (1, c) + out_spatial, 0, lib=lib)
+            return oracle.grid_sample(inp4["X"][b:b + 1], G4, "linear", "border", 0, lib=lib)
 
-    xmax = float(np.abs(inp4["X"]).max())
-    fn = lambda: gsa.affine_grid_sample_fused(th, X, w.out_spatial, "linear", "border", 0, out=Y)
-    us, _ = time_kernel(torch, fn, 20, flush)
-    warm, _ = time_kernel(torch, fn, 20)
-    record("vol3d/fused-linear-border", w.name, "gs_affine_grid_sample_fused", us, w.outputs,
-           X.numel() * 4, fp, th.numel() * 4 + w.outputs * 4, warm)
-    fn()
-    jobs.append(ErrJob("vol3d/fused-linear-border", host_values(torch, Y), vol_ref, range(n),
-                       "linear", "f32", xmax))
-    fn = lambda: gsa.grid_sample(X, grid, "linear", "border", 0, out=Y)
-    us, _ = time_kernel(torch, fn, 20, flush)
-    warm, _ = time_kernel(torch, fn, 20)
-    record("vol3d/unfused-linear-border", w.name, "gs_grid_sample_3d", us, w.outputs,
-           X.numel() * 4, fp, grid.numel() * 4 + w.outputs * 4, warm)
-    fn()
-    jobs.append(ErrJob("vol3d/unfused-linear-border", host_values(torch, Y), vol_ref, range(n),
-                       "linear", "f32", xmax))
-    del X, Y, grid, vol_size
-
-    # 2D large half precision, smooth flow
-    w = W.WORKLOADS["flow2d_half"]
-    inp5 = W.make_inputs(w)
-    n, c, h, wd = w.x_shape
-    G = torch.from_numpy(inp5["grid"]).cuda()
-    fp = footprint_elements(inp5["grid"], (h, wd), "linear", "zeros", 0) * c * 2
-    for kind, tdt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
-        X = torch.from_numpy(inp5["X_bits"][kind].view(np.int16)).cuda().view(tdt)
-        Y = torch.empty((n, c) + w.out_spatial, device="cuda", dtype=tdt)
-        fn = lambda: gsa.grid_sample(X, G, "linear", "zeros", 0, out=Y)
+        xmax = float(np.abs(inp4["X"]).max())
+        fn = lambda: gsa.affine_grid_sample_fused(th, X, w.out_spatial, "linear", "border", 0, out=Y)
         us, _ = time_kernel(torch, fn, 20, flush)
         warm, _ = time_kernel(torch, fn, 20)
-        name = "flow2d_half/%s-linear-zeros" % kind
-        record(name, w.name, "gs_grid_sample_2d", us, w.outputs, X.numel() * 2, fp,
-               G.numel() * 4 + w.outputs * 2, warm)
+        record("vol3d/fused-linear-border", w.name, "gs_affine_grid_sample_fused", us, w.outputs,
+               X.numel() * 4, fp, th.numel() * 4 + w.outputs * 4, warm)
         fn()
-        xh = inp5["X_half_as_f32"][kind]
-
-        def half_ref(lib, b, xh=xh):
-            import oracle
-            return oracle.grid_sample(xh[b:b + 1], inp5["grid"][b:b + 1], "linear", "zeros", 0,
-                                      lib=lib)
-
-        jobs.append(ErrJob(name, host_values(torch, Y), half_ref, range(n), "linear", kind,
-                           float(np.abs(xh).max())))
-        del X, Y
-    del G
-
-    # other ranks and element types (the any-rank kernel; bit-exact)
-    for name, tw in W.TYPE_WORKLOADS.items():
-        inpt = W.make_type_inputs(tw)
-        n, c = tw.x_shape[:2]
-        X = torch.from_numpy(inpt["X"]).cuda()
-        if inpt["theta"] is not None:
-            th = torch.from_numpy(inpt["theta"]).cuda()
-            G = gsa.affine_grid(th, (n, c) + tw.out_spatial, tw.align_corners)
-        else:
-            G = torch.from_numpy(inpt["grid"]).cuda()
-        Y = torch.empty((n, c) + tw.out_spatial, dtype=X.dtype, device="cuda")
-        es = X.element_size()
-        fp = footprint_elements(G.cpu().numpy(), tw.x_shape[2:], tw.mode, tw.padding,
-                                tw.align_corners) * c * es
-        fn = lambda: gsa.grid_sample(X, G, tw.mode, tw.padding, tw.align_corners, out=Y)
-        fn()
+        jobs.append(ErrJob("vol3d/fused-linear-border", host_values(torch, Y), vol_ref, range(n),
+                           "linear", "f32", xmax))
+        fn = lambda: gsa.grid_sample(X, grid, "linear", "border", 0, out=Y)
         us, _ = time_kernel(torch, fn, 20, flush)
         warm, _ = time_kernel(torch, fn, 20)
-        pname = "%s/%s-%s" % (name, tw.mode, tw.padding)
-        record(pname, name, "gs_grid_sample (any-rank kernel)", us, tw.outputs, X.numel() * es,
-               fp, G.numel() * G.element_size() + tw.outputs * es, warm)
+        record("vol3d/unfused-linear-border", w.name, "gs_grid_sample_3d", us, w.outputs,
+               X.numel() * 4, fp, grid.numel() * 4 + w.outputs * 4, warm)
         fn()
+        jobs.append(ErrJob("vol3d/unfused-linear-border", host_values(torch, Y), vol_ref, range(n),
+                           "linear", "f32", xmax))
+        del X, Y, grid, vol_size
 
-        def type_ref(lib, b, tw=tw, inpt=inpt):
-            import oracle
-            n_, c_ = inpt["x_shape"][:2]
+    if want("flow2d_half"):
+        # 2D large half precision, smooth flow
+        w = W.WORKLOADS["flow2d_half"]
+        inp5 = W.make_inputs(w)
+        n, c, h, wd = w.x_shape
+        G = torch.from_numpy(inp5["grid"]).cuda()
+        fp = footprint_elements(inp5["grid"], (h, wd), "linear", "zeros", 0) * c * 2
+        for kind, tdt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+            X = torch.from_numpy(inp5["X_bits"][kind].view(np.int16)).cuda().view(tdt)
+            Y = torch.empty((n, c) + w.out_spatial, device="cuda", dtype=tdt)
+            fn = lambda: gsa.grid_sample(X, G, "linear", "zeros", 0, out=Y)
+            us, _ = time_kernel(torch, fn, 20, flush)
+            warm, _ = time_kernel(torch, fn, 20)
+            name = "flow2d_half/%s-linear-zeros" % kind
+            record(name, w.name, "gs_grid_sample_2d", us, w.outputs, X.numel() * 2, fp,
+                   G.numel() * 4 + w.outputs * 2, warm)
+            fn()
+            xh = inp5["X_half_as_f32"][kind]
+
+            def half_ref(lib, b, xh=xh):
+                import oracle
+                return oracle.grid_sample(xh[b:b + 1], inp5["grid"][b:b + 1], "linear", "zeros", 0,
+                                          lib=lib)
+
+            jobs.append(ErrJob(name, host_values(torch, Y), half_ref, range(n), "linear", kind,
+                               float(np.abs(xh).max())))
+            del X, Y
+        del G
+
+    if want("types"):
+        # other ranks and element types (the any-rank kernel; bit-exact)
+        for name, tw in W.TYPE_WORKLOADS.items():
+            inpt = W.make_type_inputs(tw)
+            n, c = tw.x_shape[:2]
+            X = torch.from_numpy(inpt["X"]).cuda()
             if inpt["theta"] is not None:
-                Gr = oracle.affine_grid(inpt["theta"][b:b + 1], (1, c_) + tuple(tw.out_spatial),
-                                        tw.align_corners, lib=lib)
+                th = torch.from_numpy(inpt["theta"]).cuda()
+                G = gsa.affine_grid(th, (n, c) + tw.out_spatial, tw.align_corners)
             else:
-                Gr = inpt["grid"][b:b + 1]
-            v = oracle.grid_sample(inpt["X"][b:b + 1], Gr, tw.mode, tw.padding, tw.align_corners,
-                                   lib=lib)
-            if inpt["X"].dtype == np.uint8:
-                return oracle.to_integer(v, np.uint8).astype(np.float64)
-            if inpt["X"].dtype == np.float32:
-                return v.astype(np.float32).astype(np.float64)
-            return v
-
-        jobs.append(ErrJob(pname, host_values(torch, Y), type_ref, range(n), tw.mode, "exact",
-                           float(np.abs(inpt["X"].astype(np.float64)).max()), exact=True))
-        del X, Y, G, inpt
-
-    # DeformConv layers: matrix-core throughput (flops of the convolution)
-    for name, dw in W.DEFORM_WORKLOADS.items():
-        inpd = W.make_deform_inputs(dw)
-        for kind in dw.dtypes:
-            tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[kind]
-            d = {k: torch.from_numpy(v).cuda().to(tdt) for k, v in inpd.items()}
-            Y = torch.empty(dw.out_shape(), dtype=tdt, device="cuda")
-            ws = torch.empty(gsa.deform_conv_workspace_size(
-                dw.x_shape, dw.w_shape, gsa.dtype_code(d["X"]), None, list(dw.pads), None,
-                dw.group, dw.offset_group), dtype=torch.uint8, device="cuda")
-            fn = lambda: gsa.deform_conv(d["X"], d["W"], d["offset"], d["B"], d["mask"],
-                                         pads=list(dw.pads), group=dw.group,
-                                         offset_group=dw.offset_group, out=Y, workspace=ws)
+                G = torch.from_numpy(inpt["grid"]).cuda()
+            Y = torch.empty((n, c) + tw.out_spatial, dtype=X.dtype, device="cuda")
+            es = X.element_size()
+            fp = footprint_elements(G.cpu().numpy(), tw.x_shape[2:], tw.mode, tw.padding,
+                                    tw.align_corners) * c * es
+            fn = lambda: gsa.grid_sample(X, G, tw.mode, tw.padding, tw.align_corners, out=Y)
             fn()
             us, _ = time_kernel(torch, fn, 20, flush)
-            peak = 157.3 if kind == "f32" else 2500.0
-            tflops = dw.flops / (us * 1e-6) / 1e12
-            es = 4 if kind == "f32" else 2
-            io = (inpd["X"].size + inpd["W"].size + inpd["offset"].size + inpd["mask"].size
-                  + inpd["B"].size + Y.numel()) * es
-            pname = "%s/%s" % (name, kind)
-            rec = {"path": pname, "workload": name,
-                   "kernel": "gs_deform_conv (implicit GEMM, MFMA)", "kernel_us": round(us, 2),
-                   "bound": "mfma", "TFLOPs": tflops, "peak_TFLOPs": peak,
-                   "frac_mfma_peak": tflops / peak, "flops": dw.flops, "io_bytes": io,
-                   "GBps_io": io / (us * 1e-6) / 1e9}
-            attach_counters(rec, counters)
-            out.append(rec)
-            log("%-36s %8.1f us  %7.1f TFLOP/s  %.3f of the %s MFMA peak" % (
-                pname, us, tflops, tflops / peak, kind))
+            warm, _ = time_kernel(torch, fn, 20)
+            pname = "%s/%s-%s" % (name, tw.mode, tw.padding)
+            record(pname, name, "gs_grid_sample (any-rank kernel)", us, tw.outputs, X.numel() * es,
+                   fp, G.numel() * G.element_size() + tw.outputs * es, warm)
             fn()
-            exact = {k: (v.float().cpu().numpy() if kind != "f32" else inpd[k])
-                     for k, v in d.items()}
-            jobs.append(deform_job(pname, host_values(torch, Y), exact, dw, kind))
-            del d, Y, ws
 
-    # Resize workloads (fp32): at their scales every input element has a
-    # non-zero weight, so all of X is compulsory
-    for name, rw in W.RESIZE_WORKLOADS.items():
-        Xh = W.make_resize_input(rw)
-        X = torch.from_numpy(Xh).cuda()
-        rank = X.dim()
-        axes = list(range(rank - len(rw.scales), rank))
-        shape = gsa.resize_output_shape(X.shape, list(rw.scales), None, axes)
-        Y = torch.empty(shape, device="cuda")
-        scales = rw.full_scales()
-        fn = lambda: gsa.resize_to(X, shape, scales, rw.mode, rw.coordinate_transformation_mode,
-                                   out=Y)
-        fn()
-        us, _ = time_kernel(torch, fn, 20, flush)
-        warm, _ = time_kernel(torch, fn, 20)
-        record(name, name, "gs_resize", us, Y.numel(), X.numel() * 4, X.numel() * 4,
-               Y.numel() * 4, warm)
-        fn()
+            def type_ref(lib, b, tw=tw, inpt=inpt):
+                import oracle
+                n_, c_ = inpt["x_shape"][:2]
+                if inpt["theta"] is not None:
+                    Gr = oracle.affine_grid(inpt["theta"][b:b + 1], (1, c_) + tuple(tw.out_spatial),
+                                            tw.align_corners, lib=lib)
+                else:
+                    Gr = inpt["grid"][b:b + 1]
+                v = oracle.grid_sample(inpt["X"][b:b + 1], Gr, tw.mode, tw.padding, tw.align_corners,
+                                       lib=lib)
+                if inpt["X"].dtype == np.uint8:
+                    return oracle.to_integer(v, np.uint8).astype(np.float64)
+                if inpt["X"].dtype == np.float32:
+                    return v.astype(np.float32).astype(np.float64)
+                return v
 
-        def resize_ref(lib, b, Xh=Xh, shape=tuple(shape), rw=rw, scales=scales):
-            import oracle
-            return oracle.resize(Xh[b:b + 1], (1,) + shape[1:], scales, rw.mode,
-                                 rw.coordinate_transformation_mode, lib=lib)
+            jobs.append(ErrJob(pname, host_values(torch, Y), type_ref, range(n), tw.mode, "exact",
+                               float(np.abs(inpt["X"].astype(np.float64)).max()), exact=True))
+            del X, Y, G, inpt
 
-        jobs.append(ErrJob(name, host_values(torch, Y), resize_ref, range(shape[0]), rw.mode,
-                           "f32", float(np.abs(Xh).max())))
-        del X, Y
+    if want("deform"):
+        # DeformConv layers: matrix-core throughput (flops of the convolution)
+        for name, dw in W.DEFORM_WORKLOADS.items():
+            inpd = W.make_deform_inputs(dw)
+            for kind in dw.dtypes:
+                tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[kind]
+                d = {k: torch.from_numpy(v).cuda().to(tdt) for k, v in inpd.items()}
+                Y = torch.empty(dw.out_shape(), dtype=tdt, device="cuda")
+                ws = torch.empty(gsa.deform_conv_workspace_size(
+                    dw.x_shape, dw.w_shape, gsa.dtype_code(d["X"]), None, list(dw.pads), None,
+                    dw.group, dw.offset_group), dtype=torch.uint8, device="cuda")
+                fn = lambda: gsa.deform_conv(d["X"], d["W"], d["offset"], d["B"], d["mask"],
+                                             pads=list(dw.pads), group=dw.group,
+                                             offset_group=dw.offset_group, out=Y, workspace=ws)
+                fn()
+                us, _ = time_kernel(torch, fn, 20, flush)
+                peak = 157.3 if kind == "f32" else 2500.0
+                tflops = dw.flops / (us * 1e-6) / 1e12
+                es = 4 if kind == "f32" else 2
+                io = (inpd["X"].size + inpd["W"].size + inpd["offset"].size + inpd["mask"].size
+                      + inpd["B"].size + Y.numel()) * es
+                pname = "%s/%s" % (name, kind)
+                rec = {"path": pname, "workload": name,
+                       "kernel": "gs_deform_conv (implicit GEMM, MFMA)", "kernel_us": round(us, 2),
+                       "bound": "mfma", "TFLOPs": tflops, "peak_TFLOPs": peak,
+                       "frac_mfma_peak": tflops / peak, "flops": dw.flops, "io_bytes": io,
+                       "GBps_io": io / (us * 1e-6) / 1e9}
+                attach_counters(rec, counters)
+                out.append(rec)
+                log("%-36s %8.1f us  %7.1f TFLOP/s  %.3f of the %s MFMA peak" % (
+                    pname, us, tflops, tflops / peak, kind))
+                fn()
+                exact = {k: (v.float().cpu().numpy() if kind != "f32" else inpd[k])
+                         for k, v in d.items()}
+                jobs.append(deform_job(pname, host_values(torch, Y), exact, dw, kind))
+                del d, Y, ws
+
+    if want("resize"):
+        # Resize workloads (fp32): at their scales every input element has a
+        # non-zero weight, so all of X is compulsory
+        for name, rw in W.RESIZE_WORKLOADS.items():
+            Xh = W.make_resize_input(rw)
+            X = torch.from_numpy(Xh).cuda()
+            rank = X.dim()
+            axes = list(range(rank - len(rw.scales), rank))
+            shape = gsa.resize_output_shape(X.shape, list(rw.scales), None, axes)
+            Y = torch.empty(shape, device="cuda")
+            scales = rw.full_scales()
+            fn = lambda: gsa.resize_to(X, shape, scales, rw.mode, rw.coordinate_transformation_mode,
+                                       out=Y)
+            fn()
+            us, _ = time_kernel(torch, fn, 20, flush)
+            warm, _ = time_kernel(torch, fn, 20)
+            record(name, name, "gs_resize", us, Y.numel(), X.numel() * 4, X.numel() * 4,
+                   Y.numel() * 4, warm)
+            fn()
+
+            def resize_ref(lib, b, Xh=Xh, shape=tuple(shape), rw=rw, scales=scales):
+                import oracle
+                return oracle.resize(Xh[b:b + 1], (1,) + shape[1:], scales, rw.mode,
+                                     rw.coordinate_transformation_mode, lib=lib)
+
+            jobs.append(ErrJob(name, host_values(torch, Y), resize_ref, range(shape[0]), rw.mode,
+                               "f32", float(np.abs(Xh).max())))
+            del X, Y
+
     return out, jobs
 
 
@@ -824,6 +840,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-paths", action="store_true", help="skip the other workload shapes")
+    ap.add_argument("--paths", nargs="+", choices=PATH_GROUPS, metavar="GROUP",
+                    help="run only these path groups (%s)" % ", ".join(PATH_GROUPS))
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 512 MiB device copy (counter calibration)")
     ap.add_argument("--summarize-counters", nargs="+", metavar="DIR",
@@ -929,7 +947,7 @@ def main():
 
     paths, jobs = None, []
     if not args.no_paths:
-        paths, jobs = run_paths(torch, gsa, flush, counters)
+        paths, jobs = run_paths(torch, gsa, flush, counters, args.paths)
     del flush_buf
 
     cpu = None
