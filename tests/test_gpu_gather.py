@@ -12,7 +12,11 @@ the plain sampler.
   non-finite locations.
 * Near-identity affine grids: the probe keeps the staged sampler (verdicts
   sum below 32), and the result equals gs_grid_sample_2d bit for bit.  So do
-  random flows over images small enough for a tile's LDS slot.
+  random flows over images small enough for a tile's LDS slot, grids with a
+  few scattered tiles (the sampler gathers those from X), and grids mostly
+  scattered with some smooth tiles (the gather kernel writes every output).
+* The workspace's contents before the call do not matter, and the call
+  replays correctly from a captured graph.
 * Without a workspace, or one too small, the call is gs_grid_sample_2d.
 """
 
@@ -43,6 +47,8 @@ def gsa():
 
 
 def verdict_sum(ws):
+    """Probes (of 64) that found their tile scattered: the workspace's first
+    256 bytes hold their verdict words."""
     return int(ws[:256].cpu().numpy().view(np.int32)[:64].sum())
 
 
@@ -75,16 +81,17 @@ def random_grid(rng, n, ho, wo):
     return rng.uniform(-1.2, 1.2, (n, ho, wo, 2)).astype(np.float32)
 
 
-# Input planes larger than a tile's 16 KB LDS slot (fp32 and half), so that
-# scattered locations cannot be staged.
+# Input planes of more than 256 rows: the box of a tile's scattered
+# locations spans more rows than the sampler stages (256), so the probes find
+# every tile scattered, however few locations it holds.
 CASES = [
     # n, c (f32), c (half), h, w, ho, wo
-    (2, 16, 32, 96, 104, 9, 140),    # one 64-byte slice, three row segments, the last ragged
-    (1, 24, 48, 100, 110, 17, 64),   # three 32-byte slices, one ragged row segment
-    (3, 64, 128, 91, 101, 5, 13),    # 12 planes of 64-byte slices (XCD order), narrow rows
-    (2, 8, 16, 97, 99, 4, 300),      # one 32-byte slice, three row segments
-    (1, 128, 256, 96, 104, 1, 50),   # 8 slices, one row: one block per XCD (one counter)
-    (1, 128, 256, 96, 104, 2, 50),   # 8 slices, two rows: two counters per XCD
+    (2, 16, 32, 320, 104, 9, 140),   # one 64-byte slice, three row segments, the last ragged
+    (1, 24, 48, 330, 110, 17, 64),   # three 32-byte slices, one ragged row segment
+    (3, 64, 128, 321, 101, 5, 13),   # 12 planes of 64-byte slices (XCD order), narrow rows
+    (2, 8, 16, 337, 99, 4, 300),     # one 32-byte slice, three row segments
+    (1, 128, 256, 326, 104, 1, 50),  # 8 slices, one row: one block per XCD (one counter)
+    (1, 128, 256, 326, 104, 2, 50),  # 8 slices, two rows: two counters per XCD
 ]
 
 
@@ -102,7 +109,7 @@ def test_random_flow_takes_the_gather_path(gsa, kind, ci, mode, pad, ac):
 @pytest.mark.parametrize("mode", MODES)
 def test_non_finite_locations(gsa, mode):
     rng = np.random.default_rng(7)
-    X = rng.uniform(-1, 1, (1, 8, 100, 100)).astype(np.float32)
+    X = rng.uniform(-1, 1, (1, 8, 320, 100)).astype(np.float32)
     G = random_grid(rng, 1, 6, 20)
     G[0, 0, :4, 0] = np.nan
     G[0, 1, 2:5, 1] = np.inf
@@ -113,7 +120,7 @@ def test_non_finite_locations(gsa, mode):
 def test_many_slices(gsa):
     """Few output rows, 32 channel slices walked in XCD order."""
     rng = np.random.default_rng(8)
-    X = rng.uniform(-1, 1, (1, 256, 90, 91)).astype(np.float32)
+    X = rng.uniform(-1, 1, (1, 256, 320, 91)).astype(np.float32)
     G = random_grid(rng, 1, 2, 40)
     run_case(gsa, X, G, "f32", "cubic", "border", 0, True, "many slices")
 
@@ -134,6 +141,95 @@ def test_small_image_keeps_the_staged_sampler(gsa):
     X = rng.uniform(-1, 1, (2, 16, 23, 37)).astype(np.float32)
     G = random_grid(rng, 2, 9, 70)
     run_case(gsa, X, G, "f32", "linear", "border", 1, False, "small image")
+
+
+def centre_grid(n, ho, wo, zoom=1.0):
+    """Pixel-centre locations (align_corners = 0) scaled by `zoom`: a grid
+    every tile of which the sampler stages."""
+    xs = ((2.0 * np.arange(wo) + 1.0) / wo - 1.0) * zoom
+    ys = ((2.0 * np.arange(ho) + 1.0) / ho - 1.0) * zoom
+    g = np.empty((n, ho, wo, 2), np.float32)
+    g[..., 0] = xs[None, None, :]
+    g[..., 1] = ys[None, :, None]
+    return g
+
+
+@pytest.mark.parametrize("kind,mode", list(itertools.product(["f32", "bf16"], MODES)))
+def test_few_scattered_tiles_gather_from_x(gsa, kind, mode):
+    """Random locations in the first 16 output rows of one image, a smooth
+    grid elsewhere: two of the 64 probes find their tile scattered, so the
+    sampler runs and gathers those tiles' taps from X; the result equals the
+    plain sampler bit for bit."""
+    rng = np.random.default_rng(21)
+    X = rng.uniform(-1, 1, (2, 16, 320, 100)).astype(np.float32)
+    G = centre_grid(2, 256, 64, 0.9)
+    G[0, :16] = random_grid(rng, 1, 16, 64)[0]
+    run_case(gsa, X, G, kind, mode, "border", 0, False, "few scattered")
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_mostly_scattered_with_staged_tiles_takes_the_gather_path(gsa, mode):
+    """Random locations over the first 192 of 256 output rows of every image
+    and a smooth grid below: the gather path writes every output, the
+    staged tiles' included, with the same bits."""
+    rng = np.random.default_rng(22)
+    X = rng.uniform(-1, 1, (2, 16, 320, 100)).astype(np.float32)
+    G = centre_grid(2, 256, 64, 0.9)
+    G[:, :192] = random_grid(rng, 2, 192, 64)
+    run_case(gsa, X, G, "f32", mode, "zeros", 1, True, "mostly scattered")
+
+
+def test_workspace_contents_do_not_matter(gsa):
+    """The call reads nothing a previous call, or garbage, left in the
+    workspace: a smooth grid after a random one, and a random one after a
+    smooth one, on the same workspace filled with 0xff first."""
+    torch = torch_mod()
+    rng = np.random.default_rng(23)
+    X = torch.from_numpy(rng.uniform(-1, 1, (2, 16, 320, 100)).astype(np.float32)).cuda()
+    Gs = torch.from_numpy(centre_grid(2, 256, 64, 0.9)).cuda()
+    Gr = torch.from_numpy(random_grid(rng, 2, 256, 64)).cuda()
+    need = gsa.grid_sample_2d_workspace_size(tuple(X.shape), tuple(Gs.shape), 0)
+    ws = torch.full((need,), 255, dtype=torch.uint8, device="cuda")
+    for G, gather in ((Gs, False), (Gr, True), (Gs, False), (Gr, True)):
+        note("workspace reuse, gather %s" % gather)
+        Yw = gsa.grid_sample(X, G, "linear", "zeros", 0, workspace=ws)
+        Yp = gsa.grid_sample(X, G, "linear", "zeros", 0)
+        torch.cuda.synchronize()
+        assert (verdict_sum(ws) >= 32) == gather
+        assert torch.equal(Yw, Yp)
+
+
+@pytest.mark.parametrize("kind", ["smooth", "random"])
+def test_captured_graph_replays(gsa, kind):
+    """The call captured in a graph and replayed, X changed in between:
+    every replay equals the eager plain sampler on that X (the probe
+    rewrites its verdicts and resets the gather kernel's counters each
+    time; no memset node is recorded)."""
+    torch = torch_mod()
+    rng = np.random.default_rng(24)
+    X = torch.from_numpy(rng.uniform(-1, 1, (2, 16, 320, 100)).astype(np.float32)).cuda()
+    G = torch.from_numpy(centre_grid(2, 256, 64, 0.9) if kind == "smooth"
+                         else random_grid(rng, 2, 256, 64)).cuda()
+    need = gsa.grid_sample_2d_workspace_size(tuple(X.shape), tuple(G.shape), 0)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    Y = torch.empty((2, 16, 256, 64), device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gsa.grid_sample(X, G, "linear", "zeros", 0, out=Y, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gsa.grid_sample(X, G, "linear", "zeros", 0, out=Y, workspace=ws)
+    for rep in range(4):
+        note("graph replay %d (%s grid)" % (rep, kind))
+        X.copy_(torch.from_numpy(rng.uniform(-1, 1, tuple(X.shape)).astype(np.float32)).cuda())
+        graph.replay()
+        Yp = gsa.grid_sample(X, G, "linear", "zeros", 0)
+        torch.cuda.synchronize()
+        assert torch.equal(Y, Yp), "replay %d differs from the eager result" % rep
+        assert (verdict_sum(ws) >= 32) == (kind == "random")
 
 
 def test_without_workspace_is_the_plain_sampler(gsa):
