@@ -206,10 +206,15 @@ int sample(int r, const void *theta, const void *X, int x_dtype, const int64_t *
             g.xcd_pairs = L.pairs >= 8;
             g.gather_blocks = (int)L.blocks;
             p.gather_verdicts = g.verdicts;
-            const int rc = gs::launch_grid_gather(p, g, mode, padding, x_dtype,
-                                                  in.w % (16 / bytes) == 0 && (uintptr_t)X % 16 == 0,
-                                                  (hipStream_t)stream);
+            // probe, sampler (returns at once when the probe chose the
+            // gather path), copy and gather (return at once otherwise)
+            const bool vec_x = in.w % (16 / bytes) == 0 && (uintptr_t)X % 16 == 0;
+            const hipStream_t st = (hipStream_t)stream;
+            int rc = gs::launch_grid_gather(p, g, mode, padding, x_dtype, vec_x, 0, st);
             if (rc) return hip_status(rc);
+            rc = gs::launch_grid_sample(p, r, false, mode, padding, x_dtype, vec_in, st);
+            if (rc) return hip_status(rc);
+            return hip_status(gs::launch_grid_gather(p, g, mode, padding, x_dtype, vec_x, 1, st));
         }
     }
     return hip_status(gs::launch_grid_sample(p, r, theta != nullptr, mode, padding, x_dtype,

@@ -21,11 +21,14 @@
 //     planes one after another: the random taps mostly hit L2;
 //  3. otherwise the tuned sampler runs as usual.
 //
-// All four launches (probe, copy, gather, tuned sampler) are enqueued every
-// time; the ones the probe does not choose return at once.  The per-output
-// arithmetic is the tuned sampler's: the same taps and weights (GridSample
-// page: Summary; Attributes align_corners, mode, padding_mode), the same fp32
-// sum in the same tap order, one rounding to T at the store.
+// All four launches (probe, tuned sampler, copy, gather, in that order) are
+// enqueued every time; the ones the probe does not choose return at once.
+// The copy and the gather go after the sampler: a launch that returns at
+// once costs about 1 us there, against about 2.5 us ahead of it, where the
+// sampler waits for it.  The per-output arithmetic is the tuned sampler's:
+// the same taps and weights (GridSample page: Summary; Attributes
+// align_corners, mode, padding_mode), the same fp32 sum in the same tap
+// order, one rounding to T at the store.
 #include "gs_device.hpp"
 #include "gs_launch.hpp"
 #include "gs_layout.hpp"
@@ -299,16 +302,22 @@ static int resident_blocks(const void *kernel) {
 }
 
 template <int MODE, int PAD, typename T, int SB>
-static int gather_launch(const SampleParams &p, const GatherParams &g, bool vec_in, hipStream_t s) {
+static int gather_launch(const SampleParams &p, const GatherParams &g, bool vec_in, int part,
+                         hipStream_t s) {
     using raw_t = typename T::raw_t;
-    hipLaunchKernelGGL((gather_probe<MODE>), dim3(kProbes), dim3(kBlock), 0, s, p, (int)T::bytes,
-                       g.verdicts, g.counters);
+    if (part == 0) {
+        hipLaunchKernelGGL((gather_probe<MODE>), dim3(kProbes), dim3(kBlock), 0, s, p, (int)T::bytes,
+                           g.verdicts, g.counters);
+        return (int)hipGetLastError();
+    }
     const int S = p.in_h * p.in_w;
     const int c_tiles = (p.C + 63) / 64, s_tiles = (S + 63) / 64;
     const int tiles = p.N * c_tiles * s_tiles;
-    const void *prep = vec_in ? (const void *)gather_prepare<raw_t, true, SB>
-                              : (const void *)gather_prepare<raw_t, false, SB>;
-    const dim3 xg((unsigned)min(tiles, resident_blocks(prep)));
+    // (the occupancy queries run once per kernel: each costs host time that
+    // the launches after the sampler would otherwise wait for)
+    static const int res_vec = resident_blocks((const void *)gather_prepare<raw_t, true, SB>);
+    static const int res_scalar = resident_blocks((const void *)gather_prepare<raw_t, false, SB>);
+    const dim3 xg((unsigned)min(tiles, vec_in ? res_vec : res_scalar));
     if (vec_in)
         hipLaunchKernelGGL((gather_prepare<raw_t, true, SB>), xg, dim3(kBlock), 0, s, (const raw_t *)p.X,
                            (raw_t *)g.Xt, p.C, S, c_tiles, s_tiles, tiles, (const int *)g.verdicts);
@@ -316,9 +325,9 @@ static int gather_launch(const SampleParams &p, const GatherParams &g, bool vec_
         hipLaunchKernelGGL((gather_prepare<raw_t, false, SB>), xg, dim3(kBlock), 0, s, (const raw_t *)p.X,
                            (raw_t *)g.Xt, p.C, S, c_tiles, s_tiles, tiles, (const int *)g.verdicts);
     // one round of resident blocks, a multiple of 8 (one counter per XCD)
-    const void *gk = (const void *)grid_sample_gather<MODE, PAD, T, SB>;
+    static const int res_gather = resident_blocks((const void *)grid_sample_gather<MODE, PAD, T, SB>);
     const int want = (g.gather_blocks + 7) / 8 * 8;
-    const dim3 gg((unsigned)min(want, resident_blocks(gk)));
+    const dim3 gg((unsigned)min(want, res_gather));
     hipLaunchKernelGGL((grid_sample_gather<MODE, PAD, T, SB>), gg, dim3(kBlock), 0, s, p,
                        (const void *)g.Xt, (const int *)g.verdicts, g.counters, g.pairs,
                        g.tiles_per_pair, g.xcd_pairs, g.gather_blocks);
@@ -327,34 +336,34 @@ static int gather_launch(const SampleParams &p, const GatherParams &g, bool vec_
 
 template <int MODE, int PAD>
 static int gather_by_dtype(const SampleParams &p, const GatherParams &g, int dtype, bool vec_in,
-                           hipStream_t s) {
+                           int part, hipStream_t s) {
     const bool wide = g.slice_bytes == 64;
     switch (dtype) {
-    case 0: return wide ? gather_launch<MODE, PAD, F32, 64>(p, g, vec_in, s)
-                        : gather_launch<MODE, PAD, F32, 32>(p, g, vec_in, s);
-    case 1: return wide ? gather_launch<MODE, PAD, F16, 64>(p, g, vec_in, s)
-                        : gather_launch<MODE, PAD, F16, 32>(p, g, vec_in, s);
-    default: return wide ? gather_launch<MODE, PAD, BF16, 64>(p, g, vec_in, s)
-                         : gather_launch<MODE, PAD, BF16, 32>(p, g, vec_in, s);
+    case 0: return wide ? gather_launch<MODE, PAD, F32, 64>(p, g, vec_in, part, s)
+                        : gather_launch<MODE, PAD, F32, 32>(p, g, vec_in, part, s);
+    case 1: return wide ? gather_launch<MODE, PAD, F16, 64>(p, g, vec_in, part, s)
+                        : gather_launch<MODE, PAD, F16, 32>(p, g, vec_in, part, s);
+    default: return wide ? gather_launch<MODE, PAD, BF16, 64>(p, g, vec_in, part, s)
+                         : gather_launch<MODE, PAD, BF16, 32>(p, g, vec_in, part, s);
     }
 }
 
 template <int MODE>
 static int gather_by_padding(const SampleParams &p, const GatherParams &g, int padding, int dtype,
-                             bool vec_in, hipStream_t s) {
+                             bool vec_in, int part, hipStream_t s) {
     switch (padding) {
-    case PAD_ZEROS: return gather_by_dtype<MODE, PAD_ZEROS>(p, g, dtype, vec_in, s);
-    case PAD_BORDER: return gather_by_dtype<MODE, PAD_BORDER>(p, g, dtype, vec_in, s);
-    default: return gather_by_dtype<MODE, PAD_REFLECTION>(p, g, dtype, vec_in, s);
+    case PAD_ZEROS: return gather_by_dtype<MODE, PAD_ZEROS>(p, g, dtype, vec_in, part, s);
+    case PAD_BORDER: return gather_by_dtype<MODE, PAD_BORDER>(p, g, dtype, vec_in, part, s);
+    default: return gather_by_dtype<MODE, PAD_REFLECTION>(p, g, dtype, vec_in, part, s);
     }
 }
 
 int launch_grid_gather(const SampleParams &p, const GatherParams &g, int mode, int padding,
-                       int dtype, bool vec_in, hipStream_t s) {
+                       int dtype, bool vec_in, int part, hipStream_t s) {
     switch (mode) {
-    case MODE_LINEAR: return gather_by_padding<MODE_LINEAR>(p, g, padding, dtype, vec_in, s);
-    case MODE_NEAREST: return gather_by_padding<MODE_NEAREST>(p, g, padding, dtype, vec_in, s);
-    default: return gather_by_padding<MODE_CUBIC>(p, g, padding, dtype, vec_in, s);
+    case MODE_LINEAR: return gather_by_padding<MODE_LINEAR>(p, g, padding, dtype, vec_in, part, s);
+    case MODE_NEAREST: return gather_by_padding<MODE_NEAREST>(p, g, padding, dtype, vec_in, part, s);
+    default: return gather_by_padding<MODE_CUBIC>(p, g, padding, dtype, vec_in, part, s);
     }
 }
 

@@ -216,8 +216,10 @@ enum { DC_PATH_DIRECT = 0, DC_PATH_GATHER = 1, DC_PATH_CL = 2 };
 // 16-byte staging loads (input rows a whole number of 16-byte chunks).
 int launch_grid_sample(const SampleParams &p, int rank, bool fused, int mode, int padding,
                        int dtype, bool vec_in, hipStream_t stream);
+// The gather path's launches: `part` 0 the probe (before the sampler), 1
+// the copy and the gather (after it).
 int launch_grid_gather(const SampleParams &p, const GatherParams &g, int mode, int padding,
-                       int dtype, bool vec_in, hipStream_t stream);
+                       int dtype, bool vec_in, int part, hipStream_t stream);
 int launch_affine_grid(const AffineParams &p, int rank, hipStream_t stream);
 // `rank` 1..6 spatial axes; `double_grid`: the grid is double (coordinates in
 // double), else fp32 / fp16 / bf16 (coordinates in fp32).
