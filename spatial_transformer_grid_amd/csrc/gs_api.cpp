@@ -682,6 +682,13 @@ int deform_setup(int dtype, const int64_t *x_shape, int x_rank, const int64_t *w
     const int64_t w2 = cl_w2_elems(group, OCg, Cg, K, tk) * bytes;
     p.w2_bytes = w2 <= kInt32Max ? (uint32_t)w2 : 0;
     p.w2_group_bytes = (uint32_t)(w2 / group);
+    // (divisors of at least 1: K, Cgp / tk and C / offset_group are positive here)
+    const gs::FastDivHost kkd = gs::make_fastdiv((uint32_t)(K > 0 ? K : 1));
+    const gs::FastDivHost cptd = gs::make_fastdiv((uint32_t)(p.Cgp / tk > 0 ? p.Cgp / tk : 1));
+    const gs::FastDivHost cogd = gs::make_fastdiv((uint32_t)(p.Cog > 0 ? p.Cog : 1));
+    p.kk_m = kkd.m, p.kk_s = kkd.s;
+    p.cpt_m = cptd.m, p.cpt_s = cptd.s;
+    p.cog_m = cogd.m, p.cog_s = cogd.s;
     r_out = r;
     N_out = N;
     return GS_OK;

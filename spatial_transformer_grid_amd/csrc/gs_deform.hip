@@ -30,6 +30,8 @@ namespace gs {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
 
 constexpr int DC_TN = 64;   // output positions per block
@@ -381,6 +383,21 @@ __device__ __forceinline__ void chunk_coords(int i, int KK, int cpt, bool slice_
     c0 = sl * tk;
 }
 
+// As chunk_coords, dividing by KK and cpt with the launch's multipliers
+// (i < 2^31).
+__device__ __forceinline__ void chunk_coords_fd(int i, int KK, int cpt, FastDiv kk_div,
+                                                FastDiv cpt_div, bool slice_major, int tk,
+                                                int &tap, int &c0) {
+    if (slice_major) {
+        const int sl = (int)fdiv((uint32_t)i, kk_div);
+        tap = i - sl * KK;
+        c0 = sl * tk;
+    } else {
+        tap = (int)fdiv((uint32_t)i, cpt_div);
+        c0 = (i - tap * cpt) * tk;
+    }
+}
+
 // W (OC, Cg, KK) -> W2, packed in the order the matrix cores take the A
 // operand: for conv group G, 32-row block R of its OCg rows (rounded up to
 // 32), chunk i and load v, lane l's 16 bytes at
@@ -471,6 +488,13 @@ __device__ __forceinline__ void pack8(const float (&x)[8], u32x4 *v) {
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[h][e] = __builtin_bit_cast(uint32_t, x[4 * h + e]);
+    } else if constexpr (__is_same(T, BF16)) {
+        // one v_cvt_pk_bf16_f32 per pair (round to nearest even, as to_raw)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const f32x2 pr = {settle(x[2 * e]), settle(x[2 * e + 1])};
+            v[0][e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
+        }
     } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -644,11 +668,12 @@ __global__ __launch_bounds__(64 * NW) void deform_conv2d_cl(DeformParams p) {
     auto load_x = [&](int i, u32x4 (&xpre)[4][VPC], float (&wq)[4]) {
         i = min(i, nch - 1);
         int tap, c0;
-        chunk_coords(i, KK, cpt, TABLE, TK, tap, c0);
+        chunk_coords_fd(i, KK, cpt, FastDiv{0, p.kk_m, p.kk_s}, FastDiv{0, p.cpt_m, p.cpt_s}, TABLE,
+                        TK, tap, c0);
         const int cl = c0 + 8 * cgp;
         const bool cv = cl < p.Cg;                  // past Cg: padding, W2 is zero there
         const int c = G * p.Cg + (cv ? cl : 0);
-        const int g = c / p.Cog;
+        const int g = (int)fdiv((uint32_t)c, FastDiv{0, p.cog_m, p.cog_s});
         uint32_t off[4];
         if constexpr (TABLE) {
             const int e = ((g - g_first) * KK + tap) * DC_TN + pos;

@@ -205,6 +205,9 @@ struct DeformParams {
     uint32_t x_img_bytes;                    // one image of Xt (< 2^31)
     uint32_t w2_group_bytes;                 // one conv group of W2
     uint32_t w2_bytes;                       // all of W2 (< 2^31)
+    // multipliers and shifts of gs::fdiv for KK = KH * KW, the chunks per
+    // kernel position and Cog (channels-last kernel)
+    uint32_t kk_m, kk_s, cpt_m, cpt_s, cog_m, cog_s;
 };
 
 // DeformConv kernels: direct (one lane per output, double sums), implicit
