@@ -1,7 +1,7 @@
 """Write the worked examples printed on the operator pages as JSON fixtures.
 
-Reads the extracted page text at /root/reference/PAPER.md (available only in
-the build container) and writes, next to this script:
+Reads the extracted text of the pages (a markdown file with each page under
+its address; its path is the one argument) and writes, next to this script:
 
   affine_grid_examples.json  -- the four worked examples of the AffineGrid page
   grid_sample_examples.json  -- the eighteen worked examples of the
@@ -12,7 +12,7 @@ the build container) and writes, next to this script:
 
 Only numbers the pages print are stored (inputs, attributes, printed outputs),
 each with the page title and example name it came from.  Nothing here computes
-an expected value.  Run:  python tests/golden/extract_from_pages.py
+an expected value.  Run:  python tests/golden/extract_from_pages.py PAGES_TEXT
 """
 
 from __future__ import annotations
@@ -22,7 +22,6 @@ import os
 import re
 import sys
 
-PAGES = "/root/reference/PAPER.md"
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 NUM = re.compile(r"[-+]?(?:\d+\.?\d*|\.\d+)(?:[eE][-+]?\d+)?")
@@ -286,9 +285,9 @@ def deform_conv_examples(lines):
 
 
 def main():
-    if not os.path.exists(PAGES):
-        sys.exit("page text not found at " + PAGES)
-    with open(PAGES, encoding="utf-8") as f:
+    if len(sys.argv) != 2 or not os.path.exists(sys.argv[1]):
+        sys.exit("usage: extract_from_pages.py PAGES_TEXT (the extracted page text)")
+    with open(sys.argv[1], encoding="utf-8") as f:
         lines = f.read().split("\n")
     for fname, items in (("affine_grid_examples.json", affine_grid_examples(lines)),
                          ("grid_sample_examples.json", grid_sample_examples(lines)),
