@@ -8,13 +8,16 @@ theta (64,2,3) -> gs_affine_grid -> grid (64,128,128,2) -> gs_grid_sample_2d
 Prints ONE JSON line.
 
 * `value`: output elements per second of the whole step (inputs resident in
-  HBM, K back-to-back steps between two synchronisations).
+  HBM, K back-to-back steps between two synchronisations, no event records
+  among them; before the W warm-up steps the step runs untimed for 0.2 s so
+  that the GPU is at its working clock).
 * `roofline`: the dominant kernel (the sampler).  Algorithmic bytes per launch
   (distinct X elements the launch reads with a non-zero weight, the grid, and
   Y) divided by its median duration over launches that each follow a pass
   over 512 MiB, which evicts the 256 MB Infinity Cache (events on the launch
-  stream); the mean duration of the launches inside the timed steps is kept
-  beside it (`achieved_in_loop`, `frac_in_loop`).  `traffic` is the HBM byte
+  stream); the mean duration of the launches in a second run of the same
+  loop with events around each kernel is kept beside it
+  (`achieved_in_loop`, `frac_in_loop`).  `traffic` is the HBM byte
   count from rocprofv3 counters (profiles/counters_bench_paths.json) when they
   were taken on the current kernel sources, else null.
 * `cpu_baseline`: the oracle (its OpenMP build, every host core) timed on the
@@ -592,9 +595,36 @@ def deform_job(pname, got, exact, dw, kind):
                                   exact["mask"], pads=list(dw.pads), group=dw.group,
                                   offset_group=dw.offset_group, flat_index=idx, lib=lib)[None]
 
+    def scale(lib):
+        # S of each sampled output: the same sum over |X|, |W|, |mask|, plus |B|
+        import oracle
+        absn = lambda a: None if a is None else np.abs(a)
+        s = oracle.deform_conv(absn(exact["X"]), absn(exact["W"]), exact["offset"], None,
+                               absn(exact["mask"]), pads=list(dw.pads), group=dw.group,
+                               offset_group=dw.offset_group, flat_index=idx, lib=lib)
+        if exact["B"] is not None:
+            s = s + np.abs(np.asarray(exact["B"], np.float64))[(idx // (oh * ow)) % oc]
+        return s[None]
+
     job = ErrJob(pname, flat, ref, [0], "linear", "deform-" + kind, 1.0)
     job.sample = "32,768 random outputs"
+    job.scale = scale
+    job.k_terms = int(np.prod(dw.w_shape[1:]))
     return job
+
+
+def deform_tolerance(kind, k_terms):
+    """Bound on |gpu - oracle| of one DeformConv output, as the factors of S
+    (the sum of the absolute values of its products and bias) and of |ref|:
+    each sampled column value is rounded once to the element type (half an
+    ulp: 2^-8 relative for bf16, 2^-11 for fp16) before the matrix product,
+    K products are accumulated in fp32, and the output itself is rounded to
+    the element type."""
+    if kind == "f32":
+        return 2e-5, 0.0
+    u = 2.0 ** -11 if kind == "f16" else 2.0 ** -8
+    ulp = 2.0 ** -10 if kind == "f16" else 2.0 ** -7
+    return u + (k_terms + 8) * 2.0 ** -24, ulp
 
 
 def attach_counters(rec, counters):
@@ -626,8 +656,6 @@ def cpu_model() -> str:
 def tolerance_ok(err, ref, job):
     if job.exact:
         return bool(np.all(err == 0))
-    if job.kind.startswith("deform"):
-        return None  # reported only; the tests hold it to the derived bound
     if job.mode == "nearest":
         return bool(np.all(err == 0))
     if job.kind == "f32":
@@ -674,13 +702,18 @@ def cpu_baseline_leg(inp, size, jobs, paths):
             if job.kind in ("f16", "bf16"):
                 rel = err / np.maximum(np.abs(ref), 1e-3 * job.xmax)
                 worst_rel = max(worst_rel, float(rel.max(initial=0.0)))
-            r = tolerance_ok(err, ref, job)
+            if job.kind.startswith("deform"):
+                rel_s, ulp = deform_tolerance(job.kind[len("deform-"):], job.k_terms)
+                S = job.scale(par).reshape(ref.shape)
+                r = bool(np.all(err <= rel_s * S + ulp * np.abs(ref) + 1e-30))
+            else:
+                r = tolerance_ok(err, ref, job)
             ok = ok and (r is None or r)
         rec = by_path.get(job.path)
         if rec is not None:
             rec["max_err"] = {"max_abs_err": worst, "max_abs_err_over_max_abs_x":
                               worst / max(job.xmax, 1e-30),
-                              "within_tolerance": None if job.kind.startswith("deform") else ok,
+                              "within_tolerance": ok,
                               "compared": getattr(job, "sample", "every output")}
             if job.kind in ("f16", "bf16"):
                 rec["max_err"]["max_rel_err"] = worst_rel
@@ -904,17 +937,32 @@ def main():
         if ev is not None:
             ev[2].record()
 
+    # the GPU settles at its working clock only after some tens of
+    # milliseconds of work (a loop started from idle ran 113-115 us per step,
+    # 106-107 after 20 ms of steps): run the step for 0.2 s first, untimed
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < 0.2:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # the timed steps carry no event records: a record between two launches
+    # holds the second back by a few microseconds (118-128 against 107-108
+    # us per step measured on stn2d_batch)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
+    # the same loop again with events around each kernel: the in-loop
+    # duration of each (event overhead included)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
     sampler_ms = [e[1].elapsed_time(e[2]) for e in events]
     affine_ms = [e[0].elapsed_time(e[1]) for e in events]
     in_loop_us = statistics.mean(sampler_ms) * 1e3
