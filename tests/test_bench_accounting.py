@@ -112,3 +112,48 @@ def test_counter_summary_joins_runs_and_drops_skipped_launches(tmp_path, monkeyp
     assert row["hbm_write_bytes"] == 50.0 * 1024
     assert row["l2_hit_rate"] == 40.0 / 100.0               # medians 40 hits, 60 misses
     assert bench.counter_row(data, row["kernel"]) == row
+
+
+@pytest.mark.parametrize("kind", ["bf16", "f16"])
+def test_deform_bound_accepts_rounding_and_rejects_a_dropped_term(oracle_mod, kind):
+    """The bench's DeformConv bound (factors of S and of |ref|): the oracle's
+    own output rounded to the element type passes; the output with one input
+    channel's nine products dropped fails on most outputs (a single product
+    of the 144 is below bf16's resolution of S)."""
+    import workloads as W
+
+    dw = W.DEFORM_WORKLOADS["dcn2d_resnet"]
+    inp = W.make_deform_inputs(dw, x_shape=(1, 16, 6, 7), w_shape=(8, 16, 3, 3))
+    Y = oracle_mod.deform_conv(inp["X"], inp["W"], inp["offset"], inp["B"], inp["mask"],
+                               pads=list(dw.pads))
+    n, oc, oh, ow = Y.shape
+    idx = np.arange(Y.size)
+    ref = Y.reshape(-1)
+    absn = lambda a: None if a is None else np.abs(a)
+    S = oracle_mod.deform_conv(absn(inp["X"]), absn(inp["W"]), inp["offset"], None,
+                               absn(inp["mask"]), pads=list(dw.pads)).reshape(-1)
+    S = S + np.abs(inp["B"].astype(np.float64))[(idx // (oh * ow)) % oc]
+    rel_s, ulp = bench.deform_tolerance(kind, 16 * 9)
+    got = W.half_bits_to_f32(W.to_half_bits(ref.astype(np.float32), kind), kind).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= rel_s * S + ulp * np.abs(ref) + 1e-30)
+    W0 = inp["W"].copy()
+    W0[:, 0] = 0  # every tap of input channel 0
+    Yd = oracle_mod.deform_conv(inp["X"], W0, inp["offset"], inp["B"], inp["mask"],
+                                pads=list(dw.pads)).reshape(-1)
+    moved = np.abs(Yd - ref) > rel_s * S + ulp * np.abs(ref)
+    assert moved.mean() > 0.75
+
+
+def test_deform_job_scale_bounds_the_outputs(oracle_mod):
+    """S of the bench's DeformConv check (sum of |X|, |W|, |mask| products
+    plus |B|) bounds |Y| at every sampled output of the full workload."""
+    import workloads as W
+
+    dw = W.DEFORM_WORKLOADS["dcn2d_resnet"]
+    inp = W.make_deform_inputs(dw)
+    job = bench.deform_job("t", np.zeros(dw.out_shape(), np.float32), dict(inp), dw, "bf16")
+    ref = job.ref(None, 0).reshape(-1)
+    S = job.scale(None).reshape(-1)
+    assert job.k_terms == 256 * 9
+    assert np.all(S > 0) and np.all(np.abs(ref) <= S * (1 + 1e-12))
+    assert np.median(np.abs(ref) / S) < 0.5
