@@ -337,9 +337,45 @@ __global__ __launch_bounds__(kBlock) void resize_kernel(ResizeParams p) {
                     continue;
                 }
             }
+            // Nearest and linear: each tap's LDS byte address in slot 0, moved
+            // on by one slot per plane (one add per tap and plane; indexing
+            // from the slot base cost two, the LDS base being added again at
+            // every read).  Cubic keeps the row and column parts (64 taps).
+            constexpr bool PTR = MODE != RZ_CUBIC;
+            typedef __attribute__((address_space(3))) const raw_t *lds_ptr;
+            uint32_t tp[PTR ? Q : 1][PTR ? KD : 1][PTR ? K : 1][PTR ? K : 1];
+            if constexpr (PTR) {
+#pragma unroll
+                for (int q = 0; q < Q; ++q)
+#pragma unroll
+                    for (int z = 0; z < KD; ++z)
+#pragma unroll
+                        for (int y = 0; y < K; ++y)
+#pragma unroll
+                            for (int x = 0; x < K; ++x)
+                                tp[q][z][y][x] =
+                                    (uint32_t)(size_t)((lds_ptr)lds + rowpart[z][y] + colpart[q][x]);
+            }
+            const uint32_t slot_bytes = (uint32_t)SS * (uint32_t)sizeof(raw_t);
             for (int u = 0; u < nv; ++u) {
-                const raw_t *sl = lds + u * SS;
                 raw_t tv[Q][KD][K][K];
+                if constexpr (PTR) {
+#pragma unroll
+                for (int q = 0; q < Q; ++q)
+#pragma unroll
+                    for (int z = 0; z < KD; ++z)
+#pragma unroll
+                        for (int y = 0; y < K; ++y)
+#pragma unroll
+                            for (int x = 0; x < K; ++x) {
+                                tv[q][z][y][x] = *(lds_ptr)(size_t)tp[q][z][y][x];
+                                tp[q][z][y][x] += slot_bytes;
+                                // opaque to the compiler, which would otherwise
+                                // rewrite the address as base + plane offset
+                                asm volatile("" : "+v"(tp[q][z][y][x]));
+                            }
+                } else {
+                const raw_t *sl = lds + u * SS;
 #pragma unroll
                 for (int q = 0; q < Q; ++q)
 #pragma unroll
@@ -349,6 +385,7 @@ __global__ __launch_bounds__(kBlock) void resize_kernel(ResizeParams p) {
 #pragma unroll
                             for (int x = 0; x < K; ++x)
                                 tv[q][z][y][x] = sl[rowpart[z][y] + colpart[q][x]];
+                }
                 raw_t v[Q];
 #pragma unroll
                 for (int q = 0; q < Q; ++q) {
