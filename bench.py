@@ -9,8 +9,8 @@ Prints ONE JSON line.
 
 * `value`: output elements per second of the whole step (inputs resident in
   HBM, K back-to-back steps between two synchronisations, no event records
-  among them; before the W warm-up steps the step runs untimed for 0.2 s so
-  that the GPU is at its working clock).
+  among them; before the W warm-up steps the step runs 400 times untimed,
+  about 43 ms, so that the GPU is at its working clock).
 * `roofline`: the dominant kernel (the sampler).  Algorithmic bytes per launch
   (distinct X elements the launch reads with a non-zero weight, the grid, and
   Y) divided by its median duration over launches that each follow a pass
@@ -88,6 +88,9 @@ PATH_KERNELS = {
     "resize2d_down2_linear": ("gs::resize_kernel<1, gs::F32, true, false>", 524288),
     "resize3d_up2_linear": ("gs::resize_kernel<1, gs::F32, true, true>", None),
 }
+
+
+CLOCK_WARMUP_STEPS = 400  # untimed steps before the warm-up steps (clock ramp)
 
 
 def log(msg):
@@ -939,12 +942,12 @@ def main():
 
     # the GPU settles at its working clock only after some tens of
     # milliseconds of work (a loop started from idle ran 113-115 us per step,
-    # 106-107 after 20 ms of steps): run the step for 0.2 s first, untimed
-    t_warm = time.perf_counter()
-    while time.perf_counter() - t_warm < 0.2:
-        for _ in range(20):
-            step()
-        torch.cuda.synchronize()
+    # 106-107 after 20 ms of steps): run 400 steps (about 43 ms) first,
+    # untimed; a fixed count keeps the launch sequence the same from run to
+    # run, which the counter summaries rely on
+    for _ in range(CLOCK_WARMUP_STEPS):
+        step()
+    torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     # the timed steps carry no event records: a record between two launches
