@@ -618,16 +618,20 @@ def deform_job(pname, got, exact, dw, kind):
 
 def deform_tolerance(kind, k_terms):
     """Bound on |gpu - oracle| of one DeformConv output, as the factors of S
-    (the sum of the absolute values of its products and bias) and of |ref|:
-    each sampled column value is rounded once to the element type (half an
-    ulp: 2^-8 relative for bf16, 2^-11 for fp16) before the matrix product,
-    K products are accumulated in fp32, and the output itself is rounded to
-    the element type."""
+    (the sum of the absolute values of its products and bias) and of |ref|,
+    and an absolute floor: each sampled column value is rounded once to the
+    element type (half an ulp: 2^-8 relative for bf16, 2^-11 for fp16) before
+    the matrix product, K products are accumulated in fp32, and the output
+    itself is rounded to the element type; below the smallest normal value
+    the spacing is fixed (2^-24 for fp16, 2^-133 for bf16), one spacing of
+    which the floor allows for the output (the sampled values' share,
+    half a spacing times |W|, is far below it on the bench's layer)."""
     if kind == "f32":
-        return 2e-5, 0.0
+        return 2e-5, 0.0, 0.0
     u = 2.0 ** -11 if kind == "f16" else 2.0 ** -8
     ulp = 2.0 ** -10 if kind == "f16" else 2.0 ** -7
-    return u + (k_terms + 8) * 2.0 ** -24, ulp
+    sub = 2.0 ** -24 if kind == "f16" else 2.0 ** -133
+    return u + (k_terms + 8) * 2.0 ** -24, ulp, sub
 
 
 def attach_counters(rec, counters):
@@ -706,9 +710,9 @@ def cpu_baseline_leg(inp, size, jobs, paths):
                 rel = err / np.maximum(np.abs(ref), 1e-3 * job.xmax)
                 worst_rel = max(worst_rel, float(rel.max(initial=0.0)))
             if job.kind.startswith("deform"):
-                rel_s, ulp = deform_tolerance(job.kind[len("deform-"):], job.k_terms)
+                rel_s, ulp, sub = deform_tolerance(job.kind[len("deform-"):], job.k_terms)
                 S = job.scale(par).reshape(ref.shape)
-                r = bool(np.all(err <= rel_s * S + ulp * np.abs(ref) + 1e-30))
+                r = bool(np.all(err <= rel_s * S + ulp * np.abs(ref) + sub + 1e-30))
             else:
                 r = tolerance_ok(err, ref, job)
             ok = ok and (r is None or r)

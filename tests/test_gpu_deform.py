@@ -13,7 +13,11 @@
   value to the data type before its product (exact in fp32), K products per
   output are accumulated in fp32 (at most K roundings of 2^-24 relative to
   S), and 8 more cover the fp32 interpolation and mask products; plus one
-  unit in the last place of the output type.
+  unit in the last place of the output type.  Below the smallest normal
+  value (2^-14 for fp16, 2^-126 for bf16) the types have a fixed spacing
+  (2^-24, 2^-133), so a relative bound does not hold there: each sampled
+  value's rounding adds up to half that spacing times |W| of its product,
+  and the output's rounding one spacing.
 * 2-D cases whose conv and offset groups hold multiples of 8 channels run on
   the channels-last copy of X by default: channel counts that fill whole
   chunks and ones padded up to the next chunk, offset groups that change
@@ -109,7 +113,12 @@ def run(gsa, X, Wt, off, B, mask, kind, st=None, pd=None, dl=None, grp=1, og=1, 
     K = int(np.prod(Wt.shape[1:]))  # products summed per output
     rel = deform_rel_tol(kind, K)
     ulp = {"f32": 0.0, "f16": 2.0 ** -10, "bf16": 2.0 ** -7}[kind]
-    tol = rel * S + ulp * np.abs(ref) + 1e-30
+    # fixed spacing below the smallest normal value: half of it per sampled
+    # value (times |W| of its product), one for the output
+    sub = {"f32": 0.0, "f16": 2.0 ** -24, "bf16": 2.0 ** -133}[kind]
+    wsum = np.abs(np.asarray(Wo, np.float64)).reshape(Wo.shape[0], -1).sum(1)
+    wsum = wsum.reshape((1, -1) + (1,) * (ref.ndim - 2))
+    tol = rel * S + ulp * np.abs(ref) + sub * (0.5 * wsum + 1.0) + 1e-30
     err = np.abs(got - ref)
     assert (err <= tol).all(), "%s: max err/tol %.3g at %s" % (
         what, (err / tol).max(), np.unravel_index((err / tol).argmax(), err.shape))
