@@ -17,6 +17,10 @@ four grid kinds:
 probe finds the grid scattered) in a third of the cases, and the affine kind
 also through the fused entry (bit-identical to the unfused pair).  The
 tolerances are those of the other parity tests (tests/parity.py).
+
+Further sweeps: Resize, the any-rank kernel, DeformConv and the gather path
+(through the helpers of their own test files), and one graph holding every
+entry point, replayed with new inputs.
 """
 
 import numpy as np
@@ -239,3 +243,87 @@ def test_random_deform_conv_matches_oracle(gsa, seed):
                             with_mask, with_bias)
     run(gsa, X, Wt, off, B, M, kind, st, pd, dl, grp, og,
         what="sweep seed %d" % seed, no_workspace=bool(rng.integers(2)))
+
+
+# ------------------------------------------------------------- gather path
+
+@pytest.mark.parametrize("seed", range(64))
+def test_random_gather_path_matches_oracle(gsa, seed):
+    """Random scattered grids over planes taller than the sampler stages (the
+    probe chooses the gather path): channel counts that fill 32- or 64-byte
+    slices, one to three images, output rows that leave ragged row segments;
+    the gather path equals the plain sampler bit for bit and the oracle
+    within tolerance."""
+    from test_gpu_gather import run_case as run_gather_case
+
+    rng = np.random.default_rng(95000 + seed)
+    kind = KINDS[rng.integers(3)]
+    per_slice = 8 if kind == "f32" else 16          # channels in 32 bytes
+    c = per_slice * int(rng.choice([1, 2, 3, 4, 6, 8]))
+    n = int(rng.integers(1, 4))
+    h, w = int(rng.integers(300, 340)), int(rng.integers(60, 130))
+    ho, wo = int(rng.integers(1, 24)), int(rng.integers(1, 300))
+    mode, pad, ac = MODES[rng.integers(3)], PADS[rng.integers(3)], int(rng.integers(2))
+    X = rng.uniform(-1, 1, (n, c, h, w)).astype(np.float32)
+    G = rng.uniform(-1.2, 1.2, (n, ho, wo, 2)).astype(np.float32)
+    run_gather_case(gsa, X, G, kind, mode, pad, ac, True, "sweep seed %d" % seed)
+
+
+# ------------------------------------------------------------ graph capture
+
+def test_entry_points_captured_in_a_graph(gsa):
+    """AffineGrid, the sampler (unfused and fused), Resize and DeformConv with
+    a workspace captured in one graph and replayed four times, inputs changed
+    in between with eager work and synchronisations between the replays:
+    every replay equals the eager calls on the same inputs bit for bit (the
+    library records no memset)."""
+    torch = torch_mod()
+    rng = np.random.default_rng(96000)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).cuda()
+    X = dev(rng.uniform(-1, 1, (2, 16, 40, 44)))
+    theta = dev(np.eye(2, 3)[None] + 0.1 * rng.normal(size=(2, 2, 3)))
+    Xr = dev(rng.uniform(-1, 1, (2, 3, 30, 34)))
+    Xd = dev(rng.uniform(-1, 1, (1, 16, 12, 13)))
+    Wd = dev(rng.uniform(-1, 1, (24, 16, 3, 3)))
+    Od = dev(rng.uniform(-2, 2, (1, 18, 12, 13)))
+    Md = dev(rng.uniform(0, 1, (1, 9, 12, 13)))
+    Bd = dev(rng.uniform(-1, 1, 24))
+    grid = torch.empty((2, 36, 40, 2), device="cuda")
+    Y1 = torch.empty((2, 16, 36, 40), device="cuda")
+    Y2 = torch.empty_like(Y1)
+    Y3 = torch.empty((2, 3, 61, 50), device="cuda")
+    Y4 = torch.empty((1, 24, 12, 13), device="cuda")
+    ws = torch.empty(gsa.deform_conv_workspace_size((1, 16, 12, 13), (24, 16, 3, 3), 0, None,
+                                                   [1, 1, 1, 1], None, 1, 1),
+                     dtype=torch.uint8, device="cuda")
+    assert ws.numel() > 0
+
+    def calls():
+        gsa.affine_grid(theta, (2, 16, 36, 40), 0, out=grid)
+        gsa.grid_sample(X, grid, "linear", "border", 0, out=Y1)
+        gsa.affine_grid_sample_fused(theta, X, (36, 40), "cubic", "reflection", 0, out=Y2)
+        gsa.resize_to(Xr, (2, 3, 61, 50), None, "cubic", "half_pixel", out=Y3)
+        gsa.deform_conv(Xd, Wd, Od, Bd, Md, pads=[1, 1, 1, 1], out=Y4, workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    outs = (Y1, Y2, Y3, Y4)
+    for rep in range(4):
+        note("multi-entry graph replay %d" % rep)
+        for t in (X, theta, Xr, Xd, Od):
+            t.copy_(dev(rng.uniform(-1, 1, tuple(t.shape)) * (0.1 if t is theta else 1.0)
+                        + (np.eye(2, 3)[None] if t is theta else 0.0)))
+        graph.replay()
+        got = [y.clone() for y in outs]
+        torch.cuda.synchronize()
+        calls()   # eager, same inputs
+        torch.cuda.synchronize()
+        for k, (a, b) in enumerate(zip(got, outs)):
+            assert torch.equal(a, b), "replay %d, output %d differs from the eager call" % (rep, k)
