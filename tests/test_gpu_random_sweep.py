@@ -327,3 +327,36 @@ def test_entry_points_captured_in_a_graph(gsa):
         torch.cuda.synchronize()
         for k, (a, b) in enumerate(zip(got, outs)):
             assert torch.equal(a, b), "replay %d, output %d differs from the eager call" % (rep, k)
+
+
+# ---------------------------------------------------------- extreme shapes
+
+EXTREME = [
+    # N, C, input spatial, output spatial
+    (300, 3, (5, 5), (4, 6)),            # many images of one small tile each
+    (1, 3000, (3, 4), (2, 3)),           # thousands of channels, tiny planes
+    (2, 5, (1, 1000), (1, 999)),         # one-row images
+    (2, 5, (1000, 1), (999, 1)),         # one-column images
+    (1, 2, (700, 3), (2, 900)),          # tall input, wide output
+    (1, 1, (1, 1), (50, 70)),            # one-pixel input
+    (1, 2, (1, 1, 300), (1, 1, 299)),    # 3-D line
+    (1, 3, (40, 1, 2), (3, 50, 2)),      # 3-D with unit axes
+    (64, 1, (2, 2, 2), (3, 3, 3)),       # 3-D, many tiny volumes
+]
+
+
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("ci", range(len(EXTREME)))
+def test_extreme_shapes(gsa, ci, mode, kind):
+    n, c, in_sp, out_sp = EXTREME[ci]
+    rng = np.random.default_rng(97000 + ci)
+    r = len(in_sp)
+    pad, ac = PADS[ci % 3], ci % 2
+    X = rng.uniform(-1, 1, (n, c) + in_sp).astype(np.float32)
+    G = rng.uniform(-1.2, 1.2, (n,) + out_sp + (r,)).astype(np.float32)
+    what = "extreme %d: X=%s out=%s %s/%s ac=%d %s" % (ci, X.shape, out_sp, mode, pad, ac, kind)
+    note(what)
+    Xd, Xin = x_to_gpu(X, kind)
+    Y = from_gpu(gsa.grid_sample(Xd, to_gpu_f32(G), mode, pad, ac))
+    check(Y, oracle.grid_sample(Xin, G, mode, pad, ac), mode, kind, np.abs(Xin).max(), what)
