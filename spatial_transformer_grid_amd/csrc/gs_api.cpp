@@ -238,7 +238,8 @@ int sample_nd(int r, const void *X, int x_dtype, const int64_t *x_shape, const v
     if (N == 0 || C == 0 || out_count == 0) return GS_OK;
     if (in_count == 0) return GS_ERR_SHAPE;
     if (!X || !Y || !grid) return GS_ERR_NULL;
-    const int64_t tiles = (out_count + kBlockThreads - 1) / kBlockThreads;
+    const int64_t locs = (int64_t)kBlockThreads * gs::nd_locs_per_lane(r, mode);
+    const int64_t tiles = (out_count + locs - 1) / locs;
     if (N * tiles > kMaxBlocks) return GS_ERR_TOO_LARGE;
     int64_t groups = (kTargetBlocks + N * tiles - 1) / (N * tiles);
     if (groups > C) groups = C;

@@ -229,92 +229,116 @@ __device__ __forceinline__ V pick(const V (&a)[K], int s) {
 
 // ------------------------------------------------------------------ kernel
 
-// The channel loop of one lane for element type T.  Tap t selects, on axis a,
-// digit a of t in base K (the innermost axis is the least significant digit,
-// so it runs fastest).
-template <int R, int MODE, typename T>
+// A lane's location slot past the end of the output (its stores are dropped).
+constexpr uint32_t kNoLocation = 0xFFFFFFFFu;
+
+// The channel loop of one lane for element type T, over the lane's L output
+// locations yo (kNoLocation: none).  Tap t
+// selects, on axis a, digit a of t in base K (the innermost axis is the least
+// significant digit, so it runs fastest).
+template <int R, int MODE, typename T, int L>
 __device__ __forceinline__ void nd_channels(const NdParams &p, int n, int cbeg, int cend,
-                                            uint32_t o, const int (&idx)[R][NdK<MODE>::K],
-                                            const bool (&ok)[R][NdK<MODE>::K],
-                                            const double (&w)[R][NdK<MODE>::K]) {
+                                            const uint32_t (&yo)[L],
+                                            const int (&idx)[L][R][NdK<MODE>::K],
+                                            const bool (&ok)[L][R][NdK<MODE>::K],
+                                            const double (&w)[L][R][NdK<MODE>::K]) {
     constexpr int K = NdK<MODE>::K;
     constexpr int LK = K == 1 ? 0 : (K == 2 ? 1 : 2);
     constexpr int TAPS = 1 << (LK * R);
     const uint32_t ip = p.in_plane_bytes, op = p.out_plane_bytes;
     const char *xn = (const char *)p.X + ((size_t)n * p.C) * ip;
     char *yn = (char *)p.Y + ((size_t)n * p.C) * op;
-    int c = cbeg;
-    // With few taps, UC channels at a time: every load of the UC channels is
-    // issued before the first sum, so a lane keeps 8 loads in flight (16 for
-    // 8 taps; one channel of 2 taps left it waiting on 2).  Measured on the
-    // 1-D, 2-D and 3-D linear workloads: 4 channels of 4 taps were slower
-    // than 2.  Each channel's sum is the same as below, term by term.
-    constexpr int UC = TAPS > 8 ? 1 : (TAPS == 8 ? 2 : 8 / TAPS);
-    if constexpr (UC > 1) {
-        double tw[TAPS];
-        bool tv[TAPS];
-        uint32_t to[TAPS];
+    uint32_t yb[L];  // byte offsets of the outputs in a plane
 #pragma unroll
-        for (int t = 0; t < TAPS; ++t) {
-            double ww = 1.0;
-            bool valid = true;
-            uint32_t off = 0;
+    for (int l = 0; l < L; ++l) yb[l] = yo[l] == kNoLocation ? GS_OOB : yo[l] * (uint32_t)T::bytes;
+    // weight, validity and offset of tap t of location l
+    auto tap_of = [&](int l, int t, double &ww, bool &valid, uint32_t &off) {
+        ww = 1.0;
+        valid = true;
+        off = 0;
 #pragma unroll
-            for (int a = 0; a < R; ++a) {
-                const int s = (t >> (LK * (R - 1 - a))) & (K - 1);
-                ww = ww * pick(w[a], s);
-                valid = valid && pick(ok[a], s);
-                off = off * (uint32_t)p.in_ext[a] + (uint32_t)pick(idx[a], s);
-            }
-            tw[t] = ww;
-            tv[t] = valid;
-            to[t] = valid ? off * (uint32_t)T::bytes : GS_OOB;
+        for (int a = 0; a < R; ++a) {
+            const int s = (t >> (LK * (R - 1 - a))) & (K - 1);
+            ww = ww * pick(w[l][a], s);
+            valid = valid && pick(ok[l][a], s);
+            off = off * (uint32_t)p.in_ext[a] + (uint32_t)pick(idx[l][a], s);
         }
-        for (; c + UC <= cend; c += UC) {
-            double xv[UC][TAPS];
+    };
+    int c = cbeg;
+    if constexpr (TAPS <= 8) {
+        // With few taps the taps' weights and offsets are kept, and UC
+        // channels at a time have every load issued before the first sum:
+        // a lane keeps 8 to 16 loads in flight (one channel of 2 taps left
+        // it waiting on 2; 4 channels of 4 taps were slower than 2).  Each
+        // channel's sum is the same, term by term, as the loop below.
+        constexpr int UC = L > 1 ? (8 / (TAPS * L) > 1 ? 8 / (TAPS * L) : 1)
+                                 : (TAPS == 8 ? 2 : 8 / TAPS);
+        double tw[L][TAPS];
+        bool tv[L][TAPS];
+        uint32_t to[L][TAPS];
 #pragma unroll
-            for (int u = 0; u < UC; ++u) {
+        for (int l = 0; l < L; ++l)
+#pragma unroll
+            for (int t = 0; t < TAPS; ++t) {
+                uint32_t off;
+                tap_of(l, t, tw[l][t], tv[l][t], off);
+                to[l][t] = tv[l][t] ? off * (uint32_t)T::bytes : GS_OOB;
+            }
+        auto channels = [&](auto ucc) {
+            constexpr int U = decltype(ucc)::value;
+            double xv[U][L][TAPS];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
                 const rsrc_t r = make_rsrc(xn + (size_t)(c + u) * ip, ip);
 #pragma unroll
-                for (int t = 0; t < TAPS; ++t) xv[u][t] = T::load(r, to[t]);
+                for (int l = 0; l < L; ++l)
+#pragma unroll
+                    for (int t = 0; t < TAPS; ++t) xv[u][l][t] = T::load(r, to[l][t]);
             }
 #pragma unroll
-            for (int u = 0; u < UC; ++u) {
-                double acc = 0.0;
+            for (int u = 0; u < U; ++u) {
+                const rsrc_t yr = make_rsrc(yn + (size_t)(c + u) * op, op);
 #pragma unroll
-                for (int t = 0; t < TAPS; ++t) acc = tv[t] ? acc + tw[t] * xv[u][t] : acc;
-                T::store(acc, make_rsrc(yn + (size_t)(c + u) * op, op), o * (uint32_t)T::bytes);
-            }
-        }
-    }
-    for (; c < cend; ++c) {
-        const rsrc_t r = make_rsrc(xn + (size_t)c * ip, ip);
-        double acc = 0.0;
-        auto tap = [&](int t) {
-            double ww = 1.0;
-            bool valid = true;
-            uint32_t off = 0;
+                for (int l = 0; l < L; ++l) {
+                    double acc = 0.0;
 #pragma unroll
-            for (int a = 0; a < R; ++a) {
-                const int s = (t >> (LK * (R - 1 - a))) & (K - 1);
-                ww = ww * pick(w[a], s);
-                valid = valid && pick(ok[a], s);
-                off = off * (uint32_t)p.in_ext[a] + (uint32_t)pick(idx[a], s);
+                    for (int t = 0; t < TAPS; ++t)
+                        acc = tv[l][t] ? acc + tw[l][t] * xv[u][l][t] : acc;
+                    T::store(acc, yr, yb[l]);
+                }
             }
-            const double x = T::load(r, valid ? off * (uint32_t)T::bytes : GS_OOB);
-            acc = valid ? acc + ww * x : acc;
         };
-        if constexpr (TAPS <= 64) {
+        if constexpr (UC > 1)
+            for (; c + UC <= cend; c += UC) channels(std::integral_constant<int, UC>());
+        for (; c < cend; ++c) channels(std::integral_constant<int, 1>());
+    } else {
+        static_assert(L == 1, "many taps: one location per lane");
+        for (; c < cend; ++c) {
+            const rsrc_t r = make_rsrc(xn + (size_t)c * ip, ip);
+            double acc = 0.0;
+            auto tap = [&](int t) {
+                double ww;
+                bool valid;
+                uint32_t off;
+                tap_of(0, t, ww, valid, off);
+                const double x = T::load(r, valid ? off * (uint32_t)T::bytes : GS_OOB);
+                acc = valid ? acc + ww * x : acc;
+            };
+            if constexpr (TAPS <= 64) {
 #pragma unroll
-            for (int t = 0; t < TAPS; ++t) tap(t);
-        } else {
-            for (int t = 0; t < TAPS; ++t) tap(t);
+                for (int t = 0; t < TAPS; ++t) tap(t);
+            } else {
+                for (int t = 0; t < TAPS; ++t) tap(t);
+            }
+            T::store(acc, make_rsrc(yn + (size_t)c * op, op), yb[0]);
         }
-        T::store(acc, make_rsrc(yn + (size_t)c * op, op), o * (uint32_t)T::bytes);
     }
 }
 
-template <int R, int MODE, typename F>
+// L output locations per lane, 256 apart (each load and store instruction of
+// a wave stays contiguous): the per-wave set-up and the buffer resources of
+// each channel serve L times the outputs.
+template <int R, int MODE, typename F, int L>
 __global__ __launch_bounds__(kBlock) void grid_sample_nd_kernel(NdParams p) {
     constexpr int K = NdK<MODE>::K;
     const int lb = xcd_logical_block_runs(p.nblocks);
@@ -323,45 +347,54 @@ __global__ __launch_bounds__(kBlock) void grid_sample_nd_kernel(NdParams p) {
     const int ncg = lb / p.tiles;
     const int cg = ncg % p.cgroups;
     const int n = ncg / p.cgroups;
-    const uint32_t o = (uint32_t)tile * kBlock + threadIdx.x;
-    if (o >= p.out_count) return;  // no barrier in this kernel
+    const uint32_t o0 = (uint32_t)tile * (kBlock * L) + threadIdx.x;
+    if (o0 >= p.out_count) return;  // no barrier in this kernel
 
-    int idx[R][K];
-    bool ok[R][K];
-    double w[R][K];
-    bool live = true;
+    int idx[L][R][K];
+    bool ok[L][R][K];
+    double w[L][R][K];
+    uint32_t yo[L];
 #pragma unroll
-    for (int a = 0; a < R; ++a) {
-        // component k of the location vector addresses axis R-1-k
-        const F g = grid_component<F>(p.grid, p.grid_dtype,
-                                      ((size_t)n * p.out_count + o) * R + (R - 1 - a));
-        const F u = unnormalize(g, p.in_ext[a], p.align_corners);
-        const bool fin = __builtin_isfinite(u);
-        live = live && fin;
-        const F pc = fin ? clampf(u, F(-kCoordLimit), F(kCoordLimit)) : F(0);
-        nd_axis_taps<MODE, F, K>(pc, p.in_ext[a], p.padding, p.align_corners, idx[a], ok[a], w[a]);
+    for (int l = 0; l < L; ++l) {
+        const uint32_t ol = o0 + (uint32_t)(l * kBlock);
+        const bool in = ol < p.out_count;
+        const uint32_t o = in ? ol : p.out_count - 1;   // a valid grid element
+        yo[l] = in ? o : kNoLocation;
+        bool live = true;
+#pragma unroll
+        for (int a = 0; a < R; ++a) {
+            // component k of the location vector addresses axis R-1-k
+            const F g = grid_component<F>(p.grid, p.grid_dtype,
+                                          ((size_t)n * p.out_count + o) * R + (R - 1 - a));
+            const F u = unnormalize(g, p.in_ext[a], p.align_corners);
+            const bool fin = __builtin_isfinite(u);
+            live = live && fin;
+            const F pc = fin ? clampf(u, F(-kCoordLimit), F(kCoordLimit)) : F(0);
+            nd_axis_taps<MODE, F, K>(pc, p.in_ext[a], p.padding, p.align_corners, idx[l][a],
+                                     ok[l][a], w[l][a]);
+        }
+        // a location that is not finite on some axis reads nothing (output 0)
+#pragma unroll
+        for (int a = 0; a < R; ++a)
+#pragma unroll
+            for (int j = 0; j < K; ++j) ok[l][a][j] = ok[l][a][j] && live;
     }
-    // a location that is not finite on some axis reads nothing (output 0)
-#pragma unroll
-    for (int a = 0; a < R; ++a)
-#pragma unroll
-        for (int j = 0; j < K; ++j) ok[a][j] = ok[a][j] && live;
 
     const int cbeg = cg * p.cpg;
     const int cend = min(p.C, cbeg + p.cpg);
     switch (p.x_dtype) {
-    case 0: nd_channels<R, MODE, NdF32>(p, n, cbeg, cend, o, idx, ok, w); break;
-    case 1: nd_channels<R, MODE, NdF16>(p, n, cbeg, cend, o, idx, ok, w); break;
-    case 2: nd_channels<R, MODE, NdBF16>(p, n, cbeg, cend, o, idx, ok, w); break;
-    case 3: nd_channels<R, MODE, NdF64>(p, n, cbeg, cend, o, idx, ok, w); break;
-    case 4: nd_channels<R, MODE, NdInt<int8_t>>(p, n, cbeg, cend, o, idx, ok, w); break;
-    case 5: nd_channels<R, MODE, NdInt<uint8_t>>(p, n, cbeg, cend, o, idx, ok, w); break;
-    case 6: nd_channels<R, MODE, NdInt<int16_t>>(p, n, cbeg, cend, o, idx, ok, w); break;
-    case 7: nd_channels<R, MODE, NdInt<uint16_t>>(p, n, cbeg, cend, o, idx, ok, w); break;
-    case 8: nd_channels<R, MODE, NdInt<int32_t>>(p, n, cbeg, cend, o, idx, ok, w); break;
-    case 9: nd_channels<R, MODE, NdInt<uint32_t>>(p, n, cbeg, cend, o, idx, ok, w); break;
-    case 10: nd_channels<R, MODE, NdInt<int64_t>>(p, n, cbeg, cend, o, idx, ok, w); break;
-    default: nd_channels<R, MODE, NdInt<uint64_t>>(p, n, cbeg, cend, o, idx, ok, w); break;
+    case 0: nd_channels<R, MODE, NdF32, L>(p, n, cbeg, cend, yo, idx, ok, w); break;
+    case 1: nd_channels<R, MODE, NdF16, L>(p, n, cbeg, cend, yo, idx, ok, w); break;
+    case 2: nd_channels<R, MODE, NdBF16, L>(p, n, cbeg, cend, yo, idx, ok, w); break;
+    case 3: nd_channels<R, MODE, NdF64, L>(p, n, cbeg, cend, yo, idx, ok, w); break;
+    case 4: nd_channels<R, MODE, NdInt<int8_t>, L>(p, n, cbeg, cend, yo, idx, ok, w); break;
+    case 5: nd_channels<R, MODE, NdInt<uint8_t>, L>(p, n, cbeg, cend, yo, idx, ok, w); break;
+    case 6: nd_channels<R, MODE, NdInt<int16_t>, L>(p, n, cbeg, cend, yo, idx, ok, w); break;
+    case 7: nd_channels<R, MODE, NdInt<uint16_t>, L>(p, n, cbeg, cend, yo, idx, ok, w); break;
+    case 8: nd_channels<R, MODE, NdInt<int32_t>, L>(p, n, cbeg, cend, yo, idx, ok, w); break;
+    case 9: nd_channels<R, MODE, NdInt<uint32_t>, L>(p, n, cbeg, cend, yo, idx, ok, w); break;
+    case 10: nd_channels<R, MODE, NdInt<int64_t>, L>(p, n, cbeg, cend, yo, idx, ok, w); break;
+    default: nd_channels<R, MODE, NdInt<uint64_t>, L>(p, n, cbeg, cend, yo, idx, ok, w); break;
     }
 }
 
@@ -369,11 +402,12 @@ __global__ __launch_bounds__(kBlock) void grid_sample_nd_kernel(NdParams p) {
 
 template <int R, int MODE>
 static int nd_launch(const NdParams &p, bool double_grid, hipStream_t s) {
+    constexpr int L = nd_locs_per_lane(R, MODE);
     const dim3 grid(8 * kRun * ((p.nblocks + 8 * kRun - 1) / (8 * kRun)));
     if (double_grid)
-        hipLaunchKernelGGL((grid_sample_nd_kernel<R, MODE, double>), grid, dim3(kBlock), 0, s, p);
+        hipLaunchKernelGGL((grid_sample_nd_kernel<R, MODE, double, L>), grid, dim3(kBlock), 0, s, p);
     else
-        hipLaunchKernelGGL((grid_sample_nd_kernel<R, MODE, float>), grid, dim3(kBlock), 0, s, p);
+        hipLaunchKernelGGL((grid_sample_nd_kernel<R, MODE, float, L>), grid, dim3(kBlock), 0, s, p);
     return (int)hipGetLastError();
 }
 
