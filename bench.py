@@ -77,9 +77,9 @@ PATH_KERNELS = {
     "flow2d_half/bf16-linear-zeros": ("gs::grid_sample_kernel<2, 0, 0, gs::BF16, false, true>",
                                       None),
     "flow2d_half/f16-linear-zeros": ("gs::grid_sample_kernel<2, 0, 0, gs::F16, false, true>", None),
-    "stn2d_u8/linear-zeros": ("gs::grid_sample_nd_kernel<2, 0, float>", None),
-    "signal1d_f32/linear-zeros": ("gs::grid_sample_nd_kernel<1, 0, float>", None),
-    "vol3d_f64/linear-border": ("gs::grid_sample_nd_kernel<3, 0, double>", None),
+    "stn2d_u8/linear-zeros": ("gs::grid_sample_nd_kernel<2, 0, float, 2>", None),
+    "signal1d_f32/linear-zeros": ("gs::grid_sample_nd_kernel<1, 0, float, 4>", None),
+    "vol3d_f64/linear-border": ("gs::grid_sample_nd_kernel<3, 0, double, 1>", None),
     "dcn2d_resnet/bf16": ("gs::deform_conv2d_cl<gs::BF16, 1, true, 8>", None),
     "dcn2d_resnet/f32": ("gs::deform_conv2d_cl<gs::F32, 2, true, 4>", None),
     "resize2d_up2_linear": ("gs::resize_kernel<1, gs::F32, true, false>", 1048576),

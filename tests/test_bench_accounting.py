@@ -157,3 +157,13 @@ def test_deform_job_scale_bounds_the_outputs(oracle_mod):
     assert job.k_terms == 256 * 9
     assert np.all(S > 0) and np.all(np.abs(ref) <= S * (1 + 1e-12))
     assert np.median(np.abs(ref) / S) < 0.5
+
+
+def test_every_bench_path_names_a_profiled_kernel():
+    """Each bench path's kernel (and launch size, where given) has a row in
+    the stored counter summary, so the bench can attach its traffic and L2
+    hit rate (a kernel renamed without re-collecting the counters fails)."""
+    rows = bench.load_counters()
+    missing = [p for p, k in bench.PATH_KERNELS.items() if k and not bench.counter_row(rows, *k)]
+    assert not missing, missing
+    assert bench.counter_row(rows, *bench.HEADLINE_KERNEL)
