@@ -162,8 +162,10 @@ def test_deform_job_scale_bounds_the_outputs(oracle_mod):
 def test_every_bench_path_names_a_profiled_kernel():
     """Each bench path's kernel (and launch size, where given) has a row in
     the stored counter summary, so the bench can attach its traffic and L2
-    hit rate (a kernel renamed without re-collecting the counters fails)."""
-    rows = bench.load_counters()
+    hit rate (a kernel renamed without re-collecting the counters fails;
+    whether the counters match the current sources is the bench's check)."""
+    with open(bench.COUNTER_FILE) as f:
+        rows = json.load(f)   # names only: the digest of the sources is not checked here
     missing = [p for p, k in bench.PATH_KERNELS.items() if k and not bench.counter_row(rows, *k)]
     assert not missing, missing
     assert bench.counter_row(rows, *bench.HEADLINE_KERNEL)
