@@ -63,15 +63,38 @@ class GSError(RuntimeError):
         super().__init__("%s failed: %s (status %d)" % (where, msg, status))
 
 
+def hip_runtimes_mapped():
+    """Distinct HIP runtime files (libamdhip64) mapped into this process,
+    read from /proc/self/maps (empty where that file does not exist)."""
+    try:
+        with open("/proc/self/maps") as f:
+            lines = f.read().splitlines()
+    except OSError:
+        return []
+    return sorted({ln.split()[-1] for ln in lines if "libamdhip64" in ln.split()[-1]})
+
+
 def lib():
-    """The loaded libgsample (raises if it has not been built)."""
+    """The loaded libgsample (raises if it has not been built).
+
+    torch is imported first so that its HIP runtime is the one the library
+    binds to: both carry the soname libamdhip64.so.7, and whichever is loaded
+    first satisfies the other's dependency.  Loaded the other way round, the
+    process would hold two runtimes, and kernels registered with one cannot
+    be launched on streams or memory of the other.
+    """
     global _lib
     with _lock:
         if _lib is None:
             if not os.path.exists(LIB_PATH):
                 raise ImportError("libgsample.so is not built (python -m "
                                   "spatial_transformer_grid_amd.build)")
+            _torch()
             handle = ctypes.CDLL(LIB_PATH)
+            runtimes = hip_runtimes_mapped()
+            if len(runtimes) > 1:
+                raise ImportError("more than one HIP runtime is loaded (%s); libgsample must "
+                                  "share torch's" % ", ".join(runtimes))
             for name, (args, res) in SIGNATURES.items():
                 fn = getattr(handle, name)
                 fn.argtypes = args

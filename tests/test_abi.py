@@ -40,7 +40,7 @@ def test_header_declares_the_expected_entry_points():
 
 
 def test_library_exports_every_declared_symbol(gs):
-    handle = ctypes.CDLL(gs.LIB_PATH)
+    handle = gs.lib()
     for name in declared_functions():
         assert hasattr(handle, name), name
     assert set(declared_functions()) == set(gs.SIGNATURES)
@@ -53,6 +53,27 @@ def test_abi_version_and_status_strings(gs):
         s = lib.gs_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.gs_status_string(99).decode() == "unknown status"
+
+
+def test_library_shares_torchs_hip_runtime_whatever_the_import_order(gs):
+    """Loading the library before torch is imported still leaves one HIP
+    runtime in the process (a fresh interpreter, so the order is the one
+    under test); with two, every launch on a torch stream fails."""
+    import subprocess
+    import sys
+
+    code = ("import sys\n"
+            "import spatial_transformer_grid_amd as g\n"
+            "assert 'torch' not in sys.modules\n"
+            "g.lib()\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read().splitlines()\n"
+            "print(len({m.split()[-1] for m in maps if 'libamdhip64' in m.split()[-1]}))\n")
+    env = dict(os.environ, PYTHONPATH=ROOT)
+    out = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                         text=True, timeout=300)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.strip().splitlines()[-1] == "1"
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation
