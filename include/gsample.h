@@ -19,6 +19,11 @@
  * - Tensor pointers are DEVICE pointers to dense, contiguous, row-major
  *   tensors owned by the caller.  Shape arrays are HOST memory, read only
  *   during the call.
+ * - A tensor pointer needs only the alignment of its element type.  The
+ *   library takes 8- and 16-byte accesses where a pointer and the row lengths
+ *   allow them and element accesses elsewhere, with the same results bit for
+ *   bit.  A workspace is used only when it is 256-byte aligned; otherwise the
+ *   call runs the path that needs none.
  * - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream).
  *   The library allocates no memory (scratch space comes from the caller),
  *   keeps no state between calls and never synchronises; a call returns once
