@@ -21,7 +21,7 @@ namespace {
 constexpr int64_t kScratchBytes = int64_t(64) << 20;  // 64 MiB per device
 constexpr int kMaxDevices = 64;
 
-__device__ __align__(256) unsigned char scratch[kScratchBytes];
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 std::mutex g_lock;
 void *g_scratch[kMaxDevices];  // device address of `scratch`, per device
