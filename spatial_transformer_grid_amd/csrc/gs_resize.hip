@@ -152,9 +152,22 @@ __global__ __launch_bounds__(kBlock) void resize_kernel(ResizeParams p) {
     if (lb >= p.nblocks) return;
     const int tile = lb % p.tiles_per_plane;
     const int pg = lb / p.tiles_per_plane;
-    const int tx = tile % p.tiles_w;
-    const int ty = (tile / p.tiles_w) % p.tiles_h;
-    const int od = tile / (p.tiles_w * p.tiles_h);
+    // With D resized, the output depth slice varies fastest: a run of blocks
+    // on one XCD then holds consecutive slices of one tile column, which read
+    // the same input slices, and the runs of the neighbouring columns come
+    // to the same XCD a round later, so the halo rows and slices are shared
+    // in its L2 rather than fetched again by another XCD.
+    int tx, ty, od;
+    if constexpr (D3) {
+        od = tile % p.ax[2].m;
+        const int col = tile / p.ax[2].m;
+        tx = col % p.tiles_w;
+        ty = col / p.tiles_w;
+    } else {
+        tx = tile % p.tiles_w;
+        ty = (tile / p.tiles_w) % p.tiles_h;
+        od = tile / (p.tiles_w * p.tiles_h);
+    }
     const int t = threadIdx.x;
     const int lrl = p.lanes_row_log2;
     const int ox0 = tx * p.tile_w + (t & ((1 << lrl) - 1)) * Q;
