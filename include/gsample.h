@@ -167,7 +167,8 @@ int gs_grid_sample_2d(const void *X, int x_dtype, const int64_t *x_shape, const 
  *   workspace, workspace_bytes   device scratch owned by the caller (256-byte
  *                aligned), at least gs_grid_sample_2d_workspace_size() bytes;
  *                overwritten; not to be shared by calls that may run at the
- *                same time.  NULL / too small: exactly gs_grid_sample_2d.
+ *                same time.  NULL, too small or not 256-byte aligned:
+ *                exactly gs_grid_sample_2d.
  *
  * With the workspace the call first probes 64 of the sampler's output tiles
  * on the device; when most of them read from more of X than fits a tile's
