@@ -116,3 +116,51 @@ def test_calls_on_four_streams_match_sequential_calls(gsa):
             for j, (name, _, _, _) in enumerate(jobs):
                 assert torch.equal(bits(got[i][j]), bits(ref[i][j])), (
                     "round %d, input set %d, %s: differs from the sequential call" % (rnd, i, name))
+
+
+def test_calls_from_four_host_threads_match_sequential_calls(gsa):
+    """The same jobs from four host threads at once, each thread on its own
+    stream and with its own inputs and workspaces (ctypes releases the
+    interpreter lock during the calls, so the library's entry points run
+    concurrently), ten rounds per thread."""
+    import threading
+
+    torch = torch_mod()
+    sets = [make_jobs(gsa, 8900 + i) for i in range(4)]
+    ref = []
+    for jobs in sets:
+        outs = []
+        for name, fn, shape, dt in jobs:
+            y = torch.empty(shape, dtype=dt, device="cuda")
+            fn(y)
+            outs.append(y)
+        ref.append(outs)
+    torch.cuda.synchronize()
+    note("host threads")
+    errors = []
+
+    def worker(i):
+        try:
+            stream = torch.cuda.Stream()
+            jobs = sets[i]
+            outs = [torch.empty(shape, dtype=dt, device="cuda") for _, _, shape, dt in jobs]
+            for rnd in range(10):
+                with torch.cuda.stream(stream):
+                    for j, (_, fn, _, _) in enumerate(jobs):
+                        outs[j].fill_(float("nan"))
+                        fn(outs[j])
+                stream.synchronize()
+                for j, (name, _, _, _) in enumerate(jobs):
+                    if not torch.equal(bits(outs[j]), bits(ref[i][j])):
+                        errors.append("thread %d round %d %s differs" % (i, rnd, name))
+        except Exception as e:  # reported by the main thread
+            errors.append("thread %d: %r" % (i, e))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join(timeout=100)
+    assert not any(th.is_alive() for th in threads), "a worker thread did not finish"
+    torch.cuda.synchronize()
+    assert not errors, errors[:5]
