@@ -87,3 +87,35 @@ def test_beyond_the_array_is_rejected(gsa):
     assert e.value.status == 6  # GS_ERR_TOO_LARGE
     torch.cuda.synchronize()
     assert bool((Y == 7.0).all())  # nothing written
+
+
+def test_captured_in_a_graph(gsa):
+    """The callers this entry point is for include code under graph capture:
+    after one eager call (which looks the array's address up), the call is
+    captured in a graph and replayed three times with new inputs, each replay
+    equal bit for bit to gs_deform_conv with a workspace on the same inputs."""
+    torch = torch_mod()
+    dw = W.DEFORM_WORKLOADS["dcn2d_resnet"]
+    pads = list(dw.pads)
+    d = layer(dw, (2, 32, 20, 18), (48, 32, 3, 3), torch.bfloat16)
+    Y = torch.empty((2, 48, 20, 18), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        gsa.deform_conv_noalloc(d["X"], d["W"], d["offset"], d["B"], d["mask"], pads=pads, out=Y)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gsa.deform_conv_noalloc(d["X"], d["W"], d["offset"], d["B"], d["mask"], pads=pads, out=Y)
+    rng = np.random.default_rng(31)
+    for rep in range(3):
+        note("noalloc graph replay %d" % rep)
+        for k in ("X", "offset", "mask"):
+            d[k].copy_(torch.from_numpy(rng.uniform(-1, 1, tuple(d[k].shape)).astype(np.float32)))
+        graph.replay()
+        got = Y.clone()
+        torch.cuda.synchronize()
+        ref = gsa.deform_conv(d["X"], d["W"], d["offset"], d["B"], d["mask"], pads=pads)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), "replay %d" % rep
