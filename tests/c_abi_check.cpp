@@ -5,7 +5,10 @@
 // nearest (bit for bit after the fp32 rounding), and the fused theta -> sample
 // entry point (bit for bit against the unfused pair), each against the oracle
 // of this repository (liboracle.so), on seeded inputs.  Exit status 0 when
-// every check passes.  Test infrastructure: built next to the tests.
+// every check passes.  Resize (2x bilinear, within 1e-5 of max|X|) and
+// DeformConv (fp32 with a workspace, the matrix-core kernel, within 2e-5 of
+// the sum of the absolute terms) are checked the same way.  Test
+// infrastructure: built next to the tests.
 #include <hip/hip_runtime_api.h>
 #include <math.h>
 #include <stdint.h>
@@ -21,6 +24,14 @@ int oracle_affine_grid(const float *theta, int r, int64_t N, const int64_t *out_
 int oracle_grid_sample(const float *X, int r, int64_t N, int64_t C, const int64_t *in_spatial,
                        const float *grid, const int64_t *out_spatial, int mode, int padding,
                        int align_corners, double *Y);
+int oracle_resize(const float *X, int rank, const int64_t *in_shape, const int64_t *out_shape,
+                  const float *scales, int mode, int ct, int nearest_mode, double cubic_a,
+                  int exclude_outside, double *Y);
+int oracle_deform_conv(const double *X, int r, int64_t N, int64_t C, const int64_t *in_sp,
+                       const double *Wt, int64_t OC, const int64_t *ksz, const double *offset,
+                       const double *B, const double *mask, const int64_t *out_sp,
+                       const int64_t *strides, const int64_t *pads, const int64_t *dilations,
+                       int64_t group, int64_t offset_group, int coord_f32, double *Y);
 }
 
 namespace {
@@ -116,6 +127,103 @@ int main() {
         }
         expect(memcmp(hy, hyf, ny * 4) == 0, "fused equals AffineGrid then GridSample bit for bit");
     }
+    // Resize: 2x bilinear up, half_pixel
+    {
+        const int64_t ys[4] = {N, C, 2 * H, 2 * W};
+        const float sc[4] = {1.0f, 1.0f, 2.0f, 2.0f};
+        const size_t nr = (size_t)(N * C * 4 * H * W);
+        void *dr = nullptr;
+        float *hr = (float *)malloc(nr * 4);
+        double *rr = (double *)malloc(nr * 8);
+        if (hip_ok(hipMalloc(&dr, nr * 4), "hipMalloc Resize")) {
+            expect(gs_resize(dx, GS_F32, xs, 4, ys, sc, GS_RESIZE_LINEAR, GS_CT_HALF_PIXEL,
+                             GS_NEAREST_ROUND_PREFER_FLOOR, -0.75f, 0, dr, nullptr) == GS_OK,
+                   "gs_resize status");
+            hip_ok(hipDeviceSynchronize(), "hipDeviceSynchronize");
+            hip_ok(hipMemcpy(hr, dr, nr * 4, hipMemcpyDeviceToHost), "hipMemcpy Resize");
+            expect(oracle_resize(hx, 4, xs, ys, sc, 1, 0, 0, -0.75, 0, rr) == 0, "oracle_resize");
+            double err = 0.0;
+            for (size_t i = 0; i < nr; ++i) err = fmax(err, fabs((double)hr[i] - rr[i]));
+            printf("resize: max |Y - oracle| = %.3g (bound %.3g)\n", err, 1e-5 * xmax);
+            expect(err <= 1e-5 * xmax, "Resize bilinear within 1e-5 max|X| of the oracle");
+            hipFree(dr);
+        }
+        free(hr);
+        free(rr);
+    }
+
+    // DeformConv, fp32, with a workspace (channels-last copy, matrix cores)
+    {
+        const int64_t DN = 1, DC = 16, DH = 12, DW = 12, OC = 24, K = 3;
+        const int64_t dxs[4] = {DN, DC, DH, DW}, dws[4] = {OC, DC, K, K}, pads[4] = {1, 1, 1, 1};
+        const int64_t dsp[2] = {DH, DW}, ksz[2] = {K, K}, ones[2] = {1, 1};
+        const size_t nX = (size_t)(DN * DC * DH * DW), nW = (size_t)(OC * DC * K * K),
+                     nO = (size_t)(DN * 2 * K * K * DH * DW), nM = (size_t)(DN * K * K * DH * DW),
+                     nY = (size_t)(DN * OC * DH * DW);
+        float *fX = (float *)malloc(nX * 4), *fW = (float *)malloc(nW * 4), *fO = (float *)malloc(nO * 4);
+        float *fM = (float *)malloc(nM * 4), *fB = (float *)malloc(OC * 4), *fY = (float *)malloc(nY * 4);
+        double *dX = (double *)malloc(nX * 8), *dWt = (double *)malloc(nW * 8), *dO = (double *)malloc(nO * 8);
+        double *dM = (double *)malloc(nM * 8), *dB = (double *)malloc(OC * 8);
+        double *ref = (double *)malloc(nY * 8), *S = (double *)malloc(nY * 8);
+        for (size_t i = 0; i < nX; ++i) fX[i] = g.next();
+        for (size_t i = 0; i < nW; ++i) fW[i] = 0.1f * g.next();
+        for (size_t i = 0; i < nO; ++i) fO[i] = 2.0f * g.next();
+        for (size_t i = 0; i < nM; ++i) fM[i] = 0.5f * (g.next() + 1.0f);
+        for (int64_t i = 0; i < OC; ++i) fB[i] = 0.1f * g.next();
+        void *qX = nullptr, *qW = nullptr, *qO = nullptr, *qM = nullptr, *qB = nullptr, *qY = nullptr,
+             *qws = nullptr;
+        int64_t need = 0;
+        expect(gs_deform_conv_workspace_size(GS_F32, dxs, 4, dws, nullptr, pads, nullptr, 1, 1, &need) ==
+                       GS_OK && need > 0,
+               "gs_deform_conv_workspace_size");
+        if (hip_ok(hipMalloc(&qX, nX * 4), "hipMalloc") && hip_ok(hipMalloc(&qW, nW * 4), "hipMalloc") &&
+            hip_ok(hipMalloc(&qO, nO * 4), "hipMalloc") && hip_ok(hipMalloc(&qM, nM * 4), "hipMalloc") &&
+            hip_ok(hipMalloc(&qB, OC * 4), "hipMalloc") && hip_ok(hipMalloc(&qY, nY * 4), "hipMalloc") &&
+            hip_ok(hipMalloc(&qws, (size_t)(need > 0 ? need : 1)), "hipMalloc workspace")) {
+            hip_ok(hipMemcpy(qX, fX, nX * 4, hipMemcpyHostToDevice), "hipMemcpy");
+            hip_ok(hipMemcpy(qW, fW, nW * 4, hipMemcpyHostToDevice), "hipMemcpy");
+            hip_ok(hipMemcpy(qO, fO, nO * 4, hipMemcpyHostToDevice), "hipMemcpy");
+            hip_ok(hipMemcpy(qM, fM, nM * 4, hipMemcpyHostToDevice), "hipMemcpy");
+            hip_ok(hipMemcpy(qB, fB, OC * 4, hipMemcpyHostToDevice), "hipMemcpy");
+            expect(gs_deform_conv(qX, GS_F32, dxs, 4, qW, dws, qO, qB, qM, nullptr, pads, nullptr, 1, 1, qY,
+                                  qws, need, nullptr) == GS_OK,
+                   "gs_deform_conv status");
+            hip_ok(hipDeviceSynchronize(), "hipDeviceSynchronize");
+            hip_ok(hipMemcpy(fY, qY, nY * 4, hipMemcpyDeviceToHost), "hipMemcpy DeformConv");
+            for (size_t i = 0; i < nX; ++i) dX[i] = fX[i];
+            for (size_t i = 0; i < nW; ++i) dWt[i] = fW[i];
+            for (size_t i = 0; i < nO; ++i) dO[i] = fO[i];
+            for (size_t i = 0; i < nM; ++i) dM[i] = fM[i];
+            for (int64_t i = 0; i < OC; ++i) dB[i] = fB[i];
+            const int64_t st[2] = {1, 1};
+            expect(oracle_deform_conv(dX, 2, DN, DC, dsp, dWt, OC, ksz, dO, dB, dM, dsp, st, pads, ones, 1,
+                                      1, 1, ref) == 0,
+                   "oracle_deform_conv");
+            // S: the same sum over the absolute values of X, W, mask and B
+            for (size_t i = 0; i < nX; ++i) dX[i] = fabs(dX[i]);
+            for (size_t i = 0; i < nW; ++i) dWt[i] = fabs(dWt[i]);
+            for (size_t i = 0; i < nM; ++i) dM[i] = fabs(dM[i]);
+            for (int64_t i = 0; i < OC; ++i) dB[i] = fabs(dB[i]);
+            expect(oracle_deform_conv(dX, 2, DN, DC, dsp, dWt, OC, ksz, dO, dB, dM, dsp, st, pads, ones, 1,
+                                      1, 1, S) == 0,
+                   "oracle_deform_conv on absolute values");
+            double worst = 0.0;
+            for (size_t i = 0; i < nY; ++i)
+                worst = fmax(worst, fabs((double)fY[i] - ref[i]) / (2e-5 * S[i] + 1e-30));
+            printf("deform_conv: max |Y - oracle| / (2e-5 S) = %.3g\n", worst);
+            expect(worst <= 1.0, "DeformConv fp32 within 2e-5 of the sum of absolute terms");
+        }
+        hipFree(qX);
+        hipFree(qW);
+        hipFree(qO);
+        hipFree(qM);
+        hipFree(qB);
+        hipFree(qY);
+        hipFree(qws);
+        free(fX); free(fW); free(fO); free(fM); free(fB); free(fY);
+        free(dX); free(dWt); free(dO); free(dM); free(dB); free(ref); free(S);
+    }
+
     hipFree(dx);
     hipFree(dtheta);
     hipFree(dgrid);

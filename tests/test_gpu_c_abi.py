@@ -2,9 +2,11 @@
 process: tests/c_abi_check (built by build() from tests/c_abi_check.cpp)
 allocates with hipMalloc on the ROCm install's HIP runtime, calls
 gs_affine_grid, gs_grid_sample_2d (linear and nearest) and
-gs_affine_grid_sample_fused on seeded inputs, and compares with the oracle's
-C functions: AffineGrid and nearest bit for bit, linear within 1e-5 of
-max|X|, fused equal to the unfused pair bit for bit."""
+gs_affine_grid_sample_fused, gs_resize (2x bilinear) and gs_deform_conv
+(fp32 with a workspace) on seeded inputs, and compares with the oracle's C
+functions: AffineGrid and nearest bit for bit, linear and Resize within 1e-5
+of max|X|, DeformConv within 2e-5 of the sum of the absolute terms, fused
+equal to the unfused pair bit for bit."""
 
 import os
 import subprocess
