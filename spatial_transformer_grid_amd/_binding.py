@@ -71,7 +71,12 @@ def hip_runtimes_mapped():
             lines = f.read().splitlines()
     except OSError:
         return []
-    return sorted({ln.split()[-1] for ln in lines if "libamdhip64" in ln.split()[-1]})
+    paths = set()
+    for ln in lines:
+        fields = ln.split(None, 5)  # the sixth field is the path, spaces included
+        if len(fields) == 6 and "libamdhip64" in fields[5]:
+            paths.add(fields[5].strip())
+    return sorted(paths)
 
 
 def lib():
